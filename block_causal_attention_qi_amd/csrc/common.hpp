@@ -1,0 +1,57 @@
+// Shared device helpers for the gfx950 (CDNA4) kernels: bf16 packing, MFMA
+// operand types and wavefront reductions.  wave64 only.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+typedef uint16_t u16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+#define QI_DEV __device__ __forceinline__
+
+QI_DEV float bf16_to_f32(u16 b) { return __uint_as_float(uint32_t(b) << 16); }
+
+// fp32 -> bf16, round to nearest even (the hardware conversion on gfx950).
+QI_DEV u16 f32_to_bf16(float f) { return __builtin_bit_cast(u16, (__bf16)f); }
+
+QI_DEV uint32_t pack_bf16x2(float lo, float hi) {
+  return uint32_t(f32_to_bf16(lo)) | (uint32_t(f32_to_bf16(hi)) << 16);
+}
+
+QI_DEV bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+// D = A(16x32) * B(32x16) + C, bf16 inputs, fp32 accumulate.  Lane l supplies
+// A[l%16][8*(l/16) .. +8) and B[8*(l/16) .. +8)[l%16]; D is held as 4 rows
+// 4*(l/16) .. +4 of column l%16.
+QI_DEV f32x4 mfma16x16x32(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
+}
+
+QI_DEV float wave_sum(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
+  return v;
+}
+
+QI_DEV float wave_max(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m, 64));
+  return v;
+}
+
+// Sum over the whole workgroup (blockDim.x a multiple of 64, <= 1024).
+// `red` must hold blockDim.x/64 floats.  Every thread gets the total.
+QI_DEV float block_sum(float v, float *red) {
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  v = wave_sum(v);
+  if (lane == 0) red[wid] = v;
+  __syncthreads();
+  float t = 0.f;
+  for (int i = 0; i < nw; ++i) t += red[i];
+  __syncthreads();
+  return t;
+}

@@ -1,0 +1,241 @@
+// Bandwidth-bound kernels of the DiT step on gfx950: RMSNorm with modulation,
+// the time embedding and shared modulation GEMV, the image-in embed, the
+// output head and the fp32 Euler update.  Coalesced 16-byte accesses and
+// wavefront reductions; one workgroup per row where a row reduction is needed.
+#pragma once
+
+#include "common.hpp"
+
+// ----------------------------------------------------------------- RMSNorm
+// out[r] = bf16( x[r] * rsqrt(mean(x[r]^2) + eps) * w * (1 + scale[r]) ), where
+// w = gamma (zero_centred: 1 + gamma) and scale is the modulation chunk of the
+// row's kind (rows < L_rows: mod row 0, else mod row 1; mod == NULL: 1).
+// The port page's DiT row: RMSNorm with modulation (spec step list);
+// ZeroCenterRMSNorm for the text projection.  H <= 8192, H % 4 == 0.
+__global__ __launch_bounds__(256) void rmsnorm_mod_kernel(const float *x, int ldx, const float *gamma,
+                                                          int zero_centred, const float *mod,
+                                                          int mod_img_off, int L_rows, int H, float eps,
+                                                          u16 *out, int ldo) {
+  constexpr int MAXV = 8;
+  __shared__ float red[4];
+  const int r = blockIdx.x;
+  const f32x4 *xr = (const f32x4 *)(x + (size_t)r * ldx);
+  const int nv = H >> 2;
+  f32x4 v[MAXV];
+  float ss = 0.f;
+#pragma unroll
+  for (int i = 0; i < MAXV; ++i) {
+    const int idx = threadIdx.x + i * 256;
+    if (idx < nv) {
+      v[i] = xr[idx];
+      ss += v[i][0] * v[i][0] + v[i][1] * v[i][1] + v[i][2] * v[i][2] + v[i][3] * v[i][3];
+    }
+  }
+  ss = block_sum(ss, red);
+  const float inv = rsqrtf(ss / (float)H + eps);
+  const float *sc = mod ? mod + (r < L_rows ? 0 : mod_img_off) : nullptr;
+  u16 *orow = out + (size_t)r * ldo;
+#pragma unroll
+  for (int i = 0; i < MAXV; ++i) {
+    const int idx = threadIdx.x + i * 256;
+    if (idx < nv) {
+      f32x4 w = ((const f32x4 *)gamma)[idx];
+      if (zero_centred) w += 1.f;
+      f32x4 y = v[i] * inv * w;
+      if (sc) y *= ((const f32x4 *)sc)[idx] + 1.f;
+      *(u32x2 *)(orow + idx * 4) = u32x2{pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3])};
+    }
+  }
+}
+
+// ----------------------------------------------------------------- modulation
+// The one modulation Linear shared by all blocks, evaluated for tau = 0 (text
+// rows) and the sampled t (image rows):  mod[s][n] = sum_k W[n][k] e_s[k] + b[n]
+// with the time embedding e(tau)[j] = cos(1000 tau f_j), e(tau)[H/2 + j] =
+// sin(1000 tau f_j), f_j = 10000^(-j/(H/2)).  Each workgroup builds both
+// embeddings in LDS (float64 internally, rounded once to fp32), then streams
+// 16 rows of W [rows][H] bf16 from HBM, 4 per wave.
+__global__ __launch_bounds__(256) void mod_gemv_kernel(const u16 *W, const float *b, float t, int H,
+                                                       int rows, float *mod) {
+  extern __shared__ float se[];  // [2][H]
+  const int half = H >> 1;
+  for (int j = threadIdx.x; j < half; j += 256) {
+    const double f = pow(10000.0, -(double)j / (double)half);
+    const double arg = 1000.0 * (double)t * f;
+    se[j] = 1.f;
+    se[half + j] = 0.f;
+    se[H + j] = (float)cos(arg);
+    se[H + half + j] = (float)sin(arg);
+  }
+  __syncthreads();
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll 1
+  for (int rr = 0; rr < 4; ++rr) {
+    const int n = blockIdx.x * 16 + wave * 4 + rr;
+    if (n >= rows) break;
+    const u16 *wr = W + (size_t)n * H;
+    float a0 = 0.f, a1 = 0.f;
+    for (int k = lane * 8; k < H; k += 512) {
+      const u32x4 w8 = *(const u32x4 *)(wr + k);
+      const f32x4 e0a = *(const f32x4 *)(se + k), e0b = *(const f32x4 *)(se + k + 4);
+      const f32x4 e1a = *(const f32x4 *)(se + H + k), e1b = *(const f32x4 *)(se + H + k + 4);
+      float wf[8];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        wf[2 * q] = __uint_as_float(w8[q] << 16);
+        wf[2 * q + 1] = __uint_as_float(w8[q] & 0xFFFF0000u);
+      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        a0 += wf[q] * e0a[q] + wf[q + 4] * e0b[q];
+        a1 += wf[q] * e1a[q] + wf[q + 4] * e1b[q];
+      }
+    }
+    a0 = wave_sum(a0);
+    a1 = wave_sum(a1);
+    if (lane == 0) {
+      mod[n] = a0 + b[n];
+      mod[rows + n] = a1 + b[n];
+    }
+  }
+}
+
+// ----------------------------------------------------------------- embed
+// x[row0 + i][n] = sum_c X[i][c] W[n][c] + b[n]  (img-in Linear 64 -> H, fp32).
+// 16 tokens per workgroup, one output feature per thread.
+__global__ __launch_bounds__(256) void img_embed_kernel(const float *X, int N, const u16 *W,
+                                                        const float *b, int H, float *x, int ldx,
+                                                        int row0) {
+  __shared__ f32x4 sX[16][16];
+  const int t0 = blockIdx.x * 16;
+  {
+    const int tok = threadIdx.x >> 4, c4 = threadIdx.x & 15;
+    const int ti = min(t0 + tok, N - 1);
+    sX[tok][c4] = ((const f32x4 *)(X + (size_t)ti * 64))[c4];
+  }
+  __syncthreads();
+  const int n = blockIdx.y * 256 + threadIdx.x;
+  if (n >= H) return;
+  float w[64];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    const u32x4 w8 = *(const u32x4 *)(W + (size_t)n * 64 + q * 8);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      w[q * 8 + 2 * e] = __uint_as_float(w8[e] << 16);
+      w[q * 8 + 2 * e + 1] = __uint_as_float(w8[e] & 0xFFFF0000u);
+    }
+  }
+  const float bn = b[n];
+  for (int tok = 0; tok < 16; ++tok) {
+    if (t0 + tok >= N) break;
+    float acc = 0.f;
+#pragma unroll
+    for (int c4 = 0; c4 < 16; ++c4) {
+      const f32x4 xv = sX[tok][c4];
+      acc += xv[0] * w[4 * c4] + xv[1] * w[4 * c4 + 1] + xv[2] * w[4 * c4 + 2] + xv[3] * w[4 * c4 + 3];
+    }
+    x[(size_t)(row0 + t0 + tok) * ldx + n] = acc + bn;
+  }
+}
+
+// ----------------------------------------------------------------- head
+// vel[i][c] = sum_n (x[i][n] rsqrt(mean(x[i]^2) + eps) gamma[n]) W[c][n] + b[c],
+// c < 64, fp32 (proj_out on the image rows).  16 tokens per workgroup; the
+// normalised rows are staged through LDS in chunks of 256 features, each wave
+// covers a quarter of a chunk for all 16 tokens and 64 channels (lane =
+// channel), and the four partial sums are added at the end.  H % 256 == 0.
+__global__ __launch_bounds__(256) void head_kernel(const float *x, int ldx, int N, const float *gamma,
+                                                   const u16 *W, const float *b, int H, float eps,
+                                                   float *vel) {
+  constexpr int TOK = 16, KC = 256;
+  __shared__ float sX[TOK][KC];
+  __shared__ float sInv[TOK];
+  __shared__ float sRed[4][TOK][64];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int t0 = blockIdx.x * TOK;
+  for (int tt = 0; tt < 4; ++tt) {
+    const int tok = wave * 4 + tt;
+    const int ti = min(t0 + tok, N - 1);
+    const float *row = x + (size_t)ti * ldx;
+    float ss = 0.f;
+    for (int k = lane * 4; k < H; k += 256) {
+      const f32x4 v = *(const f32x4 *)(row + k);
+      ss += v[0] * v[0] + v[1] * v[1] + v[2] * v[2] + v[3] * v[3];
+    }
+    ss = wave_sum(ss);
+    if (lane == 0) sInv[tok] = rsqrtf(ss / (float)H + eps);
+  }
+  __syncthreads();
+  float acc[TOK];
+#pragma unroll
+  for (int i = 0; i < TOK; ++i) acc[i] = 0.f;
+  for (int kc = 0; kc < H; kc += KC) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int i = tid + 256 * j;        // float4 index in the [TOK][KC] chunk
+      const int tok = i / (KC / 4), k4 = i % (KC / 4);
+      const int ti = min(t0 + tok, N - 1);
+      const f32x4 v = *(const f32x4 *)(x + (size_t)ti * ldx + kc + k4 * 4);
+      const f32x4 gm = *(const f32x4 *)(gamma + kc + k4 * 4);
+      *(f32x4 *)&sX[tok][k4 * 4] = v * sInv[tok] * gm;
+    }
+    __syncthreads();
+    const u16 *wr = W + (size_t)lane * H + kc + wave * 64;
+#pragma unroll 2
+    for (int kk = 0; kk < 64; kk += 8) {
+      const u32x4 w8 = *(const u32x4 *)(wr + kk);
+      float wf[8];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        wf[2 * e] = __uint_as_float(w8[e] << 16);
+        wf[2 * e + 1] = __uint_as_float(w8[e] & 0xFFFF0000u);
+      }
+#pragma unroll
+      for (int tok = 0; tok < TOK; ++tok) {
+        const f32x4 xa = *(const f32x4 *)&sX[tok][wave * 64 + kk];
+        const f32x4 xb = *(const f32x4 *)&sX[tok][wave * 64 + kk + 4];
+        acc[tok] += xa[0] * wf[0] + xa[1] * wf[1] + xa[2] * wf[2] + xa[3] * wf[3] + xb[0] * wf[4] +
+                    xb[1] * wf[5] + xb[2] * wf[6] + xb[3] * wf[7];
+      }
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int tok = 0; tok < TOK; ++tok) sRed[wave][tok][lane] = acc[tok];
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int i = tid + 256 * j;
+    const int tok = i >> 6, ch = i & 63;
+    if (t0 + tok < N)
+      vel[(size_t)(t0 + tok) * 64 + ch] =
+          b[ch] + sRed[0][tok][ch] + sRed[1][tok][ch] + sRed[2][tok][ch] + sRed[3][tok][ch];
+  }
+}
+
+// ----------------------------------------------------------------- Euler
+// x = x + ds * vel with a separately rounded fp32 multiply and add (the host
+// contract's fp32 Euler step; a fused multiply-add would change bits).
+// Contraction is switched off for the operators written in this body (HIP's
+// *_rn helpers are contractible once inlined, so they are not used here).
+__global__ __launch_bounds__(256) void euler_kernel(float *x, const float *vel, float ds, int64_t n) {
+#pragma clang fp contract(off)
+  const int64_t n4 = n >> 2;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += stride) {
+    f32x4 xv = ((f32x4 *)x)[i];
+    const f32x4 vv = ((const f32x4 *)vel)[i];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float p = ds * vv[e];
+      xv[e] = xv[e] + p;
+    }
+    ((f32x4 *)x)[i] = xv;
+  }
+  for (int64_t i = n4 * 4 + (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride)
+  {
+    const float p = ds * vel[i];
+    x[i] = x[i] + p;
+  }
+}

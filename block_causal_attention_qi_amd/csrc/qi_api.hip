@@ -1,0 +1,393 @@
+// C ABI of the DiT step (include/qi.h): host-side validation, workspace
+// carving and the launch sequence of one block and one step.  Everything is
+// enqueued on the caller's stream; nothing here synchronises or allocates.
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+#include "../../include/qi.h"
+#include "attention.hpp"
+#include "elementwise.hpp"
+#include "gemm.hpp"
+
+namespace {
+
+constexpr float kRmsEps = 1e-6f;
+constexpr int kMaxL = 512, kMaxN = 16384;
+
+inline size_t align256(size_t b) { return (b + 255) & ~size_t(255); }
+inline int round64(int v) { return (v + 63) & ~63; }
+inline bool al16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
+bool dims_ok(const qi_dims *d) {
+  if (!d) return false;
+  if (d->head_dim != 128) return false;
+  if (d->hidden < 256 || d->hidden > 8192 || d->hidden % 256 != 0) return false;
+  if (d->heads * 128 != d->hidden) return false;
+  if (d->ffn < 64 || d->ffn % 64 != 0 || d->ffn > 65536) return false;
+  if (d->txt_dim < 64 || d->txt_dim % 64 != 0 || d->txt_dim > 8192) return false;
+  if (d->n_blocks < 1 || d->n_blocks > 256) return false;
+  return true;
+}
+
+// Workspace of one joint pass over T = L + N rows (an image-only pass uses a
+// prefix of each buffer).
+struct Layout {
+  size_t x, mod, tn, h, q_t, k_t, vt_t, q_i, k_i, vt_i, o, a, total;
+};
+
+Layout layout(const qi_dims &d, int L, int N) {
+  const size_t H = d.hidden, F = d.ffn, D = d.txt_dim, T = (size_t)L + N;
+  const size_t Lp = round64(L), Np = round64(N);
+  Layout l{};
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off += align256(bytes);
+    return o;
+  };
+  l.x = take(T * H * 4);
+  l.mod = take(2 * 4 * H * 4);
+  l.tn = take((size_t)L * D * 2);
+  l.h = take(T * H * 2);
+  l.q_t = take((size_t)L * H * 2);
+  l.k_t = take((size_t)L * H * 2);
+  l.vt_t = take(H * Lp * 2);
+  l.q_i = take((size_t)N * H * 2);
+  l.k_i = take((size_t)N * H * 2);
+  l.vt_i = take(H * Np * 2);
+  l.o = take(T * H * 2);
+  l.a = take(T * F * 2);
+  l.total = off;
+  return l;
+}
+
+size_t slot_elems(const qi_dims &d, int L) {
+  return (size_t)d.heads * 128 * ((size_t)L + round64(L));
+}
+
+qi_status last_launch() { return hipGetLastError() == hipSuccess ? QI_OK : QI_ERR_HIP; }
+
+#define QI_TRY(expr)               \
+  do {                             \
+    qi_status s__ = (expr);        \
+    if (s__ != QI_OK) return s__;  \
+  } while (0)
+
+template <int EPI>
+qi_status launch_gemm(const GemmArgs &g, hipStream_t s) {
+  const int outs_per_tile = EPI == EPI_SWIGLU ? gemm::BN / 2 : gemm::BN;
+  const int n_out = EPI == EPI_SWIGLU ? g.F : g.N;
+  dim3 grid((g.M + gemm::BM - 1) / gemm::BM, n_out / outs_per_tile);
+  hipLaunchKernelGGL(gemm_bf16_kernel<EPI>, grid, dim3(gemm::THREADS), 0, s, g);
+  return last_launch();
+}
+
+qi_status launch_norm(const float *x, int ldx, const float *gamma, int zc, const float *mod,
+                      int mod_img_off, int L_rows, int rows, int H, u16 *out, int ldo, hipStream_t s) {
+  hipLaunchKernelGGL(rmsnorm_mod_kernel, dim3(rows), dim3(256), 0, s, x, ldx, gamma, zc, mod,
+                     mod_img_off, L_rows, H, kRmsEps, out, ldo);
+  return last_launch();
+}
+
+qi_status launch_modulation(int H, const u16 *w_mod, const float *b_mod, float t, float *mod, hipStream_t s) {
+  hipLaunchKernelGGL(mod_gemv_kernel, dim3((4 * H + 15) / 16), dim3(256), 2 * H * sizeof(float), s, w_mod, b_mod,
+                     t, H, 4 * H, mod);
+  return last_launch();
+}
+
+qi_status launch_attention(int heads, int L, int N, bool joint, const u16 *q_t, const u16 *k_t,
+                           const u16 *vt_t, const u16 *q_i, const u16 *k_i, const u16 *vt_i, u16 *o,
+                           hipStream_t s) {
+  AttnArgs a{};
+  a.q_t = q_t; a.k_t = k_t; a.vt_t = vt_t;
+  a.q_i = q_i; a.k_i = k_i; a.vt_i = vt_i;
+  a.o = o;
+  a.ldo = heads * 128;
+  a.heads = heads; a.L = L; a.N = N;
+  a.ldv_t = round64(L); a.ldv_i = round64(N);
+  a.n_img_qt = (N + attn::BQ - 1) / attn::BQ;
+  a.n_txt_qt = joint ? (L + attn::BQ - 1) / attn::BQ : 0;
+  a.o_img_row0 = joint ? L : 0;
+  a.scale_log2 = (float)(1.4426950408889634 / sqrt(128.0));
+  hipLaunchKernelGGL(block_causal_attn_kernel, dim3(a.n_img_qt + a.n_txt_qt, heads), dim3(attn::THREADS),
+                     0, s, a);
+  return last_launch();
+}
+
+// The launch sequence of one block; arguments already validated.
+qi_status run_block(const qi_dims &d, const qi_block_w &w, int L, int N, bool joint, float *x,
+                    const float *mod, const float *cos_t, const float *sin_t, const float *cos_i,
+                    const float *sin_i, u16 *kv_slot, char *ws, const Layout &lay, hipStream_t s) {
+  const int H = d.hidden, F = d.ffn, heads = d.heads;
+  const int L_rows = joint ? L : 0, T = L_rows + N;
+  const int img_off = 4 * H;  // mod row 1
+  u16 *h = (u16 *)(ws + lay.h);
+  u16 *o = (u16 *)(ws + lay.o);
+  u16 *a = (u16 *)(ws + lay.a);
+  u16 *q_t = (u16 *)(ws + lay.q_t);
+  u16 *k_t = kv_slot ? kv_slot : (u16 *)(ws + lay.k_t);
+  u16 *vt_t = kv_slot ? kv_slot + (size_t)heads * L * 128 : (u16 *)(ws + lay.vt_t);
+  u16 *q_i = (u16 *)(ws + lay.q_i), *k_i = (u16 *)(ws + lay.k_i), *vt_i = (u16 *)(ws + lay.vt_i);
+
+  // norm 1 + modulation (scale1 = chunk 0)
+  QI_TRY(launch_norm(x, H, w.norm1, 0, mod, img_off, L_rows, T, H, h, H, s));
+
+  // QKV + RoPE (+ text K/V into the cache slot on a capture pass)
+  GemmArgs g{};
+  g.A = h; g.lda = H; g.W = w.w_qkv; g.ldw = H; g.M = T; g.N = 3 * H; g.K = H; g.L_rows = L_rows;
+  g.H = H;
+  g.cos_t = cos_t; g.sin_t = sin_t; g.cos_i = cos_i; g.sin_i = sin_i;
+  g.q_t = q_t; g.k_t = k_t; g.vt_t = vt_t; g.q_i = q_i; g.k_i = k_i; g.vt_i = vt_i;
+  g.seg_t = L; g.seg_i = N; g.ldv_t = round64(L); g.ldv_i = round64(N);
+  QI_TRY(launch_gemm<EPI_QKV>(g, s));
+
+  QI_TRY(launch_attention(heads, L, N, joint, q_t, k_t, vt_t, q_i, k_i, vt_i, o, s));
+
+  // O projection + gated residual 1 (gate1 = chunk 1)
+  GemmArgs r{};
+  r.A = o; r.lda = H; r.W = w.w_o; r.ldw = H; r.M = T; r.N = H; r.K = H; r.L_rows = L_rows;
+  r.X = x; r.ldx = H; r.gate = mod + H; r.gate_img_off = img_off;
+  QI_TRY(launch_gemm<EPI_RESID>(r, s));
+
+  // norm 2 + modulation (scale2 = chunk 2)
+  QI_TRY(launch_norm(x, H, w.norm2, 0, mod + 2 * H, img_off, L_rows, T, H, h, H, s));
+
+  // gate/up + SwiGLU
+  GemmArgs u{};
+  u.A = h; u.lda = H; u.W = w.w_gu; u.ldw = H; u.M = T; u.N = 2 * F; u.K = H; u.L_rows = L_rows;
+  u.out = a; u.ldo = F; u.F = F;
+  QI_TRY(launch_gemm<EPI_SWIGLU>(u, s));
+
+  // down + gated residual 2 (gate2 = chunk 3)
+  GemmArgs dn{};
+  dn.A = a; dn.lda = F; dn.W = w.w_down; dn.ldw = F; dn.M = T; dn.N = H; dn.K = F; dn.L_rows = L_rows;
+  dn.X = x; dn.ldx = H; dn.gate = mod + 3 * H; dn.gate_img_off = img_off;
+  QI_TRY(launch_gemm<EPI_RESID>(dn, s));
+  return QI_OK;
+}
+
+qi_status check_block_w(const qi_block_w *w) {
+  if (!w || !w->w_qkv || !w->w_o || !w->w_gu || !w->w_down || !w->norm1 || !w->norm2) return QI_ERR_NULL;
+  if (!al16(w->w_qkv) || !al16(w->w_o) || !al16(w->w_gu) || !al16(w->w_down) || !al16(w->norm1) ||
+      !al16(w->norm2))
+    return QI_ERR_ALIGN;
+  return QI_OK;
+}
+
+qi_status check_model_w(const qi_dims &d, const qi_model_w *w, bool need_text) {
+  if (!w || !w->blocks || !w->w_mod || !w->b_mod || !w->w_img || !w->b_img || !w->norm_out || !w->w_out ||
+      !w->b_out)
+    return QI_ERR_NULL;
+  if (need_text && (!w->txt_norm || !w->w_txt || !w->b_txt)) return QI_ERR_NULL;
+  const void *ps[] = {w->w_mod, w->b_mod, w->w_img, w->b_img, w->norm_out, w->w_out, w->b_out};
+  for (const void *p : ps)
+    if (!al16(p)) return QI_ERR_ALIGN;
+  if (need_text && (!al16(w->txt_norm) || !al16(w->w_txt) || !al16(w->b_txt))) return QI_ERR_ALIGN;
+  for (int b = 0; b < d.n_blocks; ++b) QI_TRY(check_block_w(&w->blocks[b]));
+  return QI_OK;
+}
+
+// A whole step: joint when kv == NULL or capture, image-only otherwise.
+qi_status run_step(const qi_dims &d, const qi_model_w &w, int L, int N, const float *img_tokens,
+                   const float *txt_feats, float t, const float *txt_cos, const float *txt_sin,
+                   const float *img_cos, const float *img_sin, u16 *kv, bool joint, float *vel,
+                   char *ws, hipStream_t s) {
+  const int H = d.hidden, D = d.txt_dim;
+  const Layout lay = layout(d, L, N);
+  float *x = (float *)(ws + lay.x);
+  float *mod = (float *)(ws + lay.mod);
+  const int L_rows = joint ? L : 0;
+
+  QI_TRY(launch_modulation(H, w.w_mod, w.b_mod, t, mod, s));
+
+  if (joint) {
+    u16 *tn = (u16 *)(ws + lay.tn);
+    QI_TRY(launch_norm(txt_feats, D, w.txt_norm, 1, nullptr, 0, 0, L, D, tn, D, s));
+    GemmArgs g{};
+    g.A = tn; g.lda = D; g.W = w.w_txt; g.ldw = D; g.M = L; g.N = H; g.K = D; g.L_rows = L;
+    g.C = x; g.ldc = H; g.bias = w.b_txt;
+    QI_TRY(launch_gemm<EPI_F32>(g, s));
+  }
+  hipLaunchKernelGGL(img_embed_kernel, dim3((N + 15) / 16, (H + 255) / 256), dim3(256), 0, s, img_tokens, N,
+                     w.w_img, w.b_img, H, x, H, L_rows);
+  QI_TRY(last_launch());
+
+  const size_t slot = slot_elems(d, L);
+  for (int b = 0; b < d.n_blocks; ++b) {
+    u16 *kv_slot = kv ? kv + (size_t)b * slot : nullptr;
+    QI_TRY(run_block(d, w.blocks[b], L, N, joint, x, mod, txt_cos, txt_sin, img_cos, img_sin, kv_slot, ws,
+                     lay, s));
+  }
+  if (vel) {
+    hipLaunchKernelGGL(head_kernel, dim3((N + 15) / 16), dim3(256), 0, s, x + (size_t)L_rows * H, H, N,
+                       w.norm_out, w.w_out, w.b_out, H, kRmsEps, vel);
+    QI_TRY(last_launch());
+  }
+  return QI_OK;
+}
+
+qi_status check_step_args(const qi_dims *d, const qi_model_w *w, int L, int N, const float *img_tokens,
+                          const float *txt_feats, float t, const float *txt_cos, const float *txt_sin,
+                          const float *img_cos, const float *img_sin, bool joint, const void *ws,
+                          size_t ws_bytes) {
+  if (!d) return QI_ERR_NULL;
+  if (!dims_ok(d)) return QI_ERR_SHAPE;
+  if (L < 1 || L > kMaxL || N < 1 || N > kMaxN) return QI_ERR_RANGE;
+  if (!(t >= 0.f && t <= 1.f)) return QI_ERR_RANGE;
+  if (!img_tokens || !img_cos || !img_sin || !ws) return QI_ERR_NULL;
+  if (joint && (!txt_feats || !txt_cos || !txt_sin)) return QI_ERR_NULL;
+  if (!al16(img_tokens) || !al16(img_cos) || !al16(img_sin) || !al16(ws)) return QI_ERR_ALIGN;
+  if (joint && (!al16(txt_feats) || !al16(txt_cos) || !al16(txt_sin))) return QI_ERR_ALIGN;
+  QI_TRY(check_model_w(*d, w, joint));
+  if (ws_bytes < layout(*d, L, N).total) return QI_ERR_WORKSPACE;
+  return QI_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *qi_status_str(qi_status s) {
+  switch (s) {
+    case QI_OK: return "ok";
+    case QI_ERR_NULL: return "a required pointer is NULL";
+    case QI_ERR_SHAPE: return "inconsistent dimensions";
+    case QI_ERR_RANGE: return "a size is outside its supported range";
+    case QI_ERR_ALIGN: return "a device pointer is not 16-byte aligned";
+    case QI_ERR_WORKSPACE: return "workspace smaller than qi_workspace_bytes";
+    case QI_ERR_CACHE: return "K/V cache invalid or made for another shape";
+    case QI_ERR_HIP: return "a HIP call or kernel launch failed";
+    case QI_ERR_UNSUPPORTED: return "unsupported request";
+    default: return "unknown status";
+  }
+}
+
+const char *qi_version(void) { return "qi-dit-gfx950 0.1"; }
+
+size_t qi_workspace_bytes(const qi_dims *d, int32_t L, int32_t N) {
+  if (!dims_ok(d) || L < 1 || L > kMaxL || N < 1 || N > kMaxN) return 0;
+  return layout(*d, L, N).total;
+}
+
+size_t qi_kv_slot_elems(const qi_dims *d, int32_t L) {
+  if (!dims_ok(d) || L < 1 || L > kMaxL) return 0;
+  return slot_elems(*d, L);
+}
+
+size_t qi_kv_cache_bytes(const qi_dims *d, int32_t L) {
+  if (!dims_ok(d) || L < 1 || L > kMaxL) return 0;
+  return slot_elems(*d, L) * 2 * (size_t)d->n_blocks;
+}
+
+qi_status qi_dit_block_fwd(const qi_dims *d, const qi_block_w *w, int32_t L, int32_t N, int32_t mode,
+                           float *x, const float *mod, const float *cos, const float *sin, uint16_t *kv_txt,
+                           void *ws, size_t ws_bytes, void *stream) {
+  if (!d) return QI_ERR_NULL;
+  if (!dims_ok(d)) return QI_ERR_SHAPE;
+  if (mode != QI_MODE_JOINT && mode != QI_MODE_IMAGE_ONLY) return QI_ERR_RANGE;
+  if (L < 1 || L > kMaxL || N < 1 || N > kMaxN) return QI_ERR_RANGE;
+  if (!x || !mod || !cos || !sin || !ws) return QI_ERR_NULL;
+  const bool joint = mode == QI_MODE_JOINT;
+  if (!joint && !kv_txt) return QI_ERR_CACHE;
+  if (!al16(x) || !al16(mod) || !al16(cos) || !al16(sin) || !al16(ws) || (kv_txt && !al16(kv_txt)))
+    return QI_ERR_ALIGN;
+  QI_TRY(check_block_w(w));
+  const Layout lay = layout(*d, L, N);
+  if (ws_bytes < lay.total) return QI_ERR_WORKSPACE;
+  const int L_rows = joint ? L : 0;
+  const float *cos_t = cos, *sin_t = sin;
+  const float *cos_i = cos + (size_t)L_rows * 64, *sin_i = sin + (size_t)L_rows * 64;
+  return run_block(*d, *w, L, N, joint, x, mod, cos_t, sin_t, cos_i, sin_i, kv_txt, (char *)ws, lay,
+                   (hipStream_t)stream);
+}
+
+qi_status qi_dit_step(const qi_dims *d, const qi_model_w *w, int32_t L, int32_t N, const float *img_tokens,
+                      const float *txt_feats, float timestep, const float *txt_cos, const float *txt_sin,
+                      const float *img_cos, const float *img_sin, const qi_kv_cache *cache, float *vel,
+                      void *ws, size_t ws_bytes, void *stream) {
+  const bool joint = cache == nullptr;
+  QI_TRY(check_step_args(d, w, L, N, img_tokens, txt_feats, timestep, txt_cos, txt_sin, img_cos, img_sin,
+                         joint, ws, ws_bytes));
+  if (!vel) return QI_ERR_NULL;
+  if (!al16(vel)) return QI_ERR_ALIGN;
+  if (cache) {
+    if (!cache->kv || !cache->valid || cache->L != L || cache->n_blocks != d->n_blocks ||
+        cache->hidden != d->hidden)
+      return QI_ERR_CACHE;
+    if (!al16(cache->kv)) return QI_ERR_ALIGN;
+  }
+  return run_step(*d, *w, L, N, img_tokens, txt_feats, timestep, txt_cos, txt_sin, img_cos, img_sin,
+                  cache ? cache->kv : nullptr, joint, vel, (char *)ws, (hipStream_t)stream);
+}
+
+qi_status qi_text_kv_capture(const qi_dims *d, const qi_model_w *w, int32_t L, int32_t N,
+                             const float *img_tokens, const float *txt_feats, float timestep,
+                             const float *txt_cos, const float *txt_sin, const float *img_cos,
+                             const float *img_sin, qi_kv_cache *cache, float *vel, void *ws, size_t ws_bytes,
+                             void *stream) {
+  QI_TRY(check_step_args(d, w, L, N, img_tokens, txt_feats, timestep, txt_cos, txt_sin, img_cos, img_sin,
+                         true, ws, ws_bytes));
+  if (!cache || !cache->kv) return QI_ERR_NULL;
+  if (!al16(cache->kv) || (vel && !al16(vel))) return QI_ERR_ALIGN;
+  cache->valid = 0;
+  QI_TRY(run_step(*d, *w, L, N, img_tokens, txt_feats, timestep, txt_cos, txt_sin, img_cos, img_sin, cache->kv,
+                  true, vel, (char *)ws, (hipStream_t)stream));
+  cache->L = L;
+  cache->n_blocks = d->n_blocks;
+  cache->hidden = d->hidden;
+  cache->valid = 1;
+  return QI_OK;
+}
+
+qi_status qi_euler_update(float *x, const float *vel, float sigma_cur, float sigma_next, int64_t n,
+                          void *stream) {
+  if (n < 0) return QI_ERR_RANGE;
+  if (n == 0) return QI_OK;
+  if (!x || !vel) return QI_ERR_NULL;
+  if (!al16(x) || !al16(vel)) return QI_ERR_ALIGN;
+  const float ds = sigma_next - sigma_cur;  // fp32 difference on the host
+  const int64_t n4 = (n + 3) / 4;
+  const int blocks = (int)((n4 + 255) / 256 < 4096 ? (n4 + 255) / 256 : 4096);
+  hipLaunchKernelGGL(euler_kernel, dim3(blocks), dim3(256), 0, (hipStream_t)stream, x, vel, ds, n);
+  return last_launch();
+}
+
+qi_status qi_modulation(const qi_dims *d, const uint16_t *w_mod, const float *b_mod, float timestep, float *mod,
+                        void *stream) {
+  if (!d) return QI_ERR_NULL;
+  if (!dims_ok(d)) return QI_ERR_SHAPE;
+  if (!(timestep >= 0.f && timestep <= 1.f)) return QI_ERR_RANGE;
+  if (!w_mod || !b_mod || !mod) return QI_ERR_NULL;
+  if (!al16(w_mod) || !al16(b_mod) || !al16(mod)) return QI_ERR_ALIGN;
+  return launch_modulation(d->hidden, w_mod, b_mod, timestep, mod, (hipStream_t)stream);
+}
+
+qi_status qi_block_causal_attention(int32_t heads, int32_t L, int32_t N, int32_t mode, const uint16_t *q_txt,
+                                    const uint16_t *k_txt, const uint16_t *vt_txt, const uint16_t *q_img,
+                                    const uint16_t *k_img, const uint16_t *vt_img, uint16_t *o, void *stream) {
+  if (heads < 1 || heads > 64 || L < 1 || L > kMaxL || N < 1 || N > kMaxN) return QI_ERR_RANGE;
+  if (mode != QI_MODE_JOINT && mode != QI_MODE_IMAGE_ONLY) return QI_ERR_RANGE;
+  const bool joint = mode == QI_MODE_JOINT;
+  if (!k_txt || !vt_txt || !q_img || !k_img || !vt_img || !o || (joint && !q_txt)) return QI_ERR_NULL;
+  if (!al16(k_txt) || !al16(vt_txt) || !al16(q_img) || !al16(k_img) || !al16(vt_img) || !al16(o) ||
+      (joint && !al16(q_txt)))
+    return QI_ERR_ALIGN;
+  return launch_attention(heads, L, N, joint, q_txt, k_txt, vt_txt, q_img, k_img, vt_img, o,
+                          (hipStream_t)stream);
+}
+
+qi_status qi_linear_bf16(int32_t M, int32_t N, int32_t K, const uint16_t *A, const uint16_t *W,
+                         const float *bias, float *C, void *stream) {
+  if (M < 1 || N < 128 || N % 128 != 0 || K < 64 || K % 64 != 0 || M > (1 << 20) || N > (1 << 20) ||
+      K > (1 << 20))
+    return QI_ERR_RANGE;
+  if (!A || !W || !C) return QI_ERR_NULL;
+  if (!al16(A) || !al16(W) || !al16(C) || (bias && !al16(bias))) return QI_ERR_ALIGN;
+  GemmArgs g{};
+  g.A = A; g.lda = K; g.W = W; g.ldw = K; g.M = M; g.N = N; g.K = K;
+  g.C = C; g.ldc = N; g.bias = bias;
+  return launch_gemm<EPI_F32>(g, (hipStream_t)stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,227 @@
+"""Python binding of libqi (include/qi.h): argument marshalling only.
+
+Every step of the DiT runs in the HIP library.  torch provides device memory
+(tensors whose data pointers are handed to the C ABI) and the stream; numpy
+arrays carry the host-side tables.  bf16 weights travel as uint16 bit
+patterns and are stored on the device as int16 tensors of the same bits."""
+from __future__ import annotations
+
+import ctypes
+
+import numpy as np
+
+from . import _lib
+from ._lib import (QI_MODE_IMAGE_ONLY, QI_MODE_JOINT, QiBlockW, QiDims, QiError, QiKvCache,
+                   QiModelW, check)
+
+__all__ = ["QI_MODE_JOINT", "QI_MODE_IMAGE_ONLY", "QiError", "make_dims", "rope_axis_table",
+           "rope_tables", "flow_sigmas", "workspace_bytes", "kv_cache_bytes", "kv_slot_elems",
+           "DeviceModel", "KVCache", "Workspace", "dit_step", "text_kv_capture", "dit_block_fwd",
+           "euler_update", "modulation", "block_causal_attention", "linear_bf16", "stream_handle"]
+
+
+def _np_ptr(a: np.ndarray) -> int:
+    assert a.flags["C_CONTIGUOUS"]
+    return a.ctypes.data
+
+
+def _ptr(t) -> int:
+    """Device pointer of a torch tensor (0 for None)."""
+    if t is None:
+        return 0
+    return int(t.data_ptr())
+
+
+def stream_handle(stream=None) -> int:
+    import torch
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return int(s.cuda_stream)
+
+
+def make_dims(hidden: int, ffn: int, n_blocks: int, txt_dim: int) -> QiDims:
+    return QiDims(hidden, hidden // 128, 128, ffn, n_blocks, txt_dim)
+
+
+# ------------------------------------------------------------------ host tables
+
+def rope_axis_table(d: int):
+    lib = _lib.load()
+    c = np.empty((9216, d // 2), np.float32)
+    s = np.empty_like(c)
+    check(lib.qi_rope_axis_table(d, _np_ptr(c), _np_ptr(s)), "qi_rope_axis_table")
+    return c, s
+
+
+def rope_tables(L: int, h: int, w: int):
+    """(txt_cos, txt_sin, img_cos, img_sin) host fp32 arrays [L,64], [L,64],
+    [h*w,64], [h*w,64]."""
+    lib = _lib.load()
+    tc = np.empty((max(L, 1), 64), np.float32)
+    ts = np.empty_like(tc)
+    ic = np.empty((h * w, 64), np.float32)
+    is_ = np.empty_like(ic)
+    check(lib.qi_rope_tables(L, h, w, _np_ptr(tc), _np_ptr(ts), _np_ptr(ic), _np_ptr(is_)), "qi_rope_tables")
+    return tc[:L], ts[:L], ic, is_
+
+
+def flow_sigmas(steps: int, n_img_tokens: int):
+    lib = _lib.load()
+    s = np.empty(steps + 1, np.float32)
+    t = np.empty(steps, np.float32)
+    check(lib.qi_flow_sigmas(steps, n_img_tokens, _np_ptr(s), _np_ptr(t)), "qi_flow_sigmas")
+    return s, t
+
+
+def workspace_bytes(dims: QiDims, L: int, N: int) -> int:
+    return int(_lib.load().qi_workspace_bytes(ctypes.byref(dims), L, N))
+
+
+def kv_cache_bytes(dims: QiDims, L: int) -> int:
+    return int(_lib.load().qi_kv_cache_bytes(ctypes.byref(dims), L))
+
+
+def kv_slot_elems(dims: QiDims, L: int) -> int:
+    return int(_lib.load().qi_kv_slot_elems(ctypes.byref(dims), L))
+
+
+# ------------------------------------------------------------------ device objects
+
+def to_device(a: np.ndarray, device="cuda"):
+    import torch
+    if a.dtype == np.uint16:
+        a = a.view(np.int16)
+    return torch.from_numpy(np.ascontiguousarray(a)).to(device)
+
+
+class DeviceModel:
+    """Device copies of the DiT weights and the C structs that point at them.
+
+    shared: dict of the shared tensors; blocks: sequence (or iterable) of
+    per-block dicts.  Linear weights must already be bf16 bit patterns
+    (uint16); norms and biases fp32."""
+
+    BLOCK_KEYS = ("w_qkv", "w_o", "w_gu", "w_down", "norm1", "norm2")
+    SHARED_KEYS = ("w_mod", "b_mod", "w_img", "b_img", "txt_norm", "w_txt", "b_txt",
+                   "norm_out", "w_out", "b_out")
+
+    def __init__(self, dims: QiDims, shared: dict, blocks, device="cuda"):
+        self.dims = dims
+        self.device = device
+        self.shared = {k: to_device(_as_dev(k, shared[k]), device) for k in self.SHARED_KEYS}
+        self.blocks = []
+        for bw in blocks:
+            self.blocks.append({k: to_device(_as_dev(k, bw[k]), device) for k in self.BLOCK_KEYS})
+        if len(self.blocks) != dims.n_blocks:
+            raise ValueError(f"{len(self.blocks)} blocks given, dims say {dims.n_blocks}")
+        self._bw = (QiBlockW * len(self.blocks))()
+        for i, b in enumerate(self.blocks):
+            self._bw[i] = QiBlockW(*(_ptr(b[k]) for k in self.BLOCK_KEYS))
+        sh = self.shared
+        self.w = QiModelW(ctypes.cast(self._bw, ctypes.POINTER(QiBlockW)),
+                          *(_ptr(sh[k]) for k in self.SHARED_KEYS))
+
+    def block_struct(self, b: int) -> QiBlockW:
+        return self._bw[b]
+
+
+def _as_dev(name: str, a: np.ndarray) -> np.ndarray:
+    """Linear weights go to the device as bf16 bits; fp32 arrays given for a
+    2-D weight are a caller error (the library reads bf16 only)."""
+    if a.ndim == 2 and a.dtype != np.uint16:
+        raise TypeError(f"{name}: 2-D weights must be bf16 bit patterns (uint16), got {a.dtype}")
+    if a.ndim == 1 and a.dtype != np.float32:
+        a = a.astype(np.float32)
+    return a
+
+
+class KVCache:
+    """Text K/V cache ([blocks][K heads x L x 128 | V^T heads x 128 x Lp] bf16)."""
+
+    def __init__(self, dims: QiDims, L: int, device="cuda"):
+        import torch
+        self.nbytes = kv_cache_bytes(dims, L)
+        # zero-filled so the never-written V^T padding columns hold defined bits
+        self.buf = torch.zeros(self.nbytes // 2, dtype=torch.int16, device=device)
+        self.c = QiKvCache(_ptr(self.buf), L, dims.n_blocks, dims.hidden, 0)
+        self.slot_elems = kv_slot_elems(dims, L)
+
+    @property
+    def valid(self) -> bool:
+        return bool(self.c.valid)
+
+    def slot_ptr(self, b: int) -> int:
+        return _ptr(self.buf) + 2 * b * self.slot_elems
+
+
+class Workspace:
+    def __init__(self, dims: QiDims, L: int, N: int, device="cuda"):
+        import torch
+        self.nbytes = workspace_bytes(dims, L, N)
+        if self.nbytes == 0:
+            raise ValueError("invalid dims for the workspace")
+        self.buf = torch.empty(self.nbytes, dtype=torch.uint8, device=device)
+
+    @property
+    def ptr(self) -> int:
+        return _ptr(self.buf)
+
+
+# ------------------------------------------------------------------ entry points
+
+def dit_step(model: DeviceModel, L: int, N: int, img_tokens, txt_feats, t: float, txt_cos, txt_sin,
+             img_cos, img_sin, vel, ws: Workspace, cache: KVCache | None = None, stream=None):
+    lib = _lib.load()
+    st = lib.qi_dit_step(ctypes.byref(model.dims), ctypes.byref(model.w), L, N, _ptr(img_tokens),
+                         _ptr(txt_feats), float(t), _ptr(txt_cos), _ptr(txt_sin), _ptr(img_cos),
+                         _ptr(img_sin), ctypes.byref(cache.c) if cache is not None else None,
+                         _ptr(vel), ws.ptr, ws.nbytes, stream_handle(stream))
+    check(st, "qi_dit_step")
+
+
+def text_kv_capture(model: DeviceModel, L: int, N: int, img_tokens, txt_feats, t: float, txt_cos,
+                    txt_sin, img_cos, img_sin, cache: KVCache, vel, ws: Workspace, stream=None):
+    lib = _lib.load()
+    st = lib.qi_text_kv_capture(ctypes.byref(model.dims), ctypes.byref(model.w), L, N, _ptr(img_tokens),
+                                _ptr(txt_feats), float(t), _ptr(txt_cos), _ptr(txt_sin), _ptr(img_cos),
+                                _ptr(img_sin), ctypes.byref(cache.c), _ptr(vel), ws.ptr, ws.nbytes,
+                                stream_handle(stream))
+    check(st, "qi_text_kv_capture")
+
+
+def dit_block_fwd(dims: QiDims, block: QiBlockW, L: int, N: int, mode: int, x, mod, cos, sin,
+                  kv_slot_ptr: int, ws: Workspace, stream=None):
+    lib = _lib.load()
+    st = lib.qi_dit_block_fwd(ctypes.byref(dims), ctypes.byref(block), L, N, mode, _ptr(x), _ptr(mod),
+                              _ptr(cos), _ptr(sin), kv_slot_ptr or None, ws.ptr, ws.nbytes,
+                              stream_handle(stream))
+    check(st, "qi_dit_block_fwd")
+
+
+def euler_update(x, vel, sigma_cur: float, sigma_next: float, stream=None):
+    n = x.numel()
+    if vel.numel() != n:
+        raise ValueError("x and vel sizes differ")
+    st = _lib.load().qi_euler_update(_ptr(x), _ptr(vel), float(sigma_cur), float(sigma_next), n,
+                                     stream_handle(stream))
+    check(st, "qi_euler_update")
+
+
+def modulation(dims: QiDims, w_mod, b_mod, t: float, mod, stream=None):
+    st = _lib.load().qi_modulation(ctypes.byref(dims), _ptr(w_mod), _ptr(b_mod), float(t), _ptr(mod),
+                                   stream_handle(stream))
+    check(st, "qi_modulation")
+
+
+def block_causal_attention(heads: int, L: int, N: int, mode: int, q_t, k_t, vt_t, q_i, k_i, vt_i, o,
+                           stream=None):
+    st = _lib.load().qi_block_causal_attention(heads, L, N, mode, _ptr(q_t), _ptr(k_t), _ptr(vt_t),
+                                               _ptr(q_i), _ptr(k_i), _ptr(vt_i), _ptr(o),
+                                               stream_handle(stream))
+    check(st, "qi_block_causal_attention")
+
+
+def linear_bf16(A, W, bias, C, stream=None):
+    M, K = A.shape
+    N = W.shape[0]
+    st = _lib.load().qi_linear_bf16(M, N, K, _ptr(A), _ptr(W), _ptr(bias), _ptr(C), stream_handle(stream))
+    check(st, "qi_linear_bf16")

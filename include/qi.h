@@ -1,0 +1,244 @@
+/*
+ * qi.h -- C ABI of the MI355X (gfx950) single-stream DiT denoising step with
+ * block-causal attention and exact text-K/V reuse.
+ *
+ * Pages cited (by title and section):
+ *   [PORT] "Qwen-Image-2.1 port" knowledge page of the coreai-model-zoo: the
+ *          pieces table, DiT row (32 single-stream blocks, one modulation
+ *          Linear shared by all blocks with rows for the sampled t and t = 0,
+ *          ZeroCenterRMSNorm text projection, SwiGLU x3, 3-axis interleaved
+ *          RoPE 16/56/56, block-causal attention as two SDPA calls).
+ *   [HOST] "Host contract -- RGBA-Image-2.1 (Core AI port of Qwen-Image-2.1)":
+ *          s.1 The graphs (the DiT signature), s.4 Sequence layout and RoPE,
+ *          s.6 Sampler.
+ *   [MLX]  "Qwen-Image-2.1 on MLX, faster and exact": "Text K/V reuse (exact,
+ *          on by default)".
+ *
+ * Conventions for every entry point:
+ *   - bf16 values travel as uint16_t bit patterns; fp32 as float.
+ *   - "device" pointers are HIP device memory of the current device; "host"
+ *     pointers are ordinary host memory.  The caller owns every buffer; the
+ *     library allocates nothing per call and keeps no mutable global state.
+ *   - Linear weights use the [out, in] row-major layout, so each projection is
+ *     y = x W^T.  Device pointers must be 16-byte aligned.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Work is enqueued
+ *     on it and the call returns without synchronising.
+ *   - Every argument is validated on the host before anything is enqueued; a
+ *     failed check returns a negative qi_status and enqueues nothing.  A HIP
+ *     launch error returns QI_ERR_HIP; faults inside kernels surface at the
+ *     caller's next synchronisation.  No C++ exception crosses the ABI.
+ */
+#ifndef QI_H_
+#define QI_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t qi_status;
+#define QI_OK 0
+#define QI_ERR_NULL (-1)        /* a required pointer is NULL */
+#define QI_ERR_SHAPE (-2)       /* inconsistent dimensions */
+#define QI_ERR_RANGE (-3)       /* a size outside its supported range */
+#define QI_ERR_ALIGN (-4)       /* a device pointer not 16-byte aligned */
+#define QI_ERR_WORKSPACE (-5)   /* workspace smaller than qi_workspace_bytes */
+#define QI_ERR_CACHE (-6)       /* K/V cache invalid or made for another shape */
+#define QI_ERR_HIP (-7)         /* a HIP runtime call or launch failed */
+#define QI_ERR_UNSUPPORTED (-8) /* a valid request this build does not handle */
+
+/* Pass kinds of one block.  JOINT runs the [text L | image N] sequence (step 1
+ * of a render, or full recompute); IMAGE_ONLY runs the N image rows against
+ * text K/V cached from a joint pass ([MLX] "Text K/V reuse"). */
+#define QI_MODE_JOINT 0
+#define QI_MODE_IMAGE_ONLY 1
+
+/* Model dimensions.  head_dim must be 128 and heads = hidden / 128 ([PORT] DiT
+ * row: 32 heads x 128 at hidden 4096).  hidden % 128 == 0, ffn % 64 == 0,
+ * txt_dim % 64 == 0, 1 <= n_blocks <= 256. */
+typedef struct {
+  int32_t hidden, heads, head_dim, ffn, n_blocks, txt_dim;
+} qi_dims;
+
+/* Device weights of one block (bf16 as uint16, norms fp32).
+ *   w_qkv  [3H, H]: rows [0,H) q, [H,2H) k, [2H,3H) v; head h owns rows h*128..
+ *   w_o    [H, H]
+ *   w_gu   [2F, H]: rows [0,F) gate (SiLU), [F,2F) up
+ *   w_down [H, F]
+ *   norm1, norm2 [H] fp32 RMSNorm weights. */
+typedef struct {
+  const uint16_t *w_qkv, *w_o, *w_gu, *w_down;
+  const float *norm1, *norm2;
+} qi_block_w;
+
+/* Device weights of the whole DiT.  `blocks` is a HOST array of n_blocks
+ * qi_block_w.  w_mod [4H, H] + b_mod [4H]: the one modulation Linear shared by
+ * every block; w_img [H, 64] + b_img [H]: img-in; txt_norm [D] (zero-centred
+ * weight), w_txt [H, D] + b_txt [H]: text projection; norm_out [H], w_out
+ * [64, H] + b_out [64]: proj_out. */
+typedef struct {
+  const qi_block_w *blocks;
+  const uint16_t *w_mod; const float *b_mod;
+  const uint16_t *w_img; const float *b_img;
+  const float *txt_norm; const uint16_t *w_txt; const float *b_txt;
+  const float *norm_out; const uint16_t *w_out; const float *b_out;
+} qi_model_w;
+
+/* Text K/V cache ([MLX] "Text K/V reuse": 2 x blocks x tokens x hidden bf16).
+ * kv is device memory of qi_kv_cache_bytes(dims, L) bytes.  Block b's slot
+ * starts at kv + b * qi_kv_slot_elems(dims, L) and holds
+ *   K  [heads][L][128]          (RoPE applied)
+ *   Vt [heads][128][Lp]         (V transposed, Lp = L rounded up to 64;
+ *                                columns >= L are never read as values)
+ * `valid` is set to 1 by qi_text_kv_capture; L, n_blocks and hidden must match
+ * the step that reads it. */
+typedef struct {
+  uint16_t *kv;
+  int32_t L, n_blocks, hidden, valid;
+} qi_kv_cache;
+
+/* Status text (static string). */
+const char *qi_status_str(qi_status s);
+/* Library version string (static). */
+const char *qi_version(void);
+
+/* ---------------------------------------------------------------- host tables */
+
+/* One RoPE axis table ([HOST] s.4): rows for positions -1024..8191 (row p+1024),
+ * column k the angle p * 1/10000^(2k/d), each step rounded to fp32, cos/sin of
+ * the fp32 angle evaluated in float64 and rounded once.  d in {16, 56} (any even
+ * d in 2..128 is accepted).  cos_out, sin_out: host [9216][d/2]. */
+qi_status qi_rope_axis_table(int32_t d, float *cos_out, float *sin_out);
+
+/* Per-token RoPE rows ([HOST] s.4): text token i -> position (i, i, i); image
+ * token (y, x), index y*w + x -> (L, y - (h - h/2), x - (w - w/2)); a token's 64
+ * values are its axis-0 (8), axis-1 (28) and axis-2 (28) rows concatenated.
+ * Host outputs: txt_cos/txt_sin [L][64], img_cos/img_sin [h*w][64].
+ * Errors: QI_ERR_NULL; QI_ERR_RANGE if L < 0, h or w < 1, or a position falls
+ * outside -1024..8191. */
+qi_status qi_rope_tables(int32_t L, int32_t h, int32_t w, float *txt_cos, float *txt_sin,
+                         float *img_cos, float *img_sin);
+
+/* FlowMatch Euler schedule ([HOST] s.6): sigmas = linspace(1, 1/steps, steps),
+ * exponential shift with mu = N m + b (base_shift 0.5 at 256 tokens, max_shift
+ * 0.9 at 8192), terminal stretch to 0.02, timesteps = sigmas * 1000, then
+ * sigmas ++ [0].  Each array operation in fp32.  Host outputs: sigmas
+ * [steps+1], timesteps [steps].  The DiT's timestep input for step i is
+ * timesteps[i] / 1000 in fp32.  Errors: QI_ERR_NULL; QI_ERR_RANGE if steps < 2
+ * or n_img_tokens < 1. */
+qi_status qi_flow_sigmas(int32_t steps, int32_t n_img_tokens, float *sigmas, float *timesteps);
+
+/* ---------------------------------------------------------------- sizes */
+
+/* Workspace bytes qi_dit_step / qi_text_kv_capture / qi_dit_block_fwd need for
+ * a joint pass over L text and N image tokens (enough for an image-only pass
+ * too).  0 if the dims are invalid. */
+size_t qi_workspace_bytes(const qi_dims *d, int32_t L, int32_t N);
+/* Elements (uint16) of one block's cache slot, and bytes of the whole cache. */
+size_t qi_kv_slot_elems(const qi_dims *d, int32_t L);
+size_t qi_kv_cache_bytes(const qi_dims *d, int32_t L);
+
+/* ---------------------------------------------------------------- the step */
+
+/* One single-stream block ([PORT] DiT row), in place on the fp32 residual
+ * stream x [rows][H], rows = L + N (JOINT, text rows first) or N (IMAGE_ONLY):
+ *   h  = bf16(RMSNorm(x; norm1) * (1 + scale1[row]))
+ *   q,k,v = h W_qkv^T; RoPE on q, k (adjacent pairs 2k, 2k+1 rotated by the
+ *          row's cos/sin[k]); rounded once to bf16
+ *   o  = block-causal attention: a text row i sees text keys 0..i; an image
+ *        row sees every text key and every image key; scale 1/sqrt(128)
+ *   x += gate1[row] * (o W_o^T)
+ *   h2 = bf16(RMSNorm(x; norm2) * (1 + scale2[row]))
+ *   x += gate2[row] * ((SiLU(h2 Wg^T) * (h2 Wu^T)) W_down^T)
+ * mod: device fp32 [2][4H]; row 0 is the t = 0 row (text rows), row 1 the
+ * sampled-t row (image rows); each row is (scale1, gate1, scale2, gate2).
+ * cos, sin: device fp32 [rows][64], the rows' RoPE values in row order.
+ * kv_txt: this block's cache slot (layout of qi_kv_cache) or NULL.  JOINT: if
+ * non-NULL, the text rows' K/V are written there (capture), else into the
+ * workspace.  IMAGE_ONLY: required, read.
+ * Ranges: 1 <= L <= 512, 1 <= N <= 16384 (the DiT's L axis and the 2048^2
+ * token count of [PORT]).
+ * Errors: NULL, SHAPE, RANGE, ALIGN, WORKSPACE (ws_bytes < qi_workspace_bytes),
+ * HIP. */
+qi_status qi_dit_block_fwd(const qi_dims *d, const qi_block_w *w, int32_t L, int32_t N,
+                           int32_t mode, float *x, const float *mod, const float *cos,
+                           const float *sin, uint16_t *kv_txt, void *ws, size_t ws_bytes,
+                           void *stream);
+
+/* One DiT forward, the DiT graph of [HOST] s.1: img_tokens [N][64], txt_feats
+ * [L][txt_dim] (device fp32), timestep t (host fp32, already divided by 1000),
+ * txt_cos/txt_sin [L][64], img_cos/img_sin [N][64] (device fp32) -> vel [N][64]
+ * (device fp32).
+ *   modulation rows m(0), m(t) = W_mod e(tau) + b_mod with e(tau) the width-H
+ *     sinusoid [cos | sin](1000 tau 10000^(-j/(H/2)));
+ *   x_txt = ZeroCenterRMSNorm(txt_feats) W_txt^T + b_txt;  x_img = img_tokens
+ *     W_img^T + b_img;
+ *   n_blocks blocks (qi_dit_block_fwd);
+ *   vel = RMSNorm(x_img; norm_out) W_out^T + b_out.
+ * cache NULL: joint pass (full recompute; txt_feats required).  cache valid:
+ * image rows only, text K/V read from the cache (txt_feats, txt_cos, txt_sin
+ * may be NULL).  The image rows of both give bit-identical vel.
+ * Errors: as qi_dit_block_fwd; QI_ERR_CACHE if the cache is not valid or was
+ * made for another L, n_blocks or hidden. */
+qi_status qi_dit_step(const qi_dims *d, const qi_model_w *w, int32_t L, int32_t N,
+                      const float *img_tokens, const float *txt_feats, float timestep,
+                      const float *txt_cos, const float *txt_sin, const float *img_cos,
+                      const float *img_sin, const qi_kv_cache *cache, float *vel, void *ws,
+                      size_t ws_bytes, void *stream);
+
+/* Step 1 of a render with reuse ([MLX] "Text K/V reuse"): the joint pass of
+ * qi_dit_step that also writes every block's text K/V into cache->kv, then sets
+ * cache->L, n_blocks, hidden and valid = 1.  vel may be NULL (the step-1 vel is
+ * then not written).  Errors: as qi_dit_step; QI_ERR_NULL if cache or
+ * cache->kv is NULL. */
+qi_status qi_text_kv_capture(const qi_dims *d, const qi_model_w *w, int32_t L, int32_t N,
+                             const float *img_tokens, const float *txt_feats, float timestep,
+                             const float *txt_cos, const float *txt_sin, const float *img_cos,
+                             const float *img_sin, qi_kv_cache *cache, float *vel, void *ws,
+                             size_t ws_bytes, void *stream);
+
+/* Euler update of the FlowMatch sampler ([HOST] s.6), in place on device fp32
+ * x[n]: x = x + (sigma_next - sigma_cur) * vel, the difference computed in fp32
+ * on the host, then a fp32 multiply and a fp32 add per element (no fused
+ * multiply-add).  n = 0 is a no-op.  Errors: NULL, RANGE (n < 0), ALIGN, HIP. */
+qi_status qi_euler_update(float *x, const float *vel, float sigma_cur, float sigma_next,
+                          int64_t n, void *stream);
+
+/* ---------------------------------------------------------------- components */
+
+/* The shared modulation rows alone: mod [2][4H] (device fp32) = W_mod e(0) +
+ * b_mod and W_mod e(t) + b_mod ([PORT] DiT row).  Errors: NULL, RANGE, ALIGN,
+ * HIP. */
+qi_status qi_modulation(const qi_dims *d, const uint16_t *w_mod, const float *b_mod,
+                        float timestep, float *mod, void *stream);
+
+/* Block-causal attention alone ([PORT] DiT row; [MLX] "Text K/V reuse"), bf16:
+ *   q_txt [heads][L][128], k_txt [heads][L][128], vt_txt [heads][128][Lp]
+ *   q_img [heads][N][128], k_img [heads][N][128], vt_img [heads][128][Np]
+ * (Lp, Np = L, N rounded up to 64; vt holds V transposed) ->
+ *   o [rows][heads*128] bf16, rows = L + N (JOINT: text rows 0..L-1, image rows
+ *   L..) or N (IMAGE_ONLY: q_txt unused, may be NULL; image rows 0..N-1).
+ * Text row i attends causally to text keys 0..i; image rows attend to all L
+ * text keys then all N image keys; softmax in fp32 with scale 1/sqrt(128).
+ * Errors: NULL, RANGE (heads < 1, L < 1 or > 512, N < 1 or > 16384), ALIGN,
+ * HIP. */
+qi_status qi_block_causal_attention(int32_t heads, int32_t L, int32_t N, int32_t mode,
+                                    const uint16_t *q_txt, const uint16_t *k_txt,
+                                    const uint16_t *vt_txt, const uint16_t *q_img,
+                                    const uint16_t *k_img, const uint16_t *vt_img, uint16_t *o,
+                                    void *stream);
+
+/* The bf16 MFMA GEMM of the block projections, with an fp32 store epilogue:
+ * C [M][N] (device fp32) = A [M][K] W^T (+ bias [N] if non-NULL), A and W bf16
+ * (W in [N][K] layout).  M >= 1, N % 128 == 0, K % 64 == 0.  Errors: NULL,
+ * RANGE, ALIGN, HIP. */
+qi_status qi_linear_bf16(int32_t M, int32_t N, int32_t K, const uint16_t *A, const uint16_t *W,
+                         const float *bias, float *C, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QI_H_ */

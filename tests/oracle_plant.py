@@ -35,5 +35,7 @@ def step_with(**overrides):
     ns = dict(vars(dit))
     ns.update(overrides)
     for fn in (dit.dit_block, dit.dit_step):
+        if fn.__name__ in overrides:
+            continue
         exec(compile(textwrap.dedent(inspect.getsource(fn)), f"<planted {fn.__name__}>", "exec"), ns)
     return ns["dit_step"]

@@ -1,0 +1,210 @@
+"""GPU parity of the DiT block and step through the C ABI against the oracle,
+plus the exactness properties of text-K/V reuse on the GPU:
+
+  - one block (qi_dit_block_fwd), joint and image-only, against oracle.dit_block;
+  - the step (qi_dit_step) against oracle.dit_step: vel relative L2 <= 2e-2 and
+    minimum per-token correlation >= 0.999, no NaN/Inf;
+  - the cached image-only step equals the GPU's own full recompute bit for bit;
+  - captured text K/V are bit-identical across changed image tokens, t and N;
+  - repeated runs are bit-identical;
+  - planted oracle mistakes (negative controls) fail the bar against the GPU.
+
+Workloads: the reduced block (hidden 512, L 8, N 64) and the full-width block
+(hidden 4096, L 22, N 256), plus ragged variants of the reduced one."""
+import numpy as np
+import pytest
+
+import block_causal_attention_qi_amd as qi
+import qi_synth as qs
+from oracle import dit
+from tests.gpu_util import GpuWorkload, assert_bits_equal, bf16_vals, host, log, unpack_cache_block
+from tests.oracle_plant import planted, step_with
+
+pytestmark = pytest.mark.gpu
+
+REL_L2_BAR = 2e-2
+CORR_BAR = 0.999
+
+
+def _oracle_weights(wl, n_blocks):
+    sw = qs.weights_as_f32(qs.shared_weights(wl))
+    blocks = [qs.weights_as_f32(qs.block_weights(wl, b)) for b in range(n_blocks)]
+    return sw, blocks
+
+
+def _dev(a):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+@pytest.mark.parametrize("wl_id,L,h,w", [(1, 8, 8, 8), (1, 37, 9, 7), (2, 22, 16, 16)])
+def test_block_matches_oracle_joint_and_image_only(wl_id, L, h, w):
+    import torch
+    wl = qs.workload(wl_id, L=L, h=h, w=w)
+    log(f"block wl={wl_id} L={L} N={wl.N}")
+    H, T, N = wl.hidden, L + wl.N, wl.N
+    dims = qi.make_dims(H, wl.ffn, 1, wl.txt_dim)
+    bw_bits = qs.block_weights(wl, 0, as_bf16=True)
+    model = qi.DeviceModel(dims, qs.shared_weights(wl, as_bf16=True), [bw_bits])
+    bw = qs.weights_as_f32(bw_bits)
+    x0 = qs.normal_array((T, H), seed=21)
+    mod = qs.normal_array((2, 4 * H), seed=22, scale=0.5)
+    tc, ts, ic, is_ = qi.rope_tables(L, h, w)
+    cos, sin = np.concatenate([tc, ic]), np.concatenate([ts, is_])
+    ws = qi.Workspace(dims, L, N)
+    kv = torch.zeros(qi.kv_slot_elems(dims, L), dtype=torch.int16, device="cuda")
+    xd = _dev(x0)
+    qi.dit_block_fwd(dims, model.block_struct(0), L, N, qi.QI_MODE_JOINT, xd, _dev(mod), _dev(cos), _dev(sin),
+                     int(kv.data_ptr()), ws)
+    got = host(xd)
+    otc, ots, oic, ois = dit.rope_rows(L, h, w)
+    ref, (k_ref, v_ref) = dit.dit_block(x0.astype(np.float64), L, bw, mod[0], mod[1],
+                                        np.concatenate([otc, oic]), np.concatenate([ots, ois]), wl.heads)
+    assert np.all(np.isfinite(got))
+    d_rel = dit.rel_l2(got - x0, ref - x0)
+    log(f"  joint: x rel_l2={dit.rel_l2(got, ref):.3e} delta rel_l2={d_rel:.3e}")
+    assert d_rel < 1e-2
+    # captured text K/V against the oracle's
+    k_got, v_got = unpack_cache_block(host(kv), dims, L, 0)
+    assert dit.rel_l2(k_got, k_ref) < 1e-2 and dit.rel_l2(v_got, v_ref) < 1e-2
+    # image-only pass over the image rows with the captured K/V: bit-identical rows
+    xi = _dev(x0[L:])
+    qi.dit_block_fwd(dims, model.block_struct(0), L, N, qi.QI_MODE_IMAGE_ONLY, xi, _dev(mod), _dev(ic),
+                     _dev(is_), int(kv.data_ptr()), ws)
+    assert_bits_equal(host(xi), got[L:], "image-only block rows")
+
+
+def _check_bar(vel, ref, what):
+    assert np.all(np.isfinite(vel)), f"{what}: NaN/Inf in vel"
+    rel = dit.rel_l2(vel, ref)
+    corr = dit.min_token_corr(vel, ref)
+    log(f"  {what}: vel rel_l2={rel:.3e} min_token_corr={corr:.6f}")
+    assert rel <= REL_L2_BAR and corr >= CORR_BAR, (rel, corr)
+    return rel, corr
+
+
+def _oracle_step(wl, sw, blocks, t, img=None, txt=None, **kw):
+    tc, ts, ic, is_ = dit.rope_rows(wl.L, wl.h, wl.w)
+    img = qs.img_tokens(wl) if img is None else img
+    txt = qs.txt_feats(wl) if txt is None else txt
+    return dit.dit_step(sw, blocks, wl.L, img, txt, t, tc, ts, ic, is_, wl.heads, **kw)
+
+
+@pytest.mark.parametrize("wl_id,over", [(1, {}), (1, dict(L=37, h=9, w=7)), (1, dict(n_blocks=3)), (2, {})])
+def test_step_matches_oracle(wl_id, over):
+    wl = qs.workload(wl_id, **over)
+    log(f"step wl={wl_id} {over} L={wl.L} N={wl.N} blocks={wl.n_blocks}")
+    g = GpuWorkload(wl)
+    t = np.float32(wl.timestep)
+    vel = host(g.step(t))
+    sw, blocks = _oracle_weights(wl, wl.n_blocks)
+    ref = _oracle_step(wl, sw, blocks, t)
+    _check_bar(vel, ref, "joint step")
+
+
+@pytest.mark.parametrize("wl_id,over", [(1, {}), (1, dict(L=37, h=9, w=7, n_blocks=2)), (2, {})])
+def test_cached_step_bit_equals_full_recompute(wl_id, over):
+    import torch
+    wl = qs.workload(wl_id, **over)
+    log(f"reuse wl={wl_id} {over}")
+    g = GpuWorkload(wl)
+    cache = g.new_cache()
+    vel1 = host(g.capture(np.float32(0.9), cache)).copy()
+    assert cache.valid
+    # step 1 vel equals a plain joint step
+    assert_bits_equal(host(g.step(np.float32(0.9))), vel1, "capture vel vs joint vel")
+    # later step: new latent, new t
+    g.set_inputs(qs.img_tokens(wl, seed=77), None)
+    t2 = np.float32(0.41)
+    full = host(g.step(t2)).copy()
+    cached = host(g.step(t2, cache=cache)).copy()
+    assert_bits_equal(cached, full, "cached vs full")
+    # and both match the oracle's cached step
+    sw, blocks = _oracle_weights(wl, wl.n_blocks)
+    _, ocache = _oracle_step(wl, sw, blocks, np.float32(0.9), capture=True)
+    tc, ts, ic, is_ = dit.rope_rows(wl.L, wl.h, wl.w)
+    ref = dit.dit_step(sw, blocks, wl.L, qs.img_tokens(wl, seed=77), None, t2, tc, ts, ic, is_, wl.heads,
+                       kv_cache=ocache)
+    _check_bar(cached, ref, "cached step")
+
+
+def _cache_kv(cache_np, dims, L, n_blocks):
+    """The valid K and V of every block's slot (the V^T padding columns are
+    never read as values and are excluded)."""
+    return [unpack_cache_block(cache_np, dims, L, b) for b in range(n_blocks)]
+
+
+def test_text_kv_invariant_to_image_t_and_N():
+    wl = qs.workload(1, n_blocks=2)
+    log("text K/V invariance")
+    g = GpuWorkload(wl)
+    c1 = g.new_cache()
+    g.capture(np.float32(0.9), c1)
+    a = host(c1.buf).copy()
+    kv1 = _cache_kv(a, g.dims, wl.L, 2)
+    g.set_inputs(qs.img_tokens(wl, seed=3), None)
+    c2 = g.new_cache()
+    g.capture(np.float32(0.2), c2)
+    log("  changed image tokens and t")
+    for (k1, v1), (k2, v2) in zip(kv1, _cache_kv(host(c2.buf), g.dims, wl.L, 2)):
+        assert_bits_equal(k1, k2, "K"); assert_bits_equal(v1, v2, "V")
+    # another grid (N = 12 x 10 = 120): same text, same cache bits
+    wl2 = qs.workload(1, n_blocks=2, h=12, w=10)
+    g2 = GpuWorkload(wl2)
+    c3 = g2.new_cache()
+    g2.capture(np.float32(0.5), c3)
+    log("  changed N")
+    for (k1, v1), (k3, v3) in zip(kv1, _cache_kv(host(c3.buf), g2.dims, wl.L, 2)):
+        assert_bits_equal(k1, k3, "K"); assert_bits_equal(v1, v3, "V")
+    # and the cache holds the oracle's text K/V
+    sw, blocks = _oracle_weights(wl, 2)
+    _, ocache = _oracle_step(wl, sw, blocks, np.float32(0.9), capture=True)
+    for b in range(2):
+        k, v = kv1[b]
+        assert dit.rel_l2(k, ocache[b][0]) < 1e-2 and dit.rel_l2(v, ocache[b][1]) < 1e-2
+
+
+def test_runs_are_bit_reproducible():
+    wl = qs.workload(2)
+    g = GpuWorkload(wl)
+    outs = [host(g.step(np.float32(0.7))).copy() for _ in range(3)]
+    assert_bits_equal(outs[0], outs[1], "run 2")
+    assert_bits_equal(outs[0], outs[2], "run 3")
+
+
+def test_negative_controls_fail_the_bar():
+    """Each planted oracle mistake must put the GPU's vel outside the bar, so
+    the bar has the power to catch it.  Run on the full-width block: at hidden
+    512 with N(0, 0.02) weights the attention logits are nearly flat and
+    several of these mistakes move vel by less than the bar."""
+    wl = qs.workload(2)
+    g = GpuWorkload(wl)
+    t = np.float32(0.7)
+    vel = host(g.step(t)).copy()
+    sw, blocks = _oracle_weights(wl, 1)
+    controls = {
+        "rotate-half RoPE": step_with(rope_apply=lambda x, c, s: np.concatenate(
+            [x[..., :64] * c[:, None] - x[..., 64:] * s[:, None],
+             x[..., :64] * s[:, None] + x[..., 64:] * c[:, None]], axis=-1)),
+        "text rows with mod(t)": step_with(dit_block=planted(
+            dit.dit_block, "mt, mi = split_mod(m_txt.astype(dt), H), split_mod(m_img.astype(dt), H)",
+            "mt, mi = split_mod(m_img.astype(dt), H), split_mod(m_img.astype(dt), H)")),
+        "scale instead of 1+scale": step_with(dit_block=planted(dit.dit_block, "(1.0 + s1)", "s1")),
+        "image rows causal": step_with(block_causal_attention=planted(
+            dit.block_causal_attention, "o_img = sdpa(q_img, k_all, v_all, causal=False)",
+            "o_img = sdpa(q_img, k_img, v_img, causal=True)")),
+    }
+    tc, ts, ic, is_ = dit.rope_rows(wl.L, wl.h, wl.w)
+    # swapped axis order of the RoPE rows (height/width axes before frame)
+    perm = np.r_[8:36, 36:64, 0:8]
+    ctl_rows = {"RoPE axes reordered": (tc[:, perm], ts[:, perm], ic[:, perm], is_[:, perm])}
+    fails = {}
+    for name, step in controls.items():
+        ref = step(sw, blocks, wl.L, qs.img_tokens(wl), qs.txt_feats(wl), t, tc, ts, ic, is_, wl.heads)
+        fails[name] = (dit.rel_l2(vel, ref), dit.min_token_corr(vel, ref))
+    for name, rows in ctl_rows.items():
+        ref = dit.dit_step(sw, blocks, wl.L, qs.img_tokens(wl), qs.txt_feats(wl), t, *rows, wl.heads)
+        fails[name] = (dit.rel_l2(vel, ref), dit.min_token_corr(vel, ref))
+    for name, (rel, corr) in fails.items():
+        log(f"  control {name}: rel_l2={rel:.3e} corr={corr:.5f}")
+        assert rel > REL_L2_BAR or corr < CORR_BAR, name

@@ -1,0 +1,55 @@
+"""Power of the parity bar, on the CPU: each planted mistake moves the
+oracle's vel on the full-width block (hidden 4096, L 22, N 256) by more than
+twice the 2e-2 relative-L2 bar, so a GPU result within the bar cannot carry
+any of them.  On the reduced block (hidden 512) several of them stay inside
+the bar (flat attention logits with N(0, 0.02) weights); that is recorded
+here too, so the GPU negative controls run on the full-width block."""
+import numpy as np
+import pytest
+
+import qi_synth as qs
+from oracle import dit
+from tests.oracle_plant import planted, step_with
+
+BAR = 2e-2
+
+
+def _controls():
+    return {
+        "rotate-half RoPE": step_with(rope_apply=lambda x, c, s: np.concatenate(
+            [x[..., :64] * c[:, None] - x[..., 64:] * s[:, None],
+             x[..., :64] * s[:, None] + x[..., 64:] * c[:, None]], axis=-1)),
+        "text rows with mod(t)": step_with(dit_block=planted(
+            dit.dit_block, "mt, mi = split_mod(m_txt.astype(dt), H), split_mod(m_img.astype(dt), H)",
+            "mt, mi = split_mod(m_img.astype(dt), H), split_mod(m_img.astype(dt), H)")),
+        "scale instead of 1+scale": step_with(dit_block=planted(dit.dit_block, "(1.0 + s1)", "s1")),
+        "image rows causal": step_with(block_causal_attention=planted(
+            dit.block_causal_attention, "o_img = sdpa(q_img, k_all, v_all, causal=False)",
+            "o_img = sdpa(q_img, k_img, v_img, causal=True)")),
+    }
+
+
+def _moves(wl):
+    sw = qs.weights_as_f32(qs.shared_weights(wl, threads=8))
+    blocks = [qs.weights_as_f32(qs.block_weights(wl, b, threads=8)) for b in range(wl.n_blocks)]
+    tc, ts, ic, is_ = dit.rope_rows(wl.L, wl.h, wl.w)
+    args = (sw, blocks, wl.L, qs.img_tokens(wl), qs.txt_feats(wl), np.float32(0.7))
+    base = dit.dit_step(*args, tc, ts, ic, is_, wl.heads, dtype=np.float32)
+    out = {}
+    for name, step in _controls().items():
+        out[name] = dit.rel_l2(step(*args, tc, ts, ic, is_, wl.heads, dtype=np.float32), base)
+    perm = np.r_[8:36, 36:64, 0:8]
+    out["RoPE axes reordered"] = dit.rel_l2(
+        dit.dit_step(*args, tc[:, perm], ts[:, perm], ic[:, perm], is_[:, perm], wl.heads, dtype=np.float32), base)
+    return out
+
+
+def test_controls_leave_the_bar_on_the_full_width_block():
+    for name, rel in _moves(qs.workload(2)).items():
+        assert rel > 2 * BAR, (name, rel)
+
+
+def test_reduced_block_is_too_flat_for_some_controls():
+    moves = _moves(qs.workload(1, n_blocks=2))
+    assert moves["image rows causal"] > 2 * BAR
+    assert min(moves.values()) < BAR     # the reason the GPU controls use the full-width block
