@@ -1,0 +1,231 @@
+"""Throughput of the DiT denoising loop on one MI355X.
+
+    python bench.py [--gpus 1] [--steps 40] [--warmup 3] [--workload 4]
+
+Workload (default): the full 32-block DiT at 1024^2 -- hidden 4096, 32 heads x
+128, SwiGLU 12288, L = 407 text tokens, N = 4096 image tokens (64 x 64),
+bf16 random-init weights, seeded synthetic inputs.  One step is one pass of
+the whole hot path: modulation rows, embed, 32 blocks, head and the fp32
+Euler update.  The timed region is a denoising loop of --steps steps: step 1
+is the joint pass that captures the text K/V, later steps run the image rows
+only against the cache (exact text-K/V reuse), each followed by the Euler
+update, with the FlowMatch schedule of the workload.  Inputs and weights are
+resident in HBM before the timed region starts.
+
+Printed: one JSON line with steps/s (whole job), the per-kernel durations of
+the image-only steps measured with HIP events on the launch stream, the
+roofline fraction of the dominant kernel, and the CPU oracle's throughput on
+a bounded sample (one image-only block, scaled to a step)."""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "DiT steps/sec (32 blocks, bf16) at 1024² L=407; attn+GEMM MFMA util"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=40)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--workload", type=int, default=4)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--threads", type=int, default=16, help="host threads for weight generation")
+    return p.parse_args()
+
+
+def cpu_baseline(wl):
+    """The oracle as it stands (numpy, float64), one image-only block of the
+    workload (text K/V of the right shape from the seeded generator), timed
+    with perf_counter and scaled to one step of n_blocks blocks."""
+    import qi_synth as qs
+    from oracle import dit
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count()
+    bw = qs.weights_as_f32(qs.block_weights(wl, 0, threads=8))
+    H, N, L = wl.hidden, wl.N, wl.L
+    x = qs.normal_array((N, H), seed=31).astype(np.float64)
+    mod = qs.normal_array((2, 4 * H), seed=32, scale=0.5).astype(np.float64)
+    k_txt = qs.normal_array((wl.heads, L, 128), seed=33).astype(np.float64)
+    v_txt = qs.normal_array((wl.heads, L, 128), seed=34).astype(np.float64)
+    _, _, ic, is_ = dit.rope_rows(L, wl.h, wl.w)
+    t0 = time.perf_counter()
+    dit.dit_block(x, 0, bw, mod[0], mod[1], ic, is_, wl.heads, kv_text=(k_txt, v_txt))
+    dt = time.perf_counter() - t0
+    step_s = dt * wl.n_blocks
+    return {"value": 1.0 / step_s, "unit": "steps/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"1 of {wl.n_blocks} blocks, image-only pass (T={N}, L={L} cached), float64 numpy; "
+                      f"{dt:.2f} s per block scaled x{wl.n_blocks}"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (the DiT step here is built and measured on one MI355X); "
+              f"--gpus {args.gpus} is not supported", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import block_causal_attention_qi_amd as qi
+    import qi_synth as qs
+    from block_causal_attention_qi_amd import flops
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = "cuda"
+    wl = qs.workload(args.workload)
+    H, N, L, nb = wl.hidden, wl.N, wl.L, wl.n_blocks
+    dims = qi.make_dims(H, wl.ffn, nb, wl.txt_dim)
+    t0 = time.time()
+    log(f"generating {nb} blocks of bf16 weights ({wl.name})")
+    import concurrent.futures as cf
+    with cf.ThreadPoolExecutor(args.threads) as ex:
+        blocks = ex.map(lambda b: qs.block_weights(wl, b, as_bf16=True, threads=1), range(nb))
+        model = qi.DeviceModel(dims, qs.shared_weights(wl, as_bf16=True), blocks, dev)
+    log(f"weights on device in {time.time() - t0:.1f} s")
+
+    x0 = torch.from_numpy(qs.img_tokens(wl)).to(dev)
+    txt = torch.from_numpy(qs.txt_feats(wl)).to(dev)
+    rope = [torch.from_numpy(a).to(dev) for a in qi.rope_tables(L, wl.h, wl.w)]
+    sig, ts = qi.flow_sigmas(40, N)
+    tin = [np.float32(ts[i]) / np.float32(1000) for i in range(40)]
+    ws = qi.Workspace(dims, L, N, dev)
+    cache = qi.KVCache(dims, L, dev)
+    vel = torch.empty((N, 64), dtype=torch.float32, device=dev)
+    x = torch.empty_like(x0)
+
+    def step(i):
+        k = i % 40
+        if k == 0:
+            qi.text_kv_capture(model, L, N, x, txt, tin[k], *rope, cache, vel, ws)
+        else:
+            qi.dit_step(model, L, N, x, None, tin[k], None, None, rope[2], rope[3], vel, ws, cache)
+        qi.euler_update(x, vel, sig[k], sig[k + 1])
+
+    def loop(K):
+        x.copy_(x0)
+        for i in range(K):
+            step(i)
+
+    log(f"warmup {args.warmup} steps")
+    loop(args.warmup)
+    torch.cuda.synchronize()
+
+    # ---- timed region: K steps of the denoising loop
+    K = args.steps
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    loop(K)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t_start
+    value = K / elapsed
+    log(f"timed {K} steps: {elapsed * 1e3:.1f} ms -> {value:.3f} steps/s")
+    if not torch.isfinite(vel).all():
+        raise RuntimeError("non-finite vel in the timed loop")
+
+    # ---- per-kernel durations over image-only steps (events on the launch stream)
+    x.copy_(x0)
+    step(0)
+    n_img = max(3, min(K - 1, 10))
+    qi.timing_begin(4096 * 4)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    for i in range(1, 1 + n_img):
+        step(i)
+    ev1.record()
+    timing = qi.timing_end()
+    img_step_ms = ev0.elapsed_time(ev1) / n_img
+    # joint step alone
+    x.copy_(x0)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    step(0)
+    e1.record()
+    torch.cuda.synchronize()
+    joint_step_ms = e0.elapsed_time(e1)
+
+    shape = flops.Shape(H, wl.ffn, L, N, nb, wl.txt_dim, joint=False)
+    work = flops.kernel_work(shape)
+    kernels = {}
+    for kind, (ms, cnt) in timing.items():
+        if cnt == 0:
+            continue
+        avg_ms = ms / cnt
+        f, b = work.get(kind, (0, 0))
+        ent = {"launches": cnt, "avg_us": round(avg_ms * 1e3, 2), "ms_per_step": round(ms / n_img, 3)}
+        if f and kind.startswith(("gemm", "attention")):
+            tf = f / (avg_ms * 1e-3) / 1e12
+            ent.update(tflops=round(tf, 1), frac_bf16_peak=round(tf / flops.PEAK_BF16_TFLOPS, 4))
+        elif b:
+            gbs = b / (avg_ms * 1e-3) / 1e9
+            ent.update(gbs=round(gbs, 1), frac_hbm_peak=round(gbs / flops.PEAK_HBM_GBS, 4))
+        kernels[kind] = ent
+    dom = max(kernels, key=lambda k: kernels[k]["ms_per_step"])
+    dms = timing[dom][0] / timing[dom][1]
+    df, db = work[dom]
+    if df and dom.startswith(("gemm", "attention")):
+        ach = df / (dms * 1e-3) / 1e12
+        roof = {"kernel": dom, "bound": "mfma", "achieved": round(ach, 1), "peak": flops.PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(ach / flops.PEAK_BF16_TFLOPS, 4), "traffic": None,
+                "flops_per_launch": df, "avg_launch_us": round(dms * 1e3, 2)}
+    else:
+        ach = db / (dms * 1e-3) / 1e9
+        roof = {"kernel": dom, "bound": "hbm", "achieved": round(ach, 1), "peak": flops.PEAK_HBM_GBS,
+                "unit": "GB/s", "frac": round(ach / flops.PEAK_HBM_GBS, 4), "traffic": None,
+                "bytes_per_launch": db, "avg_launch_us": round(dms * 1e3, 2)}
+    gemm_ms = sum(timing[k][0] for k in timing if k.startswith("gemm")) / n_img
+    gemm_f = sum(work[k][0] * timing[k][1] for k in work if k.startswith("gemm") and k in timing) / n_img
+    attn_ms = timing["attention"][0] / n_img
+    step_f = flops.step_flops(shape)
+    cpu = None if args.no_cpu_baseline else cpu_baseline(wl)
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 4),
+        "unit": "steps/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(elapsed * 1e3 / K, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded random-init weights and inputs)",
+        "config": {"workload": wl.name, "hidden": H, "heads": wl.heads, "ffn": wl.ffn, "blocks": nb,
+                   "L": L, "N": N, "grid": f"{wl.h}x{wl.w}", "loop": "step 1 joint + capture, then image-only "
+                   "steps on cached text K/V, fp32 Euler update each step", "parallelism": "single GPU"},
+        "image_only_step_ms": round(img_step_ms, 3),
+        "joint_step_ms": round(joint_step_ms, 3),
+        "ms_per_block_image_only": round(img_step_ms / nb, 4),
+        "step_tflops_image_only": round(step_f / (img_step_ms * 1e-3) / 1e12, 1),
+        "gemm_tflops": round(gemm_f / (gemm_ms * 1e-3) / 1e12, 1),
+        "gemm_mfma_frac": round(gemm_f / (gemm_ms * 1e-3) / 1e12 / flops.PEAK_BF16_TFLOPS, 4),
+        "attention_tflops": round(work["attention"][0] * nb / (attn_ms * 1e-3) / 1e12, 1),
+        "attention_mfma_frac": round(work["attention"][0] * nb / (attn_ms * 1e-3) / 1e12 / flops.PEAK_BF16_TFLOPS, 4),
+        "kernels": kernels,
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

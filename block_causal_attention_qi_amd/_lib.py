@@ -71,7 +71,11 @@ SIGNATURES = {
                                             c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p]),
     "qi_linear_bf16": (c_int32, [c_int32, c_int32, c_int32, c_void_p, c_void_p, c_void_p, c_void_p,
                                  c_void_p]),
+    "qi_kernel_kind_name": (c_char_p, [c_int32]),
+    "qi_timing_begin": (c_int32, [c_int32]),
+    "qi_timing_end": (c_int32, [c_void_p, c_void_p, c_void_p]),
 }
+QI_KERNEL_KINDS = 12
 
 _lib = None
 

@@ -9,17 +9,19 @@
 //              [heads][128][Tp] buffers (text rows -> text K/V, which is the
 //              cache slot on a capture pass).
 //
-// The MFMA is issued "transposed": its A operand is a 16-row slice of W
-// (output features) and its B operand a 16-row slice of the activations
-// (tokens), so each lane ends up holding 4 CONSECUTIVE output features of one
-// token.  That puts every RoPE pair (2k, 2k+1) and every float4 residual
-// update inside one lane.
+// The MFMA (32x32x16 bf16, the full-rate shape on gfx950) is issued
+// "transposed": its A operand is a 32-row slice of W (output features) and its
+// B operand a 32-row slice of the activations (tokens), so each lane ends up
+// holding groups of 4 CONSECUTIVE output features of one token.  That puts
+// every RoPE pair (2k, 2k+1) and every float4 residual update inside one lane.
 //
 // Row-count invariance (the MLX page's row-count hazard in "Text K/V reuse"):
 // every output element is produced by the same MFMA instruction over the same
 // K order whatever M is and wherever the row sits in its tile, so a row's
 // result does not depend on how many rows the pass has.  No split-K, no atomics.
 #pragma once
+
+#include <type_traits>
 
 #include "common.hpp"
 
@@ -54,158 +56,347 @@ struct GemmArgs {
 };
 
 namespace gemm {
-constexpr int BM = 128;  // tokens per tile
-constexpr int BN = 128;  // W rows per tile
 constexpr int BK = 64;
-constexpr int THREADS = 256;
+constexpr int THREADS = 256;  // 4 waves as 2 x 2; each owns (BM/2) tokens x (BN/2) W rows
 }  // namespace gemm
 
-// LDS tile: rows of 64 bf16 = 8 chunks of 16 bytes; chunk c of row r is stored
-// at slot c ^ (r & 7), so the 16 rows an MFMA operand read touches at one
-// chunk index fall on 8 distinct 16-byte bank groups.
-QI_DEV int lds_slot(int r, int c) { return r * 8 + (c ^ (r & 7)); }
+// LDS tile: rows of 64 bf16 = 8 chunks of 16 bytes.  gfx950's LDS has 64
+// banks (256 bytes), so two consecutive rows share one bank line and a
+// ds_read_b128 serves 16 lanes per pass.  Chunk c of row r is stored at slot
+// c ^ ((r >> 1) & 7): the 16 consecutive rows one pass reads at a fixed chunk
+// index land on 16 distinct 16-byte bank groups, and so do the two rows one
+// pass of the tile writes.
+QI_DEV int lds_slot(int r, int c) { return r * 8 + (c ^ ((r >> 1) & 7)); }
 
+// Workgroup -> output tile.  Workgroups are handed to the 8 XCDs round-robin
+// (id % 8), each XCD with its own L2.  When the W-tile columns split evenly
+// over the XCDs, XCD x owns a contiguous band of W columns (so a W tile is
+// fetched into one L2 only) and walks it in groups of 4 token tiles, columns
+// fastest, so the tiles that run together share both operands' K slices.
+QI_DEV void tile_of(int bid, int nTM, int nTN, int &tm, int &tn) {
+  if (nTN % 8 == 0) {
+    constexpr int GM = 4;
+    const int xcd = bid & 7, j = bid >> 3;
+    const int nTNx = nTN >> 3;
+    const int g = j / (GM * nTNx), w = j % (GM * nTNx);
+    const int rows = min(GM, nTM - g * GM);
+    tm = g * GM + w % rows;
+    tn = xcd * nTNx + w / rows;
+  } else {
+    tm = bid % nTM;
+    tn = bid / nTM;
+  }
+}
+
+// ---------------------------------------------------------------- epilogue
+// The 4 consecutive outputs n..n+3 of token m (accumulators v).
 template <int EPI>
-__global__ __launch_bounds__(gemm::THREADS, 2) void gemm_bf16_kernel(const GemmArgs g) {
+QI_DEV void store4(const GemmArgs &g, int m, int n, f32x4 v) {
+  if constexpr (EPI == EPI_F32) {
+    f32x4 o = v;
+    if (g.bias) o += *(const f32x4 *)(g.bias + n);
+    *(f32x4 *)(g.C + (size_t)m * g.ldc + n) = o;
+  } else if constexpr (EPI == EPI_RESID) {
+    const float *gp = g.gate + (m < g.L_rows ? 0 : g.gate_img_off) + n;
+    f32x4 *xp = (f32x4 *)(g.X + (size_t)m * g.ldx + n);
+    *xp = *xp + *(const f32x4 *)gp * v;
+  } else if constexpr (EPI == EPI_QKV) {
+    const int sec = n / g.H;
+    const int w = n - sec * g.H;
+    const int head = w >> 7, dh = w & 127;
+    const bool txt = m < g.L_rows;
+    const int row = txt ? m : m - g.L_rows;
+    if (sec < 2) {
+      const float *cp = (txt ? g.cos_t : g.cos_i) + (size_t)row * 64 + (dh >> 1);
+      const float *sp = (txt ? g.sin_t : g.sin_i) + (size_t)row * 64 + (dh >> 1);
+      const float c0 = cp[0], c1 = cp[1], s0 = sp[0], s1 = sp[1];
+      const float y0 = v[0] * c0 - v[1] * s0, y1 = v[0] * s0 + v[1] * c0;
+      const float y2 = v[2] * c1 - v[3] * s1, y3 = v[2] * s1 + v[3] * c1;
+      u16 *dst = sec == 0 ? (txt ? g.q_t : g.q_i) : (txt ? g.k_t : g.k_i);
+      const int seg = txt ? g.seg_t : g.seg_i;
+      *(u32x2 *)(dst + ((size_t)head * seg + row) * 128 + dh) = u32x2{pack_bf16x2(y0, y1), pack_bf16x2(y2, y3)};
+    } else {
+      u16 *vt = txt ? g.vt_t : g.vt_i;
+      const int ldv = txt ? g.ldv_t : g.ldv_i;
+      u16 *base = vt + ((size_t)head * 128 + dh) * ldv + row;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) base[(size_t)r * ldv] = f32_to_bf16(v[r]);
+    }
+  }
+}
+
+// SwiGLU outputs o..o+3 of token m from the gate and up accumulators.
+QI_DEV void store4_swiglu(const GemmArgs &g, int m, int o, f32x4 gt, f32x4 up) {
+  float y[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) y[r] = gt[r] / (1.f + __expf(-gt[r])) * up[r];
+  *(u32x2 *)(g.out + (size_t)m * g.ldo + o) = u32x2{pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3])};
+}
+
+QI_DEV f32x4 quad(const f32x16 &a, int j) { return f32x4{a[4 * j], a[4 * j + 1], a[4 * j + 2], a[4 * j + 3]}; }
+
+template <int EPI, int BM, int BN>
+__global__ __launch_bounds__(gemm::THREADS, (BM * BN >= 256 * 256) ? 1 : 2) void gemm_bf16_kernel(const GemmArgs g) {
   using namespace gemm;
+  constexpr int WT = BM / 2, WF = BN / 2;    // per-wave tokens, W rows
+  constexpr int TS = WT / 32, FS = WF / 32;  // 32-row subtiles per wave
+  constexpr int CA = BM * 8 / THREADS, CW = BN * 8 / THREADS;  // 16-byte chunks per thread
+  static_assert(FS % 2 == 0, "SwiGLU pairs gate/up subtiles inside a wave");
   __shared__ u32x4 sA[2][BM * 8];
   __shared__ u32x4 sW[2][BN * 8];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave & 1, wn = wave >> 1;  // 2 x 2 waves; each 64 tokens x 64 W rows
-  const int m0 = blockIdx.x * BM;
-  const int tn = blockIdx.y;
+  const int wm = wave & 1, wn = wave >> 1;
+  const int nTM = (g.M + BM - 1) / BM;
+  const int nTN = (EPI == EPI_SWIGLU ? g.F / (BN / 2) : g.N / BN);
+  int tm, tn;
+  tile_of(blockIdx.x, nTM, nTN, tm, tn);
+  const int m0 = tm * BM;
 
-  const u16 *pa[4], *pw[4];
-  int slot[4];
+  const u16 *pa[CA], *pw[CW];
+  int slot_a[CA], slot_w[CW];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
+  for (int j = 0; j < CA; ++j) {
     const int i = tid + THREADS * j;
     const int row = i >> 3, c = i & 7;
-    slot[j] = lds_slot(row, c);
+    slot_a[j] = lds_slot(row, c);
     const int am = min(m0 + row, g.M - 1);  // rows past M load a valid row; never stored
     pa[j] = g.A + (size_t)am * g.lda + c * 8;
+  }
+#pragma unroll
+  for (int j = 0; j < CW; ++j) {
+    const int i = tid + THREADS * j;
+    const int row = i >> 3, c = i & 7;
+    slot_w[j] = lds_slot(row, c);
     int wr;
     if constexpr (EPI == EPI_SWIGLU) {
-      // 16-row slices alternate gate / up for the same 16 outputs
-      const int s = row >> 4;
-      wr = tn * (BN / 2) + (s >> 1) * 16 + (row & 15) + (s & 1) * g.F;
+      // 32-row slices alternate gate / up for the same 32 outputs
+      const int s = row >> 5;
+      wr = tn * (BN / 2) + (s >> 1) * 32 + (row & 31) + (s & 1) * g.F;
     } else {
       wr = tn * BN + row;
     }
     pw[j] = g.W + (size_t)wr * g.ldw + c * 8;
   }
 
-  f32x4 acc[4][4];
+  f32x16 acc[FS][TS];
 #pragma unroll
-  for (int a = 0; a < 4; ++a)
+  for (int a = 0; a < FS; ++a)
 #pragma unroll
-    for (int b = 0; b < 4; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int b = 0; b < TS; ++b)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[a][b][e] = 0.f;
 
-  u32x4 ra[4], rw[4];
+  // Two register stages in flight: the K slice used at step kt+2 is fetched
+  // from global memory at step kt and written to LDS at the end of step kt+1,
+  // so its latency is covered by two steps of MFMA work (the K loop is
+  // unrolled by two to keep the stage registers static).
+  u32x4 ra[2][CA], rw[2][CW];
   const int nk = g.K / BK;
 
+  auto gload = [&](int st, int kt) {
+    const int k0 = kt * BK;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    ra[j] = *(const u32x4 *)(pa[j]);
-    rw[j] = *(const u32x4 *)(pw[j]);
-  }
+    for (int j = 0; j < CA; ++j) ra[st][j] = *(const u32x4 *)(pa[j] + k0);
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    sA[0][slot[j]] = ra[j];
-    sW[0][slot[j]] = rw[j];
-  }
-  __syncthreads();
-
-  for (int kt = 0; kt < nk; ++kt) {
-    const int b = kt & 1;
-    const bool more = kt + 1 < nk;
-    if (more) {
-      const int k0 = (kt + 1) * BK;
+    for (int j = 0; j < CW; ++j) rw[st][j] = *(const u32x4 *)(pw[j] + k0);
+  };
+  auto lstore = [&](int st, int b) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        ra[j] = *(const u32x4 *)(pa[j] + k0);
-        rw[j] = *(const u32x4 *)(pw[j] + k0);
-      }
+    for (int j = 0; j < CA; ++j) sA[b][slot_a[j]] = ra[st][j];
+#pragma unroll
+    for (int j = 0; j < CW; ++j) sW[b][slot_w[j]] = rw[st][j];
+  };
+  auto compute = [&](int b) {
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      const int ch = kk * 2 + (lane >> 5);
+      u32x4 af[FS], bt[TS];
+#pragma unroll
+      for (int f = 0; f < FS; ++f) af[f] = sW[b][lds_slot(wn * WF + f * 32 + (lane & 31), ch)];
+#pragma unroll
+      for (int t = 0; t < TS; ++t) bt[t] = sA[b][lds_slot(wm * WT + t * 32 + (lane & 31), ch)];
+#pragma unroll
+      for (int f = 0; f < FS; ++f)
+#pragma unroll
+        for (int t = 0; t < TS; ++t) acc[f][t] = mfma32x32x16(af[f], bt[t], acc[f][t]);
     }
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      const int ch = kk * 4 + (lane >> 4);
-      u32x4 af[4], bt[4];
-#pragma unroll
-      for (int f = 0; f < 4; ++f) af[f] = sW[b][lds_slot(wn * 64 + f * 16 + (lane & 15), ch)];
-#pragma unroll
-      for (int t = 0; t < 4; ++t) bt[t] = sA[b][lds_slot(wm * 64 + t * 16 + (lane & 15), ch)];
-#pragma unroll
-      for (int f = 0; f < 4; ++f)
-#pragma unroll
-        for (int t = 0; t < 4; ++t) acc[f][t] = mfma16x16x32(af[f], bt[t], acc[f][t]);
-    }
-    if (more) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        sA[b ^ 1][slot[j]] = ra[j];
-        sW[b ^ 1][slot[j]] = rw[j];
-      }
-    }
+  };
+  // step kt: stage kt sits in LDS buffer (kt & 1); register set (kt & 1) is
+  // free, register set ((kt + 1) & 1) holds slice kt+1 in flight.
+  auto step = [&](int kt, auto par) {
+    constexpr int P = decltype(par)::value;
+    if (kt + 2 < nk) gload(P, kt + 2);
+    compute(P);
+    if (kt + 1 < nk) lstore(P ^ 1, P ^ 1);
     __syncthreads();
+  };
+
+  gload(0, 0);
+  if (nk > 1) gload(1, 1);
+  lstore(0, 0);
+  __syncthreads();
+  for (int kt = 0; kt < nk; kt += 2) {
+    step(kt, std::integral_constant<int, 0>{});
+    if (kt + 1 < nk) step(kt + 1, std::integral_constant<int, 1>{});
   }
 
-  // ---------------------------------------------------------------- epilogue
-  const int g4 = 4 * (lane >> 4);
+  // lane holds, for each (f, t) subtile and j = 0..3, the 4 consecutive
+  // W rows f*32 + 8j + 4*(lane/32) + 0..3 of token t*32 + lane%32
+  const int h4 = 4 * (lane >> 5);
 #pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    const int m = m0 + wm * 64 + t * 16 + (lane & 15);
+  for (int t = 0; t < TS; ++t) {
+    const int m = m0 + wm * WT + t * 32 + (lane & 31);
     if (m >= g.M) continue;
     if constexpr (EPI == EPI_SWIGLU) {
 #pragma unroll
-      for (int p = 0; p < 2; ++p) {
-        const f32x4 gt = acc[2 * p][t], up = acc[2 * p + 1][t];
-        const int o = tn * (BN / 2) + wn * 32 + p * 16 + g4;
-        float y[4];
+      for (int p = 0; p < FS / 2; ++p)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) y[r] = gt[r] / (1.f + __expf(-gt[r])) * up[r];
-        u32x2 pk = {pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3])};
-        *(u32x2 *)(g.out + (size_t)m * g.ldo + o) = pk;
-      }
+        for (int j = 0; j < 4; ++j)
+          store4_swiglu(g, m, tn * (BN / 2) + wn * (WF / 2) + p * 32 + 8 * j + h4, quad(acc[2 * p][t], j),
+                        quad(acc[2 * p + 1][t], j));
     } else {
 #pragma unroll
-      for (int f = 0; f < 4; ++f) {
-        const int n = tn * BN + wn * 64 + f * 16 + g4;
-        const f32x4 v = acc[f][t];
-        if constexpr (EPI == EPI_F32) {
-          f32x4 o = v;
-          if (g.bias) o += *(const f32x4 *)(g.bias + n);
-          *(f32x4 *)(g.C + (size_t)m * g.ldc + n) = o;
-        } else if constexpr (EPI == EPI_RESID) {
-          const float *gp = g.gate + (m < g.L_rows ? 0 : g.gate_img_off) + n;
-          f32x4 *xp = (f32x4 *)(g.X + (size_t)m * g.ldx + n);
-          *xp = *xp + *(const f32x4 *)gp * v;
-        } else {  // EPI_QKV
-          const int sec = n / g.H;
-          const int w = n - sec * g.H;
-          const int head = w >> 7, dh = w & 127;
-          const bool txt = m < g.L_rows;
-          const int row = txt ? m : m - g.L_rows;
-          if (sec < 2) {
-            const float *cp = (txt ? g.cos_t : g.cos_i) + (size_t)row * 64 + (dh >> 1);
-            const float *sp = (txt ? g.sin_t : g.sin_i) + (size_t)row * 64 + (dh >> 1);
-            const float c0 = cp[0], c1 = cp[1], s0 = sp[0], s1 = sp[1];
-            const float y0 = v[0] * c0 - v[1] * s0, y1 = v[0] * s0 + v[1] * c0;
-            const float y2 = v[2] * c1 - v[3] * s1, y3 = v[2] * s1 + v[3] * c1;
-            u16 *dst = sec == 0 ? (txt ? g.q_t : g.q_i) : (txt ? g.k_t : g.k_i);
-            const int seg = txt ? g.seg_t : g.seg_i;
-            u32x2 pk = {pack_bf16x2(y0, y1), pack_bf16x2(y2, y3)};
-            *(u32x2 *)(dst + ((size_t)head * seg + row) * 128 + dh) = pk;
-          } else {
-            u16 *vt = txt ? g.vt_t : g.vt_i;
-            const int ldv = txt ? g.ldv_t : g.ldv_i;
-            u16 *base = vt + ((size_t)head * 128 + dh) * ldv + row;
+      for (int f = 0; f < FS; ++f)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) base[(size_t)r * ldv] = f32_to_bf16(v[r]);
-          }
-        }
-      }
+        for (int j = 0; j < 4; ++j) store4<EPI>(g, m, tn * BN + wn * WF + f * 32 + 8 * j + h4, quad(acc[f][t], j));
+    }
+  }
+}
+
+// ---------------------------------------------------------------- 256 x 256 tiles
+// Large-M shape: one 256 x 256 tile per workgroup of WMN x WNN waves (wave
+// tile (256/WMN) tokens x (256/WNN) W rows, MFMA 32x32x16), one workgroup per
+// CU.  A 256-row operand tile costs 4x fewer fetched bytes per FLOP than the
+// 128 x 128 tile.  Operands come in through buffer loads (32-bit VGPR offset
+// + per-chunk SGPR offset; rows past M read as zero), are staged in registers
+// during one K step and written into the second LDS buffer; MFMA fragments
+// are read one 16-deep step ahead into a second register set.  With 8 waves
+// each SIMD holds two, so one wave's LDS and barrier waits overlap the
+// other's MFMAs.
+namespace gemmL {
+constexpr int BM = 256, BN = 256, BK = 64;
+constexpr int RSRC_FLAGS = 0x00020000;  // raw buffer, 32-bit dwords
+}  // namespace gemmL
+
+template <int EPI, int WMN, int WNN>
+__global__ __launch_bounds__(64 * WMN * WNN, 1) void gemm_bf16_large_kernel(const GemmArgs g) {
+  using namespace gemmL;
+  constexpr int THREADS = 64 * WMN * WNN;
+  constexpr int WT = BM / WMN, WF = BN / WNN;  // wave tile
+  constexpr int TS = WT / 32, FS = WF / 32;
+  constexpr int RPP = THREADS / 8;             // rows per fetch pass
+  constexpr int NJ = BM / RPP;                 // fetch passes per operand
+  static_assert(FS % 2 == 0, "SwiGLU pairs gate/up slices inside a wave");
+  static_assert(RPP % 32 == 0, "fetch pass covers whole 32-row slices");
+  static_assert(EPI != EPI_SWIGLU || RPP % 64 == 0, "SwiGLU fetch pass covers whole gate/up slice pairs");
+  __shared__ u32x4 sA[2][BM * 8];
+  __shared__ u32x4 sW[2][BN * 8];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave % WMN, wn = wave / WMN;
+  const int nTM = (g.M + BM - 1) / BM;
+  const int nTN = EPI == EPI_SWIGLU ? g.F / (BN / 2) : g.N / BN;
+  int tm, tn;
+  tile_of(blockIdx.x, nTM, nTN, tm, tn);
+  const int m0 = tm * BM;
+
+  // operand fetch: thread t moves chunk (t & 7) of rows (t >> 3) + RPP j
+  const int lrow = tid >> 3, lc = tid & 7;
+  const __amdgpu_buffer_rsrc_t ra =
+      __builtin_amdgcn_make_buffer_rsrc((void *)g.A, (short)0, (int)((size_t)g.M * g.lda * 2), RSRC_FLAGS);
+  const int wrows = EPI == EPI_SWIGLU ? 2 * g.F : g.N;
+  const __amdgpu_buffer_rsrc_t rw =
+      __builtin_amdgcn_make_buffer_rsrc((void *)g.W, (short)0, (int)((size_t)wrows * g.ldw * 2), RSRC_FLAGS);
+  const int voff_a = ((m0 + lrow) * g.lda + lc * 8) * 2;
+  // SwiGLU: W tile rows alternate 32-row gate / up slices for the same 32
+  // outputs, i.e. tile row r reads W row tn*128 + (r>>6)*32 + (r&31) (+F when
+  // bit 5 of r is set) -- for r = lrow + RPP j with RPP a multiple of 64.
+  int wrow0;
+  if constexpr (EPI == EPI_SWIGLU)
+    wrow0 = tn * (BN / 2) + ((lrow >> 6) * 32) + (lrow & 31) + ((lrow >> 5) & 1) * g.F;
+  else
+    wrow0 = tn * BN + lrow;
+  const int voff_w = (wrow0 * g.ldw + lc * 8) * 2;
+  const int wstep = (EPI == EPI_SWIGLU ? RPP / 2 : RPP) * g.ldw * 2;  // W bytes per fetch pass
+  const int slot0 = lrow * 8 + (lc ^ ((lrow >> 1) & 7));  // row (lrow + RPP j) -> slot0 + 8 RPP j
+
+  u32x4 stA[NJ], stW[NJ];
+  auto gload = [&](int kt) {
+    const int kb = kt * BK * 2;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+      stA[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(ra, voff_a, RPP * j * g.lda * 2 + kb, 0));
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+      stW[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rw, voff_w, wstep * j + kb, 0));
+  };
+  auto lstore = [&](int b) {
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) sA[b][slot0 + 8 * RPP * j] = stA[j];
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) sW[b][slot0 + 8 * RPP * j] = stW[j];
+  };
+
+  f32x16 acc[FS][TS];
+#pragma unroll
+  for (int a = 0; a < FS; ++a)
+#pragma unroll
+    for (int b = 0; b < TS; ++b)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[a][b][e] = 0.f;
+
+  // fragment rows: (wave base + 32 i + lane % 32); swizzle term depends on lane only
+  const int fr = lane & 31, sw = (fr >> 1) & 7, half = lane >> 5;
+  const int rowA = wm * WT + fr, rowW = wn * WF + fr;
+  u32x4 fa[2][TS], fw[2][FS];
+  auto fload = [&](int b, int kk, int set) {
+    const int ch = (kk * 2 + half) ^ sw;
+#pragma unroll
+    for (int t = 0; t < TS; ++t) fa[set][t] = sA[b][(rowA + 32 * t) * 8 + ch];
+#pragma unroll
+    for (int f = 0; f < FS; ++f) fw[set][f] = sW[b][(rowW + 32 * f) * 8 + ch];
+  };
+
+  const int nk = g.K / BK;
+  gload(0);
+  lstore(0);
+  __syncthreads();
+  if (nk > 1) gload(1);
+
+  for (int kt = 0; kt < nk; ++kt) {
+    const int b = kt & 1;
+    fload(b, 0, 0);
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      if (kk < 3) fload(b, kk + 1, (kk + 1) & 1);
+#pragma unroll
+      for (int f = 0; f < FS; ++f)
+#pragma unroll
+        for (int t = 0; t < TS; ++t) acc[f][t] = mfma32x32x16(fw[kk & 1][f], fa[kk & 1][t], acc[f][t]);
+    }
+    if (kt + 1 < nk) lstore(b ^ 1);
+    __syncthreads();
+    if (kt + 2 < nk) gload(kt + 2);
+  }
+
+  const int h4 = 4 * half;
+#pragma unroll
+  for (int t = 0; t < TS; ++t) {
+    const int m = m0 + wm * WT + t * 32 + fr;
+    if (m >= g.M) continue;
+    if constexpr (EPI == EPI_SWIGLU) {
+#pragma unroll
+      for (int p = 0; p < FS / 2; ++p)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          store4_swiglu(g, m, tn * (BN / 2) + wn * (WF / 2) + p * 32 + 8 * j + h4, quad(acc[2 * p][t], j),
+                        quad(acc[2 * p + 1][t], j));
+    } else {
+#pragma unroll
+      for (int f = 0; f < FS; ++f)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) store4<EPI>(g, m, tn * BN + wn * WF + f * 32 + 8 * j + h4, quad(acc[f][t], j));
     }
   }
 }

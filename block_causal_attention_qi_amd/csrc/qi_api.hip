@@ -5,10 +5,20 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <mutex>
+#include <vector>
+
 #include "../../include/qi.h"
 #include "attention.hpp"
 #include "elementwise.hpp"
 #include "gemm.hpp"
+
+#ifndef QI_GEMM_WM
+#define QI_GEMM_WM 2  // waves along tokens in the 256 x 256 GEMM tile
+#endif
+#ifndef QI_GEMM_WN
+#define QI_GEMM_WN 4  // waves along W rows
+#endif
 
 namespace {
 
@@ -68,29 +78,84 @@ size_t slot_elems(const qi_dims &d, int L) {
 
 qi_status last_launch() { return hipGetLastError() == hipSuccess ? QI_OK : QI_ERR_HIP; }
 
+// ---------------------------------------------------------------- kernel timing
+// Optional per-kernel timing: while enabled, every launch is bracketed by two
+// events from a pool created by qi_timing_begin, on the launch's own stream.
+struct KernelTimer {
+  std::mutex mu;
+  bool on = false;
+  std::vector<hipEvent_t> pool;
+  std::vector<int> kinds;  // kind of each recorded pair
+  size_t dropped = 0;
+};
+KernelTimer g_timer;
+
+struct TimedLaunch {
+  hipStream_t s;
+  int kind;
+  int idx = -1;
+  TimedLaunch(int k, hipStream_t st) : s(st), kind(k) {
+    std::lock_guard<std::mutex> g(g_timer.mu);
+    if (!g_timer.on) return;
+    const size_t pair = g_timer.kinds.size();
+    if (2 * pair + 1 >= g_timer.pool.size()) {
+      ++g_timer.dropped;
+      return;
+    }
+    idx = (int)pair;
+    g_timer.kinds.push_back(kind);
+    hipEventRecord(g_timer.pool[2 * pair], s);
+  }
+  ~TimedLaunch() {
+    if (idx < 0) return;
+    std::lock_guard<std::mutex> g(g_timer.mu);
+    hipEventRecord(g_timer.pool[2 * idx + 1], s);
+  }
+};
+
 #define QI_TRY(expr)               \
   do {                             \
     qi_status s__ = (expr);        \
     if (s__ != QI_OK) return s__;  \
   } while (0)
 
+// Tile shape per launch: 256 x 256 (the large-tile kernel) when that still
+// gives at least one full wave of workgroups over the 256 CUs, else 128 x 128.
+// Both issue the same MFMA over the same K order for every output element, so
+// the choice never changes a result bit.
+template <int EPI, int BM, int BN>
+void launch_gemm_tile(const GemmArgs &g, hipStream_t s) {
+  const int nTM = (g.M + BM - 1) / BM;
+  const int nTN = EPI == EPI_SWIGLU ? g.F / (BN / 2) : g.N / BN;
+  hipLaunchKernelGGL((gemm_bf16_kernel<EPI, BM, BN>), dim3(nTM * nTN), dim3(gemm::THREADS), 0, s, g);
+}
+
 template <int EPI>
-qi_status launch_gemm(const GemmArgs &g, hipStream_t s) {
-  const int outs_per_tile = EPI == EPI_SWIGLU ? gemm::BN / 2 : gemm::BN;
+qi_status launch_gemm(const GemmArgs &g, int kind, hipStream_t s) {
   const int n_out = EPI == EPI_SWIGLU ? g.F : g.N;
-  dim3 grid((g.M + gemm::BM - 1) / gemm::BM, n_out / outs_per_tile);
-  hipLaunchKernelGGL(gemm_bf16_kernel<EPI>, grid, dim3(gemm::THREADS), 0, s, g);
+  const int per_tile_big = EPI == EPI_SWIGLU ? 128 : 256;
+  const int nTM_big = (g.M + 255) / 256;
+  const bool big = n_out % per_tile_big == 0 && nTM_big * (n_out / per_tile_big) >= 256 &&
+                   (size_t)g.M * g.lda * 2 < (1ull << 31) && (size_t)(EPI == EPI_SWIGLU ? 2 * g.F : g.N) * g.ldw * 2 < (1ull << 31);
+  TimedLaunch tl(kind, s);
+  if (big)
+    hipLaunchKernelGGL((gemm_bf16_large_kernel<EPI, QI_GEMM_WM, QI_GEMM_WN>), dim3(nTM_big * (n_out / per_tile_big)),
+                       dim3(64 * QI_GEMM_WM * QI_GEMM_WN), 0, s, g);
+  else
+    launch_gemm_tile<EPI, 128, 128>(g, s);
   return last_launch();
 }
 
 qi_status launch_norm(const float *x, int ldx, const float *gamma, int zc, const float *mod,
                       int mod_img_off, int L_rows, int rows, int H, u16 *out, int ldo, hipStream_t s) {
+  TimedLaunch tl(zc ? QI_KERNEL_TXT_NORM : QI_KERNEL_NORM_MOD, s);
   hipLaunchKernelGGL(rmsnorm_mod_kernel, dim3(rows), dim3(256), 0, s, x, ldx, gamma, zc, mod,
                      mod_img_off, L_rows, H, kRmsEps, out, ldo);
   return last_launch();
 }
 
 qi_status launch_modulation(int H, const u16 *w_mod, const float *b_mod, float t, float *mod, hipStream_t s) {
+  TimedLaunch tl(QI_KERNEL_MODULATION, s);
   hipLaunchKernelGGL(mod_gemv_kernel, dim3((4 * H + 15) / 16), dim3(256), 2 * H * sizeof(float), s, w_mod, b_mod,
                      t, H, 4 * H, mod);
   return last_launch();
@@ -110,6 +175,7 @@ qi_status launch_attention(int heads, int L, int N, bool joint, const u16 *q_t, 
   a.n_txt_qt = joint ? (L + attn::BQ - 1) / attn::BQ : 0;
   a.o_img_row0 = joint ? L : 0;
   a.scale_log2 = (float)(1.4426950408889634 / sqrt(128.0));
+  TimedLaunch tl(QI_KERNEL_ATTENTION, s);
   hipLaunchKernelGGL(block_causal_attn_kernel, dim3(a.n_img_qt + a.n_txt_qt, heads), dim3(attn::THREADS),
                      0, s, a);
   return last_launch();
@@ -140,7 +206,7 @@ qi_status run_block(const qi_dims &d, const qi_block_w &w, int L, int N, bool jo
   g.cos_t = cos_t; g.sin_t = sin_t; g.cos_i = cos_i; g.sin_i = sin_i;
   g.q_t = q_t; g.k_t = k_t; g.vt_t = vt_t; g.q_i = q_i; g.k_i = k_i; g.vt_i = vt_i;
   g.seg_t = L; g.seg_i = N; g.ldv_t = round64(L); g.ldv_i = round64(N);
-  QI_TRY(launch_gemm<EPI_QKV>(g, s));
+  QI_TRY(launch_gemm<EPI_QKV>(g, QI_KERNEL_GEMM_QKV, s));
 
   QI_TRY(launch_attention(heads, L, N, joint, q_t, k_t, vt_t, q_i, k_i, vt_i, o, s));
 
@@ -148,7 +214,7 @@ qi_status run_block(const qi_dims &d, const qi_block_w &w, int L, int N, bool jo
   GemmArgs r{};
   r.A = o; r.lda = H; r.W = w.w_o; r.ldw = H; r.M = T; r.N = H; r.K = H; r.L_rows = L_rows;
   r.X = x; r.ldx = H; r.gate = mod + H; r.gate_img_off = img_off;
-  QI_TRY(launch_gemm<EPI_RESID>(r, s));
+  QI_TRY(launch_gemm<EPI_RESID>(r, QI_KERNEL_GEMM_O, s));
 
   // norm 2 + modulation (scale2 = chunk 2)
   QI_TRY(launch_norm(x, H, w.norm2, 0, mod + 2 * H, img_off, L_rows, T, H, h, H, s));
@@ -157,13 +223,13 @@ qi_status run_block(const qi_dims &d, const qi_block_w &w, int L, int N, bool jo
   GemmArgs u{};
   u.A = h; u.lda = H; u.W = w.w_gu; u.ldw = H; u.M = T; u.N = 2 * F; u.K = H; u.L_rows = L_rows;
   u.out = a; u.ldo = F; u.F = F;
-  QI_TRY(launch_gemm<EPI_SWIGLU>(u, s));
+  QI_TRY(launch_gemm<EPI_SWIGLU>(u, QI_KERNEL_GEMM_GATE_UP, s));
 
   // down + gated residual 2 (gate2 = chunk 3)
   GemmArgs dn{};
   dn.A = a; dn.lda = F; dn.W = w.w_down; dn.ldw = F; dn.M = T; dn.N = H; dn.K = F; dn.L_rows = L_rows;
   dn.X = x; dn.ldx = H; dn.gate = mod + 3 * H; dn.gate_img_off = img_off;
-  QI_TRY(launch_gemm<EPI_RESID>(dn, s));
+  QI_TRY(launch_gemm<EPI_RESID>(dn, QI_KERNEL_GEMM_DOWN, s));
   return QI_OK;
 }
 
@@ -207,10 +273,13 @@ qi_status run_step(const qi_dims &d, const qi_model_w &w, int L, int N, const fl
     GemmArgs g{};
     g.A = tn; g.lda = D; g.W = w.w_txt; g.ldw = D; g.M = L; g.N = H; g.K = D; g.L_rows = L;
     g.C = x; g.ldc = H; g.bias = w.b_txt;
-    QI_TRY(launch_gemm<EPI_F32>(g, s));
+    QI_TRY(launch_gemm<EPI_F32>(g, QI_KERNEL_GEMM_TXT, s));
   }
-  hipLaunchKernelGGL(img_embed_kernel, dim3((N + 15) / 16, (H + 255) / 256), dim3(256), 0, s, img_tokens, N,
-                     w.w_img, w.b_img, H, x, H, L_rows);
+  {
+    TimedLaunch tl(QI_KERNEL_IMG_EMBED, s);
+    hipLaunchKernelGGL(img_embed_kernel, dim3((N + 15) / 16, (H + 255) / 256), dim3(256), 0, s, img_tokens, N,
+                       w.w_img, w.b_img, H, x, H, L_rows);
+  }
   QI_TRY(last_launch());
 
   const size_t slot = slot_elems(d, L);
@@ -220,6 +289,7 @@ qi_status run_step(const qi_dims &d, const qi_model_w &w, int L, int N, const fl
                      lay, s));
   }
   if (vel) {
+    TimedLaunch tl(QI_KERNEL_HEAD, s);
     hipLaunchKernelGGL(head_kernel, dim3((N + 15) / 16), dim3(256), 0, s, x + (size_t)L_rows * H, H, N,
                        w.norm_out, w.w_out, w.b_out, H, kRmsEps, vel);
     QI_TRY(last_launch());
@@ -349,6 +419,7 @@ qi_status qi_euler_update(float *x, const float *vel, float sigma_cur, float sig
   const float ds = sigma_next - sigma_cur;  // fp32 difference on the host
   const int64_t n4 = (n + 3) / 4;
   const int blocks = (int)((n4 + 255) / 256 < 4096 ? (n4 + 255) / 256 : 4096);
+  TimedLaunch tl(QI_KERNEL_EULER, (hipStream_t)stream);
   hipLaunchKernelGGL(euler_kernel, dim3(blocks), dim3(256), 0, (hipStream_t)stream, x, vel, ds, n);
   return last_launch();
 }
@@ -387,7 +458,50 @@ qi_status qi_linear_bf16(int32_t M, int32_t N, int32_t K, const uint16_t *A, con
   GemmArgs g{};
   g.A = A; g.lda = K; g.W = W; g.ldw = K; g.M = M; g.N = N; g.K = K;
   g.C = C; g.ldc = N; g.bias = bias;
-  return launch_gemm<EPI_F32>(g, (hipStream_t)stream);
+  return launch_gemm<EPI_F32>(g, QI_KERNEL_GEMM_TXT, (hipStream_t)stream);
+}
+
+const char *qi_kernel_kind_name(int32_t kind) {
+  static const char *names[QI_KERNEL_KINDS] = {"modulation", "txt_norm",   "gemm_txt",  "img_embed",
+                                               "norm_mod",   "gemm_qkv",   "attention", "gemm_o",
+                                               "gemm_gate_up", "gemm_down", "head",     "euler"};
+  return (kind >= 0 && kind < QI_KERNEL_KINDS) ? names[kind] : "?";
+}
+
+qi_status qi_timing_begin(int32_t max_launches) {
+  if (max_launches < 1 || max_launches > (1 << 20)) return QI_ERR_RANGE;
+  std::lock_guard<std::mutex> g(g_timer.mu);
+  const size_t need = 2 * (size_t)max_launches;
+  while (g_timer.pool.size() < need) {
+    hipEvent_t e;
+    if (hipEventCreate(&e) != hipSuccess) return QI_ERR_HIP;
+    g_timer.pool.push_back(e);
+  }
+  g_timer.kinds.clear();
+  g_timer.dropped = 0;
+  g_timer.on = true;
+  return QI_OK;
+}
+
+qi_status qi_timing_end(double *ms_total, int64_t *launches, int64_t *dropped) {
+  std::lock_guard<std::mutex> g(g_timer.mu);
+  g_timer.on = false;
+  if (!ms_total || !launches) return QI_ERR_NULL;
+  for (int k = 0; k < QI_KERNEL_KINDS; ++k) {
+    ms_total[k] = 0.0;
+    launches[k] = 0;
+  }
+  const size_t n = g_timer.kinds.size();
+  if (n && hipEventSynchronize(g_timer.pool[2 * n - 1]) != hipSuccess) return QI_ERR_HIP;
+  for (size_t i = 0; i < n; ++i) {
+    float ms = 0.f;
+    if (hipEventElapsedTime(&ms, g_timer.pool[2 * i], g_timer.pool[2 * i + 1]) != hipSuccess) return QI_ERR_HIP;
+    ms_total[g_timer.kinds[i]] += ms;
+    launches[g_timer.kinds[i]] += 1;
+  }
+  if (dropped) *dropped = (int64_t)g_timer.dropped;
+  g_timer.kinds.clear();
+  return QI_OK;
 }
 
 }  // extern "C"

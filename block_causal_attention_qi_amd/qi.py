@@ -17,7 +17,8 @@ from ._lib import (QI_MODE_IMAGE_ONLY, QI_MODE_JOINT, QiBlockW, QiDims, QiError,
 __all__ = ["QI_MODE_JOINT", "QI_MODE_IMAGE_ONLY", "QiError", "make_dims", "rope_axis_table",
            "rope_tables", "flow_sigmas", "workspace_bytes", "kv_cache_bytes", "kv_slot_elems",
            "DeviceModel", "KVCache", "Workspace", "dit_step", "text_kv_capture", "dit_block_fwd",
-           "euler_update", "modulation", "block_causal_attention", "linear_bf16", "stream_handle"]
+           "euler_update", "modulation", "block_causal_attention", "linear_bf16", "stream_handle",
+           "timing_begin", "timing_end", "KERNEL_KINDS"]
 
 
 def _np_ptr(a: np.ndarray) -> int:
@@ -225,3 +226,26 @@ def linear_bf16(A, W, bias, C, stream=None):
     N = W.shape[0]
     st = _lib.load().qi_linear_bf16(M, N, K, _ptr(A), _ptr(W), _ptr(bias), _ptr(C), stream_handle(stream))
     check(st, "qi_linear_bf16")
+
+
+# ------------------------------------------------------------------ kernel timing
+
+KERNEL_KINDS = ["modulation", "txt_norm", "gemm_txt", "img_embed", "norm_mod", "gemm_qkv", "attention",
+                "gemm_o", "gemm_gate_up", "gemm_down", "head", "euler"]
+
+
+def timing_begin(max_launches: int = 65536):
+    check(_lib.load().qi_timing_begin(int(max_launches)), "qi_timing_begin")
+
+
+def timing_end() -> dict:
+    """{kind: (total_ms, launches)} for the launches since timing_begin()."""
+    n = _lib.QI_KERNEL_KINDS
+    ms = (ctypes.c_double * n)()
+    cnt = (ctypes.c_int64 * n)()
+    dropped = ctypes.c_int64(0)
+    check(_lib.load().qi_timing_end(ms, cnt, ctypes.byref(dropped)), "qi_timing_end")
+    if dropped.value:
+        raise RuntimeError(f"kernel timing dropped {dropped.value} launches; raise max_launches")
+    lib = _lib.load()
+    return {lib.qi_kernel_kind_name(k).decode(): (ms[k], int(cnt[k])) for k in range(n)}

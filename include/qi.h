@@ -18,7 +18,8 @@
  *   - bf16 values travel as uint16_t bit patterns; fp32 as float.
  *   - "device" pointers are HIP device memory of the current device; "host"
  *     pointers are ordinary host memory.  The caller owns every buffer; the
- *     library allocates nothing per call and keeps no mutable global state.
+ *     library allocates nothing per call and keeps no mutable global state
+ *     beyond the optional kernel-timing facility at the end of this header.
  *   - Linear weights use the [out, in] row-major layout, so each projection is
  *     y = x W^T.  Device pointers must be 16-byte aligned.
  *   - `stream` is a hipStream_t (NULL = the default stream).  Work is enqueued
@@ -236,6 +237,39 @@ qi_status qi_block_causal_attention(int32_t heads, int32_t L, int32_t N, int32_t
  * RANGE, ALIGN, HIP. */
 qi_status qi_linear_bf16(int32_t M, int32_t N, int32_t K, const uint16_t *A, const uint16_t *W,
                          const float *bias, float *C, void *stream);
+
+/* ---------------------------------------------------------------- kernel timing */
+
+/* Kernel kinds reported by the timing facility. */
+#define QI_KERNEL_MODULATION 0   /* shared modulation GEMV (+ time embedding) */
+#define QI_KERNEL_TXT_NORM 1     /* ZeroCenterRMSNorm of the text features */
+#define QI_KERNEL_GEMM_TXT 2     /* text projection GEMM (and qi_linear_bf16) */
+#define QI_KERNEL_IMG_EMBED 3    /* img-in Linear 64 -> H */
+#define QI_KERNEL_NORM_MOD 4     /* RMSNorm with modulation (two per block) */
+#define QI_KERNEL_GEMM_QKV 5     /* QKV GEMM + RoPE epilogue */
+#define QI_KERNEL_ATTENTION 6    /* block-causal attention */
+#define QI_KERNEL_GEMM_O 7       /* output projection + gated residual */
+#define QI_KERNEL_GEMM_GATE_UP 8 /* gate/up GEMM + SwiGLU */
+#define QI_KERNEL_GEMM_DOWN 9    /* down GEMM + gated residual */
+#define QI_KERNEL_HEAD 10        /* final RMSNorm + proj_out */
+#define QI_KERNEL_EULER 11       /* fp32 Euler update */
+#define QI_KERNEL_KINDS 12
+
+/* Name of a kernel kind (static string, "?" if out of range). */
+const char *qi_kernel_kind_name(int32_t kind);
+
+/* Start timing: from now on every kernel the library launches is bracketed by
+ * two HIP events recorded on the stream it is launched on, for at most
+ * max_launches launches (later ones are counted as dropped).  Creates the event
+ * pool on first use (the only allocation the library makes; the pool lives
+ * until the process ends).  Not meant for graph capture.  Errors: RANGE, HIP. */
+qi_status qi_timing_begin(int32_t max_launches);
+
+/* Stop timing, wait for the last recorded event, and report per kind the total
+ * milliseconds and the number of launches: ms_total[QI_KERNEL_KINDS],
+ * launches[QI_KERNEL_KINDS] (host arrays); dropped (may be NULL) receives the
+ * launches that did not fit the pool.  Errors: NULL, HIP. */
+qi_status qi_timing_end(double *ms_total, int64_t *launches, int64_t *dropped);
 
 #ifdef __cplusplus
 }

@@ -20,7 +20,8 @@ def _dev(a):
     return torch.from_numpy(np.ascontiguousarray(a)).cuda()
 
 
-@pytest.mark.parametrize("M,N,K", [(1, 128, 64), (200, 256, 192), (278, 384, 512), (1070, 512, 4096)])
+@pytest.mark.parametrize("M,N,K", [(1, 128, 64), (200, 256, 192), (278, 384, 512), (1070, 512, 4096),
+                                   (4096, 4096, 256), (4000, 4096, 192)])
 def test_linear_bf16_matches_fp64_matmul(M, N, K):
     import torch
     log(f"linear M={M} N={N} K={K}")
