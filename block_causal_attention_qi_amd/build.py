@@ -44,6 +44,8 @@ def _run(cmd):
 
 def build(verbose: bool = False) -> str:
     os.makedirs(OUT_DIR, exist_ok=True)
+    if os.path.exists(LIB):
+        os.remove(LIB)  # a failed build must not leave an older library behind
     obj_dir = os.path.join(OUT_DIR, "obj")
     os.makedirs(obj_dir, exist_ok=True)
     hipcc = _hipcc()

@@ -11,14 +11,20 @@
 // image row computes bit-identical results in a joint pass and in an
 // image-only pass that reads the cached text K/V.
 //
-// Per workgroup: 128 queries (4 waves x 32), key tiles of 64 staged through
-// LDS (double buffered).  S^T = K Q^T on MFMA 16x16x32 bf16 leaves each lane
-// with 4 consecutive keys of one query; those exp'd probabilities are reused
-// in registers as the B operand of O^T = V^T P^T by pairing key slots
-// {4g..4g+3, 16+4g..16+4g+3} on both operands (a permutation of the MFMA's
-// k index, which a dot product does not see).  V is consumed as V^T
-// [heads][128][Tp], which the QKV epilogue writes directly.  Softmax
-// statistics are fp32, in the log2 domain.
+// Per workgroup: 256 queries (8 waves x 32), key tiles of 64 staged through
+// LDS (double buffered), MFMA 32x32x16 bf16 (the full-rate shape on gfx950).
+// S^T = K Q^T: the A operand takes the tile's K rows in the order
+// kappa(i) = 16*(i/16) + 8*((i/4)&1) + 4*((i/8)&1) + (i&3), which leaves each
+// lane holding 8 CONSECUTIVE keys of one query per 16-key step.  Those
+// exponentiated scores, packed to bf16, are directly the B operand of
+// O^T = V^T P^T, whose A operand is then one contiguous 16-byte read of a V^T
+// row.  V is consumed as V^T [heads][128][Tp], which the QKV epilogue writes.
+// Softmax statistics are fp32 in the log2 domain; each query's 64 scores of a
+// tile are split over two lanes (l and l^32).  The running max is raised only
+// when a tile's max exceeds it by more than 8 (a factor of 256), so the
+// accumulator rescale is rare; the probabilities then stay below 2^8, far from
+// fp32 or bf16 overflow, and the final division by the running sum cancels the
+// choice exactly in real arithmetic.
 #pragma once
 
 #include "common.hpp"
@@ -30,24 +36,30 @@ struct AttnArgs {
   int ldo;                       // heads * 128
   int heads, L, N;
   int ldv_t, ldv_i;              // V^T row strides (>= segment length rounded up to 64)
-  int n_img_qt, n_txt_qt;        // query tiles of 128 per head
+  int n_img_qt, n_txt_qt;        // query tiles of BQ per head
   int o_img_row0;                // output row of image query 0 (L in a joint pass, else 0)
   float scale_log2;              // log2(e) / sqrt(128)
 };
 
 namespace attn {
-constexpr int BQ = 128;
+constexpr int BQ = 256;
 constexpr int BKV = 64;
-constexpr int THREADS = 256;
+constexpr int THREADS = 512;
+constexpr int NLD = BKV * 16 / THREADS;  // 16-byte K (and V^T) chunks per thread per tile
+constexpr float RESCALE_SLACK = 8.f;   // log2 units
 }  // namespace attn
 
-__global__ __launch_bounds__(attn::THREADS, 2) void block_causal_attn_kernel(const AttnArgs a) {
+// key (within a 32-key block) fed by A-operand row i, so that output row
+// 8j + 4h + r holds key 16*(j>>1) + 8h + 4*(j&1) + r
+QI_DEV int kappa(int i) { return ((i >> 4) << 4) + (((i >> 2) & 1) << 3) + (((i >> 3) & 1) << 2) + (i & 3); }
+
+__global__ __launch_bounds__(attn::THREADS, 1) void block_causal_attn_kernel(const AttnArgs a) {
   using namespace attn;
   __shared__ u32x4 sK[2][BKV * 16];  // [key][16 chunks of 8 d], chunk c at c ^ (key & 15)
-  __shared__ u32x2 sV[2][128 * 16];  // [d][16 chunks of 4 keys], chunk c at c ^ (d & 15)
+  __shared__ u32x4 sV[2][128 * 8];   // [d][8 chunks of 8 keys], chunk c at c ^ ((d >> 1) & 7)
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int l16 = lane & 15, grp = lane >> 4;
+  const int l32 = lane & 31, h = lane >> 5;
   const int head = blockIdx.y;
   int qt = blockIdx.x;
   const bool img = qt < a.n_img_qt;
@@ -56,14 +68,13 @@ __global__ __launch_bounds__(attn::THREADS, 2) void block_causal_attn_kernel(con
   const int seg_q = img ? a.N : a.L;
   const u16 *Q = (img ? a.q_i : a.q_t) + (size_t)head * seg_q * 128;
 
-  int qrow[2];
-  u32x4 qreg[2][4];
+  // B operand of S^T: Q[q][16 ds + 8 h .. +8] for this lane's query
+  const int qrow = q0 + wave * 32 + l32;
+  u32x4 qreg[8];
+  {
+    const int r = min(qrow, seg_q - 1);
 #pragma unroll
-  for (int qs = 0; qs < 2; ++qs) {
-    qrow[qs] = q0 + wave * 32 + qs * 16 + l16;
-    const int r = min(qrow[qs], seg_q - 1);
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) qreg[qs][kk] = *(const u32x4 *)(Q + (size_t)r * 128 + kk * 32 + 8 * grp);
+    for (int ds = 0; ds < 8; ++ds) qreg[ds] = *(const u32x4 *)(Q + (size_t)r * 128 + ds * 16 + 8 * h);
   }
 
   int nt_t, nt_i;
@@ -81,7 +92,7 @@ __global__ __launch_bounds__(attn::THREADS, 2) void block_causal_attn_kernel(con
   const u16 *Ki = a.k_i + (size_t)head * a.N * 128;
   const u16 *Vti = a.vt_i + (size_t)head * 128 * a.ldv_i;
 
-  u32x4 rk[4], rv[4];
+  u32x4 rk[NLD], rv[NLD];
   auto gload = [&](int t) {
     const bool tx = t < nt_t;
     const u16 *K = tx ? Kt : Ki;
@@ -90,7 +101,7 @@ __global__ __launch_bounds__(attn::THREADS, 2) void block_causal_attn_kernel(con
     const int klen = tx ? a.L : a.N;
     const int ldv = tx ? a.ldv_t : a.ldv_i;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < NLD; ++j) {
       const int i = tid + THREADS * j;
       const int kr = i >> 4, kc = i & 15;
       const int key = min(key0 + kr, klen - 1);  // rows past the segment: masked below
@@ -102,7 +113,7 @@ __global__ __launch_bounds__(attn::THREADS, 2) void block_causal_attn_kernel(con
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int k2 = kb + 2 * e;
-          uint32_t keep = (k2 < klen ? 0x0000FFFFu : 0u) | (k2 + 1 < klen ? 0xFFFF0000u : 0u);
+          const uint32_t keep = (k2 < klen ? 0x0000FFFFu : 0u) | (k2 + 1 < klen ? 0xFFFF0000u : 0u);
           v[e] &= keep;
         }
       }
@@ -111,23 +122,25 @@ __global__ __launch_bounds__(attn::THREADS, 2) void block_causal_attn_kernel(con
   };
   auto lstore = [&](int b) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < NLD; ++j) {
       const int i = tid + THREADS * j;
       const int kr = i >> 4, kc = i & 15;
       sK[b][kr * 16 + (kc ^ (kr & 15))] = rk[j];
       const int vr = i >> 3, vc = i & 7;
-      sV[b][vr * 16 + ((2 * vc) ^ (vr & 15))] = u32x2{rv[j][0], rv[j][1]};
-      sV[b][vr * 16 + ((2 * vc + 1) ^ (vr & 15))] = u32x2{rv[j][2], rv[j][3]};
+      sV[b][vr * 8 + (vc ^ ((vr >> 1) & 7))] = rv[j];
     }
   };
 
-  float m_run[2] = {-INFINITY, -INFINITY};
-  float l_run[2] = {0.f, 0.f};
-  f32x4 oacc[8][2];
+  float m_run = -INFINITY, l_run = 0.f;
+  f32x16 oacc[4];
 #pragma unroll
-  for (int d = 0; d < 8; ++d)
+  for (int d = 0; d < 4; ++d)
 #pragma unroll
-    for (int qs = 0; qs < 2; ++qs) oacc[d][qs] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int e = 0; e < 16; ++e) oacc[d][e] = 0.f;
+
+  // K row this lane feeds to the S^T MFMA in each 32-key block
+  const int krow_l = kappa(l32);
+  const int vsw = (l32 >> 1) & 7;
 
   gload(0);
   lstore(0);
@@ -138,20 +151,19 @@ __global__ __launch_bounds__(attn::THREADS, 2) void block_causal_attn_kernel(con
     const bool more = t + 1 < ntiles;
     if (more) gload(t + 1);
 
-    // S^T[key][q] for 64 keys x 32 queries
-    f32x4 s[4][2];
+    // S^T for 64 keys (2 blocks of 32) x this wave's 32 queries
+    f32x16 s[2];
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int qs = 0; qs < 2; ++qs) s[ks][qs] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int e = 0; e < 16; ++e) s[kb][e] = 0.f;
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
+    for (int ds = 0; ds < 8; ++ds) {
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const int kr = ks * 16 + l16;
-        const u32x4 ka = sK[b][kr * 16 + ((kk * 4 + grp) ^ (kr & 15))];
-#pragma unroll
-        for (int qs = 0; qs < 2; ++qs) s[ks][qs] = mfma16x16x32(ka, qreg[qs][kk], s[ks][qs]);
+      for (int kb = 0; kb < 2; ++kb) {
+        const int kr = kb * 32 + krow_l;
+        const u32x4 ka = sK[b][kr * 16 + ((2 * ds + h) ^ (kr & 15))];
+        s[kb] = mfma32x32x16(ka, qreg[ds], s[kb]);
       }
     }
 
@@ -161,60 +173,60 @@ __global__ __launch_bounds__(attn::THREADS, 2) void block_causal_attn_kernel(con
     const bool causal = !img;
     const bool need_mask = (key0 + BKV > klen) || (causal && key0 + BKV - 1 > q0 + wave * 32);
 
-    u32x4 pb[2][2];
+    // element e of block kb holds key key0 + 32 kb + 16 (e >> 3) + 8 h + (e & 7)
+    float mx = -INFINITY;
 #pragma unroll
-    for (int qs = 0; qs < 2; ++qs) {
-      float mx = -INFINITY;
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          float v = s[ks][qs][r] * a.scale_log2;
-          if (need_mask) {
-            const int key = key0 + ks * 16 + 4 * grp + r;
-            const bool ok = key < klen && (!causal || key <= qrow[qs]);
-            v = ok ? v : -INFINITY;
-          }
-          s[ks][qs][r] = v;
-          mx = fmaxf(mx, v);
+      for (int e = 0; e < 16; ++e) {
+        float v = s[kb][e] * a.scale_log2;
+        if (need_mask) {
+          const int key = key0 + 32 * kb + 16 * (e >> 3) + 8 * h + (e & 7);
+          const bool ok = key < klen && (!causal || key <= qrow);
+          v = ok ? v : -INFINITY;
         }
-      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      const float m_new = fmaxf(m_run[qs], mx);
-      const float base = m_new == -INFINITY ? 0.f : m_new;
-      const float alpha = exp2f(m_run[qs] - base);
-      m_run[qs] = m_new;
-      float psum = 0.f;
+        s[kb][e] = v;
+        mx = fmaxf(mx, v);
+      }
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    // raise the running max only past the slack; every lane of the wave
+    // follows the same rule, and only a raised max costs a rescale
+    const bool raise = mx > m_run + RESCALE_SLACK;
+    float alpha = 1.f;
+    if (raise) {
+      alpha = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - mx);
+      m_run = mx;
+    }
+    const float base = m_run == -INFINITY ? 0.f : m_run;
+    float psum = 0.f;
+    u32x4 pb[4];  // B operand per 16-key step c4 = 2 kb + c: keys 16 c4 + 8 h .. +8
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks)
+    for (int kb = 0; kb < 2; ++kb) {
+      float p[16];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float p = exp2f(s[ks][qs][r] - base);
-          s[ks][qs][r] = p;
-          psum += p;
-        }
-      l_run[qs] = l_run[qs] * alpha + psum;
-#pragma unroll
-      for (int d = 0; d < 8; ++d) oacc[d][qs] *= alpha;
+      for (int e = 0; e < 16; ++e) {
+        p[e] = __builtin_amdgcn_exp2f(s[kb][e] - base);
+        psum += p[e];
+      }
 #pragma unroll
       for (int c = 0; c < 2; ++c)
-        pb[c][qs] = u32x4{pack_bf16x2(s[2 * c][qs][0], s[2 * c][qs][1]),
-                          pack_bf16x2(s[2 * c][qs][2], s[2 * c][qs][3]),
-                          pack_bf16x2(s[2 * c + 1][qs][0], s[2 * c + 1][qs][1]),
-                          pack_bf16x2(s[2 * c + 1][qs][2], s[2 * c + 1][qs][3])};
+        pb[2 * kb + c] = u32x4{pack_bf16x2(p[8 * c], p[8 * c + 1]), pack_bf16x2(p[8 * c + 2], p[8 * c + 3]),
+                               pack_bf16x2(p[8 * c + 4], p[8 * c + 5]), pack_bf16x2(p[8 * c + 6], p[8 * c + 7])};
+    }
+    l_run = l_run * alpha + psum;
+    if (__any(raise)) {
+#pragma unroll
+      for (int d = 0; d < 4; ++d) oacc[d] *= alpha;
     }
 
-    // O^T[d][q] += V^T[d][keys] P^T[keys][q]
+    // O^T[d][q] += V^T[d][16 c4 + 8h .. +8] P^T
 #pragma unroll
-    for (int ds = 0; ds < 8; ++ds) {
-      const int vr = ds * 16 + l16;
+    for (int c4 = 0; c4 < 4; ++c4) {
 #pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        const u32x2 lo = sV[b][vr * 16 + ((8 * c + grp) ^ (vr & 15))];
-        const u32x2 hi = sV[b][vr * 16 + ((8 * c + 4 + grp) ^ (vr & 15))];
-        const u32x4 va = {lo[0], lo[1], hi[0], hi[1]};
-#pragma unroll
-        for (int qs = 0; qs < 2; ++qs) oacc[ds][qs] = mfma16x16x32(va, pb[c][qs], oacc[ds][qs]);
+      for (int db = 0; db < 4; ++db) {
+        const int vr = db * 32 + l32;
+        const u32x4 va = sV[b][vr * 8 + ((2 * c4 + h) ^ vsw)];
+        oacc[db] = mfma32x32x16(va, pb[c4], oacc[db]);
       }
     }
 
@@ -222,20 +234,17 @@ __global__ __launch_bounds__(attn::THREADS, 2) void block_causal_attn_kernel(con
     __syncthreads();
   }
 
+  float l = l_run + __shfl_xor(l_run, 32, 64);
+  const float inv = 1.f / l;
+  if (qrow < seg_q) {
+    const int orow = (img ? a.o_img_row0 : 0) + qrow;
+    u16 *op = a.o + (size_t)orow * a.ldo + head * 128 + 4 * h;
 #pragma unroll
-  for (int qs = 0; qs < 2; ++qs) {
-    float l = l_run[qs];
-    l += __shfl_xor(l, 16, 64);
-    l += __shfl_xor(l, 32, 64);
-    const float inv = 1.f / l;
-    if (qrow[qs] < seg_q) {
-      const int orow = (img ? a.o_img_row0 : 0) + qrow[qs];
-      u16 *op = a.o + (size_t)orow * a.ldo + head * 128 + 4 * grp;
+    for (int db = 0; db < 4; ++db)
 #pragma unroll
-      for (int ds = 0; ds < 8; ++ds) {
-        const f32x4 v = oacc[ds][qs] * inv;
-        *(u32x2 *)(op + ds * 16) = u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+      for (int j = 0; j < 4; ++j) {
+        const f32x4 v = quad(oacc[db], j) * inv;
+        *(u32x2 *)(op + db * 32 + 8 * j) = u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
       }
-    }
   }
 }

@@ -40,6 +40,9 @@ QI_DEV f32x16 mfma32x32x16(u32x4 a, u32x4 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
 }
 
+// The 4 accumulators 4j .. 4j+3 of a 32x32 MFMA result (rows 8j + 4*(l/32) + 0..3).
+QI_DEV f32x4 quad(const f32x16 &a, int j) { return f32x4{a[4 * j], a[4 * j + 1], a[4 * j + 2], a[4 * j + 3]}; }
+
 QI_DEV float wave_sum(float v) {
 #pragma unroll
   for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);

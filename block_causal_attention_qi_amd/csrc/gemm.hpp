@@ -133,8 +133,6 @@ QI_DEV void store4_swiglu(const GemmArgs &g, int m, int o, f32x4 gt, f32x4 up) {
   *(u32x2 *)(g.out + (size_t)m * g.ldo + o) = u32x2{pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3])};
 }
 
-QI_DEV f32x4 quad(const f32x16 &a, int j) { return f32x4{a[4 * j], a[4 * j + 1], a[4 * j + 2], a[4 * j + 3]}; }
-
 template <int EPI, int BM, int BN>
 __global__ __launch_bounds__(gemm::THREADS, (BM * BN >= 256 * 256) ? 1 : 2) void gemm_bf16_kernel(const GemmArgs g) {
   using namespace gemm;

@@ -104,12 +104,12 @@ struct TimedLaunch {
     }
     idx = (int)pair;
     g_timer.kinds.push_back(kind);
-    hipEventRecord(g_timer.pool[2 * pair], s);
+    (void)hipEventRecord(g_timer.pool[2 * pair], s);
   }
   ~TimedLaunch() {
     if (idx < 0) return;
     std::lock_guard<std::mutex> g(g_timer.mu);
-    hipEventRecord(g_timer.pool[2 * idx + 1], s);
+    (void)hipEventRecord(g_timer.pool[2 * idx + 1], s);
   }
 };
 
