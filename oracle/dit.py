@@ -33,6 +33,14 @@ Readings of points the pages leave open (each is stated where it is used):
   S9  final layer = RMSNorm then Linear(H -> 64) with bias, image rows only.
   S10 SwiGLU: rows [0,F) of the gate/up weight are the gate (SiLU), [F,2F)
       the up projection.
+  S11 precision: the host contract fixes the DiT as "bf16 weights and
+      compute, fp32 boundary" without listing rounding points.  exact mode
+      (default) computes the definition in float64; bf16 mode (bf16=True)
+      rounds every matmul operand once to bf16 (round to nearest even) --
+      the block's normed inputs, q, k, v after RoPE, the attention
+      probabilities (relative to the row max), the attention output, the
+      SwiGLU output and the normed text features -- with fp32-or-better
+      accumulation, residual stream, norm statistics and softmax sums.
   S12 RoPE tables: each step of the printed formula rounded to fp32, pow and
       cos/sin correctly rounded (evaluated in float64, rounded once).
   S14 Euler: the sigma difference in fp32, then a fp32 multiply and a fp32
@@ -56,6 +64,14 @@ ROPE_POS_MIN, ROPE_POS_MAX = -1024, 8191   # table rows [HOST] s.4
 RMS_EPS = 1e-6                    # S3
 
 F32 = np.float32
+
+
+def round_bf16(a: np.ndarray) -> np.ndarray:
+    """Round to the nearest bf16 value (ties to even), keeping a's dtype:
+    the 16 high bits of the float32 representation after rounding."""
+    u = np.ascontiguousarray(a, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    u = (u + 0x7FFF + ((u >> 16) & 1)) >> 16 << 16
+    return u.astype(np.uint32).view(np.float32).astype(a.dtype)
 
 
 # ------------------------------------------------------------------ RoPE
@@ -163,10 +179,12 @@ def silu(u: np.ndarray) -> np.ndarray:
 
 # ------------------------------------------------------------------ attention
 
-def sdpa(q: np.ndarray, k: np.ndarray, v: np.ndarray, causal: bool) -> np.ndarray:
+def sdpa(q: np.ndarray, k: np.ndarray, v: np.ndarray, causal: bool, bf16: bool = False) -> np.ndarray:
     """Scaled dot-product attention for one segment, [heads, Tq, d] x
     [heads, Tk, d] -> [heads, Tq, d], scale 1/sqrt(d) (S7).  causal: query i
-    sees keys 0..i (requires Tq == Tk)."""
+    sees keys 0..i (requires Tq == Tk).  bf16 (reading S11): the
+    probabilities relative to the row max are rounded to bf16 before they
+    multiply v; the normalising sum uses the unrounded values."""
     d = q.shape[-1]
     s = np.matmul(q, np.swapaxes(k, -1, -2)) / math.sqrt(d)
     if causal:
@@ -175,34 +193,37 @@ def sdpa(q: np.ndarray, k: np.ndarray, v: np.ndarray, causal: bool) -> np.ndarra
         s = np.where(mask, -np.inf, s)
     s = s - np.max(s, axis=-1, keepdims=True)
     p = np.exp(s)
-    p = p / np.sum(p, axis=-1, keepdims=True)
-    return np.matmul(p, v)
+    l = np.sum(p, axis=-1, keepdims=True)
+    if bf16:
+        p = round_bf16(p)
+    return np.matmul(p, v) / l
 
 
-def block_causal_attention(q_txt, k_txt, v_txt, q_img, k_img, v_img):
+def block_causal_attention(q_txt, k_txt, v_txt, q_img, k_img, v_img, bf16: bool = False):
     """The two-SDPA decomposition of block-causal attention ([PORT] DiT row:
     text->text causal, image->all; [MLX] "Text K/V reuse": text rows never see
     the image).  Inputs [heads, T_seg, d]; q_txt may have zero rows (an
     image-only step).  Returns (o_txt, o_img)."""
-    o_txt = sdpa(q_txt, k_txt, v_txt, causal=True) if q_txt.shape[1] else q_txt.copy()
+    o_txt = sdpa(q_txt, k_txt, v_txt, causal=True, bf16=bf16) if q_txt.shape[1] else q_txt.copy()
     k_all = np.concatenate([k_txt, k_img], axis=1)
     v_all = np.concatenate([v_txt, v_img], axis=1)
-    o_img = sdpa(q_img, k_all, v_all, causal=False)
+    o_img = sdpa(q_img, k_all, v_all, causal=False, bf16=bf16)
     return o_txt, o_img
 
 
 # ------------------------------------------------------------------ block / step
 
 def dit_block(x: np.ndarray, L_rows: int, bw: dict, m_txt, m_img, cos, sin,
-              heads: int, kv_text=None):
+              heads: int, kv_text=None, bf16: bool = False):
     """One single-stream block (spec step list; [PORT] DiT row).
 
     x: [T, H] residual stream, rows [text L_rows | image].  L_rows = L for a
     joint pass, 0 for an image-only pass (then kv_text = (k_txt, v_txt) from
     the cache, [heads, L, 128] each).  cos/sin: [T, 64] rows of those tokens.
     Returns (x_new, (k_txt, v_txt)) where the pair is this pass's text K/V
-    (joint) or the cached pair passed in (image-only)."""
+    (joint) or the cached pair passed in (image-only).  bf16: reading S11."""
     dt = x.dtype
+    rb = round_bf16 if bf16 else (lambda a: a)
     T, H = x.shape
     mt, mi = split_mod(m_txt.astype(dt), H), split_mod(m_img.astype(dt), H)
     is_txt = (np.arange(T) < L_rows)[:, None]
@@ -212,13 +233,13 @@ def dit_block(x: np.ndarray, L_rows: int, bw: dict, m_txt, m_img, cos, sin,
 
     s1, g1, s2, g2 = mrow(0), mrow(1), mrow(2), mrow(3)
 
-    h = rms_norm(x, bw["norm1"]) * (1.0 + s1)
+    h = rb(rms_norm(x, bw["norm1"]) * (1.0 + s1))
     qkv = h @ bw["w_qkv"].astype(dt).T                                  # [T, 3H]
     q = qkv[:, 0:H].reshape(T, heads, HEAD_DIM)
     k = qkv[:, H:2 * H].reshape(T, heads, HEAD_DIM)
-    v = qkv[:, 2 * H:3 * H].reshape(T, heads, HEAD_DIM)
-    q = rope_apply(q, cos, sin)
-    k = rope_apply(k, cos, sin)
+    v = rb(qkv[:, 2 * H:3 * H].reshape(T, heads, HEAD_DIM))
+    q = rb(rope_apply(q, cos, sin))
+    k = rb(rope_apply(k, cos, sin))
     qh, kh, vh = (np.ascontiguousarray(a.transpose(1, 0, 2)) for a in (q, k, v))
 
     if L_rows > 0:
@@ -226,19 +247,66 @@ def dit_block(x: np.ndarray, L_rows: int, bw: dict, m_txt, m_img, cos, sin,
     else:
         k_txt, v_txt = (a.astype(dt) for a in kv_text)
     o_txt, o_img = block_causal_attention(qh[:, :L_rows], k_txt, v_txt,
-                                          qh[:, L_rows:], kh[:, L_rows:], vh[:, L_rows:])
-    o = np.concatenate([o_txt, o_img], axis=1).transpose(1, 0, 2).reshape(T, H)
+                                          qh[:, L_rows:], kh[:, L_rows:], vh[:, L_rows:], bf16=bf16)
+    o = rb(np.concatenate([o_txt, o_img], axis=1).transpose(1, 0, 2).reshape(T, H))
 
     x = x + g1 * (o @ bw["w_o"].astype(dt).T)
-    h2 = rms_norm(x, bw["norm2"]) * (1.0 + s2)
+    h2 = rb(rms_norm(x, bw["norm2"]) * (1.0 + s2))
     u = h2 @ bw["w_gu"].astype(dt).T
     F = u.shape[1] // 2
-    a = silu(u[:, :F]) * u[:, F:]
+    a = rb(silu(u[:, :F]) * u[:, F:])
     x = x + g2 * (a @ bw["w_down"].astype(dt).T)
     return x, (k_txt, v_txt)
 
 
-def embed(sw: dict, img_tokens: np.ndarray, txt_feats, dtype=np.float64):
+def dit_block_rows(x: np.ndarray, L_rows: int, bw: dict, m_txt, m_img, cos, sin, heads: int,
+                   rows, kv_text=None):
+    """dit_block evaluated for the output rows `rows` only (indices into x):
+    the keys and values of every row, then attention, the output projection
+    and the MLP of the selected rows, with the same definition as dit_block.
+    Returns x_new[rows]."""
+    dt = x.dtype
+    T, H = x.shape
+    rows = np.asarray(rows)
+    mt, mi = split_mod(m_txt.astype(dt), H), split_mod(m_img.astype(dt), H)
+    is_txt_all = (np.arange(T) < L_rows)[:, None]
+    s1 = np.where(is_txt_all, mt[0][None, :], mi[0][None, :])
+    h = rms_norm(x, bw["norm1"]) * (1.0 + s1)
+    w_qkv = bw["w_qkv"].astype(dt)
+    kv = h @ w_qkv[H:3 * H].T                                            # [T, 2H]
+    k = rope_apply(kv[:, :H].reshape(T, heads, HEAD_DIM), cos, sin)
+    v = kv[:, H:].reshape(T, heads, HEAD_DIM)
+    q = rope_apply((h[rows] @ w_qkv[0:H].T).reshape(len(rows), heads, HEAD_DIM), cos[rows], sin[rows])
+    kh, vh = (np.ascontiguousarray(a.transpose(1, 0, 2)) for a in (k, v))
+    if L_rows > 0:
+        k_txt, v_txt = kh[:, :L_rows], vh[:, :L_rows]
+    else:
+        k_txt, v_txt = (a.astype(dt) for a in kv_text)
+    k_all = np.concatenate([k_txt, kh[:, L_rows:]], axis=1)
+    v_all = np.concatenate([v_txt, vh[:, L_rows:]], axis=1)
+    o = np.empty((len(rows), heads, HEAD_DIM), dtype=dt)
+    for i, r in enumerate(rows):
+        if r < L_rows:      # text row: causal over text keys 0..r
+            kk, vv = k_txt[:, :r + 1], v_txt[:, :r + 1]
+        else:               # image row: every text key, then every image key
+            kk, vv = k_all, v_all
+        o[i] = sdpa(q[i][:, None, :], kk, vv, causal=False)[:, 0, :]
+    o = o.reshape(len(rows), H)
+    is_txt = (rows < L_rows)[:, None]
+
+    def mrow(j):
+        return np.where(is_txt, mt[j][None, :], mi[j][None, :])
+
+    g1, s2, g2 = mrow(1), mrow(2), mrow(3)
+    xr = x[rows] + g1 * (o @ bw["w_o"].astype(dt).T)
+    h2 = rms_norm(xr, bw["norm2"]) * (1.0 + s2)
+    u = h2 @ bw["w_gu"].astype(dt).T
+    F = u.shape[1] // 2
+    a = silu(u[:, :F]) * u[:, F:]
+    return xr + g2 * (a @ bw["w_down"].astype(dt).T)
+
+
+def embed(sw: dict, img_tokens: np.ndarray, txt_feats, dtype=np.float64, bf16: bool = False):
     """img-in Linear(64 -> H) on the image tokens; for a joint pass also the
     text projection ZeroCenterRMSNorm -> Linear(D -> H) (readings S4, S5).
     Returns x [T, H] with rows [text | image] (text omitted if txt_feats is
@@ -247,6 +315,8 @@ def embed(sw: dict, img_tokens: np.ndarray, txt_feats, dtype=np.float64):
     if txt_feats is None:
         return x_img
     e = zero_center_rms_norm(txt_feats.astype(dtype), sw["txt_norm"])
+    if bf16:
+        e = round_bf16(e)
     x_txt = e @ sw["w_txt"].astype(dtype).T + sw["b_txt"].astype(dtype)
     return np.concatenate([x_txt, x_img], axis=0)
 
@@ -260,7 +330,7 @@ def head(sw: dict, x_img: np.ndarray) -> np.ndarray:
 def dit_step(sw: dict, blocks, L: int, img_tokens, txt_feats, t: float,
              txt_cos, txt_sin, img_cos, img_sin, heads: int,
              kv_cache=None, capture: bool = False, dtype=np.float64,
-             return_x: bool = False):
+             return_x: bool = False, bf16: bool = False):
     """One DiT forward: img_tokens [N,64], txt_feats [L,D], t -> vel [N,64]
     (the DiT graph contract, [HOST] s.1).
 
@@ -269,12 +339,13 @@ def dit_step(sw: dict, blocks, L: int, img_tokens, txt_feats, t: float,
     kv_cache list of (k_txt, v_txt) per block: image rows only, text K/V read
     from the cache ([MLX] "Text K/V reuse").  capture=True returns the joint
     pass's text K/V per block as well.
+    bf16: the bf16-compute reading S11 (default: exact).
     Returns vel, or (vel, cache) when capture, plus x when return_x."""
     H = sw["w_img"].shape[0]
     n_blocks = len(blocks) if hasattr(blocks, "__len__") else None
     m_txt, m_img = modulation_rows(sw["w_mod"], sw["b_mod"], t, H, dtype)
     joint = kv_cache is None
-    x = embed(sw, img_tokens, txt_feats if joint else None, dtype)
+    x = embed(sw, img_tokens, txt_feats if joint else None, dtype, bf16=bf16)
     L_rows = L if joint else 0
     if joint:
         cos = np.concatenate([txt_cos, img_cos], axis=0)
@@ -285,7 +356,7 @@ def dit_step(sw: dict, blocks, L: int, img_tokens, txt_feats, t: float,
     it = blocks() if callable(blocks) else blocks
     for b, bw in enumerate(it):
         kv = None if joint else kv_cache[b]
-        x, kv_out = dit_block(x, L_rows, bw, m_txt, m_img, cos, sin, heads, kv)
+        x, kv_out = dit_block(x, L_rows, bw, m_txt, m_img, cos, sin, heads, kv, bf16=bf16)
         if capture:
             cache.append(kv_out)
     if n_blocks is not None and not joint:

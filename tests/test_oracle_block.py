@@ -212,8 +212,8 @@ def test_negative_control_causal_image_rows_move_vel():
     X = qs.img_tokens(WL); E = qs.txt_feats(WL)
     good = _step(sw, [bw], X, E, 0.6)
     bad_attn = planted(dit.block_causal_attention,
-                       "o_img = sdpa(q_img, k_all, v_all, causal=False)",
-                       "o_img = sdpa(q_img, k_img, v_img, causal=True)")
+                       "o_img = sdpa(q_img, k_all, v_all, causal=False, bf16=bf16)",
+                       "o_img = sdpa(q_img, k_img, v_img, causal=True, bf16=bf16)")
     bad = _step(sw, [bw], X, E, 0.6, step=step_with(block_causal_attention=bad_attn))
     assert dit.rel_l2(bad, good) > 2e-2
 
@@ -224,3 +224,47 @@ def test_metrics():
     b = a.copy(); b[3] = -b[3]
     assert dit.min_token_corr(b, a) < -0.99
     assert abs(dit.rel_l2(2 * a, a) - 1.0) < 1e-12
+
+
+def test_block_rows_equals_full_block():
+    """The row-sampled block (used for parity at full sizes) is the full block
+    restricted to the chosen rows, joint and image-only."""
+    sw, bw = _weights()
+    X = qs.img_tokens(WL); E = qs.txt_feats(WL)
+    tc, ts, ic, is_ = _rows()
+    m_txt, m_img = dit.modulation_rows(sw["w_mod"], sw["b_mod"], 0.7, WL.hidden)
+    x0 = dit.embed(sw, X, E)
+    cos, sin = np.concatenate([tc, ic]), np.concatenate([ts, is_])
+    full, kv = dit.dit_block(x0, WL.L, bw, m_txt, m_img, cos, sin, WL.heads)
+    rows = [0, 3, WL.L - 1, WL.L, WL.L + 17, WL.L + WL.N - 1]
+    part = dit.dit_block_rows(x0, WL.L, bw, m_txt, m_img, cos, sin, WL.heads, rows)
+    assert np.max(np.abs(part - full[rows])) < 1e-12 * np.max(np.abs(full))
+    fi, _ = dit.dit_block(x0[WL.L:], 0, bw, m_txt, m_img, ic, is_, WL.heads, kv_text=kv)
+    pi = dit.dit_block_rows(x0[WL.L:], 0, bw, m_txt, m_img, ic, is_, WL.heads, [0, 5, WL.N - 1], kv_text=kv)
+    assert np.max(np.abs(pi - fi[[0, 5, WL.N - 1]])) < 1e-12 * np.max(np.abs(fi))
+
+
+def test_round_bf16_closed_forms():
+    r = dit.round_bf16
+    one = np.float64(1.0)
+    assert r(np.array([one]))[0] == 1.0
+    assert r(np.array([1 + 2.0 ** -8]))[0] == 1.0                 # tie -> even mantissa
+    assert r(np.array([1 + 3 * 2.0 ** -8]))[0] == 1 + 2.0 ** -6    # tie -> even mantissa
+    assert r(np.array([1 + 2.0 ** -8 + 2.0 ** -20]))[0] == 1 + 2.0 ** -7
+    assert r(np.array([-3.0]))[0] == -3.0 and r(np.array([0.0]))[0] == 0.0
+    x = np.random.default_rng(0).standard_normal(10000)
+    y = r(x)
+    assert np.max(np.abs(y - x) / np.abs(x)) <= 2.0 ** -8
+    assert np.array_equal(r(y), y)
+
+
+def test_bf16_mode_stays_within_the_rounding_envelope():
+    """One block in the bf16-compute reading differs from the exact block by
+    more than round-off of fp64 and less than the bf16 band."""
+    sw, bw = _weights()
+    X = qs.img_tokens(WL); E = qs.txt_feats(WL)
+    tc, ts, ic, is_ = _rows()
+    exact = dit.dit_step(sw, [bw], WL.L, X, E, 0.7, tc, ts, ic, is_, WL.heads)
+    b16 = dit.dit_step(sw, [bw], WL.L, X, E, 0.7, tc, ts, ic, is_, WL.heads, bf16=True)
+    rel = dit.rel_l2(b16, exact)
+    assert 1e-4 < rel < 1e-2, rel

@@ -24,8 +24,8 @@ def _controls():
             "mt, mi = split_mod(m_img.astype(dt), H), split_mod(m_img.astype(dt), H)")),
         "scale instead of 1+scale": step_with(dit_block=planted(dit.dit_block, "(1.0 + s1)", "s1")),
         "image rows causal": step_with(block_causal_attention=planted(
-            dit.block_causal_attention, "o_img = sdpa(q_img, k_all, v_all, causal=False)",
-            "o_img = sdpa(q_img, k_img, v_img, causal=True)")),
+            dit.block_causal_attention, "o_img = sdpa(q_img, k_all, v_all, causal=False, bf16=bf16)",
+            "o_img = sdpa(q_img, k_img, v_img, causal=True, bf16=bf16)")),
     }
 
 
