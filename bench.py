@@ -45,7 +45,64 @@ def parse():
     p.add_argument("--workload", type=int, default=4)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--threads", type=int, default=16, help="host threads for weight generation")
+    p.add_argument("--calibrate-copy", action="store_true",
+                   help="only copy 1 GiB device-to-device (10 times): the known-size reference for "
+                        "scaling the HBM byte counters")
+    p.add_argument("--calibrate", action="store_true",
+                   help="only measure this GPU: register-only MFMA rates, copy bandwidth, vendor GEMM")
     return p.parse_args()
+
+
+def calibrate_copy():
+    import torch
+    n = (1 << 30) // 4
+    a = torch.ones(n, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(10):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibration": "device copy", "bytes_read": 4 * n, "bytes_written": 4 * n, "repeats": 10}))
+
+
+def calibrate():
+    """Sustained rates of the running part: the library's register-only MFMA
+    loops and copy kernel, and torch's (vendor library) bf16 GEMM on the four
+    projection shapes of the 1024^2 step."""
+    import ctypes
+
+    import torch
+    import torch.nn.functional as F
+
+    from block_causal_attention_qi_amd import _lib
+    lib = _lib.load()
+    res = {}
+    for shape, name in ((0, "mfma_32x32x16_bf16_tflops"), (1, "mfma_16x16x32_bf16_tflops")):
+        v = ctypes.c_double(0)
+        _lib.check(lib.qi_calib_mfma_tflops(shape, 20000, ctypes.byref(v)), "qi_calib_mfma_tflops")
+        res[name] = round(v.value, 1)
+    n = 1 << 30
+    a = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    v = ctypes.c_double(0)
+    _lib.check(lib.qi_calib_copy_gbs(a.data_ptr(), b.data_ptr(), n, 5, ctypes.byref(v)), "qi_calib_copy_gbs")
+    res["copy_gbs_read_plus_write"] = round(v.value, 1)
+    del a, b
+    gemm = {}
+    for (M, N, K) in [(4096, 24576, 4096), (4096, 12288, 4096), (4096, 4096, 12288), (4096, 4096, 4096)]:
+        A = torch.randn(M, K, device="cuda", dtype=torch.bfloat16)
+        W = torch.randn(N, K, device="cuda", dtype=torch.bfloat16)
+        for _ in range(3):
+            F.linear(A, W)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(10):
+            F.linear(A, W)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / 10
+        gemm[f"{M}x{N}x{K}"] = round(2 * M * N * K / (ms * 1e-3) / 1e12, 1)
+    res["vendor_bf16_gemm_tflops"] = gemm
+    print(json.dumps({"calibration": "MI355X", **res}))
 
 
 def cpu_baseline(wl):
@@ -75,8 +132,35 @@ def cpu_baseline(wl):
                       f"{dt:.2f} s per block scaled x{wl.n_blocks}"}
 
 
+def measured_traffic(kind: str):
+    """HBM bytes per image-only launch of `kind` from the committed rocprofv3
+    counter summary (FETCH_SIZE / WRITE_SIZE scaled by a 1 GiB copy), or None
+    when the kernel sources have changed since the counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "dit32_1024px_hbm_traffic.json")
+    try:
+        rec = json.load(open(path))
+    except (OSError, ValueError):
+        return None, "no counter summary"
+    csrc = os.path.join(ROOT, "block_causal_attention_qi_amd", "csrc")
+    src = "".join(open(os.path.join(csrc, f)).read()
+                  for f in ("common.hpp", "gemm.hpp", "attention.hpp", "elementwise.hpp"))
+    if hashlib.sha256(src.encode()).hexdigest() != rec.get("kernel_source_sha256"):
+        return None, "kernels changed since the counters were taken"
+    ent = rec.get("kernels", {}).get(kind, {}).get("image-only")
+    if not ent:
+        return None, "kernel not in the counter summary"
+    return int(ent["hbm_bytes"]), "profiles/dit32_1024px_hbm_traffic.json"
+
+
 def main():
     args = parse()
+    if args.calibrate_copy:
+        calibrate_copy()
+        return
+    if args.calibrate:
+        calibrate()
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (the DiT step here is built and measured on one MI355X); "
               f"--gpus {args.gpus} is not supported", file=sys.stderr)
@@ -190,6 +274,7 @@ def main():
         roof = {"kernel": dom, "bound": "hbm", "achieved": round(ach, 1), "peak": flops.PEAK_HBM_GBS,
                 "unit": "GB/s", "frac": round(ach / flops.PEAK_HBM_GBS, 4), "traffic": None,
                 "bytes_per_launch": db, "avg_launch_us": round(dms * 1e3, 2)}
+    roof["traffic"], roof["traffic_source"] = measured_traffic(dom)
     gemm_ms = sum(timing[k][0] for k in timing if k.startswith("gemm")) / n_img
     gemm_f = sum(work[k][0] * timing[k][1] for k in work if k.startswith("gemm") and k in timing) / n_img
     attn_ms = timing["attention"][0] / n_img

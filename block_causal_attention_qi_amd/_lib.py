@@ -74,6 +74,8 @@ SIGNATURES = {
     "qi_kernel_kind_name": (c_char_p, [c_int32]),
     "qi_timing_begin": (c_int32, [c_int32]),
     "qi_timing_end": (c_int32, [c_void_p, c_void_p, c_void_p]),
+    "qi_calib_mfma_tflops": (c_int32, [c_int32, c_int32, c_void_p]),
+    "qi_calib_copy_gbs": (c_int32, [c_void_p, c_void_p, c_int64, c_int32, c_void_p]),
 }
 QI_KERNEL_KINDS = 12
 

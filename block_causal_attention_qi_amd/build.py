@@ -59,6 +59,9 @@ def build(verbose: bool = False) -> str:
     if verbose and out.strip():
         print(out)
     objs.append(api_obj)
+    calib_obj = os.path.join(obj_dir, "calib.o")
+    _run([hipcc, *HIP_FLAGS, "-c", os.path.join(CSRC, "calib.hip"), "-o", calib_obj])
+    objs.append(calib_obj)
     tmp = LIB + ".tmp"
     _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp])
     os.replace(tmp, LIB)

@@ -1,0 +1,37 @@
+/*
+ * qi_calib.h -- calibration microbenchmarks of the MI355X the library runs on.
+ *
+ * Roofline fractions are quoted against the vendor peaks and against what this
+ * part measurably sustains: register-only MFMA throughput and a device copy.
+ * These calls are diagnostics for the benchmark, not part of the DiT step.
+ */
+#ifndef QI_CALIB_H_
+#define QI_CALIB_H_
+
+#include <stdint.h>
+
+#include "qi.h"
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Sustained bf16 MFMA throughput from a register-only loop on every CU:
+ * shape 0 = v_mfma_f32_32x32x16_bf16, shape 1 = v_mfma_f32_16x16x32_bf16.
+ * Runs `iters` iterations of 8 independent MFMA chains per wave on 8 workgroups
+ * of 256 threads per CU, timed with HIP events on an internal stream, and
+ * BLOCKS until done.  *tflops receives the result.  Errors: NULL, RANGE
+ * (shape not 0/1, iters < 1), HIP. */
+qi_status qi_calib_mfma_tflops(int32_t shape, int32_t iters, double *tflops);
+
+/* Sustained device-to-device copy bandwidth (bytes read + written per second,
+ * in GB/s) over `bytes` bytes (multiple of 16) between two caller buffers src
+ * and dst (device, 16-byte aligned, not overlapping), best of `reps` timed
+ * copies with HIP events; BLOCKS until done.  Errors: NULL, RANGE, ALIGN, HIP. */
+qi_status qi_calib_copy_gbs(const void *src, void *dst, int64_t bytes, int32_t reps, double *gbs);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QI_CALIB_H_ */

@@ -19,7 +19,8 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
 def _declared_symbols():
-    src = open(os.path.join(ROOT, "include", "qi.h")).read()
+    inc = os.path.join(ROOT, "include")
+    src = "".join(open(os.path.join(inc, f)).read() for f in sorted(os.listdir(inc)) if f.endswith(".h"))
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
     return sorted(set(re.findall(r"\b(qi_[a-z0-9_]+)\s*\(", src)))
 
@@ -38,7 +39,7 @@ no_gpu_only = pytest.mark.skipif(_gpu_visible(), reason="fake-pointer validation
 def test_library_loads_and_exports_every_declared_symbol():
     lib = _lib.load()
     decl = _declared_symbols()
-    assert len(decl) >= 15
+    assert len(decl) >= 20 and "qi_calib_mfma_tflops" in decl
     for name in decl:
         assert hasattr(lib, name), name
         assert name in _lib.SIGNATURES, f"binding misses {name}"
@@ -198,6 +199,12 @@ def test_capture_block_and_component_reject_bad_arguments():
     assert g(64, 100, 64, FAKE, FAKE, None, FAKE, None) == _lib.QI_ERR_RANGE
     assert g(64, 128, 96, FAKE, FAKE, None, FAKE, None) == _lib.QI_ERR_RANGE
     assert g(64, 128, 64, None, FAKE, None, FAKE, None) == _lib.QI_ERR_NULL
+    c = lib.qi_calib_mfma_tflops
+    out = ctypes.c_double(0)
+    assert c(2, 10, ctypes.byref(out)) == _lib.QI_ERR_RANGE
+    assert c(0, 10, None) == _lib.QI_ERR_NULL
+    assert lib.qi_calib_copy_gbs(FAKE, FAKE, 15, 1, ctypes.byref(out)) == _lib.QI_ERR_RANGE
+    assert lib.qi_calib_copy_gbs(FAKE_MIS, FAKE, 64, 1, ctypes.byref(out)) == _lib.QI_ERR_ALIGN
     m = lib.qi_modulation
     assert m(ctypes.byref(d), FAKE, FAKE, 2.0, FAKE, None) == _lib.QI_ERR_RANGE
     assert m(ctypes.byref(d), None, FAKE, 0.5, FAKE, None) == _lib.QI_ERR_NULL
