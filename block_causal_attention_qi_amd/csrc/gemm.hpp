@@ -319,21 +319,25 @@ __global__ __launch_bounds__(64 * WMN * WNN, 1) void gemm_bf16_large_kernel(cons
   const int wstep = (EPI == EPI_SWIGLU ? RPP / 2 : RPP) * g.ldw * 2;  // W bytes per fetch pass
   const int slot0 = lrow * 8 + (lc ^ ((lrow >> 1) & 7));  // row (lrow + RPP j) -> slot0 + 8 RPP j
 
-  u32x4 stA[NJ], stW[NJ];
-  auto gload = [&](int kt) {
+  // two register stages: slice kt+3 is fetched at the end of step kt and
+  // written to LDS at the end of step kt+2, so its latency is covered by two
+  // steps of MFMA work; the loop is unrolled by two to keep the stage index
+  // static
+  u32x4 stA[2][NJ], stW[2][NJ];
+  auto gload = [&](int st, int kt) {
     const int kb = kt * BK * 2;
 #pragma unroll
     for (int j = 0; j < NJ; ++j)
-      stA[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(ra, voff_a, RPP * j * g.lda * 2 + kb, 0));
+      stA[st][j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(ra, voff_a, RPP * j * g.lda * 2 + kb, 0));
 #pragma unroll
     for (int j = 0; j < NJ; ++j)
-      stW[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rw, voff_w, wstep * j + kb, 0));
+      stW[st][j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rw, voff_w, wstep * j + kb, 0));
   };
-  auto lstore = [&](int b) {
+  auto lstore = [&](int st, int b) {
 #pragma unroll
-    for (int j = 0; j < NJ; ++j) sA[b][slot0 + 8 * RPP * j] = stA[j];
+    for (int j = 0; j < NJ; ++j) sA[b][slot0 + 8 * RPP * j] = stA[st][j];
 #pragma unroll
-    for (int j = 0; j < NJ; ++j) sW[b][slot0 + 8 * RPP * j] = stW[j];
+    for (int j = 0; j < NJ; ++j) sW[b][slot0 + 8 * RPP * j] = stW[st][j];
   };
 
   f32x16 acc[FS][TS];
@@ -355,27 +359,63 @@ __global__ __launch_bounds__(64 * WMN * WNN, 1) void gemm_bf16_large_kernel(cons
 #pragma unroll
     for (int f = 0; f < FS; ++f) fw[set][f] = sW[b][(rowW + 32 * f) * 8 + ch];
   };
+  auto mfma_kk = [&](int set) {
+#pragma unroll
+    for (int f = 0; f < FS; ++f)
+#pragma unroll
+      for (int t = 0; t < TS; ++t) acc[f][t] = mfma32x32x16(fw[set][f], fa[set][t], acc[f][t]);
+  };
+  // Interleave n MFMAs with the LDS traffic issued next to them in program
+  // order: reads (and writes) of the next operands ride in the shadow of the
+  // MFMA pipe instead of stalling the wave between sub-steps.
+  auto interleave = [&](auto n_mfma, auto n_rd, auto n_wr) {
+    constexpr int NM = decltype(n_mfma)::value, NR = decltype(n_rd)::value, NW = decltype(n_wr)::value;
+#pragma unroll
+    for (int i = 0; i < NM; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);          // one MFMA
+      if (i < NR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+      if (i < NW) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);  // one LDS write
+    }
+  };
+  using I0 = std::integral_constant<int, 0>;
+  using I8 = std::integral_constant<int, FS * TS>;
+  using IR = std::integral_constant<int, FS + TS>;
+  using IW = std::integral_constant<int, 2 * NJ>;
 
   const int nk = g.K / BK;
-  gload(0);
-  lstore(0);
-  __syncthreads();
-  if (nk > 1) gload(1);
-
-  for (int kt = 0; kt < nk; ++kt) {
-    const int b = kt & 1;
-    fload(b, 0, 0);
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      if (kk < 3) fload(b, kk + 1, (kk + 1) & 1);
-#pragma unroll
-      for (int f = 0; f < FS; ++f)
-#pragma unroll
-        for (int t = 0; t < TS; ++t) acc[f][t] = mfma32x32x16(fw[kk & 1][f], fa[kk & 1][t], acc[f][t]);
-    }
-    if (kt + 1 < nk) lstore(b ^ 1);
+  // Step kt computes LDS buffer (kt & 1) whose 16-deep sub-step 0 fragments
+  // are already in register set 0.  During the MFMAs of sub-step kk the
+  // fragments of kk+1 are read; during sub-step 1 the staged slice kt+1 is
+  // written to the other LDS buffer.  After the barrier the freed register
+  // set receives slice kt+3 and sub-step 0 of the next buffer is read.  The
+  // body has no branches: past the last slice the loads repeat the last
+  // slice (in bounds, never used) and the stores fill a buffer never read.
+  auto step = [&](int kt, auto par) {
+    constexpr int P = decltype(par)::value;  // kt & 1
+    fload(P, 1, 1);
+    mfma_kk(0);
+    interleave(I8{}, IR{}, I0{});
+    lstore(P ^ 1, P ^ 1);
+    fload(P, 2, 0);
+    mfma_kk(1);
+    interleave(I8{}, IR{}, IW{});
+    fload(P, 3, 1);
+    mfma_kk(0);
+    interleave(I8{}, IR{}, I0{});
+    mfma_kk(1);
     __syncthreads();
-    if (kt + 2 < nk) gload(kt + 2);
+    gload(P ^ 1, min(kt + 3, nk - 1));
+    fload(P ^ 1, 0, 0);
+  };
+  gload(0, 0);
+  lstore(0, 0);
+  gload(1, min(1, nk - 1));
+  gload(0, min(2, nk - 1));
+  __syncthreads();
+  fload(0, 0, 0);
+  for (int kt = 0; kt < nk; kt += 2) {
+    step(kt, std::integral_constant<int, 0>{});
+    if (kt + 1 < nk) step(kt + 1, std::integral_constant<int, 1>{});
   }
 
   const int h4 = 4 * half;
