@@ -11,34 +11,37 @@
 // w = gamma (zero_centred: 1 + gamma) and scale is the modulation chunk of the
 // row's kind (rows < L_rows: mod row 0, else mod row 1; mod == NULL: 1).
 // The port page's DiT row: RMSNorm with modulation (spec step list);
-// ZeroCenterRMSNorm for the text projection.  H <= 8192, H % 4 == 0.
+// ZeroCenterRMSNorm for the text projection.  One wave per row (4 rows per
+// workgroup): each lane keeps VPL float4 of the row in registers, so the whole
+// row is in flight at once and the reduction is a pure wavefront reduction.
+// H % 256 == 0, H <= 256 * VPL.
+template <int VPL>
 __global__ __launch_bounds__(256) void rmsnorm_mod_kernel(const float *x, int ldx, const float *gamma,
                                                           int zero_centred, const float *mod,
-                                                          int mod_img_off, int L_rows, int H, float eps,
-                                                          u16 *out, int ldo) {
-  constexpr int MAXV = 8;
-  __shared__ float red[4];
-  const int r = blockIdx.x;
+                                                          int mod_img_off, int L_rows, int rows, int H,
+                                                          float eps, u16 *out, int ldo) {
+  const int lane = threadIdx.x & 63;
+  const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (r >= rows) return;
   const f32x4 *xr = (const f32x4 *)(x + (size_t)r * ldx);
-  const int nv = H >> 2;
-  f32x4 v[MAXV];
+  const int nv = H >> 8;  // float4 per lane
+  f32x4 v[VPL];
   float ss = 0.f;
 #pragma unroll
-  for (int i = 0; i < MAXV; ++i) {
-    const int idx = threadIdx.x + i * 256;
-    if (idx < nv) {
-      v[i] = xr[idx];
+  for (int i = 0; i < VPL; ++i) {
+    if (i < nv) {
+      v[i] = xr[lane + 64 * i];
       ss += v[i][0] * v[i][0] + v[i][1] * v[i][1] + v[i][2] * v[i][2] + v[i][3] * v[i][3];
     }
   }
-  ss = block_sum(ss, red);
+  ss = wave_sum(ss);
   const float inv = rsqrtf(ss / (float)H + eps);
   const float *sc = mod ? mod + (r < L_rows ? 0 : mod_img_off) : nullptr;
   u16 *orow = out + (size_t)r * ldo;
 #pragma unroll
-  for (int i = 0; i < MAXV; ++i) {
-    const int idx = threadIdx.x + i * 256;
-    if (idx < nv) {
+  for (int i = 0; i < VPL; ++i) {
+    if (i < nv) {
+      const int idx = lane + 64 * i;
       f32x4 w = ((const f32x4 *)gamma)[idx];
       if (zero_centred) w += 1.f;
       f32x4 y = v[i] * inv * w;

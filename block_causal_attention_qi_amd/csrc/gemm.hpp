@@ -287,7 +287,7 @@ __global__ __launch_bounds__(64 * WMN * WNN, 1) void gemm_bf16_large_kernel(cons
   constexpr int NJ = BM / RPP;                 // fetch passes per operand
   static_assert(FS % 2 == 0, "SwiGLU pairs gate/up slices inside a wave");
   static_assert(RPP % 32 == 0, "fetch pass covers whole 32-row slices");
-  static_assert(EPI != EPI_SWIGLU || RPP % 64 == 0, "SwiGLU fetch pass covers whole gate/up slice pairs");
+  static_assert(RPP == 32 || RPP == 64, "fetch pass of 32 or 64 rows");
   __shared__ u32x4 sA[2][BM * 8];
   __shared__ u32x4 sW[2][BN * 8];
 
@@ -309,14 +309,22 @@ __global__ __launch_bounds__(64 * WMN * WNN, 1) void gemm_bf16_large_kernel(cons
   const int voff_a = ((m0 + lrow) * g.lda + lc * 8) * 2;
   // SwiGLU: W tile rows alternate 32-row gate / up slices for the same 32
   // outputs, i.e. tile row r reads W row tn*128 + (r>>6)*32 + (r&31) (+F when
-  // bit 5 of r is set) -- for r = lrow + RPP j with RPP a multiple of 64.
+  // bit 5 of r is set).  For r = lrow + RPP j the lrow part goes into the VGPR
+  // offset and the pass part (uniform) into the SGPR offset.
   int wrow0;
   if constexpr (EPI == EPI_SWIGLU)
     wrow0 = tn * (BN / 2) + ((lrow >> 6) * 32) + (lrow & 31) + ((lrow >> 5) & 1) * g.F;
   else
     wrow0 = tn * BN + lrow;
   const int voff_w = (wrow0 * g.ldw + lc * 8) * 2;
-  const int wstep = (EPI == EPI_SWIGLU ? RPP / 2 : RPP) * g.ldw * 2;  // W bytes per fetch pass
+  auto soff_w = [&](int j) {
+    if constexpr (EPI == EPI_SWIGLU) {
+      const int s32 = RPP * j / 32;  // 32-row slices before pass j
+      return ((s32 >> 1) * 32 + (s32 & 1) * g.F) * g.ldw * 2;
+    } else {
+      return RPP * j * g.ldw * 2;
+    }
+  };
   const int slot0 = lrow * 8 + (lc ^ ((lrow >> 1) & 7));  // row (lrow + RPP j) -> slot0 + 8 RPP j
 
   // two register stages: slice kt+3 is fetched at the end of step kt and
@@ -331,7 +339,7 @@ __global__ __launch_bounds__(64 * WMN * WNN, 1) void gemm_bf16_large_kernel(cons
       stA[st][j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(ra, voff_a, RPP * j * g.lda * 2 + kb, 0));
 #pragma unroll
     for (int j = 0; j < NJ; ++j)
-      stW[st][j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rw, voff_w, wstep * j + kb, 0));
+      stW[st][j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rw, voff_w, soff_w(j) + kb, 0));
   };
   auto lstore = [&](int st, int b) {
 #pragma unroll

@@ -35,7 +35,7 @@ bool dims_ok(const qi_dims *d) {
   if (d->hidden < 256 || d->hidden > 8192 || d->hidden % 256 != 0) return false;
   if (d->heads * 128 != d->hidden) return false;
   if (d->ffn < 64 || d->ffn % 64 != 0 || d->ffn > 65536) return false;
-  if (d->txt_dim < 64 || d->txt_dim % 64 != 0 || d->txt_dim > 8192) return false;
+  if (d->txt_dim < 256 || d->txt_dim % 256 != 0 || d->txt_dim > 8192) return false;
   if (d->n_blocks < 1 || d->n_blocks > 256) return false;
   return true;
 }
@@ -149,8 +149,13 @@ qi_status launch_gemm(const GemmArgs &g, int kind, hipStream_t s) {
 qi_status launch_norm(const float *x, int ldx, const float *gamma, int zc, const float *mod,
                       int mod_img_off, int L_rows, int rows, int H, u16 *out, int ldo, hipStream_t s) {
   TimedLaunch tl(zc ? QI_KERNEL_TXT_NORM : QI_KERNEL_NORM_MOD, s);
-  hipLaunchKernelGGL(rmsnorm_mod_kernel, dim3(rows), dim3(256), 0, s, x, ldx, gamma, zc, mod,
-                     mod_img_off, L_rows, H, kRmsEps, out, ldo);
+  const dim3 grid((rows + 3) / 4);
+  if (H <= 4096)
+    hipLaunchKernelGGL(rmsnorm_mod_kernel<16>, grid, dim3(256), 0, s, x, ldx, gamma, zc, mod, mod_img_off, L_rows,
+                       rows, H, kRmsEps, out, ldo);
+  else
+    hipLaunchKernelGGL(rmsnorm_mod_kernel<32>, grid, dim3(256), 0, s, x, ldx, gamma, zc, mod, mod_img_off, L_rows,
+                       rows, H, kRmsEps, out, ldo);
   return last_launch();
 }
 

@@ -57,8 +57,8 @@ typedef int32_t qi_status;
 #define QI_MODE_IMAGE_ONLY 1
 
 /* Model dimensions.  head_dim must be 128 and heads = hidden / 128 ([PORT] DiT
- * row: 32 heads x 128 at hidden 4096).  hidden % 128 == 0, ffn % 64 == 0,
- * txt_dim % 64 == 0, 1 <= n_blocks <= 256. */
+ * row: 32 heads x 128 at hidden 4096).  hidden % 256 == 0 (256..8192),
+ * ffn % 64 == 0, txt_dim % 256 == 0 (256..8192), 1 <= n_blocks <= 256. */
 typedef struct {
   int32_t hidden, heads, head_dim, ffn, n_blocks, txt_dim;
 } qi_dims;
