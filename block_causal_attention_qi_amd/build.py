@@ -24,6 +24,9 @@ HIP_FLAGS = [
     # packed fp32 ops stay off: hipcc would otherwise form v_pk_* fp32 math
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-munsafe-fp-atomics", "-Wno-unused-result",
+    # MFMA accumulators in the VGPR form: the attention kernel (one wave per
+    # SIMD, 512 registers) otherwise spills its softmax state to scratch
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
 ]
 
 

@@ -11,21 +11,30 @@
 // image row computes bit-identical results in a joint pass and in an
 // image-only pass that reads the cached text K/V.
 //
-// Per workgroup: 256 queries (8 waves x 32), key tiles of 64 staged through
-// LDS (double buffered), MFMA 32x32x16 bf16 (the full-rate shape on gfx950).
+// Per workgroup: 256 queries (8 waves x 32, two waves per SIMD), key tiles of
+// 64 copied global -> LDS directly and double buffered.  A single wave issues
+// VALU work at about half rate and hides only a few VALU instructions behind
+// each of its own MFMAs (measured on MI355X), so each wave is software
+// pipelined (the exponentials of tile t run between the score MFMAs of tile
+// t+1) and the second wave on each SIMD fills the rest.  MFMA 32x32x16 bf16
+// (the full-rate shape on gfx950).
 // S^T = K Q^T: the A operand takes the tile's K rows in the order
 // kappa(i) = 16*(i/16) + 8*((i/4)&1) + 4*((i/8)&1) + (i&3), which leaves each
 // lane holding 8 CONSECUTIVE keys of one query per 16-key step.  Those
 // exponentiated scores, packed to bf16, are directly the B operand of
 // O^T = V^T P^T, whose A operand is then one contiguous 16-byte read of a V^T
 // row.  V is consumed as V^T [heads][128][Tp], which the QKV epilogue writes.
-// Softmax statistics are fp32 in the log2 domain; each query's 64 scores of a
-// tile are split over two lanes (l and l^32).  The running max is raised only
+// Softmax statistics are fp32 in the log2 domain (scores enter exp2 through
+// one FMA with the folded scale); each query's 64 scores of a tile are split
+// over two lanes (l and l^32).  The running sum adds the bf16-rounded
+// probabilities (the values the PV product multiplies), two per dot2.  The running max is raised only
 // when a tile's max exceeds it by more than 8 (a factor of 256), so the
 // accumulator rescale is rare; the probabilities then stay below 2^8, far from
 // fp32 or bf16 overflow, and the final division by the running sum cancels the
 // choice exactly in real arithmetic.
 #pragma once
+
+#include <type_traits>
 
 #include "common.hpp"
 
@@ -42,34 +51,63 @@ struct AttnArgs {
 };
 
 namespace attn {
-constexpr int BQ = 256;
+constexpr int WAVES = 8;
+constexpr int BQ = WAVES * 32;           // queries per workgroup, 32 per wave
 constexpr int BKV = 64;
-constexpr int THREADS = 512;
+constexpr int THREADS = 64 * WAVES;
 constexpr int NLD = BKV * 16 / THREADS;  // 16-byte K (and V^T) chunks per thread per tile
-constexpr float RESCALE_SLACK = 8.f;   // log2 units
+constexpr float RESCALE_SLACK = 8.f;     // log2 units
 }  // namespace attn
 
 // key (within a 32-key block) fed by A-operand row i, so that output row
 // 8j + 4h + r holds key 16*(j>>1) + 8h + 4*(j&1) + r
 QI_DEV int kappa(int i) { return ((i >> 4) << 4) + (((i >> 2) & 1) << 3) + (((i >> 3) & 1) << 2) + (i & 3); }
 
+// Schedule of one 16-read / 16-MFMA phase: each LDS fragment read is issued
+// two MFMAs ahead of the one that consumes it.
+QI_DEV void interleave_reads_mfma() {
+  __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+#pragma unroll
+  for (int i = 0; i < 14; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+}
+
+// sum += lo + hi of a packed bf16 pair, in fp32
+QI_DEV float add_bf16x2(uint32_t pair, float sum) {
+  const bf16x2 one = {(__bf16)1.f, (__bf16)1.f};
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pair), one, sum, false);
+}
+
 __global__ __launch_bounds__(attn::THREADS, 1) void block_causal_attn_kernel(const AttnArgs a) {
   using namespace attn;
-  __shared__ u32x4 sK[2][BKV * 16];  // [key][16 chunks of 8 d], chunk c at c ^ (key & 15)
-  __shared__ u32x4 sV[2][128 * 8];   // [d][8 chunks of 8 keys], chunk c at c ^ ((d >> 1) & 7)
+  // Double buffers as four separate objects, always indexed by a constant:
+  // the compiler then knows that a copy into one buffer does not alias reads
+  // of the other and does not make those reads wait for the copy.
+  __shared__ u32x4 sK0[BKV * 16], sK1[BKV * 16];  // [key][16 chunks of 8 d], chunk c at c ^ (key & 15)
+  __shared__ u32x4 sV0[128 * 8], sV1[128 * 8];    // [d][8 chunks of 8 keys], chunk c at c ^ ((d >> 1) & 7)
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, h = lane >> 5;
-  const int head = blockIdx.y;
-  int qt = blockIdx.x;
+  // Workgroups are dispatched round-robin over the 8 XCDs (each with its own
+  // L2); renumber them so that each XCD works through whole heads, whose
+  // query tiles then stream the same K/V tiles at about the same time.
+  const int tiles_per_head = gridDim.x, G = gridDim.x * gridDim.y;
+  int wg = blockIdx.x + gridDim.x * blockIdx.y;
+  if ((G & 7) == 0) wg = (wg & 7) * (G >> 3) + (wg >> 3);
+  const int head = wg / tiles_per_head;
+  int qt = wg - head * tiles_per_head;
   const bool img = qt < a.n_img_qt;
   if (!img) qt -= a.n_img_qt;
   const int q0 = qt * BQ;
+  const int wq0 = q0 + wave * 32;  // this wave's first query
   const int seg_q = img ? a.N : a.L;
+  const int qrow = wq0 + l32;
   const u16 *Q = (img ? a.q_i : a.q_t) + (size_t)head * seg_q * 128;
 
   // B operand of S^T: Q[q][16 ds + 8 h .. +8] for this lane's query
-  const int qrow = q0 + wave * 32 + l32;
   u32x4 qreg[8];
   {
     const int r = min(qrow, seg_q - 1);
@@ -92,42 +130,88 @@ __global__ __launch_bounds__(attn::THREADS, 1) void block_causal_attn_kernel(con
   const u16 *Ki = a.k_i + (size_t)head * a.N * 128;
   const u16 *Vti = a.vt_i + (size_t)head * 128 * a.ldv_i;
 
-  u32x4 rk[NLD], rv[NLD];
-  auto gload = [&](int t) {
+  // Tiles are copied global -> LDS directly (no register staging): lane l of
+  // a wave-wide copy lands at 16 l past the wave's base, so the swizzle is
+  // applied on the global side by choosing which chunk each lane fetches.
+  auto tile_src = [&](int t, const u16 *&K, const u16 *&Vt, int &key0, int &klen, int &ldv) {
     const bool tx = t < nt_t;
-    const u16 *K = tx ? Kt : Ki;
-    const u16 *Vt = tx ? Vtt : Vti;
-    const int key0 = (tx ? t : t - nt_t) * BKV;
-    const int klen = tx ? a.L : a.N;
-    const int ldv = tx ? a.ldv_t : a.ldv_i;
+    K = tx ? Kt : Ki;
+    Vt = tx ? Vtt : Vti;
+    key0 = (tx ? t : t - nt_t) * BKV;
+    klen = tx ? a.L : a.N;
+    ldv = tx ? a.ldv_t : a.ldv_i;
+  };
+  auto copy_k = [&](int t, auto B) {
+    u32x4 *sk = B.value ? sK1 : sK0;
+    const u16 *K, *Vt;
+    int key0, klen, ldv;
+    tile_src(t, K, Vt, key0, klen, ldv);
 #pragma unroll
     for (int j = 0; j < NLD; ++j) {
-      const int i = tid + THREADS * j;
-      const int kr = i >> 4, kc = i & 15;
+      const int slot0 = (j * WAVES + wave) * 64;
+      const int i = slot0 + lane;
+      const int kr = i >> 4, kc = (i & 15) ^ (kr & 15);
       const int key = min(key0 + kr, klen - 1);  // rows past the segment: masked below
-      rk[j] = *(const u32x4 *)(K + (size_t)key * 128 + kc * 8);
-      const int vr = i >> 3, vc = i & 7;
-      const int kb = key0 + vc * 8;  // in bounds: ldv >= key0 + 64
-      u32x4 v = *(const u32x4 *)(Vt + (size_t)vr * ldv + kb);
-      if (kb + 8 > klen) {  // tail of the segment: padding columns become exact zeros
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int k2 = kb + 2 * e;
-          const uint32_t keep = (k2 < klen ? 0x0000FFFFu : 0u) | (k2 + 1 < klen ? 0xFFFF0000u : 0u);
-          v[e] &= keep;
-        }
-      }
-      rv[j] = v;
+      __builtin_amdgcn_global_load_lds((const void *)(K + (size_t)key * 128 + kc * 8),
+                                       (__attribute__((address_space(3))) void *)&sk[slot0], 16, 0, 0);
     }
   };
-  auto lstore = [&](int b) {
+  auto copy_v = [&](int t, auto B) {
+    u32x4 *sv = B.value ? sV1 : sV0;
+    const u16 *K, *Vt;
+    int key0, klen, ldv;
+    tile_src(t, K, Vt, key0, klen, ldv);
 #pragma unroll
     for (int j = 0; j < NLD; ++j) {
-      const int i = tid + THREADS * j;
-      const int kr = i >> 4, kc = i & 15;
-      sK[b][kr * 16 + (kc ^ (kr & 15))] = rk[j];
-      const int vr = i >> 3, vc = i & 7;
-      sV[b][vr * 8 + (vc ^ ((vr >> 1) & 7))] = rv[j];
+      const int slot0 = (j * WAVES + wave) * 64;
+      const int i = slot0 + lane;
+      const int vr = i >> 3, vc = (i & 7) ^ ((vr >> 1) & 7);
+      // in bounds: ldv >= key0 + 64
+      __builtin_amdgcn_global_load_lds((const void *)(Vt + (size_t)vr * ldv + key0 + vc * 8),
+                                       (__attribute__((address_space(3))) void *)&sv[slot0], 16, 0, 0);
+    }
+  };
+  // V^T columns past the segment's end (padding, any bit pattern) become exact
+  // zeros, so that their zero probabilities contribute exact zeros.  Only the
+  // segment's last tile has them; the caller brackets this with barriers.
+  auto zero_v_tail = [&](int t, auto B) {
+    const u16 *K, *Vt;
+    int key0, klen, ldv;
+    tile_src(t, K, Vt, key0, klen, ldv);
+    const int valid = klen - key0;
+    if (valid >= BKV) return;
+    const int npad = BKV - valid;
+    u16 *sv = (u16 *)(B.value ? sV1 : sV0);
+    for (int i = tid; i < 128 * npad; i += THREADS) {
+      const int vr = i / npad, col = valid + i % npad;
+      sv[(vr * 8 + ((col >> 3) ^ ((vr >> 1) & 7))) * 8 + (col & 7)] = 0;
+    }
+  };
+  auto v_tail = [&](int t) {
+    const bool tx = t < nt_t;
+    return ((tx ? t : t - nt_t) + 1) * BKV > (tx ? a.L : a.N);
+  };
+
+  // K row this lane feeds to the S^T MFMA in each 32-key block
+  const int krow_l = kappa(l32);
+  const int vsw = (l32 >> 1) & 7;
+  const float c = a.scale_log2;
+
+  // S^T for 64 keys (2 blocks of 32) x this wave's 32 queries from sK[b]
+  auto scores = [&](auto B, f32x16 *s) {
+    const u32x4 *sk = B.value ? sK1 : sK0;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) s[kb][e] = 0.f;
+#pragma unroll
+    for (int ds = 0; ds < 8; ++ds) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const int kr = kb * 32 + krow_l;
+        const u32x4 ka = sk[kr * 16 + ((2 * ds + h) ^ (kr & 15))];
+        s[kb] = mfma32x32x16(ka, qreg[ds], s[kb]);
+      }
     }
   };
 
@@ -138,86 +222,96 @@ __global__ __launch_bounds__(attn::THREADS, 1) void block_causal_attn_kernel(con
 #pragma unroll
     for (int e = 0; e < 16; ++e) oacc[d][e] = 0.f;
 
-  // K row this lane feeds to the S^T MFMA in each 32-key block
-  const int krow_l = kappa(l32);
-  const int vsw = (l32 >> 1) & 7;
-
-  gload(0);
-  lstore(0);
+  // Software pipeline: iteration t exponentiates the scores of tile t while
+  // the MFMAs of tile t+1's scores run, then accumulates tile t's P V.  K runs
+  // two tiles ahead in LDS and V one: iteration t copies K(t+2) into sK[t&1]
+  // and V(t+1) into sV[(t+1)&1], both freed by the previous iteration.
+  constexpr std::integral_constant<int, 0> B0{};
+  constexpr std::integral_constant<int, 1> B1{};
+  copy_k(0, B0);
+  copy_v(0, B0);
+  if (ntiles > 1) copy_k(1, B1);
   __syncthreads();
+  if (v_tail(0)) {
+    zero_v_tail(0, B0);
+    __syncthreads();
+  }
+  f32x16 s_cur[2];
+  scores(B0, s_cur);
+  __syncthreads();  // sK0 is overwritten next
 
-  for (int t = 0; t < ntiles; ++t) {
-    const int b = t & 1;
-    const bool more = t + 1 < ntiles;
-    if (more) gload(t + 1);
+  // one iteration; B = t & 1 as a constant
+  auto iteration = [&](int t, auto B) {
+    constexpr std::integral_constant<int, 1 - B.value> NB{};
+    if (t + 2 < ntiles) copy_k(t + 2, B);
+    if (t + 1 < ntiles) copy_v(t + 1, NB);
 
-    // S^T for 64 keys (2 blocks of 32) x this wave's 32 queries
-    f32x16 s[2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) s[kb][e] = 0.f;
-#pragma unroll
-    for (int ds = 0; ds < 8; ++ds) {
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const int kr = kb * 32 + krow_l;
-        const u32x4 ka = sK[b][kr * 16 + ((2 * ds + h) ^ (kr & 15))];
-        s[kb] = mfma32x32x16(ka, qreg[ds], s[kb]);
-      }
-    }
-
+    // element e of block kb holds key key0 + 32 kb + 16 (e >> 3) + 8 h + (e & 7)
     const bool tx = t < nt_t;
     const int key0 = (tx ? t : t - nt_t) * BKV;
     const int klen = tx ? a.L : a.N;
     const bool causal = !img;
-    const bool need_mask = (key0 + BKV > klen) || (causal && key0 + BKV - 1 > q0 + wave * 32);
-
-    // element e of block kb holds key key0 + 32 kb + 16 (e >> 3) + 8 h + (e & 7)
-    float mx = -INFINITY;
+    if ((key0 + BKV > klen) || (causal && key0 + BKV - 1 > wq0)) {
+      // keys at or past lim are masked: the segment's end, and for text
+      // queries every key after the query (block-causal inside the text)
+      const int lim = min(klen, causal ? qrow + 1 : klen) - key0 - 8 * h;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        float v = s[kb][e] * a.scale_log2;
-        if (need_mask) {
-          const int key = key0 + 32 * kb + 16 * (e >> 3) + 8 * h + (e & 7);
-          const bool ok = key < klen && (!causal || key <= qrow);
-          v = ok ? v : -INFINITY;
-        }
-        s[kb][e] = v;
-        mx = fmaxf(mx, v);
-      }
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    // raise the running max only past the slack; every lane of the wave
-    // follows the same rule, and only a raised max costs a rescale
+        for (int e = 0; e < 16; ++e)
+          if (32 * kb + 16 * (e >> 3) + (e & 7) >= lim) s_cur[kb][e] = -INFINITY;
+    }
+    // tile max over this lane's 32 scores (three-way max) and the partner lane's
+    float mx = fmaxf(s_cur[0][0], s_cur[0][1]);
+#pragma unroll
+    for (int e = 2; e < 32; e += 2) mx = fmaxf(fmaxf(mx, s_cur[e >> 4][e & 15]), s_cur[e >> 4][(e & 15) + 1]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * c;
+    // raise the running max only past the slack; only a raised max costs
+    // a rescale of the accumulators
     const bool raise = mx > m_run + RESCALE_SLACK;
     float alpha = 1.f;
     if (raise) {
       alpha = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - mx);
       m_run = mx;
     }
-    const float base = m_run == -INFINITY ? 0.f : m_run;
-    float psum = 0.f;
-    u32x4 pb[4];  // B operand per 16-key step c4 = 2 kb + c: keys 16 c4 + 8 h .. +8
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      float p[16];
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        p[e] = __builtin_amdgcn_exp2f(s[kb][e] - base);
-        psum += p[e];
-      }
-#pragma unroll
-      for (int c = 0; c < 2; ++c)
-        pb[2 * kb + c] = u32x4{pack_bf16x2(p[8 * c], p[8 * c + 1]), pack_bf16x2(p[8 * c + 2], p[8 * c + 3]),
-                               pack_bf16x2(p[8 * c + 4], p[8 * c + 5]), pack_bf16x2(p[8 * c + 6], p[8 * c + 7])};
-    }
-    l_run = l_run * alpha + psum;
     if (__any(raise)) {
 #pragma unroll
       for (int d = 0; d < 4; ++d) oacc[d] *= alpha;
     }
+    const float nbase = m_run == -INFINITY ? 0.f : -m_run;
+
+    // scores of tile t+1 (discarded past the last tile: sK[b^1] then holds
+    // stale or uninitialised data, never used)
+    f32x16 s_next[2];
+    scores(NB, s_next);
+
+    u32x4 pb[4];  // B operand per 16-key step c4 = 2 kb + cc: keys 16 c4 + 8 h .. +8
+    float psum = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int cc = 0; cc < 2; ++cc) {
+        u32x4 w;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const int e = 8 * cc + 2 * k;
+          w[k] = pack_bf16x2(__builtin_amdgcn_exp2f(__builtin_fmaf(s_cur[kb][e], c, nbase)),
+                             __builtin_amdgcn_exp2f(__builtin_fmaf(s_cur[kb][e + 1], c, nbase)));
+          psum = add_bf16x2(w[k], psum);
+        }
+        pb[2 * kb + cc] = w;
+      }
+    l_run = l_run * alpha + psum;
+    // interleave: the 16 score MFMAs of tile t+1 with their K reads and the
+    // exponentials of tile t
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+#pragma unroll
+    for (int i = 0; i < 14; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
 
     // O^T[d][q] += V^T[d][16 c4 + 8h .. +8] P^T
 #pragma unroll
@@ -225,16 +319,26 @@ __global__ __launch_bounds__(attn::THREADS, 1) void block_causal_attn_kernel(con
 #pragma unroll
       for (int db = 0; db < 4; ++db) {
         const int vr = db * 32 + l32;
-        const u32x4 va = sV[b][vr * 8 + ((2 * c4 + h) ^ vsw)];
+        const u32x4 va = (B.value ? sV1 : sV0)[vr * 8 + ((2 * c4 + h) ^ vsw)];
         oacc[db] = mfma32x32x16(va, pb[c4], oacc[db]);
       }
     }
+    interleave_reads_mfma();
 
-    if (more) lstore(b ^ 1);
+    s_cur[0] = s_next[0];
+    s_cur[1] = s_next[1];
     __syncthreads();
+    if (t + 1 < ntiles && v_tail(t + 1)) {
+      zero_v_tail(t + 1, NB);
+      __syncthreads();
+    }
+  };
+  for (int t = 0; t < ntiles; t += 2) {
+    iteration(t, B0);
+    if (t + 1 < ntiles) iteration(t + 1, B1);
   }
 
-  float l = l_run + __shfl_xor(l_run, 32, 64);
+  const float l = l_run + __shfl_xor(l_run, 32, 64);
   const float inv = 1.f / l;
   if (qrow < seg_q) {
     const int orow = (img ? a.o_img_row0 : 0) + qrow;

@@ -7,6 +7,7 @@
 
 typedef uint16_t u16;
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -19,8 +20,10 @@ QI_DEV float bf16_to_f32(u16 b) { return __uint_as_float(uint32_t(b) << 16); }
 // fp32 -> bf16, round to nearest even (the hardware conversion on gfx950).
 QI_DEV u16 f32_to_bf16(float f) { return __builtin_bit_cast(u16, (__bf16)f); }
 
+// Two fp32 -> one packed bf16 pair (lo in bits 0..15), one v_cvt_pk_bf16_f32.
 QI_DEV uint32_t pack_bf16x2(float lo, float hi) {
-  return uint32_t(f32_to_bf16(lo)) | (uint32_t(f32_to_bf16(hi)) << 16);
+  const bf16x2 v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
 }
 
 QI_DEV bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
