@@ -144,7 +144,7 @@ def measured_traffic(kind: str):
         return None, "no counter summary"
     csrc = os.path.join(ROOT, "block_causal_attention_qi_amd", "csrc")
     src = "".join(open(os.path.join(csrc, f)).read()
-                  for f in ("common.hpp", "gemm.hpp", "attention.hpp", "elementwise.hpp"))
+                  for f in ("common.hpp", "gemm.hpp", "attention_args.hpp", "attention.hpp", "elementwise.hpp"))
     if hashlib.sha256(src.encode()).hexdigest() != rec.get("kernel_source_sha256"):
         return None, "kernels changed since the counters were taken"
     ent = rec.get("kernels", {}).get(kind, {}).get("image-only")

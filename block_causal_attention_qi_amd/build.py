@@ -24,10 +24,11 @@ HIP_FLAGS = [
     # packed fp32 ops stay off: hipcc would otherwise form v_pk_* fp32 math
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-munsafe-fp-atomics", "-Wno-unused-result",
-    # MFMA accumulators in the VGPR form: the attention kernel (one wave per
-    # SIMD, 512 registers) otherwise spills its softmax state to scratch
-    "-mllvm", "-amdgpu-mfma-vgpr-form",
 ]
+# The attention kernel's translation unit keeps MFMA accumulators in VGPRs
+# (two waves per SIMD share the VGPR file with the softmax state); the GEMM
+# kernels keep the default AGPR accumulators (256 per lane in the 4-wave tile).
+ATTN_FLAGS = ["-mllvm", "-amdgpu-mfma-vgpr-form"]
 
 
 def _hipcc() -> str:
@@ -59,9 +60,12 @@ def build(verbose: bool = False) -> str:
     objs.append(host_obj)
     api_obj = os.path.join(obj_dir, "qi_api.o")
     out = _run([hipcc, *HIP_FLAGS, "-c", os.path.join(CSRC, "qi_api.hip"), "-o", api_obj])
+    attn_obj = os.path.join(obj_dir, "attention.o")
+    out += _run([hipcc, *HIP_FLAGS, *ATTN_FLAGS, "-c", os.path.join(CSRC, "attention.hip"), "-o", attn_obj])
     if verbose and out.strip():
         print(out)
     objs.append(api_obj)
+    objs.append(attn_obj)
     calib_obj = os.path.join(obj_dir, "calib.o")
     _run([hipcc, *HIP_FLAGS, "-c", os.path.join(CSRC, "calib.hip"), "-o", calib_obj])
     objs.append(calib_obj)

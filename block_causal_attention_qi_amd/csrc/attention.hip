@@ -1,0 +1,9 @@
+// Translation unit of the attention kernel.  It is compiled with
+// -amdgpu-mfma-vgpr-form: with two waves per SIMD and 256 registers each, the
+// score and output accumulators must share the VGPR file with the softmax
+// state; in the default (AGPR) form the compiler spills.
+#include "attention.hpp"
+
+void launch_block_causal_attn(const AttnArgs &a, hipStream_t s) {
+  hipLaunchKernelGGL(block_causal_attn_kernel, dim3(a.n_img_qt + a.n_txt_qt, a.heads), dim3(attn::THREADS), 0, s, a);
+}

@@ -27,37 +27,19 @@
 // Softmax statistics are fp32 in the log2 domain (scores enter exp2 through
 // one FMA with the folded scale); each query's 64 scores of a tile are split
 // over two lanes (l and l^32).  The running sum adds the bf16-rounded
-// probabilities (the values the PV product multiplies), two per dot2.  The running max is raised only
-// when a tile's max exceeds it by more than 8 (a factor of 256), so the
-// accumulator rescale is rare; the probabilities then stay below 2^8, far from
-// fp32 or bf16 overflow, and the final division by the running sum cancels the
-// choice exactly in real arithmetic.
+// probabilities (the values the PV product multiplies), two per dot2.  The
+// running max is raised only when a tile's max exceeds it by more than 8 (a
+// factor of 256), so the accumulator rescale is rare; the probabilities then
+// stay below 2^8, far from fp32 or bf16 overflow, and the final division by
+// the running sum cancels the choice exactly in real arithmetic.
 #pragma once
 
 #include <type_traits>
 
 #include "common.hpp"
 
-struct AttnArgs {
-  const u16 *q_t, *k_t, *vt_t;  // text segment  (q_t unused when n_txt_qt == 0)
-  const u16 *q_i, *k_i, *vt_i;  // image segment
-  u16 *o;
-  int ldo;                       // heads * 128
-  int heads, L, N;
-  int ldv_t, ldv_i;              // V^T row strides (>= segment length rounded up to 64)
-  int n_img_qt, n_txt_qt;        // query tiles of BQ per head
-  int o_img_row0;                // output row of image query 0 (L in a joint pass, else 0)
-  float scale_log2;              // log2(e) / sqrt(128)
-};
+#include "attention_args.hpp"
 
-namespace attn {
-constexpr int WAVES = 8;
-constexpr int BQ = WAVES * 32;           // queries per workgroup, 32 per wave
-constexpr int BKV = 64;
-constexpr int THREADS = 64 * WAVES;
-constexpr int NLD = BKV * 16 / THREADS;  // 16-byte K (and V^T) chunks per thread per tile
-constexpr float RESCALE_SLACK = 8.f;     // log2 units
-}  // namespace attn
 
 // key (within a 32-key block) fed by A-operand row i, so that output row
 // 8j + 4h + r holds key 16*(j>>1) + 8h + 4*(j&1) + r

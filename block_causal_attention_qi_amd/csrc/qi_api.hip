@@ -9,7 +9,7 @@
 #include <vector>
 
 #include "../../include/qi.h"
-#include "attention.hpp"
+#include "attention_args.hpp"
 #include "elementwise.hpp"
 #include "gemm.hpp"
 
@@ -135,11 +135,12 @@ qi_status launch_gemm(const GemmArgs &g, int kind, hipStream_t s) {
   const int n_out = EPI == EPI_SWIGLU ? g.F : g.N;
   const int per_tile_big = EPI == EPI_SWIGLU ? 128 : 256;
   const int nTM_big = (g.M + 255) / 256;
-  const bool big = n_out % per_tile_big == 0 && nTM_big * (n_out / per_tile_big) >= 256 &&
-                   (size_t)g.M * g.lda * 2 < (1ull << 31) && (size_t)(EPI == EPI_SWIGLU ? 2 * g.F : g.N) * g.ldw * 2 < (1ull << 31);
+  const int tiles_big = n_out % per_tile_big == 0 ? nTM_big * (n_out / per_tile_big) : 0;
+  const bool fits32 = (size_t)g.M * g.lda * 2 < (1ull << 31) &&
+                      (size_t)(EPI == EPI_SWIGLU ? 2 * g.F : g.N) * g.ldw * 2 < (1ull << 31);
   TimedLaunch tl(kind, s);
-  if (big)
-    hipLaunchKernelGGL((gemm_bf16_large_kernel<EPI, QI_GEMM_WM, QI_GEMM_WN>), dim3(nTM_big * (n_out / per_tile_big)),
+  if (fits32 && tiles_big >= 256)
+    hipLaunchKernelGGL((gemm_bf16_large_kernel<EPI, QI_GEMM_WM, QI_GEMM_WN>), dim3(tiles_big),
                        dim3(64 * QI_GEMM_WM * QI_GEMM_WN), 0, s, g);
   else
     launch_gemm_tile<EPI, 128, 128>(g, s);
@@ -181,8 +182,7 @@ qi_status launch_attention(int heads, int L, int N, bool joint, const u16 *q_t, 
   a.o_img_row0 = joint ? L : 0;
   a.scale_log2 = (float)(1.4426950408889634 / sqrt(128.0));
   TimedLaunch tl(QI_KERNEL_ATTENTION, s);
-  hipLaunchKernelGGL(block_causal_attn_kernel, dim3(a.n_img_qt + a.n_txt_qt, heads), dim3(attn::THREADS),
-                     0, s, a);
+  launch_block_causal_attn(a, s);
   return last_launch();
 }
 
