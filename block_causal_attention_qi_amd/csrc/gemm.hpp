@@ -100,27 +100,61 @@ QI_DEV void store4(const GemmArgs &g, int m, int n, f32x4 v) {
     const float *gp = g.gate + (m < g.L_rows ? 0 : g.gate_img_off) + n;
     f32x4 *xp = (f32x4 *)(g.X + (size_t)m * g.ldx + n);
     *xp = *xp + *(const f32x4 *)gp * v;
-  } else if constexpr (EPI == EPI_QKV) {
-    const int sec = n / g.H;
-    const int w = n - sec * g.H;
-    const int head = w >> 7, dh = w & 127;
+  }
+}
+
+// QKV epilogue of one wave tile: FS blocks of 32 W rows starting at n0 and TS
+// blocks of 32 tokens starting at mbase.  The wave's W rows lie in one section
+// (q, k or v) and one head (n0 % 64 == 0, FS * 32 <= 64), so section, head and
+// segment come out once, and each token's cos/sin pairs are fetched together
+// before any of its outputs is rotated.
+template <int TS, int FS>
+QI_DEV void store_qkv_wave(const GemmArgs &g, int mbase, int n0, const f32x16 (&acc)[FS][TS], int lane) {
+  static_assert(FS * 32 <= 64, "a wave tile stays inside one half head");
+  const int sec = n0 / g.H;
+  const int w0 = n0 - sec * g.H;
+  const int head = w0 >> 7, dh0 = w0 & 127;
+  const int h4 = 4 * (lane >> 5), fr = lane & 31;
+#pragma unroll
+  for (int t = 0; t < TS; ++t) {
+    const int m = mbase + 32 * t + fr;
+    if (m >= g.M) continue;
     const bool txt = m < g.L_rows;
     const int row = txt ? m : m - g.L_rows;
     if (sec < 2) {
-      const float *cp = (txt ? g.cos_t : g.cos_i) + (size_t)row * 64 + (dh >> 1);
-      const float *sp = (txt ? g.sin_t : g.sin_i) + (size_t)row * 64 + (dh >> 1);
-      const float c0 = cp[0], c1 = cp[1], s0 = sp[0], s1 = sp[1];
-      const float y0 = v[0] * c0 - v[1] * s0, y1 = v[0] * s0 + v[1] * c0;
-      const float y2 = v[2] * c1 - v[3] * s1, y3 = v[2] * s1 + v[3] * c1;
-      u16 *dst = sec == 0 ? (txt ? g.q_t : g.q_i) : (txt ? g.k_t : g.k_i);
-      const int seg = txt ? g.seg_t : g.seg_i;
-      *(u32x2 *)(dst + ((size_t)head * seg + row) * 128 + dh) = u32x2{pack_bf16x2(y0, y1), pack_bf16x2(y2, y3)};
-    } else {
-      u16 *vt = txt ? g.vt_t : g.vt_i;
-      const int ldv = txt ? g.ldv_t : g.ldv_i;
-      u16 *base = vt + ((size_t)head * 128 + dh) * ldv + row;
+      // outputs dh0 + 32 f + 8 j + h4 + 0..3 are RoPE pairs (dh0 + h4)/2 + 16 f + 4 j + 0..1
+      const int poff = row * 64 + ((dh0 + h4) >> 1);
+      const float *cp = (txt ? g.cos_t : g.cos_i) + poff;
+      const float *sp = (txt ? g.sin_t : g.sin_i) + poff;
+      float2 cs[FS][4], sn[FS][4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) base[(size_t)r * ldv] = f32_to_bf16(v[r]);
+      for (int f = 0; f < FS; ++f)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          cs[f][j] = *(const float2 *)(cp + 16 * f + 4 * j);
+          sn[f][j] = *(const float2 *)(sp + 16 * f + 4 * j);
+        }
+      u16 *dst = (sec == 0 ? (txt ? g.q_t : g.q_i) : (txt ? g.k_t : g.k_i)) +
+                 ((size_t)head * (txt ? g.seg_t : g.seg_i) + row) * 128 + dh0 + h4;
+#pragma unroll
+      for (int f = 0; f < FS; ++f)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const f32x4 v = quad(acc[f][t], j);
+          const float c0 = cs[f][j].x, c1 = cs[f][j].y, s0 = sn[f][j].x, s1 = sn[f][j].y;
+          const float y0 = v[0] * c0 - v[1] * s0, y1 = v[0] * s0 + v[1] * c0;
+          const float y2 = v[2] * c1 - v[3] * s1, y3 = v[2] * s1 + v[3] * c1;
+          *(u32x2 *)(dst + 32 * f + 8 * j) = u32x2{pack_bf16x2(y0, y1), pack_bf16x2(y2, y3)};
+        }
+    } else {
+      const int ldv = txt ? g.ldv_t : g.ldv_i;
+      u16 *base = (txt ? g.vt_t : g.vt_i) + ((size_t)head * 128 + dh0 + h4) * ldv + row;
+#pragma unroll
+      for (int f = 0; f < FS; ++f)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) base[(size_t)(32 * f + 8 * j + r) * ldv] = f32_to_bf16(acc[f][t][4 * j + r]);
     }
   }
 }
@@ -242,6 +276,10 @@ __global__ __launch_bounds__(gemm::THREADS, (BM * BN >= 256 * 256) ? 1 : 2) void
   // lane holds, for each (f, t) subtile and j = 0..3, the 4 consecutive
   // W rows f*32 + 8j + 4*(lane/32) + 0..3 of token t*32 + lane%32
   const int h4 = 4 * (lane >> 5);
+  if constexpr (EPI == EPI_QKV) {
+    store_qkv_wave<TS, FS>(g, m0 + wm * WT, tn * BN + wn * WF, acc, lane);
+    return;
+  }
 #pragma unroll
   for (int t = 0; t < TS; ++t) {
     const int m = m0 + wm * WT + t * 32 + (lane & 31);
@@ -427,6 +465,10 @@ __global__ __launch_bounds__(64 * WMN * WNN, 1) void gemm_bf16_large_kernel(cons
   }
 
   const int h4 = 4 * half;
+  if constexpr (EPI == EPI_QKV) {
+    store_qkv_wave<TS, FS>(g, m0 + wm * WT, tn * BN + wn * WF, acc, lane);
+    return;
+  }
 #pragma unroll
   for (int t = 0; t < TS; ++t) {
     const int m = m0 + wm * WT + t * 32 + fr;
