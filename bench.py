@@ -14,8 +14,10 @@ resident in HBM before the timed region starts.
 
 Printed: one JSON line with steps/s (whole job), the per-kernel durations of
 the image-only steps measured with HIP events on the launch stream, the
-roofline fraction of the dominant kernel, and the CPU oracle's throughput on
-a bounded sample (one image-only block, scaled to a step)."""
+roofline fraction of the dominant kernel, the CPU oracle's throughput on a
+bounded sample (one image-only block, scaled to a step), and, as an extra,
+true CFG on the same workload (a negative prompt of half the length in a
+second K/V slot, both branches through every block at once)."""
 from __future__ import annotations
 
 import argparse
@@ -31,6 +33,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 METRIC = "DiT steps/sec (32 blocks, bf16) at 1024² L=407; attn+GEMM MFMA util"
+CFG_STEPS = 10
 
 
 def log(*a):
@@ -44,6 +47,7 @@ def parse():
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--workload", type=int, default=4)
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-cfg", action="store_true", help="skip the true-CFG extra measurement")
     p.add_argument("--threads", type=int, default=16, help="host threads for weight generation")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="only copy 1 GiB device-to-device (10 times): the known-size reference for "
@@ -151,6 +155,47 @@ def measured_traffic(kind: str):
     if not ent:
         return None, "kernel not in the counter summary"
     return int(ent["hbm_bytes"]), "profiles/dit32_1024px_hbm_traffic.json"
+
+
+def measure_cfg(qi, qs, wl, model, dims, x0, rope, sig, tin, img_step_ms):
+    """True CFG on the same workload (a reported extra, not the headline): both
+    prompts captured on step 1, then image-only CFG steps running both
+    branches through every block at once, each followed by the fused CFG
+    Euler update.  Timed over CFG_STEPS steps with events."""
+    import torch
+    N, L = wl.N, wl.L
+    Ln = qs.neg_prompt_len(wl)
+    dev = "cuda"
+    txt = torch.from_numpy(qs.txt_feats(wl)).to(dev)
+    txt_neg = torch.from_numpy(qs.neg_txt_feats(wl)).to(dev)
+    rope_n = [torch.from_numpy(a).to(dev) for a in qi.rope_tables(Ln, wl.h, wl.w)]
+    cos2 = torch.cat([rope[2], rope_n[2]]).contiguous()
+    sin2 = torch.cat([rope[3], rope_n[3]]).contiguous()
+    c_pos, c_neg = qi.KVCache(dims, L, dev), qi.KVCache(dims, Ln, dev)
+    ws = qi.Workspace(dims, max(L, Ln), N, dev)
+    cws = qi.CfgWorkspace(dims, N, dev)
+    vel = torch.empty((N, 64), dtype=torch.float32, device=dev)
+    vel2 = torch.empty((2, N, 64), dtype=torch.float32, device=dev)
+    x = x0.clone()
+    g = 2.5
+    qi.text_kv_capture(model, L, N, x, txt, tin[0], *rope, c_pos, vel, ws)
+    qi.text_kv_capture(model, Ln, N, x, txt_neg, tin[0], *rope_n, c_neg, vel, ws)
+    qi.dit_step_cfg(model, N, x, tin[1], cos2, sin2, c_pos, c_neg, vel2, cws)   # warm
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for k in range(1, 1 + CFG_STEPS):
+        qi.dit_step_cfg(model, N, x, tin[k], cos2, sin2, c_pos, c_neg, vel2, cws)
+        qi.euler_update_cfg(x, vel2, g, sig[k], sig[k + 1])
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / CFG_STEPS
+    if not torch.isfinite(x).all():
+        raise RuntimeError("non-finite latents in the CFG loop")
+    log(f"CFG: {ms:.2f} ms per image-only CFG step (two single steps: {2 * img_step_ms:.2f} ms)")
+    return {"guidance": g, "L_pos": L, "L_neg": Ln, "steps": CFG_STEPS,
+            "image_only_step_ms": round(ms, 3), "steps_per_s": round(1e3 / ms, 3),
+            "vs_two_single_steps": round(2 * img_step_ms / ms, 3)}
 
 
 def main():
@@ -279,6 +324,7 @@ def main():
     gemm_f = sum(work[k][0] * timing[k][1] for k in work if k.startswith("gemm") and k in timing) / n_img
     attn_ms = timing["attention"][0] / n_img
     step_f = flops.step_flops(shape)
+    cfg = None if args.no_cfg else measure_cfg(qi, qs, wl, model, dims, x0, rope, sig, tin, img_step_ms)
     cpu = None if args.no_cpu_baseline else cpu_baseline(wl)
 
     out = {
@@ -308,6 +354,7 @@ def main():
         "kernels": kernels,
         "roofline": roof,
         "cpu_baseline": cpu,
+        "cfg": cfg,
     }
     print(json.dumps(out))
 

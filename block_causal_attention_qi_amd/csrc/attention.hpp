@@ -63,7 +63,7 @@ QI_DEV float add_bf16x2(uint32_t pair, float sum) {
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pair), one, sum, false);
 }
 
-__global__ __launch_bounds__(attn::THREADS, 1) void block_causal_attn_kernel(const AttnArgs a) {
+__global__ __launch_bounds__(attn::THREADS, 1) void block_causal_attn_kernel(const AttnBatch ab) {
   using namespace attn;
   // Double buffers as four separate objects, always indexed by a constant:
   // the compiler then knows that a copy into one buffer does not alias reads
@@ -76,11 +76,15 @@ __global__ __launch_bounds__(attn::THREADS, 1) void block_causal_attn_kernel(con
   // Workgroups are dispatched round-robin over the 8 XCDs (each with its own
   // L2); renumber them so that each XCD works through whole heads, whose
   // query tiles then stream the same K/V tiles at about the same time.
+  // (grid.y enumerates branch-major (branch, head) pairs)
   const int tiles_per_head = gridDim.x, G = gridDim.x * gridDim.y;
   int wg = blockIdx.x + gridDim.x * blockIdx.y;
   if ((G & 7) == 0) wg = (wg & 7) * (G >> 3) + (wg >> 3);
-  const int head = wg / tiles_per_head;
-  int qt = wg - head * tiles_per_head;
+  const int head_c = wg / tiles_per_head;
+  int qt = wg - head_c * tiles_per_head;
+  const int branch = head_c >= ab.br[0].heads ? 1 : 0;
+  const AttnArgs a = branch ? ab.br[1] : ab.br[0];
+  const int head = head_c - branch * a.heads;
   const bool img = qt < a.n_img_qt;
   if (!img) qt -= a.n_img_qt;
   const int q0 = qt * BQ;

@@ -28,6 +28,15 @@ constexpr int NLD = BKV * 16 / THREADS;  // 16-byte K (and V^T) chunks per threa
 constexpr float RESCALE_SLACK = 8.f;     // log2 units
 }  // namespace attn
 
+// One launch over up to two independent problems of the same shape apart from
+// the text segment (true CFG: the positive and the negative prompt's image
+// rows, each against its own cached text K/V).  Both must have the same heads,
+// N and query-tile counts.
+struct AttnBatch {
+  AttnArgs br[2];
+  int nbranch;  // 1 or 2
+};
+
 // Launches the kernel (defined in attention.hip, which is compiled with MFMA
-// accumulators in VGPRs) over grid (n_img_qt + n_txt_qt, heads).
-void launch_block_causal_attn(const AttnArgs &a, hipStream_t s);
+// accumulators in VGPRs) over grid (n_img_qt + n_txt_qt, heads * nbranch).
+void launch_block_causal_attn(const AttnBatch &ab, hipStream_t s);

@@ -242,3 +242,37 @@ __global__ __launch_bounds__(256) void euler_kernel(float *x, const float *vel, 
     x[i] = x[i] + p;
   }
 }
+
+// True-CFG Euler step ([MLX] "Optional modes": noise = neg + g (pos - neg)),
+// fused: x[i] += ds * (neg[i] + g * (pos[i] - neg[i])), every operation a
+// separately rounded fp32 operation in that order (no contraction), vel =
+// [pos | neg], n elements each.
+__global__ __launch_bounds__(256) void euler_cfg_kernel(float *x, const float *vel, float g, float ds, int64_t n) {
+#pragma clang fp contract(off)
+  const float *pos = vel, *neg = vel + n;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  if ((n & 3) == 0) {
+    const int64_t n4 = n >> 2;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += stride) {
+      f32x4 xv = ((f32x4 *)x)[i];
+      const f32x4 pv = ((const f32x4 *)pos)[i], nv = ((const f32x4 *)neg)[i];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float d = pv[e] - nv[e];
+        const float gd = g * d;
+        const float noise = nv[e] + gd;
+        const float p = ds * noise;
+        xv[e] = xv[e] + p;
+      }
+      ((f32x4 *)x)[i] = xv;
+    }
+  } else {
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) {
+      const float d = pos[i] - neg[i];
+      const float gd = g * d;
+      const float noise = neg[i] + gd;
+      const float p = ds * noise;
+      x[i] = x[i] + p;
+    }
+  }
+}

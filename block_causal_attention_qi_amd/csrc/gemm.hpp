@@ -53,6 +53,8 @@ struct GemmArgs {
   u16 *q_t, *k_t, *vt_t, *q_i, *k_i, *vt_i;
   int seg_t, seg_i;  // text / image segment lengths (rows of Q, K per head)
   int ldv_t, ldv_i;  // V^T row strides (segment length rounded up to 64)
+  int batch;         // image rows form `batch` branches of seg_i rows each (true CFG: 2),
+                     // each with its own Q, K [heads][seg_i][128] and V^T [heads][128][ldv_i]
 };
 
 namespace gemm {
@@ -120,7 +122,10 @@ QI_DEV void store_qkv_wave(const GemmArgs &g, int mbase, int n0, const f32x16 (&
     const int m = mbase + 32 * t + fr;
     if (m >= g.M) continue;
     const bool txt = m < g.L_rows;
-    const int row = txt ? m : m - g.L_rows;
+    const int row = txt ? m : m - g.L_rows;  // cos/sin row (image tables hold every branch)
+    // branch of an image row and its row inside the branch's Q/K/V^T
+    const int br = (txt || g.batch <= 1) ? 0 : row / g.seg_i;
+    const int brow = row - br * g.seg_i;
     if (sec < 2) {
       // outputs dh0 + 32 f + 8 j + h4 + 0..3 are RoPE pairs (dh0 + h4)/2 + 16 f + 4 j + 0..1
       const int poff = row * 64 + ((dh0 + h4) >> 1);
@@ -134,8 +139,8 @@ QI_DEV void store_qkv_wave(const GemmArgs &g, int mbase, int n0, const f32x16 (&
           cs[f][j] = *(const float2 *)(cp + 16 * f + 4 * j);
           sn[f][j] = *(const float2 *)(sp + 16 * f + 4 * j);
         }
-      u16 *dst = (sec == 0 ? (txt ? g.q_t : g.q_i) : (txt ? g.k_t : g.k_i)) +
-                 ((size_t)head * (txt ? g.seg_t : g.seg_i) + row) * 128 + dh0 + h4;
+      u16 *dst = (sec == 0 ? (txt ? g.q_t : g.q_i) : (txt ? g.k_t : g.k_i)) + (size_t)br * g.H * g.seg_i +
+                 ((size_t)head * (txt ? g.seg_t : g.seg_i) + brow) * 128 + dh0 + h4;
 #pragma unroll
       for (int f = 0; f < FS; ++f)
 #pragma unroll
@@ -148,7 +153,7 @@ QI_DEV void store_qkv_wave(const GemmArgs &g, int mbase, int n0, const f32x16 (&
         }
     } else {
       const int ldv = txt ? g.ldv_t : g.ldv_i;
-      u16 *base = (txt ? g.vt_t : g.vt_i) + ((size_t)head * 128 + dh0 + h4) * ldv + row;
+      u16 *base = (txt ? g.vt_t : g.vt_i) + (size_t)br * g.H * ldv + ((size_t)head * 128 + dh0 + h4) * ldv + brow;
 #pragma unroll
       for (int f = 0; f < FS; ++f)
 #pragma unroll

@@ -2,6 +2,8 @@
 // carving and the launch sequence of one block and one step.  Everything is
 // enqueued on the caller's stream; nothing here synchronises or allocates.
 #include <math.h>
+
+#include <cmath>
 #include <stdint.h>
 #include <string.h>
 
@@ -68,6 +70,30 @@ Layout layout(const qi_dims &d, int L, int N) {
   l.vt_i = take(H * Np * 2);
   l.o = take(T * H * 2);
   l.a = take(T * F * 2);
+  l.total = off;
+  return l;
+}
+
+// Workspace of one true-CFG image-only pass: two branches of N image rows
+// (no text rows), each with its own Q, K, V^T.
+Layout layout_cfg(const qi_dims &d, int N) {
+  const size_t H = d.hidden, F = d.ffn, R = 2 * (size_t)N, Np = round64(N);
+  Layout l{};
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off += align256(bytes);
+    return o;
+  };
+  l.x = take(R * H * 4);
+  l.mod = take(2 * 4 * H * 4);
+  l.tn = l.q_t = l.k_t = l.vt_t = 0;  // unused
+  l.h = take(R * H * 2);
+  l.q_i = take(R * H * 2);
+  l.k_i = take(R * H * 2);
+  l.vt_i = take(2 * H * Np * 2);
+  l.o = take(R * H * 2);
+  l.a = take(R * F * 2);
   l.total = off;
   return l;
 }
@@ -167,9 +193,8 @@ qi_status launch_modulation(int H, const u16 *w_mod, const float *b_mod, float t
   return last_launch();
 }
 
-qi_status launch_attention(int heads, int L, int N, bool joint, const u16 *q_t, const u16 *k_t,
-                           const u16 *vt_t, const u16 *q_i, const u16 *k_i, const u16 *vt_i, u16 *o,
-                           hipStream_t s) {
+AttnArgs attn_args(int heads, int L, int N, bool joint, const u16 *q_t, const u16 *k_t, const u16 *vt_t,
+                   const u16 *q_i, const u16 *k_i, const u16 *vt_i, u16 *o) {
   AttnArgs a{};
   a.q_t = q_t; a.k_t = k_t; a.vt_t = vt_t;
   a.q_i = q_i; a.k_i = k_i; a.vt_i = vt_i;
@@ -181,17 +206,37 @@ qi_status launch_attention(int heads, int L, int N, bool joint, const u16 *q_t, 
   a.n_txt_qt = joint ? (L + attn::BQ - 1) / attn::BQ : 0;
   a.o_img_row0 = joint ? L : 0;
   a.scale_log2 = (float)(1.4426950408889634 / sqrt(128.0));
+  return a;
+}
+
+qi_status launch_attention_batch(const AttnBatch &ab, hipStream_t s) {
   TimedLaunch tl(QI_KERNEL_ATTENTION, s);
-  launch_block_causal_attn(a, s);
+  launch_block_causal_attn(ab, s);
   return last_launch();
 }
 
+qi_status launch_attention(int heads, int L, int N, bool joint, const u16 *q_t, const u16 *k_t,
+                           const u16 *vt_t, const u16 *q_i, const u16 *k_i, const u16 *vt_i, u16 *o,
+                           hipStream_t s) {
+  AttnBatch ab{};
+  ab.br[0] = attn_args(heads, L, N, joint, q_t, k_t, vt_t, q_i, k_i, vt_i, o);
+  ab.nbranch = 1;
+  return launch_attention_batch(ab, s);
+}
+
 // The launch sequence of one block; arguments already validated.
+//
+// Two-branch form (true CFG, image-only): nb = 2, rows [branch 0 | branch 1]
+// of N image rows each, cos_i/sin_i holding 2N rows, branch b reading its text
+// K/V from kv_slot (b = 0, L rows) or kv_slot2 (b = 1, L2 rows).  Every GEMM,
+// norm and the attention run once over both branches; each row's result is
+// the one the single-branch pass computes (row-count invariance).
 qi_status run_block(const qi_dims &d, const qi_block_w &w, int L, int N, bool joint, float *x,
                     const float *mod, const float *cos_t, const float *sin_t, const float *cos_i,
-                    const float *sin_i, u16 *kv_slot, char *ws, const Layout &lay, hipStream_t s) {
+                    const float *sin_i, u16 *kv_slot, char *ws, const Layout &lay, hipStream_t s,
+                    int nb = 1, u16 *kv_slot2 = nullptr, int L2 = 0) {
   const int H = d.hidden, F = d.ffn, heads = d.heads;
-  const int L_rows = joint ? L : 0, T = L_rows + N;
+  const int L_rows = joint ? L : 0, T = L_rows + nb * N;
   const int img_off = 4 * H;  // mod row 1
   u16 *h = (u16 *)(ws + lay.h);
   u16 *o = (u16 *)(ws + lay.o);
@@ -211,9 +256,20 @@ qi_status run_block(const qi_dims &d, const qi_block_w &w, int L, int N, bool jo
   g.cos_t = cos_t; g.sin_t = sin_t; g.cos_i = cos_i; g.sin_i = sin_i;
   g.q_t = q_t; g.k_t = k_t; g.vt_t = vt_t; g.q_i = q_i; g.k_i = k_i; g.vt_i = vt_i;
   g.seg_t = L; g.seg_i = N; g.ldv_t = round64(L); g.ldv_i = round64(N);
+  g.batch = nb;
   QI_TRY(launch_gemm<EPI_QKV>(g, QI_KERNEL_GEMM_QKV, s));
 
-  QI_TRY(launch_attention(heads, L, N, joint, q_t, k_t, vt_t, q_i, k_i, vt_i, o, s));
+  if (nb == 1) {
+    QI_TRY(launch_attention(heads, L, N, joint, q_t, k_t, vt_t, q_i, k_i, vt_i, o, s));
+  } else {
+    AttnBatch ab{};
+    ab.nbranch = 2;
+    ab.br[0] = attn_args(heads, L, N, false, nullptr, k_t, vt_t, q_i, k_i, vt_i, o);
+    ab.br[1] = attn_args(heads, L2, N, false, nullptr, kv_slot2, kv_slot2 + (size_t)heads * L2 * 128,
+                         q_i + (size_t)H * N, k_i + (size_t)H * N, vt_i + (size_t)H * round64(N),
+                         o + (size_t)N * H);
+    QI_TRY(launch_attention_batch(ab, s));
+  }
 
   // O projection + gated residual 1 (gate1 = chunk 1)
   GemmArgs r{};
@@ -300,6 +356,32 @@ qi_status run_step(const qi_dims &d, const qi_model_w &w, int L, int N, const fl
     QI_TRY(last_launch());
   }
   return QI_OK;
+}
+
+// A true-CFG image-only step: both branches through every block at once,
+// vel = [pos | neg] ([2N, 64]).
+qi_status run_step_cfg(const qi_dims &d, const qi_model_w &w, int N, const float *img_tokens, float t,
+                       const float *img_cos, const float *img_sin, u16 *kv_pos, int L_pos, u16 *kv_neg,
+                       int L_neg, float *vel, char *ws, hipStream_t s) {
+  const int H = d.hidden;
+  const Layout lay = layout_cfg(d, N);
+  float *x = (float *)(ws + lay.x);
+  float *mod = (float *)(ws + lay.mod);
+  QI_TRY(launch_modulation(H, w.w_mod, w.b_mod, t, mod, s));
+  for (int b = 0; b < 2; ++b) {
+    TimedLaunch tl(QI_KERNEL_IMG_EMBED, s);
+    hipLaunchKernelGGL(img_embed_kernel, dim3((N + 15) / 16, (H + 255) / 256), dim3(256), 0, s, img_tokens, N,
+                       w.w_img, w.b_img, H, x, H, b * N);
+    QI_TRY(last_launch());
+  }
+  const size_t slot_p = slot_elems(d, L_pos), slot_n = slot_elems(d, L_neg);
+  for (int b = 0; b < d.n_blocks; ++b)
+    QI_TRY(run_block(d, w.blocks[b], L_pos, N, false, x, mod, nullptr, nullptr, img_cos, img_sin,
+                     kv_pos + (size_t)b * slot_p, ws, lay, s, 2, kv_neg + (size_t)b * slot_n, L_neg));
+  TimedLaunch tl(QI_KERNEL_HEAD, s);
+  hipLaunchKernelGGL(head_kernel, dim3((2 * N + 15) / 16), dim3(256), 0, s, x, H, 2 * N, w.norm_out, w.w_out,
+                     w.b_out, H, kRmsEps, vel);
+  return last_launch();
 }
 
 qi_status check_step_args(const qi_dims *d, const qi_model_w *w, int L, int N, const float *img_tokens,
@@ -413,6 +495,47 @@ qi_status qi_text_kv_capture(const qi_dims *d, const qi_model_w *w, int32_t L, i
   cache->hidden = d->hidden;
   cache->valid = 1;
   return QI_OK;
+}
+
+size_t qi_cfg_workspace_bytes(const qi_dims *d, int32_t N) {
+  if (!d || !dims_ok(d) || N < 1 || N > kMaxN) return 0;
+  return layout_cfg(*d, N).total;
+}
+
+qi_status qi_dit_step_cfg(const qi_dims *d, const qi_model_w *w, int32_t N, const float *img_tokens,
+                          float timestep, const float *img_cos, const float *img_sin, const qi_kv_cache *cache_pos,
+                          const qi_kv_cache *cache_neg, float *vel, void *ws, size_t ws_bytes, void *stream) {
+  if (!d) return QI_ERR_NULL;
+  if (!dims_ok(d)) return QI_ERR_SHAPE;
+  if (N < 1 || N > kMaxN) return QI_ERR_RANGE;
+  if (!(timestep >= 0.f && timestep <= 1.f)) return QI_ERR_RANGE;
+  if (!img_tokens || !img_cos || !img_sin || !vel || !ws || !cache_pos || !cache_neg) return QI_ERR_NULL;
+  if (!al16(img_tokens) || !al16(img_cos) || !al16(img_sin) || !al16(vel) || !al16(ws)) return QI_ERR_ALIGN;
+  QI_TRY(check_model_w(*d, w, false));
+  for (const qi_kv_cache *c : {cache_pos, cache_neg}) {
+    if (!c->kv || !c->valid || c->L < 1 || c->L > kMaxL || c->n_blocks != d->n_blocks || c->hidden != d->hidden)
+      return QI_ERR_CACHE;
+    if (!al16(c->kv)) return QI_ERR_ALIGN;
+  }
+  if (cache_pos->kv == cache_neg->kv) return QI_ERR_CACHE;
+  if (ws_bytes < layout_cfg(*d, N).total) return QI_ERR_WORKSPACE;
+  return run_step_cfg(*d, *w, N, img_tokens, timestep, img_cos, img_sin, cache_pos->kv, cache_pos->L,
+                      cache_neg->kv, cache_neg->L, vel, (char *)ws, (hipStream_t)stream);
+}
+
+qi_status qi_euler_update_cfg(float *x, const float *vel, float guidance, float sigma_cur, float sigma_next,
+                              int64_t n, void *stream) {
+  if (n < 0) return QI_ERR_RANGE;
+  if (n == 0) return QI_OK;
+  if (!x || !vel) return QI_ERR_NULL;
+  if (!al16(x) || !al16(vel)) return QI_ERR_ALIGN;
+  if (!std::isfinite(guidance)) return QI_ERR_RANGE;
+  const float ds = sigma_next - sigma_cur;  // fp32 difference on the host
+  const int64_t n4 = (n + 3) / 4;
+  const int blocks = (int)((n4 + 255) / 256 < 4096 ? (n4 + 255) / 256 : 4096);
+  TimedLaunch tl(QI_KERNEL_EULER, (hipStream_t)stream);
+  hipLaunchKernelGGL(euler_cfg_kernel, dim3(blocks), dim3(256), 0, (hipStream_t)stream, x, vel, guidance, ds, n);
+  return last_launch();
 }
 
 qi_status qi_euler_update(float *x, const float *vel, float sigma_cur, float sigma_next, int64_t n,

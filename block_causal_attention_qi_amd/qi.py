@@ -18,7 +18,8 @@ __all__ = ["QI_MODE_JOINT", "QI_MODE_IMAGE_ONLY", "QiError", "make_dims", "rope_
            "rope_tables", "flow_sigmas", "workspace_bytes", "kv_cache_bytes", "kv_slot_elems",
            "DeviceModel", "KVCache", "Workspace", "dit_step", "text_kv_capture", "dit_block_fwd",
            "euler_update", "modulation", "block_causal_attention", "linear_bf16", "stream_handle",
-           "timing_begin", "timing_end", "KERNEL_KINDS"]
+           "timing_begin", "timing_end", "KERNEL_KINDS", "cfg_workspace_bytes", "CfgWorkspace", "dit_step_cfg",
+           "euler_update_cfg"]
 
 
 def _np_ptr(a: np.ndarray) -> int:
@@ -154,6 +155,25 @@ class KVCache:
         return _ptr(self.buf) + 2 * b * self.slot_elems
 
 
+def cfg_workspace_bytes(dims: QiDims, N: int) -> int:
+    return int(_lib.load().qi_cfg_workspace_bytes(ctypes.byref(dims), N))
+
+
+class CfgWorkspace:
+    """Workspace of a true-CFG image-only step (both branches)."""
+
+    def __init__(self, dims: QiDims, N: int, device="cuda"):
+        import torch
+        self.nbytes = cfg_workspace_bytes(dims, N)
+        if self.nbytes == 0:
+            raise ValueError("invalid dims or N for the CFG workspace")
+        self.buf = torch.empty(self.nbytes, dtype=torch.uint8, device=device)
+
+    @property
+    def ptr(self) -> int:
+        return _ptr(self.buf)
+
+
 class Workspace:
     def __init__(self, dims: QiDims, L: int, N: int, device="cuda"):
         import torch
@@ -205,6 +225,27 @@ def euler_update(x, vel, sigma_cur: float, sigma_next: float, stream=None):
     st = _lib.load().qi_euler_update(_ptr(x), _ptr(vel), float(sigma_cur), float(sigma_next), n,
                                      stream_handle(stream))
     check(st, "qi_euler_update")
+
+
+def dit_step_cfg(model: DeviceModel, N: int, img_tokens, t: float, img_cos2, img_sin2, cache_pos: KVCache,
+                 cache_neg: KVCache, vel2, ws: CfgWorkspace, stream=None):
+    """True-CFG image-only step: img_cos2/img_sin2 [2, N, 64] (branch rows),
+    vel2 [2, N, 64] out ([pos | neg])."""
+    st = _lib.load().qi_dit_step_cfg(ctypes.byref(model.dims), ctypes.byref(model.w), N, _ptr(img_tokens),
+                                     float(t), _ptr(img_cos2), _ptr(img_sin2), ctypes.byref(cache_pos.c),
+                                     ctypes.byref(cache_neg.c), _ptr(vel2), ws.ptr, ws.nbytes,
+                                     stream_handle(stream))
+    check(st, "qi_dit_step_cfg")
+
+
+def euler_update_cfg(x, vel2, guidance: float, sigma_cur: float, sigma_next: float, stream=None):
+    """x += (sigma_next - sigma_cur) * (neg + g (pos - neg)), vel2 = [pos | neg]."""
+    n = x.numel()
+    if vel2.numel() != 2 * n:
+        raise ValueError("vel2 must hold 2 * x.numel() values")
+    st = _lib.load().qi_euler_update_cfg(_ptr(x), _ptr(vel2), float(guidance), float(sigma_cur),
+                                         float(sigma_next), n, stream_handle(stream))
+    check(st, "qi_euler_update_cfg")
 
 
 def modulation(dims: QiDims, w_mod, b_mod, t: float, mod, stream=None):

@@ -207,6 +207,43 @@ qi_status qi_text_kv_capture(const qi_dims *d, const qi_model_w *w, int32_t L, i
 qi_status qi_euler_update(float *x, const float *vel, float sigma_cur, float sigma_next,
                           int64_t n, void *stream);
 
+/* ---------------------------------------------------------------- true CFG */
+
+/* Workspace bytes qi_dit_step_cfg needs (0 for invalid dims or N). */
+size_t qi_cfg_workspace_bytes(const qi_dims *d, int32_t N);
+
+/* One image-only step of true classifier-free guidance with reuse ([MLX]
+ * "Optional modes": a second forward per step, on the negative prompt; "Text
+ * K/V reuse": the negative prompt's K/V in a second slot).  Both branches run
+ * through every block together as 2N image rows: branch 0 (positive prompt)
+ * reads its text K/V from cache_pos, branch 1 (negative prompt) from
+ * cache_neg, each captured by qi_text_kv_capture with its own prompt (the two
+ * L may differ).  Each branch's vel is bit-identical to qi_dit_step on that
+ * branch's cache alone (and so to its full joint recompute).
+ *   img_tokens: device fp32 [N][64], the same latents for both branches;
+ *   img_cos, img_sin: device fp32 [2][N][64], branch b's image RoPE rows (they
+ *     depend on the branch's L, see qi_rope_tables);
+ *   vel: device fp32 [2][N][64] out, [pos | neg].
+ * Combine with qi_euler_update_cfg.  Errors: NULL, SHAPE, RANGE, ALIGN,
+ * WORKSPACE (ws_bytes < qi_cfg_workspace_bytes), CACHE (a cache not valid,
+ * made for another n_blocks or hidden, or both caches the same buffer), HIP. */
+qi_status qi_dit_step_cfg(const qi_dims *d, const qi_model_w *w, int32_t N,
+                          const float *img_tokens, float timestep, const float *img_cos,
+                          const float *img_sin, const qi_kv_cache *cache_pos,
+                          const qi_kv_cache *cache_neg, float *vel, void *ws, size_t ws_bytes,
+                          void *stream);
+
+/* The Euler update with the guidance combination fused in ([MLX] "Optional
+ * modes", noise = neg + g (pos - neg); [HOST] s.6 for the update): in place on
+ * device fp32 x[n], with vel = [pos | neg] (2n floats),
+ *   x = x + (sigma_next - sigma_cur) * (neg + g * (pos - neg)),
+ * the sigma difference computed in fp32 on the host and every other operation
+ * a separately rounded fp32 operation in the order written (no fused
+ * multiply-add).  n = 0 is a no-op.  Errors: NULL, RANGE (n < 0, guidance not
+ * finite), ALIGN, HIP. */
+qi_status qi_euler_update_cfg(float *x, const float *vel, float guidance, float sigma_cur,
+                              float sigma_next, int64_t n, void *stream);
+
 /* ---------------------------------------------------------------- components */
 
 /* The shared modulation rows alone: mod [2][4H] (device fp32) = W_mod e(0) +

@@ -11,7 +11,8 @@ Pages cited (by title and section):
   [HOST]  "Host contract -- RGBA-Image-2.1 (Core AI port of Qwen-Image-2.1)",
           sections 1-6.
   [MLX]   "Qwen-Image-2.1 on MLX, faster and exact", sections "Text K/V reuse
-          (exact, on by default)" and "Where the time goes".
+          (exact, on by default)", "Where the time goes" and "Optional modes
+          (approximate or slower)".
 
 Floating point: the DiT forward runs in float64 (the `dtype` argument can
 lower it).  The RoPE tables, the sampler arrays and the Euler update are fp32
@@ -48,6 +49,12 @@ Readings of points the pages leave open (each is stated where it is used):
   S15 sampler constants base_shift 0.5 at 256 tokens, max_shift 0.9 at 8192
       tokens, mu linear in N with no clamp, 1000 train timesteps; each array
       operation in fp32 as the host contract states, mu and e^mu in float64.
+  S16 true CFG: noise = neg + g * (pos - neg) exactly as [MLX] "Optional
+      modes" writes it (no rescaling of the combined prediction), evaluated
+      in fp32 as written -- difference, product, sum, each rounded once -- and
+      fed to the S14 Euler update; each branch is an ordinary step on its own
+      prompt (its own text K/V and its own image RoPE rows, which depend on
+      its L).
 Parity pins live in tests/test_oracle_*.py.  The whole-step vel has no
 printed value on the pages: beyond the invariants and component pins it is
 "parity unpinned" externally.
@@ -411,6 +418,21 @@ def euler_update(x: np.ndarray, vel: np.ndarray, sigma_cur, sigma_next) -> np.nd
     difference, product and sum each rounded to fp32 (numpy never fuses)."""
     ds = F32(sigma_next) - F32(sigma_cur)
     return (x.astype(F32) + (ds * vel.astype(F32)).astype(F32)).astype(F32)
+
+
+def cfg_combine(pos: np.ndarray, neg: np.ndarray, g) -> np.ndarray:
+    """True-CFG prediction ([MLX] "Optional modes"), reading S16:
+    neg + g * (pos - neg), each operation rounded to fp32 in that order."""
+    pos = pos.astype(F32)
+    neg = neg.astype(F32)
+    d = (pos - neg).astype(F32)
+    gd = (F32(g) * d).astype(F32)
+    return (neg + gd).astype(F32)
+
+
+def euler_update_cfg(x: np.ndarray, pos: np.ndarray, neg: np.ndarray, g, sigma_cur, sigma_next) -> np.ndarray:
+    """The S14 Euler update on the S16 guided prediction."""
+    return euler_update(x, cfg_combine(pos, neg, g), sigma_cur, sigma_next)
 
 
 # ------------------------------------------------------------------ metrics

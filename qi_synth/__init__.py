@@ -31,6 +31,7 @@ MASTER_SEED = 0
 SHARED_BLOCK_ID = 100000          # stream id for the tensors outside the blocks
 NOISE_SEED = 1234                 # the seed of the Core AI port's oracle run
 TXT_SEED = 1235
+NEG_TXT_SEED = 1236               # the negative prompt of a true-CFG render
 
 # tensor ids inside a block
 _BLOCK_TENSORS = ("w_qkv", "w_o", "w_gu", "w_down", "norm1", "norm2")
@@ -209,3 +210,14 @@ def normal_array(shape, seed: int, scale: float = 1.0) -> np.ndarray:
     if scale != 1.0:
         a *= np.float32(scale)
     return a
+
+
+def neg_prompt_len(wl: Workload) -> int:
+    """Length of the stand-in negative prompt of a true-CFG render: half the
+    positive prompt (at least 1), so the two K/V slots differ in L."""
+    return max(1, wl.L // 2)
+
+
+def neg_txt_feats(wl: Workload) -> np.ndarray:
+    """N(0,1) stand-in negative-prompt embeddings [neg_prompt_len, txt_dim]."""
+    return txt_feats(wl, seed=NEG_TXT_SEED, L=neg_prompt_len(wl))

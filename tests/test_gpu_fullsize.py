@@ -220,3 +220,35 @@ def test_dit32_2048px_block_rows_match_oracle(model32):
 @pytest.mark.timeout(900)
 def test_dit32_2048px_reuse_exact(model32):
     _reuse_properties(model32, qs.workload(5))
+
+
+@pytest.mark.timeout(900)
+def test_dit32_1024px_cfg_branches_exact(model32):
+    """True CFG at 1024^2 with 32 blocks: both branches through every block at
+    once (8192 image rows), each branch bit-equal to the single-branch cached
+    step on its own K/V slot (L 407 and the 203-token negative prompt)."""
+    import torch
+    wl = qs.workload(4)
+    r = Run(model32, wl)
+    Ln = qs.neg_prompt_len(wl)
+    log(f"cfg at {wl.name}: L_pos={wl.L} L_neg={Ln}")
+    txt_neg = _dev(qs.neg_txt_feats(wl))
+    rope_n = [_dev(a) for a in qi.rope_tables(Ln, wl.h, wl.w)]
+    ws_n = qi.Workspace(model32["dims"], Ln, wl.N)
+    c_pos, c_neg = qi.KVCache(model32["dims"], wl.L), qi.KVCache(model32["dims"], Ln)
+    vel_n = torch.empty((wl.N, 64), dtype=torch.float32, device="cuda")
+    _, ts = qi.flow_sigmas(40, wl.N)
+    t0, t1 = np.float32(ts[0]) / np.float32(1000), np.float32(ts[20]) / np.float32(1000)
+    r.capture(t0, c_pos)
+    qi.text_kv_capture(model32["model"], Ln, wl.N, r.img, txt_neg, t0, *rope_n, c_neg, vel_n, ws_n)
+    cws = qi.CfgWorkspace(model32["dims"], wl.N)
+    vel2 = torch.empty((2, wl.N, 64), dtype=torch.float32, device="cuda")
+    cos2 = torch.cat([r.rope[2], rope_n[2]]).contiguous()
+    sin2 = torch.cat([r.rope[3], rope_n[3]]).contiguous()
+    qi.dit_step_cfg(model32["model"], wl.N, r.img, t1, cos2, sin2, c_pos, c_neg, vel2, cws)
+    got = host(vel2).copy()
+    assert np.all(np.isfinite(got))
+    assert_bits_equal(got[0], r.step(t1, c_pos), "CFG pos branch vs single cached step")
+    qi.dit_step(model32["model"], Ln, wl.N, r.img, None, t1, None, None, rope_n[2], rope_n[3], vel_n, ws_n, c_neg)
+    assert_bits_equal(got[1], host(vel_n), "CFG neg branch vs single cached step")
+    log("  both branches bit-equal")
