@@ -84,6 +84,7 @@ __global__ __launch_bounds__(attn::THREADS, 1) void block_causal_attn_kernel(con
   int qt = wg - head_c * tiles_per_head;
   const int branch = head_c >= ab.br[0].heads ? 1 : 0;
   const AttnArgs a = branch ? ab.br[1] : ab.br[0];
+  if (a.skip && *a.skip) return;
   const int head = head_c - branch * a.heads;
   const bool img = qt < a.n_img_qt;
   if (!img) qt -= a.n_img_qt;

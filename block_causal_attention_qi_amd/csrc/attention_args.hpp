@@ -17,6 +17,7 @@ struct AttnArgs {
   int n_img_qt, n_txt_qt;        // query tiles of BQ per head
   int o_img_row0;                // output row of image query 0 (L in a joint pass, else 0)
   float scale_log2;              // log2(e) / sqrt(128)
+  const int *skip;               // first-block cache: when non-NULL and *skip, do nothing
 };
 
 namespace attn {

@@ -19,7 +19,8 @@ template <int VPL>
 __global__ __launch_bounds__(256) void rmsnorm_mod_kernel(const float *x, int ldx, const float *gamma,
                                                           int zero_centred, const float *mod,
                                                           int mod_img_off, int L_rows, int rows, int H,
-                                                          float eps, u16 *out, int ldo) {
+                                                          float eps, u16 *out, int ldo, const int *skip) {
+  if (skip && *skip) return;  // first-block cache: this block is skipped this step
   const int lane = threadIdx.x & 63;
   const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (r >= rows) return;
@@ -275,4 +276,118 @@ __global__ __launch_bounds__(256) void euler_cfg_kernel(float *x, const float *v
       x[i] = x[i] + p;
     }
   }
+}
+
+// ---------------------------------------------------------------- first-block cache
+// [MLX] "Optional modes": "Fast mode" runs block 0 every step and skips blocks
+// 1..n-1 while block 0's residual changes less than a threshold; a skipped
+// step adds the residual that blocks 1..n-1 produced at the last step that ran
+// them.  State on the device (so the loop needs no host sync): the flag every
+// kernel of blocks 1..n-1 reads, the validity of the cached residuals, counts,
+// and the change the last decision saw.
+struct FbcState {
+  int skip;         // this step: 1 = blocks 1..n-1 skipped
+  int valid;        // cached residuals hold a full step
+  int n_steps;      // steps seen since the last reset
+  int n_skipped;    // of which skipped
+  float last_change;
+  int pad[3];
+};
+
+// x0 = x (n floats)
+__global__ __launch_bounds__(256) void fbc_copy_kernel(float *dst, const float *src, int64_t n4) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += stride)
+    ((f32x4 *)dst)[i] = ((const f32x4 *)src)[i];
+}
+
+// Per-workgroup partial sums of |(x1 - x0) - r0p| and |r0p| (the block-0
+// residual against the cached one), fp32 differences, float64 sums in a fixed
+// order: part[2 wg], part[2 wg + 1].
+__global__ __launch_bounds__(256) void fbc_partial_kernel(const float *x1, const float *x0, const float *r0p,
+                                                          int64_t n4, double *part) {
+  __shared__ double red[2][4];
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  double s1 = 0.0, s2 = 0.0;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += stride) {
+    const f32x4 a = ((const f32x4 *)x1)[i], b = ((const f32x4 *)x0)[i], p = ((const f32x4 *)r0p)[i];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float r = a[e] - b[e];
+      s1 += (double)fabsf(r - p[e]);
+      s2 += (double)fabsf(p[e]);
+    }
+  }
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) {
+    s1 += __shfl_xor(s1, m, 64);
+    s2 += __shfl_xor(s2, m, 64);
+  }
+  const int w = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) {
+    red[0][w] = s1;
+    red[1][w] = s2;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    part[2 * blockIdx.x] = ((red[0][0] + red[0][1]) + red[0][2]) + red[0][3];
+    part[2 * blockIdx.x + 1] = ((red[1][0] + red[1][1]) + red[1][2]) + red[1][3];
+  }
+}
+
+// One workgroup: total the partial sums in a fixed order and decide.  The
+// change is sum|r0 - r0p| / sum|r0p|; blocks 1..n-1 are skipped when the
+// cache is valid and the change is below the threshold.
+__global__ __launch_bounds__(64) void fbc_decide_kernel(const double *part, int nparts, float threshold,
+                                                        FbcState *st) {
+  double s1 = 0.0, s2 = 0.0;
+  for (int i = threadIdx.x; i < nparts; i += 64) {
+    s1 += part[2 * i];
+    s2 += part[2 * i + 1];
+  }
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) {
+    s1 += __shfl_xor(s1, m, 64);
+    s2 += __shfl_xor(s2, m, 64);
+  }
+  if (threadIdx.x == 0) {
+    const bool have = st->valid != 0 && s2 > 0.0;
+    const double change = have ? s1 / s2 : INFINITY;
+    const int skip = (have && change < (double)threshold) ? 1 : 0;
+    st->skip = skip;
+    st->last_change = (float)change;
+    st->n_steps += 1;
+    st->n_skipped += skip;
+  }
+}
+
+// After the decision: a skipped step adds the cached residual of blocks
+// 1..n-1 to x (= x1); a computed step caches r0 = x1 - x0 and x1.
+__global__ __launch_bounds__(256) void fbc_apply_kernel(float *x, const float *x0, float *r0p, float *x1s,
+                                                        const float *rem, int64_t n4, const FbcState *st) {
+  const int skip = st->skip;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += stride) {
+    const f32x4 a = ((f32x4 *)x)[i];
+    if (skip) {
+      ((f32x4 *)x)[i] = a + ((const f32x4 *)rem)[i];
+    } else {
+      ((f32x4 *)r0p)[i] = a - ((const f32x4 *)x0)[i];
+      ((f32x4 *)x1s)[i] = a;
+    }
+  }
+}
+
+// After blocks 1..n-1 of a computed step: cache their residual x - x1.
+__global__ __launch_bounds__(256) void fbc_finish_kernel(const float *x, const float *x1s, float *rem, int64_t n4,
+                                                         FbcState *st) {
+  if (st->skip) return;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += stride)
+    ((f32x4 *)rem)[i] = ((const f32x4 *)x)[i] - ((const f32x4 *)x1s)[i];
+  if (blockIdx.x == 0 && threadIdx.x == 0) st->valid = 1;
+}
+
+__global__ void fbc_reset_kernel(FbcState *st) {
+  if (threadIdx.x == 0) *st = FbcState{};
 }

@@ -55,6 +55,7 @@ struct GemmArgs {
   int ldv_t, ldv_i;  // V^T row strides (segment length rounded up to 64)
   int batch;         // image rows form `batch` branches of seg_i rows each (true CFG: 2),
                      // each with its own Q, K [heads][seg_i][128] and V^T [heads][128][ldv_i]
+  const int *skip;   // first-block cache: when non-NULL and *skip, the launch does nothing
 };
 
 namespace gemm {
@@ -175,6 +176,7 @@ QI_DEV void store4_swiglu(const GemmArgs &g, int m, int o, f32x4 gt, f32x4 up) {
 template <int EPI, int BM, int BN>
 __global__ __launch_bounds__(gemm::THREADS, (BM * BN >= 256 * 256) ? 1 : 2) void gemm_bf16_kernel(const GemmArgs g) {
   using namespace gemm;
+  if (g.skip && *g.skip) return;
   constexpr int WT = BM / 2, WF = BN / 2;    // per-wave tokens, W rows
   constexpr int TS = WT / 32, FS = WF / 32;  // 32-row subtiles per wave
   constexpr int CA = BM * 8 / THREADS, CW = BN * 8 / THREADS;  // 16-byte chunks per thread
@@ -323,6 +325,7 @@ constexpr int RSRC_FLAGS = 0x00020000;  // raw buffer, 32-bit dwords
 template <int EPI, int WMN, int WNN>
 __global__ __launch_bounds__(64 * WMN * WNN, 1) void gemm_bf16_large_kernel(const GemmArgs g) {
   using namespace gemmL;
+  if (g.skip && *g.skip) return;
   constexpr int THREADS = 64 * WMN * WNN;
   constexpr int WT = BM / WMN, WF = BN / WNN;  // wave tile
   constexpr int TS = WT / 32, FS = WF / 32;

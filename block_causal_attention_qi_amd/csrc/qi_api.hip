@@ -174,15 +174,16 @@ qi_status launch_gemm(const GemmArgs &g, int kind, hipStream_t s) {
 }
 
 qi_status launch_norm(const float *x, int ldx, const float *gamma, int zc, const float *mod,
-                      int mod_img_off, int L_rows, int rows, int H, u16 *out, int ldo, hipStream_t s) {
+                      int mod_img_off, int L_rows, int rows, int H, u16 *out, int ldo, hipStream_t s,
+                      const int *skip = nullptr) {
   TimedLaunch tl(zc ? QI_KERNEL_TXT_NORM : QI_KERNEL_NORM_MOD, s);
   const dim3 grid((rows + 3) / 4);
   if (H <= 4096)
     hipLaunchKernelGGL(rmsnorm_mod_kernel<16>, grid, dim3(256), 0, s, x, ldx, gamma, zc, mod, mod_img_off, L_rows,
-                       rows, H, kRmsEps, out, ldo);
+                       rows, H, kRmsEps, out, ldo, skip);
   else
     hipLaunchKernelGGL(rmsnorm_mod_kernel<32>, grid, dim3(256), 0, s, x, ldx, gamma, zc, mod, mod_img_off, L_rows,
-                       rows, H, kRmsEps, out, ldo);
+                       rows, H, kRmsEps, out, ldo, skip);
   return last_launch();
 }
 
@@ -217,9 +218,10 @@ qi_status launch_attention_batch(const AttnBatch &ab, hipStream_t s) {
 
 qi_status launch_attention(int heads, int L, int N, bool joint, const u16 *q_t, const u16 *k_t,
                            const u16 *vt_t, const u16 *q_i, const u16 *k_i, const u16 *vt_i, u16 *o,
-                           hipStream_t s) {
+                           hipStream_t s, const int *skip = nullptr) {
   AttnBatch ab{};
   ab.br[0] = attn_args(heads, L, N, joint, q_t, k_t, vt_t, q_i, k_i, vt_i, o);
+  ab.br[0].skip = skip;
   ab.nbranch = 1;
   return launch_attention_batch(ab, s);
 }
@@ -234,7 +236,7 @@ qi_status launch_attention(int heads, int L, int N, bool joint, const u16 *q_t, 
 qi_status run_block(const qi_dims &d, const qi_block_w &w, int L, int N, bool joint, float *x,
                     const float *mod, const float *cos_t, const float *sin_t, const float *cos_i,
                     const float *sin_i, u16 *kv_slot, char *ws, const Layout &lay, hipStream_t s,
-                    int nb = 1, u16 *kv_slot2 = nullptr, int L2 = 0) {
+                    int nb = 1, u16 *kv_slot2 = nullptr, int L2 = 0, const int *skip = nullptr) {
   const int H = d.hidden, F = d.ffn, heads = d.heads;
   const int L_rows = joint ? L : 0, T = L_rows + nb * N;
   const int img_off = 4 * H;  // mod row 1
@@ -247,7 +249,7 @@ qi_status run_block(const qi_dims &d, const qi_block_w &w, int L, int N, bool jo
   u16 *q_i = (u16 *)(ws + lay.q_i), *k_i = (u16 *)(ws + lay.k_i), *vt_i = (u16 *)(ws + lay.vt_i);
 
   // norm 1 + modulation (scale1 = chunk 0)
-  QI_TRY(launch_norm(x, H, w.norm1, 0, mod, img_off, L_rows, T, H, h, H, s));
+  QI_TRY(launch_norm(x, H, w.norm1, 0, mod, img_off, L_rows, T, H, h, H, s, skip));
 
   // QKV + RoPE (+ text K/V into the cache slot on a capture pass)
   GemmArgs g{};
@@ -257,10 +259,11 @@ qi_status run_block(const qi_dims &d, const qi_block_w &w, int L, int N, bool jo
   g.q_t = q_t; g.k_t = k_t; g.vt_t = vt_t; g.q_i = q_i; g.k_i = k_i; g.vt_i = vt_i;
   g.seg_t = L; g.seg_i = N; g.ldv_t = round64(L); g.ldv_i = round64(N);
   g.batch = nb;
+  g.skip = skip;
   QI_TRY(launch_gemm<EPI_QKV>(g, QI_KERNEL_GEMM_QKV, s));
 
   if (nb == 1) {
-    QI_TRY(launch_attention(heads, L, N, joint, q_t, k_t, vt_t, q_i, k_i, vt_i, o, s));
+    QI_TRY(launch_attention(heads, L, N, joint, q_t, k_t, vt_t, q_i, k_i, vt_i, o, s, skip));
   } else {
     AttnBatch ab{};
     ab.nbranch = 2;
@@ -268,6 +271,7 @@ qi_status run_block(const qi_dims &d, const qi_block_w &w, int L, int N, bool jo
     ab.br[1] = attn_args(heads, L2, N, false, nullptr, kv_slot2, kv_slot2 + (size_t)heads * L2 * 128,
                          q_i + (size_t)H * N, k_i + (size_t)H * N, vt_i + (size_t)H * round64(N),
                          o + (size_t)N * H);
+    ab.br[0].skip = ab.br[1].skip = skip;
     QI_TRY(launch_attention_batch(ab, s));
   }
 
@@ -275,21 +279,24 @@ qi_status run_block(const qi_dims &d, const qi_block_w &w, int L, int N, bool jo
   GemmArgs r{};
   r.A = o; r.lda = H; r.W = w.w_o; r.ldw = H; r.M = T; r.N = H; r.K = H; r.L_rows = L_rows;
   r.X = x; r.ldx = H; r.gate = mod + H; r.gate_img_off = img_off;
+  r.skip = skip;
   QI_TRY(launch_gemm<EPI_RESID>(r, QI_KERNEL_GEMM_O, s));
 
   // norm 2 + modulation (scale2 = chunk 2)
-  QI_TRY(launch_norm(x, H, w.norm2, 0, mod + 2 * H, img_off, L_rows, T, H, h, H, s));
+  QI_TRY(launch_norm(x, H, w.norm2, 0, mod + 2 * H, img_off, L_rows, T, H, h, H, s, skip));
 
   // gate/up + SwiGLU
   GemmArgs u{};
   u.A = h; u.lda = H; u.W = w.w_gu; u.ldw = H; u.M = T; u.N = 2 * F; u.K = H; u.L_rows = L_rows;
   u.out = a; u.ldo = F; u.F = F;
+  u.skip = skip;
   QI_TRY(launch_gemm<EPI_SWIGLU>(u, QI_KERNEL_GEMM_GATE_UP, s));
 
   // down + gated residual 2 (gate2 = chunk 3)
   GemmArgs dn{};
   dn.A = a; dn.lda = F; dn.W = w.w_down; dn.ldw = F; dn.M = T; dn.N = H; dn.K = F; dn.L_rows = L_rows;
   dn.X = x; dn.ldx = H; dn.gate = mod + 3 * H; dn.gate_img_off = img_off;
+  dn.skip = skip;
   QI_TRY(launch_gemm<EPI_RESID>(dn, QI_KERNEL_GEMM_DOWN, s));
   return QI_OK;
 }
@@ -356,6 +363,79 @@ qi_status run_step(const qi_dims &d, const qi_model_w &w, int L, int N, const fl
     QI_TRY(last_launch());
   }
   return QI_OK;
+}
+
+// First-block-cache buffer: state, partial sums, then x0, r0p (cached block-0
+// residual), x1s (x after block 0 on the last computed step) and rem (cached
+// residual of blocks 1..n-1), each [N][H] fp32.
+constexpr int kFbcParts = 512;
+struct FbcLayout {
+  size_t state, part, x0, r0p, x1s, rem, total;
+};
+FbcLayout fbc_layout(const qi_dims &d, int N) {
+  const size_t X = (size_t)N * d.hidden * 4;
+  FbcLayout l{};
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off += align256(bytes);
+    return o;
+  };
+  l.state = take(sizeof(FbcState));
+  l.part = take(2 * kFbcParts * sizeof(double));
+  l.x0 = take(X);
+  l.r0p = take(X);
+  l.x1s = take(X);
+  l.rem = take(X);
+  l.total = off;
+  return l;
+}
+
+// An image-only step with the first-block cache ([MLX] "Optional modes", Fast
+// mode): block 0, the on-device decision, then blocks 1..n-1 whose kernels all
+// return at once when the step is skipped.  No host synchronisation.
+qi_status run_step_fbc(const qi_dims &d, const qi_model_w &w, int L, int N, const float *img_tokens, float t,
+                       const float *img_cos, const float *img_sin, u16 *kv, float threshold, char *fbc,
+                       float *vel, char *ws, hipStream_t s) {
+  const int H = d.hidden;
+  const Layout lay = layout(d, L, N);
+  const FbcLayout fl = fbc_layout(d, N);
+  float *x = (float *)(ws + lay.x);
+  float *mod = (float *)(ws + lay.mod);
+  FbcState *st = (FbcState *)(fbc + fl.state);
+  double *part = (double *)(fbc + fl.part);
+  float *x0 = (float *)(fbc + fl.x0), *r0p = (float *)(fbc + fl.r0p), *x1s = (float *)(fbc + fl.x1s),
+        *rem = (float *)(fbc + fl.rem);
+  const int64_t n4 = (int64_t)N * H / 4;
+  const int eblocks = (int)((n4 + 255) / 256 < 2048 ? (n4 + 255) / 256 : 2048);
+  const int pblocks = (int)((n4 + 255) / 256 < kFbcParts ? (n4 + 255) / 256 : kFbcParts);
+
+  QI_TRY(launch_modulation(H, w.w_mod, w.b_mod, t, mod, s));
+  {
+    TimedLaunch tl(QI_KERNEL_IMG_EMBED, s);
+    hipLaunchKernelGGL(img_embed_kernel, dim3((N + 15) / 16, (H + 255) / 256), dim3(256), 0, s, img_tokens, N,
+                       w.w_img, w.b_img, H, x, H, 0);
+  }
+  QI_TRY(last_launch());
+  hipLaunchKernelGGL(fbc_copy_kernel, dim3(eblocks), dim3(256), 0, s, x0, x, n4);
+  QI_TRY(last_launch());
+  const size_t slot = slot_elems(d, L);
+  QI_TRY(run_block(d, w.blocks[0], L, N, false, x, mod, nullptr, nullptr, img_cos, img_sin, kv, ws, lay, s));
+  hipLaunchKernelGGL(fbc_partial_kernel, dim3(pblocks), dim3(256), 0, s, x, x0, r0p, n4, part);
+  QI_TRY(last_launch());
+  hipLaunchKernelGGL(fbc_decide_kernel, dim3(1), dim3(64), 0, s, part, pblocks, threshold, st);
+  QI_TRY(last_launch());
+  hipLaunchKernelGGL(fbc_apply_kernel, dim3(eblocks), dim3(256), 0, s, x, x0, r0p, x1s, rem, n4, st);
+  QI_TRY(last_launch());
+  for (int b = 1; b < d.n_blocks; ++b)
+    QI_TRY(run_block(d, w.blocks[b], L, N, false, x, mod, nullptr, nullptr, img_cos, img_sin,
+                     kv + (size_t)b * slot, ws, lay, s, 1, nullptr, 0, &st->skip));
+  hipLaunchKernelGGL(fbc_finish_kernel, dim3(eblocks), dim3(256), 0, s, x, x1s, rem, n4, st);
+  QI_TRY(last_launch());
+  TimedLaunch tl(QI_KERNEL_HEAD, s);
+  hipLaunchKernelGGL(head_kernel, dim3((N + 15) / 16), dim3(256), 0, s, x, H, N, w.norm_out, w.w_out, w.b_out, H,
+                     kRmsEps, vel);
+  return last_launch();
 }
 
 // A true-CFG image-only step: both branches through every block at once,
@@ -536,6 +616,49 @@ qi_status qi_euler_update_cfg(float *x, const float *vel, float guidance, float 
   TimedLaunch tl(QI_KERNEL_EULER, (hipStream_t)stream);
   hipLaunchKernelGGL(euler_cfg_kernel, dim3(blocks), dim3(256), 0, (hipStream_t)stream, x, vel, guidance, ds, n);
   return last_launch();
+}
+
+size_t qi_fbc_bytes(const qi_dims *d, int32_t N) {
+  if (!d || !dims_ok(d) || N < 1 || N > kMaxN) return 0;
+  return fbc_layout(*d, N).total;
+}
+
+qi_status qi_fbc_reset(void *fbc, size_t fbc_bytes, void *stream) {
+  if (!fbc) return QI_ERR_NULL;
+  if (!al16(fbc)) return QI_ERR_ALIGN;
+  if (fbc_bytes < sizeof(FbcState)) return QI_ERR_WORKSPACE;
+  hipLaunchKernelGGL(fbc_reset_kernel, dim3(1), dim3(64), 0, (hipStream_t)stream, (FbcState *)fbc);
+  return last_launch();
+}
+
+qi_status qi_fbc_stats(const void *fbc, int32_t *n_steps, int32_t *n_skipped, float *last_change, void *stream) {
+  if (!fbc || !n_steps || !n_skipped || !last_change) return QI_ERR_NULL;
+  if (!al16(fbc)) return QI_ERR_ALIGN;
+  FbcState h{};
+  if (hipMemcpyAsync(&h, fbc, sizeof(h), hipMemcpyDeviceToHost, (hipStream_t)stream) != hipSuccess ||
+      hipStreamSynchronize((hipStream_t)stream) != hipSuccess)
+    return QI_ERR_HIP;
+  *n_steps = h.n_steps;
+  *n_skipped = h.n_skipped;
+  *last_change = h.last_change;
+  return QI_OK;
+}
+
+qi_status qi_dit_step_fbc(const qi_dims *d, const qi_model_w *w, int32_t L, int32_t N, const float *img_tokens,
+                          float timestep, const float *img_cos, const float *img_sin, const qi_kv_cache *cache,
+                          float threshold, void *fbc, size_t fbc_bytes, float *vel, void *ws, size_t ws_bytes,
+                          void *stream) {
+  QI_TRY(check_step_args(d, w, L, N, img_tokens, nullptr, timestep, nullptr, nullptr, img_cos, img_sin, false, ws,
+                         ws_bytes));
+  if (!vel || !fbc || !cache) return QI_ERR_NULL;
+  if (!al16(vel) || !al16(fbc)) return QI_ERR_ALIGN;
+  if (!(threshold >= 0.f) || !std::isfinite(threshold)) return QI_ERR_RANGE;
+  if (fbc_bytes < fbc_layout(*d, N).total) return QI_ERR_WORKSPACE;
+  if (!cache->kv || !cache->valid || cache->L != L || cache->n_blocks != d->n_blocks || cache->hidden != d->hidden)
+    return QI_ERR_CACHE;
+  if (!al16(cache->kv)) return QI_ERR_ALIGN;
+  return run_step_fbc(*d, *w, L, N, img_tokens, timestep, img_cos, img_sin, cache->kv, threshold, (char *)fbc, vel,
+                      (char *)ws, (hipStream_t)stream);
 }
 
 qi_status qi_euler_update(float *x, const float *vel, float sigma_cur, float sigma_next, int64_t n,

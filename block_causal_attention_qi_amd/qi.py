@@ -19,7 +19,7 @@ __all__ = ["QI_MODE_JOINT", "QI_MODE_IMAGE_ONLY", "QiError", "make_dims", "rope_
            "DeviceModel", "KVCache", "Workspace", "dit_step", "text_kv_capture", "dit_block_fwd",
            "euler_update", "modulation", "block_causal_attention", "linear_bf16", "stream_handle",
            "timing_begin", "timing_end", "KERNEL_KINDS", "cfg_workspace_bytes", "CfgWorkspace", "dit_step_cfg",
-           "euler_update_cfg"]
+           "euler_update_cfg", "fbc_bytes", "FirstBlockCache", "dit_step_fbc"]
 
 
 def _np_ptr(a: np.ndarray) -> int:
@@ -174,6 +174,36 @@ class CfgWorkspace:
         return _ptr(self.buf)
 
 
+def fbc_bytes(dims: QiDims, N: int) -> int:
+    return int(_lib.load().qi_fbc_bytes(ctypes.byref(dims), N))
+
+
+class FirstBlockCache:
+    """Device buffer of the first-block cache (Fast mode) for N image rows."""
+
+    def __init__(self, dims: QiDims, N: int, device="cuda", stream=None):
+        import torch
+        self.nbytes = fbc_bytes(dims, N)
+        if self.nbytes == 0:
+            raise ValueError("invalid dims or N for the first-block cache")
+        self.buf = torch.empty(self.nbytes, dtype=torch.uint8, device=device)
+        self.reset(stream)
+
+    @property
+    def ptr(self) -> int:
+        return _ptr(self.buf)
+
+    def reset(self, stream=None):
+        check(_lib.load().qi_fbc_reset(self.ptr, self.nbytes, stream_handle(stream)), "qi_fbc_reset")
+
+    def stats(self, stream=None) -> dict:
+        """{'steps', 'skipped', 'last_change'} (synchronises the stream)."""
+        n, k, c = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_float()
+        check(_lib.load().qi_fbc_stats(self.ptr, ctypes.byref(n), ctypes.byref(k), ctypes.byref(c),
+                                       stream_handle(stream)), "qi_fbc_stats")
+        return {"steps": n.value, "skipped": k.value, "last_change": c.value}
+
+
 class Workspace:
     def __init__(self, dims: QiDims, L: int, N: int, device="cuda"):
         import torch
@@ -236,6 +266,16 @@ def dit_step_cfg(model: DeviceModel, N: int, img_tokens, t: float, img_cos2, img
                                      ctypes.byref(cache_neg.c), _ptr(vel2), ws.ptr, ws.nbytes,
                                      stream_handle(stream))
     check(st, "qi_dit_step_cfg")
+
+
+def dit_step_fbc(model: DeviceModel, L: int, N: int, img_tokens, t: float, img_cos, img_sin, cache: KVCache,
+                 threshold: float, fbc: FirstBlockCache, vel, ws: Workspace, stream=None):
+    """Image-only step with the first-block cache (Fast mode)."""
+    st = _lib.load().qi_dit_step_fbc(ctypes.byref(model.dims), ctypes.byref(model.w), L, N, _ptr(img_tokens),
+                                     float(t), _ptr(img_cos), _ptr(img_sin), ctypes.byref(cache.c),
+                                     float(threshold), fbc.ptr, fbc.nbytes, _ptr(vel), ws.ptr, ws.nbytes,
+                                     stream_handle(stream))
+    check(st, "qi_dit_step_fbc")
 
 
 def euler_update_cfg(x, vel2, guidance: float, sigma_cur: float, sigma_next: float, stream=None):

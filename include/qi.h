@@ -244,6 +244,45 @@ qi_status qi_dit_step_cfg(const qi_dims *d, const qi_model_w *w, int32_t N,
 qi_status qi_euler_update_cfg(float *x, const float *vel, float guidance, float sigma_cur,
                               float sigma_next, int64_t n, void *stream);
 
+/* ---------------------------------------------------------------- first-block cache */
+
+/* Device bytes of a first-block-cache buffer for N image rows (0 for invalid
+ * dims or N).  The caller allocates it (16-byte aligned) and calls
+ * qi_fbc_reset before the first step of a render. */
+size_t qi_fbc_bytes(const qi_dims *d, int32_t N);
+
+/* Marks the buffer's cached residuals invalid and zeroes its counts (one small
+ * kernel on the stream; no memset, so it may sit in a captured graph).
+ * Errors: NULL, ALIGN, WORKSPACE (fbc_bytes too small for the state), HIP. */
+qi_status qi_fbc_reset(void *fbc, size_t fbc_bytes, void *stream);
+
+/* An image-only step with the first-block cache ([MLX] "Optional modes",
+ * Fast mode; the option table's threshold is 0.08).  Block 0 always runs.
+ * Its residual r0 = x1 - x0 (x0 after the embed, x1 after block 0) is
+ * compared with the one cached at the last step that ran every block:
+ *   change = sum |r0 - r0_cached| / sum |r0_cached|  (over all image rows and
+ *   features; fp32 differences, float64 sums in a fixed order).
+ * If the cache is valid and change < threshold, blocks 1..n_blocks-1 are
+ * skipped and x = x1 + rem_cached; otherwise they run, and r0 and their
+ * residual rem = x_out - x1 are cached.  The decision is taken on the device:
+ * the kernels of blocks 1.. read a device flag and return at once when the
+ * step is skipped, so the loop needs no host synchronisation.  Approximate:
+ * a skipped step differs from the exact step.  Other arguments as qi_dit_step
+ * with a valid cache (txt inputs not needed).  threshold 0 never skips.
+ * Errors: as qi_dit_step; NULL (fbc or cache NULL), RANGE (threshold negative
+ * or not finite), WORKSPACE (fbc_bytes < qi_fbc_bytes), CACHE. */
+qi_status qi_dit_step_fbc(const qi_dims *d, const qi_model_w *w, int32_t L, int32_t N,
+                          const float *img_tokens, float timestep, const float *img_cos,
+                          const float *img_sin, const qi_kv_cache *cache, float threshold,
+                          void *fbc, size_t fbc_bytes, float *vel, void *ws, size_t ws_bytes,
+                          void *stream);
+
+/* Reporting only (it synchronises the stream): the steps seen since the last
+ * reset, how many skipped blocks 1.., and the change the last decision saw
+ * (+inf when the cache was not valid).  Errors: NULL, ALIGN, HIP. */
+qi_status qi_fbc_stats(const void *fbc, int32_t *n_steps, int32_t *n_skipped, float *last_change,
+                       void *stream);
+
 /* ---------------------------------------------------------------- components */
 
 /* The shared modulation rows alone: mod [2][4H] (device fp32) = W_mod e(0) +

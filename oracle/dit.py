@@ -12,7 +12,7 @@ Pages cited (by title and section):
           sections 1-6.
   [MLX]   "Qwen-Image-2.1 on MLX, faster and exact", sections "Text K/V reuse
           (exact, on by default)", "Where the time goes" and "Optional modes
-          (approximate or slower)".
+          (approximate or slower)", including its Fast mode.
 
 Floating point: the DiT forward runs in float64 (the `dtype` argument can
 lower it).  The RoPE tables, the sampler arrays and the Euler update are fp32
@@ -55,6 +55,17 @@ Readings of points the pages leave open (each is stated where it is used):
       fed to the S14 Euler update; each branch is an ordinary step on its own
       prompt (its own text K/V and its own image RoPE rows, which depend on
       its L).
+  S17 first-block cache (Fast mode): block 0 always runs; its residual
+      r0 = x1 - x0 (after the embed, after block 0) is compared with the r0
+      cached at the last step that ran every block, change = sum|r0 - r0c| /
+      sum|r0c| over all image rows and features; below the threshold blocks
+      1.. are skipped and x = x1 + remc, the residual x_out - x1 that blocks
+      1.. produced at that last full step; otherwise they run and r0, remc
+      are cached.  (The page says only that blocks 1.. are skipped while block
+      0's residual changes less than the threshold; comparing against the last
+      full step rather than the previous step keeps slow drift from adding up
+      unchecked, and reusing the last full step's residual is the plainest
+      value for the skipped work.)
 Parity pins live in tests/test_oracle_*.py.  The whole-step vel has no
 printed value on the pages: beyond the invariants and component pins it is
 "parity unpinned" externally.
@@ -418,6 +429,41 @@ def euler_update(x: np.ndarray, vel: np.ndarray, sigma_cur, sigma_next) -> np.nd
     difference, product and sum each rounded to fp32 (numpy never fuses)."""
     ds = F32(sigma_next) - F32(sigma_cur)
     return (x.astype(F32) + (ds * vel.astype(F32)).astype(F32)).astype(F32)
+
+
+def fbc_new_state() -> dict:
+    """Empty first-block-cache state (reading S17)."""
+    return {"valid": False, "r0": None, "rem": None, "steps": 0, "skipped": 0, "last_change": math.inf}
+
+
+def first_block_cache_step(sw: dict, blocks, img_tokens, t: float, img_cos, img_sin, heads: int,
+                           kv_cache, state: dict, threshold: float, dtype=np.float64):
+    """An image-only step with the first-block cache ([MLX] "Optional
+    modes", Fast mode), reading S17.  blocks: a list of block weights;
+    kv_cache: the captured text K/V per block; state: fbc_new_state(),
+    updated in place.  Returns vel [N, 64]."""
+    H = sw["w_img"].shape[0]
+    m_txt, m_img = modulation_rows(sw["w_mod"], sw["b_mod"], t, H, dtype)
+    x0 = embed(sw, img_tokens, None, dtype)
+    x1, _ = dit_block(x0, 0, blocks[0], m_txt, m_img, img_cos, img_sin, heads, kv_cache[0])
+    r0 = x1 - x0
+    change = math.inf
+    if state["valid"]:
+        den = float(np.sum(np.abs(state["r0"])))
+        if den > 0.0:
+            change = float(np.sum(np.abs(r0 - state["r0"]))) / den
+    skip = change < threshold
+    if skip:
+        x = x1 + state["rem"]
+    else:
+        x = x1
+        for b in range(1, len(blocks)):
+            x, _ = dit_block(x, 0, blocks[b], m_txt, m_img, img_cos, img_sin, heads, kv_cache[b])
+        state.update(valid=True, r0=r0, rem=x - x1)
+    state["steps"] += 1
+    state["skipped"] += int(skip)
+    state["last_change"] = change
+    return head(sw, x)
 
 
 def cfg_combine(pos: np.ndarray, neg: np.ndarray, g) -> np.ndarray:
