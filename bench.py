@@ -17,7 +17,8 @@ the image-only steps measured with HIP events on the launch stream, the
 roofline fraction of the dominant kernel, the CPU oracle's throughput on a
 bounded sample (one image-only block, scaled to a step), and, as an extra,
 true CFG on the same workload (a negative prompt of half the length in a
-second K/V slot, both branches through every block at once)."""
+second K/V slot, both branches through every block at once) and the
+first-block cache (Fast mode)."""
 from __future__ import annotations
 
 import argparse
@@ -34,6 +35,7 @@ if ROOT not in sys.path:
 
 METRIC = "DiT steps/sec (32 blocks, bf16) at 1024² L=407; attn+GEMM MFMA util"
 CFG_STEPS = 10
+FBC_STEPS = 10
 
 
 def log(*a):
@@ -47,7 +49,7 @@ def parse():
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--workload", type=int, default=4)
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--no-cfg", action="store_true", help="skip the true-CFG extra measurement")
+    p.add_argument("--no-cfg", action="store_true", help="skip the true-CFG and first-block-cache extras")
     p.add_argument("--threads", type=int, default=16, help="host threads for weight generation")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="only copy 1 GiB device-to-device (10 times): the known-size reference for "
@@ -198,6 +200,44 @@ def measure_cfg(qi, qs, wl, model, dims, x0, rope, sig, tin, img_step_ms):
             "vs_two_single_steps": round(2 * img_step_ms / ms, 3)}
 
 
+def measure_fbc(qi, qs, wl, model, dims, x0, rope, sig, tin, img_step_ms):
+    """First-block cache (Fast mode) on the same workload, a reported extra:
+    FBC_STEPS image-only steps at the page's threshold 0.08 (on random-init
+    weights block 0's residual changes far more than that, so nothing is
+    skipped: the figure is the bookkeeping overhead), then the same steps with
+    every step after the first skipped (an unbounded threshold): the cost of a
+    skipped step."""
+    import torch
+    N, L = wl.N, wl.L
+    dev = "cuda"
+    txt = torch.from_numpy(qs.txt_feats(wl)).to(dev)
+    cache = qi.KVCache(dims, L, dev)
+    ws = qi.Workspace(dims, L, N, dev)
+    fbc = qi.FirstBlockCache(dims, N, dev)
+    vel = torch.empty((N, 64), dtype=torch.float32, device=dev)
+    out = {}
+    for name, thr in (("threshold_0.08", 0.08), ("always_skip", 3.0e38)):
+        x = x0.clone()
+        qi.text_kv_capture(model, L, N, x, txt, tin[0], *rope, cache, vel, ws)
+        fbc.reset()
+        qi.dit_step_fbc(model, L, N, x, tin[1], rope[2], rope[3], cache, thr, fbc, vel, ws)   # fills the cache
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for k in range(2, 2 + FBC_STEPS):
+            qi.dit_step_fbc(model, L, N, x, tin[k], rope[2], rope[3], cache, thr, fbc, vel, ws)
+            qi.euler_update(x, vel, sig[k], sig[k + 1])
+        e1.record()
+        st = fbc.stats()
+        ms = e0.elapsed_time(e1) / FBC_STEPS
+        out[name] = {"image_only_step_ms": round(ms, 3), "skipped": st["skipped"], "steps_incl_first": st["steps"],
+                     "last_change": round(st["last_change"], 4)}
+        log(f"FBC {name}: {ms:.2f} ms per step, {st['skipped']} of {st['steps']} skipped, "
+            f"last change {st['last_change']:.3f}")
+    out["exact_image_only_step_ms"] = round(img_step_ms, 3)
+    return out
+
+
 def main():
     args = parse()
     if args.calibrate_copy:
@@ -325,6 +365,7 @@ def main():
     attn_ms = timing["attention"][0] / n_img
     step_f = flops.step_flops(shape)
     cfg = None if args.no_cfg else measure_cfg(qi, qs, wl, model, dims, x0, rope, sig, tin, img_step_ms)
+    fbc = None if args.no_cfg else measure_fbc(qi, qs, wl, model, dims, x0, rope, sig, tin, img_step_ms)
     cpu = None if args.no_cpu_baseline else cpu_baseline(wl)
 
     out = {
@@ -355,6 +396,7 @@ def main():
         "roofline": roof,
         "cpu_baseline": cpu,
         "cfg": cfg,
+        "first_block_cache": fbc,
     }
     print(json.dumps(out))
 
