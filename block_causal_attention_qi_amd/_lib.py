@@ -71,6 +71,9 @@ SIGNATURES = {
                                   _P(QiKvCache), _P(QiKvCache), c_void_p, c_void_p, c_size_t, c_void_p]),
     "qi_euler_update_cfg": (c_int32, [c_void_p, c_void_p, c_float, c_float, c_float, c_int64, c_void_p]),
     "qi_fbc_bytes": (c_size_t, [_P(QiDims), c_int32]),
+    "qi_dpmpp_2m_coeffs": (c_int32, [c_int32, c_float, c_float, c_float, c_void_p]),
+    "qi_dpmpp_2m_update": (c_int32, [c_void_p, c_void_p, c_void_p, c_int32, c_float, c_float, c_float, c_int64,
+                                     c_void_p]),
     "qi_fbc_reset": (c_int32, [c_void_p, c_size_t, c_void_p]),
     "qi_dit_step_fbc": (c_int32, [_P(QiDims), _P(QiModelW), c_int32, c_int32, c_void_p, c_float, c_void_p,
                                   c_void_p, _P(QiKvCache), c_float, c_void_p, c_size_t, c_void_p, c_void_p,

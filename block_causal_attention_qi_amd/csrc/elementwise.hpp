@@ -391,3 +391,28 @@ __global__ __launch_bounds__(256) void fbc_finish_kernel(const float *x, const f
 __global__ void fbc_reset_kernel(FbcState *st) {
   if (threadIdx.x == 0) *st = FbcState{};
 }
+
+// One DPM++ 2M update in fp32 (coefficients from qi_dpmpp_2m_coeffs, rounded
+// once to fp32 on the host): p = sigma_cur v, x0 = x - p, D = x0 (order 1) or
+// c1 x0 - c2 x0_prev (order 2), x = a x - b D, each operation rounded once in
+// that order (no contraction); x0 is left in x0_prev for the next step.
+__global__ __launch_bounds__(256) void dpmpp_2m_kernel(float *x, const float *vel, float *x0_prev, float sigma,
+                                                       float a, float b, float c1, float c2, int order, int64_t n) {
+#pragma clang fp contract(off)
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) {
+    const float xv = x[i];
+    const float p = sigma * vel[i];
+    const float x0 = xv - p;
+    float d = x0;
+    if (order == 2) {
+      const float t1 = c1 * x0;
+      const float t2 = c2 * x0_prev[i];
+      d = t1 - t2;
+    }
+    const float u = a * xv;
+    const float w = b * d;
+    x[i] = u - w;
+    x0_prev[i] = x0;
+  }
+}

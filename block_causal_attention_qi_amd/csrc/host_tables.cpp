@@ -112,4 +112,36 @@ qi_status qi_flow_sigmas(int32_t steps, int32_t n_img_tokens, float *sigmas, flo
   return QI_OK;
 }
 
+// DPM++ 2M coefficients (DPM-Solver++(2M), Lu et al. 2022, written for the
+// flow x = (1 - sigma) x0 + sigma eps): alpha = 1 - sigma, lambda =
+// log(alpha / sigma), x_next = a x - b D with a = sigma_next / sigma_cur,
+// b = alpha_next (e^-h - 1), h = lambda_next - lambda_cur, and
+// D = c1 x0 - c2 x0_prev, c2 = 1 / (2 r), r = h_prev / h, c1 = 1 + c2.  First
+// order (c1 = 1, c2 = 0) without a previous prediction, after sigma = 1 (r
+// infinite) and at the final step (sigma_next = 0: a = 0, b = -1, x_next = x0).
+// Returns the order (1 or 2).  Double precision throughout.
+static double flow_lambda(double s) { return s >= 1.0 ? -INFINITY : std::log1p(-s) - std::log(s); }
+
+qi_status qi_dpmpp_2m_coeffs(int32_t has_prev, float sigma_prev, float sigma_cur, float sigma_next, double *coef) {
+  if (!coef) return QI_ERR_NULL;
+  const double sp = sigma_prev, sc = sigma_cur, sn = sigma_next;
+  if (!(sc > 0.0 && sc <= 1.0) || !(sn >= 0.0 && sn < sc) || (has_prev && !(sp > sc && sp <= 1.0)))
+    return QI_ERR_RANGE;
+  if (sn <= 0.0) {
+    coef[0] = 0.0; coef[1] = -1.0; coef[2] = 1.0; coef[3] = 0.0;
+    return 1;
+  }
+  const double h = flow_lambda(sn) - flow_lambda(sc);
+  coef[0] = sn / sc;
+  coef[1] = (1.0 - sn) * std::expm1(-h);
+  coef[2] = 1.0;
+  coef[3] = 0.0;
+  if (!has_prev) return 1;
+  const double r = (flow_lambda(sc) - flow_lambda(sp)) / h;
+  if (std::isinf(r)) return 1;
+  coef[3] = 1.0 / (2.0 * r);
+  coef[2] = 1.0 + coef[3];
+  return 2;
+}
+
 }  // extern "C"

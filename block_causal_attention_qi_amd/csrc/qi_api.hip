@@ -618,6 +618,22 @@ qi_status qi_euler_update_cfg(float *x, const float *vel, float guidance, float 
   return last_launch();
 }
 
+qi_status qi_dpmpp_2m_update(float *x, const float *vel, float *x0_prev, int32_t has_prev, float sigma_prev,
+                             float sigma_cur, float sigma_next, int64_t n, void *stream) {
+  if (n < 0) return QI_ERR_RANGE;
+  if (!x || !vel || !x0_prev) return QI_ERR_NULL;
+  double c[4];
+  const qi_status order = qi_dpmpp_2m_coeffs(has_prev, sigma_prev, sigma_cur, sigma_next, c);
+  if (order < 0) return order;
+  if (n == 0) return QI_OK;
+  const int64_t blocks64 = (n + 255) / 256;
+  const int blocks = (int)(blocks64 < 4096 ? blocks64 : 4096);
+  TimedLaunch tl(QI_KERNEL_EULER, (hipStream_t)stream);
+  hipLaunchKernelGGL(dpmpp_2m_kernel, dim3(blocks), dim3(256), 0, (hipStream_t)stream, x, vel, x0_prev, sigma_cur,
+                     (float)c[0], (float)c[1], (float)c[2], (float)c[3], (int)order, n);
+  return last_launch();
+}
+
 size_t qi_fbc_bytes(const qi_dims *d, int32_t N) {
   if (!d || !dims_ok(d) || N < 1 || N > kMaxN) return 0;
   return fbc_layout(*d, N).total;

@@ -19,7 +19,8 @@ __all__ = ["QI_MODE_JOINT", "QI_MODE_IMAGE_ONLY", "QiError", "make_dims", "rope_
            "DeviceModel", "KVCache", "Workspace", "dit_step", "text_kv_capture", "dit_block_fwd",
            "euler_update", "modulation", "block_causal_attention", "linear_bf16", "stream_handle",
            "timing_begin", "timing_end", "KERNEL_KINDS", "cfg_workspace_bytes", "CfgWorkspace", "dit_step_cfg",
-           "euler_update_cfg", "fbc_bytes", "FirstBlockCache", "dit_step_fbc"]
+           "euler_update_cfg", "fbc_bytes", "FirstBlockCache", "dit_step_fbc", "dpmpp_2m_coeffs",
+           "dpmpp_2m_update"]
 
 
 def _np_ptr(a: np.ndarray) -> int:
@@ -286,6 +287,31 @@ def euler_update_cfg(x, vel2, guidance: float, sigma_cur: float, sigma_next: flo
     st = _lib.load().qi_euler_update_cfg(_ptr(x), _ptr(vel2), float(guidance), float(sigma_cur),
                                          float(sigma_next), n, stream_handle(stream))
     check(st, "qi_euler_update_cfg")
+
+
+def dpmpp_2m_coeffs(sigma_prev, sigma_cur: float, sigma_next: float):
+    """(a, b, c1, c2, order) of one DPM++ 2M step (host, float64);
+    sigma_prev None on the first step."""
+    c = (ctypes.c_double * 4)()
+    has = sigma_prev is not None
+    r = _lib.load().qi_dpmpp_2m_coeffs(int(has), float(sigma_prev) if has else 0.0, float(sigma_cur),
+                                       float(sigma_next), c)
+    if r < 0:
+        check(r, "qi_dpmpp_2m_coeffs")
+    return c[0], c[1], c[2], c[3], int(r)
+
+
+def dpmpp_2m_update(x, vel, x0_prev, sigma_prev, sigma_cur: float, sigma_next: float, stream=None):
+    """In-place DPM++ 2M step; x0_prev (same size as x) carries the data
+    prediction between steps; sigma_prev None on the first step."""
+    n = x.numel()
+    if vel.numel() != n or x0_prev.numel() != n:
+        raise ValueError("x, vel and x0_prev sizes differ")
+    has = sigma_prev is not None
+    st = _lib.load().qi_dpmpp_2m_update(_ptr(x), _ptr(vel), _ptr(x0_prev), int(has),
+                                        float(sigma_prev) if has else 0.0, float(sigma_cur), float(sigma_next),
+                                        n, stream_handle(stream))
+    check(st, "qi_dpmpp_2m_update")
 
 
 def modulation(dims: QiDims, w_mod, b_mod, t: float, mod, stream=None):

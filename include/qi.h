@@ -207,6 +207,33 @@ qi_status qi_text_kv_capture(const qi_dims *d, const qi_model_w *w, int32_t L, i
 qi_status qi_euler_update(float *x, const float *vel, float sigma_cur, float sigma_next,
                           int64_t n, void *stream);
 
+/* DPM++ 2M sampler coefficients ([MLX] "Optional modes" names the sampler;
+ * the method is DPM-Solver++(2M), Lu et al. 2022, the multistep second-order
+ * data-prediction solver, written for the flow x = (1 - sigma) x0 + sigma eps
+ * with alpha = 1 - sigma, lambda = log(alpha / sigma), x0 = x - sigma v).  One
+ * step sigma_cur -> sigma_next: x_next = a x - b D with a = sigma_next /
+ * sigma_cur, b = alpha_next (e^-h - 1), h = lambda_next - lambda_cur; D = x0
+ * (first order) or c1 x0 - c2 x0_prev with c2 = 1 / (2 r), r = h_prev / h,
+ * c1 = 1 + c2 (second order).  First order when has_prev = 0, after sigma_prev
+ * = 1 (r infinite) and at the final step (sigma_next = 0: a = 0, b = -1).
+ * Host, double precision: coef[4] = {a, b, c1, c2}.  Returns the order (1 or
+ * 2), or QI_ERR_NULL, or QI_ERR_RANGE unless 0 < sigma_cur <= 1, 0 <=
+ * sigma_next < sigma_cur and (without a previous step) sigma_cur < sigma_prev
+ * <= 1. */
+qi_status qi_dpmpp_2m_coeffs(int32_t has_prev, float sigma_prev, float sigma_cur, float sigma_next,
+                             double *coef);
+
+/* One DPM++ 2M update on the device, in place on fp32 x[n] (same sigmas as the
+ * Euler sampler, qi_flow_sigmas): p = sigma_cur vel, x0 = x - p, D = x0 or
+ * c1 x0 - c2 x0_prev, x = a x - b D, each a separately rounded fp32 operation
+ * in that order with the coefficients of qi_dpmpp_2m_coeffs rounded once to
+ * fp32; x0 is written to x0_prev (device fp32 [n]) for the next step, which
+ * passes has_prev = 1 and this step's sigma_cur as sigma_prev.  n = 0 is a
+ * no-op.  Errors: NULL, RANGE, HIP. */
+qi_status qi_dpmpp_2m_update(float *x, const float *vel, float *x0_prev, int32_t has_prev,
+                             float sigma_prev, float sigma_cur, float sigma_next, int64_t n,
+                             void *stream);
+
 /* ---------------------------------------------------------------- true CFG */
 
 /* Workspace bytes qi_dit_step_cfg needs (0 for invalid dims or N). */

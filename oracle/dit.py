@@ -66,6 +66,21 @@ Readings of points the pages leave open (each is stated where it is used):
       full step rather than the previous step keeps slow drift from adding up
       unchecked, and reusing the last full step's residual is the plainest
       value for the skipped work.)
+  S18 DPM++ 2M sampler: the page only names it.  Read as DPM-Solver++(2M)
+      (Lu et al., "DPM-Solver++: Fast Solver for Guided Sampling of
+      Diffusion Probabilistic Models", 2022, the multistep second-order
+      data-prediction solver) written for the flow x = (1 - sigma) x0 +
+      sigma eps: alpha = 1 - sigma, lambda = log(alpha / sigma), data
+      prediction x0 = x - sigma * v.  Step sigma_s -> sigma_t with
+      h = lambda_t - lambda_s:
+        x_t = (sigma_t / sigma_s) x_s - alpha_t (e^-h - 1) D,
+        D = x0_s (first order) or (1 + 1/(2r)) x0_s - 1/(2r) x0_prev with
+        r = h_prev / h (second order);
+      first order at the first step and at the final step (sigma_t = 0,
+      where h is infinite), as the reference implementations of the method
+      do; the same FlowMatch sigmas as Euler.  Coefficients in float64; the
+      update in fp32 in the order p = sigma_s v, x0 = x - p, D = c1 x0 -
+      c2 x0_prev, x_t = a x - b D (each operation rounded once).
 Parity pins live in tests/test_oracle_*.py.  The whole-step vel has no
 printed value on the pages: beyond the invariants and component pins it is
 "parity unpinned" externally.
@@ -429,6 +444,62 @@ def euler_update(x: np.ndarray, vel: np.ndarray, sigma_cur, sigma_next) -> np.nd
     difference, product and sum each rounded to fp32 (numpy never fuses)."""
     ds = F32(sigma_next) - F32(sigma_cur)
     return (x.astype(F32) + (ds * vel.astype(F32)).astype(F32)).astype(F32)
+
+
+def dpmpp_2m_coeffs(sigma_prev, sigma_cur, sigma_next):
+    """Float64 coefficients (a, b, c1, c2, order) of one DPM++ 2M step
+    sigma_cur -> sigma_next (reading S18): x_next = a x - b D, D = c1 x0 -
+    c2 x0_prev.  sigma_prev None: no previous data prediction (first step)."""
+    def lam(sg):
+        sg = float(sg)
+        if sg >= 1.0:
+            return -math.inf
+        return math.log1p(-sg) - math.log(sg)
+
+    s_cur, s_next = float(sigma_cur), float(sigma_next)
+    if s_next <= 0.0:                              # final step: x_next = x0
+        return 0.0, -1.0, 1.0, 0.0, 1
+    h = lam(s_next) - lam(s_cur)
+    a = s_next / s_cur
+    b = (1.0 - s_next) * math.expm1(-h)
+    if sigma_prev is None:
+        return a, b, 1.0, 0.0, 1
+    r = (lam(s_cur) - lam(sigma_prev)) / h
+    if math.isinf(r):                              # previous sigma was 1 (alpha 0)
+        return a, b, 1.0, 0.0, 1
+    c2 = 1.0 / (2.0 * r)
+    return a, b, 1.0 + c2, c2, 2
+
+
+def dpmpp_2m_step(x, vel, x0_prev, sigma_prev, sigma_cur, sigma_next):
+    """One DPM++ 2M update in fp32 (reading S18).  Returns (x_next, x0), x0
+    being the data prediction to pass as x0_prev to the next step."""
+    a, b, c1, c2, order = dpmpp_2m_coeffs(sigma_prev, sigma_cur, sigma_next)
+    x = x.astype(F32)
+    p = (F32(sigma_cur) * vel.astype(F32)).astype(F32)
+    x0 = (x - p).astype(F32)
+    if order == 1:
+        d = x0
+    else:
+        d = ((F32(c1) * x0).astype(F32) - (F32(c2) * x0_prev.astype(F32)).astype(F32)).astype(F32)
+    u = (F32(a) * x).astype(F32)
+    w = (F32(b) * d).astype(F32)
+    return (u - w).astype(F32), x0
+
+
+def dpmpp_2m_sample(vel_fn, x, sigmas):
+    """A whole DPM++ 2M loop in float64 with velocity vel_fn(x, sigma) (the
+    method itself, for its convergence pins)."""
+    x = np.asarray(x, dtype=np.float64)
+    x0_prev, s_prev = None, None
+    for i in range(len(sigmas) - 1):
+        s_cur, s_next = float(sigmas[i]), float(sigmas[i + 1])
+        a, b, c1, c2, order = dpmpp_2m_coeffs(s_prev, s_cur, s_next)
+        x0 = x - s_cur * vel_fn(x, s_cur)
+        d = x0 if order == 1 else c1 * x0 - c2 * x0_prev
+        x = a * x - b * d
+        x0_prev, s_prev = x0, s_cur
+    return x
 
 
 def fbc_new_state() -> dict:
