@@ -221,3 +221,83 @@ def neg_prompt_len(wl: Workload) -> int:
 def neg_txt_feats(wl: Workload) -> np.ndarray:
     """N(0,1) stand-in negative-prompt embeddings [neg_prompt_len, txt_dim]."""
     return txt_feats(wl, seed=NEG_TXT_SEED, L=neg_prompt_len(wl))
+
+
+# ---------------------------------------------------------------- text encoder
+
+@dataclass(frozen=True)
+class EncWorkload:
+    """A Qwen3-VL-8B-style text stack: width, GQA heads, depth, vocabulary and
+    the full prompt length Lfull (system prefix included)."""
+    name: str
+    hidden: int
+    heads: int
+    kv_heads: int
+    ffn: int
+    n_layers: int
+    vocab: int
+    L_full: int
+    head_dim: int = 128
+    rope_theta: float = 5.0e6
+
+
+# 1: CPU-oracle size; 2: full width, 2 layers, the pages' oracle length 32;
+# 3: the full 36-layer stack at the 1024^2 prompt (407 DiT tokens + 14).
+ENC_WORKLOADS = {
+    1: EncWorkload("enc-reduced-h512-2L-L24", 512, 4, 1, 1536, 2, 1024, 24),
+    2: EncWorkload("enc-h4096-2L-L32", 4096, 32, 8, 12288, 2, 151936, 32),
+    3: EncWorkload("enc36-L421", 4096, 32, 8, 12288, 36, 151936, 421),
+}
+
+ENC_LAYER_BASE = 200000           # stream id of encoder layer i: ENC_LAYER_BASE + i
+ENC_EMBED_ID = 300000
+ENC_IDS_SEED = 1237
+# the system part of the text-to-image template, as token ids (host contract, s.2)
+SYSTEM_PREFIX_IDS = (151644, 8948, 198, 1092, 30782, 408, 323, 23643, 279, 3897, 9934, 13, 151645, 198)
+
+_ENC_TENSORS = ("w_q", "w_k", "w_v", "q_norm", "k_norm", "w_o", "w_gate", "w_up", "w_down", "in_norm",
+                "post_norm")
+
+
+def enc_workload(k: int, **over) -> EncWorkload:
+    ew = ENC_WORKLOADS[k]
+    return replace(ew, **over) if over else ew
+
+
+def _enc_shapes(ew: EncWorkload):
+    H, F, d = ew.hidden, ew.ffn, ew.head_dim
+    return {
+        "w_q": ((ew.heads * d, H), LIN_STD, 0.0),
+        "w_k": ((ew.kv_heads * d, H), LIN_STD, 0.0),
+        "w_v": ((ew.kv_heads * d, H), LIN_STD, 0.0),
+        "q_norm": ((d,), LIN_STD, 1.0),
+        "k_norm": ((d,), LIN_STD, 1.0),
+        "w_o": ((H, ew.heads * d), LIN_STD, 0.0),
+        "w_gate": ((F, H), LIN_STD, 0.0),
+        "w_up": ((F, H), LIN_STD, 0.0),
+        "w_down": ((H, F), LIN_STD, 0.0),
+        "in_norm": ((H,), LIN_STD, 1.0),
+        "post_norm": ((H,), LIN_STD, 1.0),
+    }
+
+
+def enc_layer_weights(ew: EncWorkload, layer: int, as_bf16: bool = True, threads: int = 4) -> dict:
+    """Weights of encoder layer `layer` (2-D ones as bf16 bits when as_bf16)."""
+    return _draw(ENC_LAYER_BASE + layer, _ENC_TENSORS, _enc_shapes(ew), as_bf16, threads)
+
+
+def enc_embed(ew: EncWorkload, as_bf16: bool = True) -> np.ndarray:
+    """Token embedding table [vocab, hidden], N(0, 0.02)."""
+    a = _normal(ENC_EMBED_ID, 0, (ew.vocab, ew.hidden), LIN_STD)
+    return f32_to_bf16_bits(a) if as_bf16 else a
+
+
+def enc_input_ids(ew: EncWorkload, seed: int = ENC_IDS_SEED, L: int | None = None) -> np.ndarray:
+    """int32 ids [L]: the printed system prefix when the vocabulary holds it,
+    then seeded uniform ids."""
+    L = ew.L_full if L is None else L
+    g = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed])))
+    ids = g.integers(0, ew.vocab, size=L, dtype=np.int64)
+    if ew.vocab > max(SYSTEM_PREFIX_IDS) and L >= len(SYSTEM_PREFIX_IDS):
+        ids[:len(SYSTEM_PREFIX_IDS)] = SYSTEM_PREFIX_IDS
+    return ids.astype(np.int32)

@@ -10,11 +10,11 @@ import textwrap
 from oracle import dit
 
 
-def planted(func, old: str, new: str, count: int = 1):
+def planted(func, old: str, new: str, count: int = 1, module=None):
     src = textwrap.dedent(inspect.getsource(func))
     assert src.count(old) >= count, f"plant target not found: {old!r}"
     src = src.replace(old, new, count)
-    ns = dict(vars(dit))
+    ns = dict(vars(module or dit))
     exec(compile(src, f"<planted {func.__name__}>", "exec"), ns)
     return ns[func.__name__]
 
