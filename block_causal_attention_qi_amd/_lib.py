@@ -46,6 +46,20 @@ class QiKvCache(Structure):
                 ("hidden", c_int32), ("valid", c_int32)]
 
 
+class QiEncDims(Structure):
+    _fields_ = [("hidden", c_int32), ("heads", c_int32), ("kv_heads", c_int32), ("head_dim", c_int32),
+                ("ffn", c_int32), ("n_layers", c_int32), ("vocab", c_int32)]
+
+
+class QiEncLayerW(Structure):
+    _fields_ = [("w_qkv", c_void_p), ("q_norm", c_void_p), ("k_norm", c_void_p), ("w_o", c_void_p),
+                ("w_gu", c_void_p), ("w_down", c_void_p), ("in_norm", c_void_p), ("post_norm", c_void_p)]
+
+
+class QiEncModelW(Structure):
+    _fields_ = [("layers", POINTER(QiEncLayerW)), ("embed", c_void_p)]
+
+
 _P = POINTER
 # name -> (restype, argtypes); every symbol include/qi.h declares
 SIGNATURES = {
@@ -71,6 +85,10 @@ SIGNATURES = {
                                   _P(QiKvCache), _P(QiKvCache), c_void_p, c_void_p, c_size_t, c_void_p]),
     "qi_euler_update_cfg": (c_int32, [c_void_p, c_void_p, c_float, c_float, c_float, c_int64, c_void_p]),
     "qi_fbc_bytes": (c_size_t, [_P(QiDims), c_int32]),
+    "qi_enc_rope_table": (c_int32, [c_int32, c_float, c_void_p, c_void_p]),
+    "qi_enc_workspace_bytes": (c_size_t, [_P(QiEncDims), c_int32]),
+    "qi_text_encoder_fwd": (c_int32, [_P(QiEncDims), _P(QiEncModelW), c_void_p, c_int32, c_void_p, c_void_p,
+                                      c_void_p, c_void_p, c_size_t, c_void_p]),
     "qi_dpmpp_2m_coeffs": (c_int32, [c_int32, c_float, c_float, c_float, c_void_p]),
     "qi_dpmpp_2m_update": (c_int32, [c_void_p, c_void_p, c_void_p, c_int32, c_float, c_float, c_float, c_int64,
                                      c_void_p]),
@@ -90,7 +108,7 @@ SIGNATURES = {
     "qi_calib_mfma_tflops": (c_int32, [c_int32, c_int32, c_void_p]),
     "qi_calib_copy_gbs": (c_int32, [c_void_p, c_void_p, c_int64, c_int32, c_void_p]),
 }
-QI_KERNEL_KINDS = 12
+QI_KERNEL_KINDS = 15
 
 _lib = None
 

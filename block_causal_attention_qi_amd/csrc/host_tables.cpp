@@ -112,6 +112,26 @@ qi_status qi_flow_sigmas(int32_t steps, int32_t n_img_tokens, float *sigmas, flo
   return QI_OK;
 }
 
+// Encoder RoPE rows (the encoder declaration's rule): steps rounded to fp32,
+// pow / cos / sin evaluated in double and rounded once.
+qi_status qi_enc_rope_table(int32_t L, float theta, float *cos_out, float *sin_out) {
+  if (!cos_out || !sin_out) return QI_ERR_NULL;
+  if (L < 1 || L > 1000000 || !(theta > 1.0f)) return QI_ERR_RANGE;
+  float inv[64];
+  for (int i = 0; i < 64; ++i) {
+    const float e = (float)(2 * i) / 128.0f;
+    const float pw = (float)std::pow((double)theta, (double)e);
+    inv[i] = 1.0f / pw;
+  }
+  for (int p = 0; p < L; ++p)
+    for (int i = 0; i < 64; ++i) {
+      const float a = (float)p * inv[i];
+      cos_out[(size_t)p * 64 + i] = (float)std::cos((double)a);
+      sin_out[(size_t)p * 64 + i] = (float)std::sin((double)a);
+    }
+  return QI_OK;
+}
+
 // DPM++ 2M coefficients (DPM-Solver++(2M), Lu et al. 2022, written for the
 // flow x = (1 - sigma) x0 + sigma eps): alpha = 1 - sigma, lambda =
 // log(alpha / sigma), x_next = a x - b D with a = sigma_next / sigma_cur,

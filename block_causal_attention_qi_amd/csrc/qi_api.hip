@@ -13,6 +13,7 @@
 #include "../../include/qi.h"
 #include "attention_args.hpp"
 #include "elementwise.hpp"
+#include "encoder.hpp"
 #include "gemm.hpp"
 
 #ifndef QI_GEMM_WM
@@ -365,6 +366,104 @@ qi_status run_step(const qi_dims &d, const qi_model_w &w, int L, int N, const fl
   return QI_OK;
 }
 
+// ---------------------------------------------------------------- text encoder
+bool enc_dims_ok(const qi_enc_dims *d) {
+  if (!d) return false;
+  if (d->head_dim != 128 || d->heads < 1 || d->kv_heads < 1 || d->heads % d->kv_heads != 0) return false;
+  if (d->hidden < 256 || d->hidden > 16384 || d->hidden % 256 != 0) return false;
+  if (d->ffn < 64 || d->ffn % 64 != 0 || d->ffn > 65536) return false;
+  if (d->n_layers < 1 || d->n_layers > 256 || d->vocab < 1) return false;
+  if ((size_t)d->heads * 128 > 65536) return false;
+  return true;
+}
+
+struct EncLayout {
+  size_t h, qkv, q, k, v, o, a, total;
+};
+EncLayout enc_layout(const qi_enc_dims &d, int L) {
+  const size_t H = d.hidden, NQ = (size_t)d.heads * 128, NKV = (size_t)d.kv_heads * 128, F = d.ffn;
+  EncLayout l{};
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off += align256(bytes);
+    return o;
+  };
+  l.h = take((size_t)L * (H > F ? H : F) * 4);
+  l.qkv = take((size_t)L * (NQ + 2 * NKV) * 4);
+  l.q = take((size_t)L * NQ * 4);
+  l.k = take((size_t)L * NKV * 4);
+  l.v = take((size_t)L * NKV * 4);
+  l.o = take((size_t)L * NQ * 4);
+  l.a = take((size_t)L * F * 4);
+  l.total = off;
+  return l;
+}
+
+template <int EPI>
+qi_status launch_enc_gemm(const EncGemmArgs &g, hipStream_t s) {
+  const int nTM = (g.M + enc::BM - 1) / enc::BM;
+  const int nTN = EPI == ENC_SWIGLU ? g.F / (enc::BN / 2) : g.N / enc::BN;
+  TimedLaunch tl(QI_KERNEL_ENC_GEMM, s);
+  hipLaunchKernelGGL((enc_gemm_kernel<EPI>), dim3(nTM * nTN), dim3(enc::THREADS), 0, s, g);
+  return last_launch();
+}
+
+// The encoder forward; arguments validated.  x is the caller's hidden buffer.
+qi_status run_encoder(const qi_enc_dims &d, const qi_enc_model_w &w, const int32_t *ids, int L, const float *cos,
+                      const float *sin, float *x, char *ws, hipStream_t s) {
+  const int H = d.hidden, F = d.ffn, NQ = d.heads * 128, NKV = d.kv_heads * 128, NT = NQ + 2 * NKV;
+  const EncLayout lay = enc_layout(d, L);
+  float *h = (float *)(ws + lay.h), *qkv = (float *)(ws + lay.qkv), *Q = (float *)(ws + lay.q),
+        *K = (float *)(ws + lay.k), *V = (float *)(ws + lay.v), *O = (float *)(ws + lay.o),
+        *a = (float *)(ws + lay.a);
+  {
+    TimedLaunch tl(QI_KERNEL_ENC_MISC, s);
+    hipLaunchKernelGGL(enc_embed_kernel, dim3(L), dim3(256), 0, s, ids, d.vocab, w.embed, H, x);
+  }
+  QI_TRY(last_launch());
+  for (int li = 0; li < d.n_layers; ++li) {
+    const qi_enc_layer_w &lw = w.layers[li];
+    {
+      TimedLaunch tl(QI_KERNEL_ENC_MISC, s);
+      hipLaunchKernelGGL(enc_rmsnorm_kernel, dim3((L + 3) / 4), dim3(256), 0, s, x, lw.in_norm, L, H, kRmsEps, h);
+    }
+    QI_TRY(last_launch());
+    EncGemmArgs g{};
+    g.A = h; g.lda = H; g.W = lw.w_qkv; g.ldw = H; g.M = L; g.N = NT; g.K = H; g.C = qkv; g.ldc = NT;
+    QI_TRY(launch_enc_gemm<ENC_F32>(g, s));
+    {
+      TimedLaunch tl(QI_KERNEL_ENC_MISC, s);
+      const int waves = L * (d.heads + 2 * d.kv_heads);
+      hipLaunchKernelGGL(enc_qk_prep_kernel, dim3((waves + 3) / 4), dim3(256), 0, s, qkv, L, d.heads, d.kv_heads,
+                         lw.q_norm, lw.k_norm, cos, sin, kRmsEps, Q, K, V);
+    }
+    QI_TRY(last_launch());
+    {
+      TimedLaunch tl(QI_KERNEL_ENC_ATTN, s);
+      hipLaunchKernelGGL(enc_attention_kernel, dim3((L + enca::BQ - 1) / enca::BQ, d.heads), dim3(256), 0, s, Q,
+                         K, V, O, L, d.heads, d.kv_heads);
+    }
+    QI_TRY(last_launch());
+    EncGemmArgs r{};
+    r.A = O; r.lda = NQ; r.W = lw.w_o; r.ldw = NQ; r.M = L; r.N = H; r.K = NQ; r.X = x; r.ldx = H;
+    QI_TRY(launch_enc_gemm<ENC_RESID>(r, s));
+    {
+      TimedLaunch tl(QI_KERNEL_ENC_MISC, s);
+      hipLaunchKernelGGL(enc_rmsnorm_kernel, dim3((L + 3) / 4), dim3(256), 0, s, x, lw.post_norm, L, H, kRmsEps,
+                         h);
+    }
+    QI_TRY(last_launch());
+    EncGemmArgs u{};
+    u.A = h; u.lda = H; u.W = lw.w_gu; u.ldw = H; u.M = L; u.N = 2 * F; u.K = H; u.out = a; u.ldo = F; u.F = F;
+    QI_TRY(launch_enc_gemm<ENC_SWIGLU>(u, s));
+    EncGemmArgs dn{};
+    dn.A = a; dn.lda = F; dn.W = lw.w_down; dn.ldw = F; dn.M = L; dn.N = H; dn.K = F; dn.X = x; dn.ldx = H;
+    QI_TRY(launch_enc_gemm<ENC_RESID>(dn, s));
+  }
+  return QI_OK;
+}
+
 // First-block-cache buffer: state, partial sums, then x0, r0p (cached block-0
 // residual), x1s (x after block 0 on the last computed step) and rem (cached
 // residual of blocks 1..n-1), each [N][H] fp32.
@@ -634,6 +733,31 @@ qi_status qi_dpmpp_2m_update(float *x, const float *vel, float *x0_prev, int32_t
   return last_launch();
 }
 
+size_t qi_enc_workspace_bytes(const qi_enc_dims *d, int32_t L) {
+  if (!enc_dims_ok(d) || L < 1 || L > kMaxL) return 0;
+  return enc_layout(*d, L).total;
+}
+
+qi_status qi_text_encoder_fwd(const qi_enc_dims *d, const qi_enc_model_w *w, const int32_t *ids, int32_t L,
+                              const float *cos, const float *sin, float *hidden, void *ws, size_t ws_bytes,
+                              void *stream) {
+  if (!d || !w) return QI_ERR_NULL;
+  if (!enc_dims_ok(d)) return QI_ERR_SHAPE;
+  if (L < 1 || L > kMaxL) return QI_ERR_RANGE;
+  if (!ids || !cos || !sin || !hidden || !ws || !w->layers || !w->embed) return QI_ERR_NULL;
+  if (!al16(cos) || !al16(sin) || !al16(hidden) || !al16(ws) || !al16(w->embed)) return QI_ERR_ALIGN;
+  for (int i = 0; i < d->n_layers; ++i) {
+    const qi_enc_layer_w &lw = w->layers[i];
+    const void *ps[] = {lw.w_qkv, lw.q_norm, lw.k_norm, lw.w_o, lw.w_gu, lw.w_down, lw.in_norm, lw.post_norm};
+    for (const void *p : ps) {
+      if (!p) return QI_ERR_NULL;
+      if (!al16(p)) return QI_ERR_ALIGN;
+    }
+  }
+  if (ws_bytes < enc_layout(*d, L).total) return QI_ERR_WORKSPACE;
+  return run_encoder(*d, *w, ids, L, cos, sin, hidden, (char *)ws, (hipStream_t)stream);
+}
+
 size_t qi_fbc_bytes(const qi_dims *d, int32_t N) {
   if (!d || !dims_ok(d) || N < 1 || N > kMaxN) return 0;
   return fbc_layout(*d, N).total;
@@ -731,7 +855,8 @@ qi_status qi_linear_bf16(int32_t M, int32_t N, int32_t K, const uint16_t *A, con
 const char *qi_kernel_kind_name(int32_t kind) {
   static const char *names[QI_KERNEL_KINDS] = {"modulation", "txt_norm",   "gemm_txt",  "img_embed",
                                                "norm_mod",   "gemm_qkv",   "attention", "gemm_o",
-                                               "gemm_gate_up", "gemm_down", "head",     "euler"};
+                                               "gemm_gate_up", "gemm_down", "head",     "euler",
+                                               "enc_gemm",   "enc_attention", "enc_misc"};
   return (kind >= 0 && kind < QI_KERNEL_KINDS) ? names[kind] : "?";
 }
 

@@ -11,8 +11,8 @@ import ctypes
 import numpy as np
 
 from . import _lib
-from ._lib import (QI_MODE_IMAGE_ONLY, QI_MODE_JOINT, QiBlockW, QiDims, QiError, QiKvCache,
-                   QiModelW, check)
+from ._lib import (QI_MODE_IMAGE_ONLY, QI_MODE_JOINT, QiBlockW, QiDims, QiEncDims, QiEncLayerW, QiEncModelW,
+                   QiError, QiKvCache, QiModelW, check)
 
 __all__ = ["QI_MODE_JOINT", "QI_MODE_IMAGE_ONLY", "QiError", "make_dims", "rope_axis_table",
            "rope_tables", "flow_sigmas", "workspace_bytes", "kv_cache_bytes", "kv_slot_elems",
@@ -20,7 +20,8 @@ __all__ = ["QI_MODE_JOINT", "QI_MODE_IMAGE_ONLY", "QiError", "make_dims", "rope_
            "euler_update", "modulation", "block_causal_attention", "linear_bf16", "stream_handle",
            "timing_begin", "timing_end", "KERNEL_KINDS", "cfg_workspace_bytes", "CfgWorkspace", "dit_step_cfg",
            "euler_update_cfg", "fbc_bytes", "FirstBlockCache", "dit_step_fbc", "dpmpp_2m_coeffs",
-           "dpmpp_2m_update"]
+           "dpmpp_2m_update", "make_enc_dims", "enc_rope_table", "enc_workspace_bytes", "DeviceEncoder",
+           "EncWorkspace", "text_encoder_fwd"]
 
 
 def _np_ptr(a: np.ndarray) -> int:
@@ -218,6 +219,72 @@ class Workspace:
         return _ptr(self.buf)
 
 
+# ------------------------------------------------------------------ text encoder
+
+def make_enc_dims(hidden: int, heads: int, kv_heads: int, ffn: int, n_layers: int, vocab: int) -> QiEncDims:
+    return QiEncDims(hidden, heads, kv_heads, 128, ffn, n_layers, vocab)
+
+
+def enc_rope_table(L: int, theta: float = 5.0e6):
+    """Host fp32 RoPE rows (cos, sin) [L, 64] of positions 0..L-1."""
+    c = np.empty((L, 64), np.float32)
+    s = np.empty((L, 64), np.float32)
+    check(_lib.load().qi_enc_rope_table(L, float(theta), _np_ptr(c), _np_ptr(s)), "qi_enc_rope_table")
+    return c, s
+
+
+def enc_workspace_bytes(dims: QiEncDims, L: int) -> int:
+    return int(_lib.load().qi_enc_workspace_bytes(ctypes.byref(dims), L))
+
+
+class EncWorkspace:
+    def __init__(self, dims: QiEncDims, L: int, device="cuda"):
+        import torch
+        self.nbytes = enc_workspace_bytes(dims, L)
+        if self.nbytes == 0:
+            raise ValueError("invalid encoder dims or L")
+        self.buf = torch.empty(self.nbytes, dtype=torch.uint8, device=device)
+
+    @property
+    def ptr(self) -> int:
+        return _ptr(self.buf)
+
+
+class DeviceEncoder:
+    """Device copies of the encoder weights.  layers: iterable of per-layer
+    dicts with w_q, w_k, w_v, q_norm, k_norm, w_o, w_gate, w_up, w_down,
+    in_norm, post_norm (2-D weights as bf16 bits); embed: [vocab, hidden] bf16
+    bits.  q/k/v and gate/up are concatenated into the layouts the library
+    reads (w_qkv: q rows, k rows, v rows; w_gu: gate rows, up rows)."""
+
+    def __init__(self, dims: QiEncDims, embed: np.ndarray, layers, device="cuda"):
+        self.dims = dims
+        self.embed = to_device(_as_dev("embed", embed), device)
+        self.layers = []
+        for lw in layers:
+            d = {
+                "w_qkv": np.concatenate([lw["w_q"], lw["w_k"], lw["w_v"]], axis=0),
+                "q_norm": lw["q_norm"], "k_norm": lw["k_norm"], "w_o": lw["w_o"],
+                "w_gu": np.concatenate([lw["w_gate"], lw["w_up"]], axis=0),
+                "w_down": lw["w_down"], "in_norm": lw["in_norm"], "post_norm": lw["post_norm"],
+            }
+            self.layers.append({k: to_device(_as_dev(k, v), device) for k, v in d.items()})
+        if len(self.layers) != dims.n_layers:
+            raise ValueError(f"{len(self.layers)} layers given, dims say {dims.n_layers}")
+        keys = ("w_qkv", "q_norm", "k_norm", "w_o", "w_gu", "w_down", "in_norm", "post_norm")
+        self._lw = (QiEncLayerW * len(self.layers))()
+        for i, lw in enumerate(self.layers):
+            self._lw[i] = QiEncLayerW(*(_ptr(lw[k]) for k in keys))
+        self.w = QiEncModelW(ctypes.cast(self._lw, ctypes.POINTER(QiEncLayerW)), _ptr(self.embed))
+
+
+def text_encoder_fwd(enc: DeviceEncoder, ids, L: int, cos, sin, hidden, ws: EncWorkspace, stream=None):
+    """hidden [L, hidden] (device fp32) <- the encoder on ids [L] (device int32)."""
+    st = _lib.load().qi_text_encoder_fwd(ctypes.byref(enc.dims), ctypes.byref(enc.w), _ptr(ids), L, _ptr(cos),
+                                         _ptr(sin), _ptr(hidden), ws.ptr, ws.nbytes, stream_handle(stream))
+    check(st, "qi_text_encoder_fwd")
+
+
 # ------------------------------------------------------------------ entry points
 
 def dit_step(model: DeviceModel, L: int, N: int, img_tokens, txt_feats, t: float, txt_cos, txt_sin,
@@ -338,7 +405,7 @@ def linear_bf16(A, W, bias, C, stream=None):
 # ------------------------------------------------------------------ kernel timing
 
 KERNEL_KINDS = ["modulation", "txt_norm", "gemm_txt", "img_embed", "norm_mod", "gemm_qkv", "attention",
-                "gemm_o", "gemm_gate_up", "gemm_down", "head", "euler"]
+                "gemm_o", "gemm_gate_up", "gemm_down", "head", "euler", "enc_gemm", "enc_attention", "enc_misc"]
 
 
 def timing_begin(max_launches: int = 65536):

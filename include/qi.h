@@ -310,6 +310,58 @@ qi_status qi_dit_step_fbc(const qi_dims *d, const qi_model_w *w, int32_t L, int3
 qi_status qi_fbc_stats(const void *fbc, int32_t *n_steps, int32_t *n_skipped, float *last_change,
                        void *stream);
 
+/* ---------------------------------------------------------------- text encoder */
+
+/* The text encoder of the port page's pieces table ("Text encoder" row: the
+ * Qwen3-VL-8B text stack) and of the host contract s.1 and s.3: input_ids
+ * [L] -> hidden [L][hidden], the residual stream after the last layer with no
+ * final norm; bf16 weights, fp32 compute (the page's "<|im_start|> tokens
+ * need fp32 compute" paragraph).  Per layer (Qwen3 decoder layer):
+ *   h = RMSNorm(x; in_norm); q, k, v = h W_qkv^T split [heads | kv | kv] x 128;
+ *   q, k = RoPE(RMSNorm_head(q; q_norm)), RoPE(RMSNorm_head(k; k_norm))
+ *     (rotate-half: feature i pairs with i + 64, angle p theta^(-2i/128));
+ *   o = causal GQA attention (query head h reads kv head h / (heads/kv_heads),
+ *     scale 1/sqrt(128)); x += o W_o^T;
+ *   h = RMSNorm(x; post_norm); x += (SiLU(h Wg^T) * (h Wu^T)) W_down^T;
+ * RMSNorm eps 1e-6.  Sizes of the page: hidden 4096, heads 32, kv_heads 8,
+ * head_dim 128, ffn 12288, n_layers 36. */
+typedef struct {
+  int32_t hidden, heads, kv_heads, head_dim, ffn, n_layers, vocab;
+} qi_enc_dims;
+
+typedef struct {
+  const uint16_t *w_qkv;          /* [(heads + 2 kv_heads) * 128][hidden] bf16: q rows, k rows, v rows */
+  const float *q_norm, *k_norm;   /* [128] */
+  const uint16_t *w_o;            /* [hidden][heads * 128] */
+  const uint16_t *w_gu;           /* [2 ffn][hidden]: gate rows then up rows */
+  const uint16_t *w_down;         /* [hidden][ffn] */
+  const float *in_norm, *post_norm; /* [hidden] */
+} qi_enc_layer_w;
+
+typedef struct {
+  const qi_enc_layer_w *layers;   /* host array [n_layers] of device pointers */
+  const uint16_t *embed;          /* [vocab][hidden] bf16 */
+} qi_enc_model_w;
+
+/* Host fp32 RoPE rows of positions 0..L-1: cos, sin [L][64] with angle
+ * p * theta^(-2i/128), each step rounded to fp32 (the exponent 2i/128, the
+ * power -- correctly rounded --, its reciprocal, the product with p) and cos /
+ * sin correctly rounded.  Errors: NULL, RANGE (L < 1, theta <= 1). */
+qi_status qi_enc_rope_table(int32_t L, float theta, float *cos, float *sin);
+
+/* Workspace bytes of qi_text_encoder_fwd (0 for invalid dims or L). */
+size_t qi_enc_workspace_bytes(const qi_enc_dims *d, int32_t L);
+
+/* One encoder forward.  ids: device int32 [L] (an id outside 0..vocab-1 gives
+ * a NaN row); cos, sin: device fp32 [L][64] from qi_enc_rope_table; hidden:
+ * device fp32 [L][hidden] out.  Causal: the first L' outputs do not depend on
+ * later tokens (bit for bit).  Ranges: 1 <= L <= 512; head_dim 128; hidden %
+ * 256 == 0; heads % kv_heads == 0; ffn % 64 == 0.  Errors: NULL, SHAPE, RANGE,
+ * ALIGN, WORKSPACE, HIP. */
+qi_status qi_text_encoder_fwd(const qi_enc_dims *d, const qi_enc_model_w *w, const int32_t *ids,
+                              int32_t L, const float *cos, const float *sin, float *hidden, void *ws,
+                              size_t ws_bytes, void *stream);
+
 /* ---------------------------------------------------------------- components */
 
 /* The shared modulation rows alone: mod [2][4H] (device fp32) = W_mod e(0) +
@@ -355,8 +407,11 @@ qi_status qi_linear_bf16(int32_t M, int32_t N, int32_t K, const uint16_t *A, con
 #define QI_KERNEL_GEMM_GATE_UP 8 /* gate/up GEMM + SwiGLU */
 #define QI_KERNEL_GEMM_DOWN 9    /* down GEMM + gated residual */
 #define QI_KERNEL_HEAD 10        /* final RMSNorm + proj_out */
-#define QI_KERNEL_EULER 11       /* fp32 Euler update */
-#define QI_KERNEL_KINDS 12
+#define QI_KERNEL_EULER 11       /* fp32 Euler update (and the DPM++ 2M update) */
+#define QI_KERNEL_ENC_GEMM 12    /* text encoder: fp32-activation GEMMs */
+#define QI_KERNEL_ENC_ATTN 13    /* text encoder: fp32 attention */
+#define QI_KERNEL_ENC_MISC 14    /* text encoder: embed, norms, q/k prep */
+#define QI_KERNEL_KINDS 15
 
 /* Name of a kernel kind (static string, "?" if out of range). */
 const char *qi_kernel_kind_name(int32_t kind);

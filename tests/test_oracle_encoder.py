@@ -135,3 +135,13 @@ def test_planted_mistakes_fail_the_library_comparison(fn, old, new):
     good = enc.text_encoder(emb, layers, ids, cos, sin, wide.heads, wide.kv_heads)
     assert np.abs(good - ref).max() / np.abs(ref).max() < 1e-6
     assert np.abs(got - ref).max() / np.abs(ref).max() > 1e-3
+
+
+def test_library_host_rope_rows_equal_the_oracle():
+    """The library's host RoPE rows (qi_enc_rope_table) are bit-identical to
+    the oracle's reading-E3 table (host logic, no GPU)."""
+    import block_causal_attention_qi_amd as qi
+    for L in (1, 32, 421, 512):
+        c, s = qi.enc_rope_table(L)
+        oc, os_ = enc.rope_table(L)
+        assert np.array_equal(c, oc) and np.array_equal(s, os_)
