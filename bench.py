@@ -17,8 +17,9 @@ the image-only steps measured with HIP events on the launch stream, the
 roofline fraction of the dominant kernel, the CPU oracle's throughput on a
 bounded sample (one image-only block, scaled to a step), and, as an extra,
 true CFG on the same workload (a negative prompt of half the length in a
-second K/V slot, both branches through every block at once) and the
-first-block cache (Fast mode)."""
+second K/V slot, both branches through every block at once), the
+first-block cache (Fast mode) and the 36-layer text encoder on the 1024^2
+prompt."""
 from __future__ import annotations
 
 import argparse
@@ -36,6 +37,7 @@ if ROOT not in sys.path:
 METRIC = "DiT steps/sec (32 blocks, bf16) at 1024² L=407; attn+GEMM MFMA util"
 CFG_STEPS = 10
 FBC_STEPS = 10
+ENC_REPS = 5
 
 
 def log(*a):
@@ -50,6 +52,9 @@ def parse():
     p.add_argument("--workload", type=int, default=4)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-cfg", action="store_true", help="skip the true-CFG and first-block-cache extras")
+    p.add_argument("--no-encoder", action="store_true", help="skip the text-encoder extra")
+    p.add_argument("--only-encoder", action="store_true",
+                   help="run only the text-encoder measurement and print its JSON (for profiling)")
     p.add_argument("--threads", type=int, default=16, help="host threads for weight generation")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="only copy 1 GiB device-to-device (10 times): the known-size reference for "
@@ -238,6 +243,59 @@ def measure_fbc(qi, qs, wl, model, dims, x0, rope, sig, tin, img_step_ms):
     return out
 
 
+def measure_encoder(qi, qs, threads):
+    """The 36-layer text encoder on the 1024^2 prompt (407 DiT tokens plus
+    the 14-token system prefix, L = 421), a reported extra: ENC_REPS forwards
+    timed with events, per-kernel durations from the library's launch timer,
+    FLOPs of the plain definition.  Each fp32 GEMM product runs as three bf16
+    MFMA passes over the exact 3-plane split of the activations, so the MFMA
+    work issued is three times the GEMM FLOPs."""
+    import concurrent.futures as cf
+
+    import torch
+
+    from block_causal_attention_qi_amd import flops
+    ew = qs.enc_workload(3)
+    L = ew.L_full
+    dims = qi.make_enc_dims(ew.hidden, ew.heads, ew.kv_heads, ew.ffn, ew.n_layers, ew.vocab)
+    t0 = time.time()
+    with cf.ThreadPoolExecutor(threads) as ex:
+        layers = ex.map(lambda i: qs.enc_layer_weights(ew, i, threads=1), range(ew.n_layers))
+        model = qi.DeviceEncoder(dims, qs.enc_embed(ew), layers)
+    log(f"encoder weights ({ew.n_layers} layers) on device in {time.time() - t0:.1f} s")
+    ids = torch.from_numpy(qs.enc_input_ids(ew).astype(np.int32)).cuda()
+    c, s = (torch.from_numpy(a).cuda() for a in qi.enc_rope_table(L, ew.rope_theta))
+    out = torch.empty((L, ew.hidden), dtype=torch.float32, device="cuda")
+    ws = qi.EncWorkspace(dims, L)
+    qi.text_encoder_fwd(model, ids, L, c, s, out, ws)      # warm
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(ENC_REPS):
+        qi.text_encoder_fwd(model, ids, L, c, s, out, ws)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / ENC_REPS
+    qi.timing_begin(4096)
+    qi.text_encoder_fwd(model, ids, L, c, s, out, ws)
+    timing = qi.timing_end()
+    if not torch.isfinite(out).all():
+        raise RuntimeError("non-finite encoder output")
+    fl = flops.encoder_flops(ew.hidden, ew.heads, ew.kv_heads, ew.ffn, ew.n_layers, L)
+    kern = {}
+    for kind in ("enc_gemm", "enc_attention", "enc_misc"):
+        t, n = timing[kind]
+        kern[kind] = {"launches": n, "ms": round(t, 3)}
+    g_ms, a_ms = timing["enc_gemm"][0], timing["enc_attention"][0]
+    kern["enc_gemm"].update(fp32_tflops=round(fl["gemm"] / (g_ms * 1e-3) / 1e12, 1),
+                            bf16_mfma_tflops_issued=round(3 * fl["gemm"] / (g_ms * 1e-3) / 1e12, 1))
+    kern["enc_attention"].update(fp32_tflops=round(fl["attention"] / (a_ms * 1e-3) / 1e12, 1))
+    log(f"encoder: {ms:.2f} ms per forward ({ew.n_layers} layers, L {L})")
+    return {"workload": ew.name, "layers": ew.n_layers, "L": L, "hidden": ew.hidden, "reps": ENC_REPS,
+            "ms_per_forward": round(ms, 3), "tflops_fp32_effective": round(fl["total"] / (ms * 1e-3) / 1e12, 1),
+            "flops_per_forward": fl["total"], "kernels": kern}
+
+
 def main():
     args = parse()
     if args.calibrate_copy:
@@ -245,6 +303,11 @@ def main():
         return
     if args.calibrate:
         calibrate()
+        return
+    if args.only_encoder:
+        import block_causal_attention_qi_amd as qi
+        import qi_synth as qs
+        print(json.dumps({"text_encoder": measure_encoder(qi, qs, args.threads)}))
         return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (the DiT step here is built and measured on one MI355X); "
@@ -366,6 +429,7 @@ def main():
     step_f = flops.step_flops(shape)
     cfg = None if args.no_cfg else measure_cfg(qi, qs, wl, model, dims, x0, rope, sig, tin, img_step_ms)
     fbc = None if args.no_cfg else measure_fbc(qi, qs, wl, model, dims, x0, rope, sig, tin, img_step_ms)
+    enc = None if args.no_encoder else measure_encoder(qi, qs, args.threads)
     cpu = None if args.no_cpu_baseline else cpu_baseline(wl)
 
     out = {
@@ -397,6 +461,7 @@ def main():
         "cpu_baseline": cpu,
         "cfg": cfg,
         "first_block_cache": fbc,
+        "text_encoder": enc,
     }
     print(json.dumps(out))
 

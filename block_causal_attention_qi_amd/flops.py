@@ -78,3 +78,15 @@ def step_flops(s: Shape, include_shared: bool = False) -> int:
         kw = kernel_work(s)
         f += sum(kw[k][0] for k in ("modulation", "img_embed", "head", "gemm_txt") if k in kw)
     return f
+
+
+def encoder_flops(hidden: int, heads: int, kv_heads: int, ffn: int, n_layers: int, L: int,
+                  head_dim: int = 128) -> dict:
+    """Algorithmic FLOPs of one causal forward of the text encoder over L
+    tokens (no masked work, no padding): the projections 2 L (H (heads +
+    2 kv_heads) d + heads d H + 3 F H) per layer and attention 4 d heads per
+    allowed (query, key) pair, L (L + 1) / 2 of them."""
+    H, F, d = hidden, ffn, head_dim
+    gemm = 2 * L * (H * (heads + 2 * kv_heads) * d + heads * d * H + 3 * F * H) * n_layers
+    attn = 4 * d * heads * (L * (L + 1) // 2) * n_layers
+    return {"gemm": gemm, "attention": attn, "total": gemm + attn}
