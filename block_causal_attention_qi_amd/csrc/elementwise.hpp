@@ -10,7 +10,7 @@
 // out[r] = bf16( x[r] * rsqrt(mean(x[r]^2) + eps) * w * (1 + scale[r]) ), where
 // w = gamma (zero_centred: 1 + gamma) and scale is the modulation chunk of the
 // row's kind (rows < L_rows: mod row 0, else mod row 1; mod == NULL: 1).
-// The port page's DiT row: RMSNorm with modulation (spec step list);
+// The port page's DiT row: RMSNorm with modulation inside every block;
 // ZeroCenterRMSNorm for the text projection.  One wave per row (4 rows per
 // workgroup): each lane keeps VPL float4 of the row in registers, so the whole
 // row is in flight at once and the reduction is a pure wavefront reduction.

@@ -48,7 +48,7 @@ typedef int32_t qi_status;
 #define QI_ERR_WORKSPACE (-5)   /* workspace smaller than qi_workspace_bytes */
 #define QI_ERR_CACHE (-6)       /* K/V cache invalid or made for another shape */
 #define QI_ERR_HIP (-7)         /* a HIP runtime call or launch failed */
-#define QI_ERR_UNSUPPORTED (-8) /* a valid request this build does not handle */
+#define QI_ERR_UNSUPPORTED (-8) /* a valid request this library does not handle */
 
 /* Pass kinds of one block.  JOINT runs the [text L | image N] sequence (step 1
  * of a render, or full recompute); IMAGE_ONLY runs the N image rows against

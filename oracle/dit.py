@@ -248,7 +248,7 @@ def block_causal_attention(q_txt, k_txt, v_txt, q_img, k_img, v_img, bf16: bool 
 
 def dit_block(x: np.ndarray, L_rows: int, bw: dict, m_txt, m_img, cos, sin,
               heads: int, kv_text=None, bf16: bool = False):
-    """One single-stream block (spec step list; [PORT] DiT row).
+    """One single-stream block ([PORT] pieces table, DiT row).
 
     x: [T, H] residual stream, rows [text L_rows | image].  L_rows = L for a
     joint pass, 0 for an image-only pass (then kv_text = (k_txt, v_txt) from
