@@ -143,6 +143,15 @@ def cpu_baseline(wl):
                       f"{dt:.2f} s per block scaled x{wl.n_blocks}"}
 
 
+def kernel_code_text(src: str) -> str:
+    """The kernel sources without comments and with whitespace runs collapsed:
+    what the counters' validity depends on (a comment edit changes no kernel)."""
+    import re
+    src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
+    src = re.sub(r"//[^\n]*", " ", src)
+    return " ".join(src.split())
+
+
 def measured_traffic(kind: str):
     """HBM bytes per image-only launch of `kind` from the committed rocprofv3
     counter summary (FETCH_SIZE / WRITE_SIZE scaled by a 1 GiB copy), or None
@@ -156,7 +165,7 @@ def measured_traffic(kind: str):
     csrc = os.path.join(ROOT, "block_causal_attention_qi_amd", "csrc")
     src = "".join(open(os.path.join(csrc, f)).read()
                   for f in ("common.hpp", "gemm.hpp", "attention_args.hpp", "attention.hpp", "elementwise.hpp"))
-    if hashlib.sha256(src.encode()).hexdigest() != rec.get("kernel_source_sha256"):
+    if hashlib.sha256(kernel_code_text(src).encode()).hexdigest() != rec.get("kernel_source_sha256"):
         return None, "kernels changed since the counters were taken"
     ent = rec.get("kernels", {}).get(kind, {}).get("image-only")
     if not ent:
