@@ -72,19 +72,28 @@ constexpr int THREADS = 256;  // 4 waves as 2 x 2; each owns (BM/2) tokens x (BN
 QI_DEV int lds_slot(int r, int c) { return r * 8 + (c ^ ((r >> 1) & 7)); }
 
 // Workgroup -> output tile.  Workgroups are handed to the 8 XCDs round-robin
-// (id % 8), each XCD with its own L2.  When the W-tile columns split evenly
-// over the XCDs, XCD x owns a contiguous band of W columns (so a W tile is
-// fetched into one L2 only) and walks it in groups of 4 token tiles, columns
+// (id % 8), each XCD with its own L2.  The tile grid is cut into 8 equal
+// regions, XM bands of token tiles by 8/XM bands of W-tile columns, one per
+// XCD, and each XCD walks its region in groups of 4 token tiles, columns
 // fastest, so the tiles that run together share both operands' K slices.
+// Wide outputs (32 or more W-tile columns) keep whole token bands (XM = 1: a
+// W tile is fetched into one L2 only); narrow ones (16 columns: O-proj and
+// down) take 4 x 2 or 2 x 4 regions, so an XCD's 32 concurrent tiles read 4
+// token slices and 8 W slices per K step instead of 16 and 2.
 QI_DEV void tile_of(int bid, int nTM, int nTN, int &tm, int &tn) {
-  if (nTN % 8 == 0) {
+  int XM = 0;
+  if (nTN % 8 == 0 && nTN >= 32) XM = 1;
+  else if (nTM % 4 == 0 && nTN % 2 == 0) XM = 4;
+  else if (nTM % 2 == 0 && nTN % 4 == 0) XM = 2;
+  else if (nTN % 8 == 0) XM = 1;
+  if (XM) {
     constexpr int GM = 4;
+    const int XN = 8 / XM, RM = nTM / XM, RN = nTN / XN;
     const int xcd = bid & 7, j = bid >> 3;
-    const int nTNx = nTN >> 3;
-    const int g = j / (GM * nTNx), w = j % (GM * nTNx);
-    const int rows = min(GM, nTM - g * GM);
-    tm = g * GM + w % rows;
-    tn = xcd * nTNx + w / rows;
+    const int g = j / (GM * RN), w = j % (GM * RN);
+    const int rows = min(GM, RM - g * GM);
+    tm = (xcd / XN) * RM + g * GM + w % rows;
+    tn = (xcd % XN) * RN + w / rows;
   } else {
     tm = bid % nTM;
     tn = bid / nTM;
@@ -106,16 +115,46 @@ QI_DEV void store4(const GemmArgs &g, int m, int n, f32x4 v) {
   }
 }
 
-// QKV epilogue of one wave tile: FS blocks of 32 W rows starting at n0 and TS
-// blocks of 32 tokens starting at mbase.  The wave's W rows lie in one section
-// (q, k or v) and one head (n0 % 64 == 0, FS * 32 <= 64), so section, head and
-// segment come out once, and each token's cos/sin pairs are fetched together
-// before any of its outputs is rotated.
+// RoPE rows of a QKV tile, staged in LDS once the K loop is done (the operand
+// buffers are free then).  Each lane rotates 32 pairs of each of its tokens,
+// and 32 lanes hold 32 different tokens: read straight from the tables, every
+// load instruction would touch 32 rows, which the vector cache serves one row
+// at a time.  Staged, the tables are read in whole contiguous rows instead.
+// Layout: the float2 (pairs 2q, 2q+1) of tile row r sits at slot
+// r * 32 + (q ^ (r & 31)), so the 32 rows one half-wave reads at a fixed q hit
+// 32 distinct bank pairs.  A 16-byte chunk k (q = 2k, 2k + 1) of the table row
+// lands at the even slot (2k) ^ (r & 30), its halves swapped when r is odd.
+template <int BM, int THREADS>
+QI_DEV void stage_rope_rows(const GemmArgs &g, int m0, u32x4 *cl, u32x4 *sl, int tid) {
+  static_assert((BM * 16) % THREADS == 0, "whole passes over the tile's rows");
+#pragma unroll
+  for (int it = 0; it < BM * 16 / THREADS; ++it) {
+    const int i = tid + THREADS * it;
+    const int r = i >> 4, k = i & 15;
+    const int m = m0 + r;
+    if (m >= g.M) continue;
+    const bool txt = m < g.L_rows;
+    const size_t off = (size_t)(txt ? m : m - g.L_rows) * 64 + 4 * k;
+    u32x4 c = *(const u32x4 *)((txt ? g.cos_t : g.cos_i) + off);
+    u32x4 sn = *(const u32x4 *)((txt ? g.sin_t : g.sin_i) + off);
+    if (r & 1) {
+      c = u32x4{c[2], c[3], c[0], c[1]};
+      sn = u32x4{sn[2], sn[3], sn[0], sn[1]};
+    }
+    const int chunk = r * 16 + (k ^ ((r & 30) >> 1));
+    cl[chunk] = c;
+    sl[chunk] = sn;
+  }
+}
+
+// The V section of a QKV wave tile: FS blocks of 32 W rows starting at n0
+// (one head, n0 % 64 == 0) and TS blocks of 32 tokens starting at mbase,
+// stored transposed into V^T [heads][128][ldv].  For one output feature the
+// 32 lanes of a half-wave hold 32 consecutive tokens, so each store writes
+// 64 contiguous bytes.
 template <int TS, int FS>
-QI_DEV void store_qkv_wave(const GemmArgs &g, int mbase, int n0, const f32x16 (&acc)[FS][TS], int lane) {
-  static_assert(FS * 32 <= 64, "a wave tile stays inside one half head");
-  const int sec = n0 / g.H;
-  const int w0 = n0 - sec * g.H;
+QI_DEV void store_v_wave(const GemmArgs &g, int mbase, int n0, const f32x16 (&acc)[FS][TS], int lane) {
+  const int w0 = n0 - 2 * g.H;
   const int head = w0 >> 7, dh0 = w0 & 127;
   const int h4 = 4 * (lane >> 5), fr = lane & 31;
 #pragma unroll
@@ -123,45 +162,103 @@ QI_DEV void store_qkv_wave(const GemmArgs &g, int mbase, int n0, const f32x16 (&
     const int m = mbase + 32 * t + fr;
     if (m >= g.M) continue;
     const bool txt = m < g.L_rows;
-    const int row = txt ? m : m - g.L_rows;  // cos/sin row (image tables hold every branch)
-    // branch of an image row and its row inside the branch's Q/K/V^T
-    const int br = (txt || g.batch <= 1) ? 0 : row / g.seg_i;
+    const int row = txt ? m : m - g.L_rows;
+    const int br = (txt || g.batch <= 1) ? 0 : row / g.seg_i;  // branch of an image row
     const int brow = row - br * g.seg_i;
-    if (sec < 2) {
-      // outputs dh0 + 32 f + 8 j + h4 + 0..3 are RoPE pairs (dh0 + h4)/2 + 16 f + 4 j + 0..1
-      const int poff = row * 64 + ((dh0 + h4) >> 1);
-      const float *cp = (txt ? g.cos_t : g.cos_i) + poff;
-      const float *sp = (txt ? g.sin_t : g.sin_i) + poff;
-      float2 cs[FS][4], sn[FS][4];
+    const int ldv = txt ? g.ldv_t : g.ldv_i;
+    u16 *base = (txt ? g.vt_t : g.vt_i) + (size_t)br * g.H * ldv + ((size_t)head * 128 + dh0 + h4) * ldv + brow;
 #pragma unroll
-      for (int f = 0; f < FS; ++f)
+    for (int f = 0; f < FS; ++f)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          cs[f][j] = *(const float2 *)(cp + 16 * f + 4 * j);
-          sn[f][j] = *(const float2 *)(sp + 16 * f + 4 * j);
-        }
-      u16 *dst = (sec == 0 ? (txt ? g.q_t : g.q_i) : (txt ? g.k_t : g.k_i)) + (size_t)br * g.H * g.seg_i +
-                 ((size_t)head * (txt ? g.seg_t : g.seg_i) + brow) * 128 + dh0 + h4;
+      for (int j = 0; j < 4; ++j)
 #pragma unroll
-      for (int f = 0; f < FS; ++f)
+        for (int r = 0; r < 4; ++r) base[(size_t)(32 * f + 8 * j + r) * ldv] = f32_to_bf16(acc[f][t][4 * j + r]);
+  }
+}
+
+// The QKV epilogue of a BM-token workgroup tile whose W rows start at n_tile
+// (the section is uniform over the tile: H is a multiple of the tile width).
+// Wave (wrow / WT, n0) holds WT = 32 TS tokens x 64 W rows, half of one q or
+// k head, as 4 consecutive features of one token per lane and register quad.
+// Stored straight from there, every store instruction would touch 32 token
+// rows; so the q / k tiles go through LDS twice once the K loop is done:
+//   1. the RoPE rows of the tile's tokens are staged (stage_rope_rows), each
+//      lane rotates its pairs and rounds them once to bf16;
+//   2. each wave writes its 128-byte token half-rows to its own LDS region
+//      and reads them back as 16-byte chunks, 8 lanes per token, so a store
+//      instruction writes 8 whole half-rows of Q or K [heads][T][128].
+// Region layout: 8-byte slot s (features 4 s .. 4 s + 3) of wave row rr sits
+// at rr * 16 + (s ^ ((rr >> 1) & 15)): the 32 rows a half-wave writes at a
+// fixed s cover all 64 banks, and a 16-byte read of slots 2k, 2k + 1 stays
+// one aligned chunk (halves swapped when the XOR term is odd).
+template <int BM, int THREADS, int TS, int FS>
+QI_DEV void qkv_epilogue(const GemmArgs &g, int m0, int n_tile, int wrow, int n0, const f32x16 (&acc)[FS][TS],
+                         int tid, u32x4 *cl, u32x4 *sl) {
+  static_assert(FS == 2, "a wave tile is half a head: 64 W rows");
+  constexpr int WT = 32 * TS;
+  static_assert((THREADS / 64) * WT * 8 <= 2 * BM * 16, "the waves' regions fit in the staged-table space");
+  const int lane = tid & 63, wave = tid >> 6;
+  const int fr = lane & 31, hf = lane >> 5;
+  if (n_tile / g.H >= 2) {
+    store_v_wave<TS, FS>(g, m0 + wrow, n0, acc, lane);
+    return;
+  }
+  const int sec = n0 / g.H;
+  const int w0 = n0 - sec * g.H;
+  const int head = w0 >> 7, dh0 = w0 & 127;
+  __syncthreads();
+  stage_rope_rows<BM, THREADS>(g, m0, cl, sl, tid);
+  __syncthreads();
+  // outputs dh0 + 32 f + 8 j + 4 hf + 0..3 are RoPE pairs 2q, 2q + 1 with
+  // q = dh0 / 4 + hf + 8 f + 2 j
+  const u32x2 *cl2 = (const u32x2 *)cl, *sl2 = (const u32x2 *)sl;
+  const int q0 = (dh0 >> 2) + hf;
+  u32x2 y[TS][FS][4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const f32x4 v = quad(acc[f][t], j);
-          const float c0 = cs[f][j].x, c1 = cs[f][j].y, s0 = sn[f][j].x, s1 = sn[f][j].y;
-          const float y0 = v[0] * c0 - v[1] * s0, y1 = v[0] * s0 + v[1] * c0;
-          const float y2 = v[2] * c1 - v[3] * s1, y3 = v[2] * s1 + v[3] * c1;
-          *(u32x2 *)(dst + 32 * f + 8 * j) = u32x2{pack_bf16x2(y0, y1), pack_bf16x2(y2, y3)};
-        }
-    } else {
-      const int ldv = txt ? g.ldv_t : g.ldv_i;
-      u16 *base = (txt ? g.vt_t : g.vt_i) + (size_t)br * g.H * ldv + ((size_t)head * 128 + dh0 + h4) * ldv + brow;
+  for (int t = 0; t < TS; ++t) {
+    const int r = wrow + 32 * t + fr;
 #pragma unroll
-      for (int f = 0; f < FS; ++f)
+    for (int f = 0; f < FS; ++f)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < 4; ++j) {
+        const int slot = r * 32 + ((q0 + 8 * f + 2 * j) ^ (r & 31));
+        const float2 cs = __builtin_bit_cast(float2, cl2[slot]);
+        const float2 sn = __builtin_bit_cast(float2, sl2[slot]);
+        const f32x4 v = quad(acc[f][t], j);
+        const float y0 = v[0] * cs.x - v[1] * sn.x, y1 = v[0] * sn.x + v[1] * cs.x;
+        const float y2 = v[2] * cs.y - v[3] * sn.y, y3 = v[2] * sn.y + v[3] * cs.y;
+        y[t][f][j] = u32x2{pack_bf16x2(y0, y1), pack_bf16x2(y2, y3)};
+      }
+  }
+  __syncthreads();  // every wave is done with the staged tables
+  const int roff = wave * WT * 8;
+  u32x4 *reg = roff < BM * 16 ? cl + roff : sl + (roff - BM * 16);
+  u32x2 *reg2 = (u32x2 *)reg;
 #pragma unroll
-          for (int r = 0; r < 4; ++r) base[(size_t)(32 * f + 8 * j + r) * ldv] = f32_to_bf16(acc[f][t][4 * j + r]);
-    }
+  for (int t = 0; t < TS; ++t) {
+    const int rr = 32 * t + fr;
+#pragma unroll
+    for (int f = 0; f < FS; ++f)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) reg2[rr * 16 + ((8 * f + 2 * j + hf) ^ ((rr >> 1) & 15))] = y[t][f][j];
+  }
+  __syncthreads();
+  u16 *qk_t = sec == 0 ? g.q_t : g.k_t, *qk_i = sec == 0 ? g.q_i : g.k_i;
+#pragma unroll
+  for (int it = 0; it < WT * 8 / 64; ++it) {
+    const int i = lane + 64 * it;
+    const int rr = i >> 3, k = i & 7, x = (rr >> 1) & 15;
+    u32x4 v = reg[rr * 8 + (k ^ (x >> 1))];
+    if (x & 1) v = u32x4{v[2], v[3], v[0], v[1]};
+    const int m = m0 + wrow + rr;
+    if (m >= g.M) continue;
+    const bool txt = m < g.L_rows;
+    const int row = txt ? m : m - g.L_rows;
+    const int br = (txt || g.batch <= 1) ? 0 : row / g.seg_i;  // branch of an image row
+    const int brow = row - br * g.seg_i;
+    u16 *dst = (txt ? qk_t : qk_i) + (size_t)br * g.H * g.seg_i +
+               ((size_t)head * (txt ? g.seg_t : g.seg_i) + brow) * 128 + dh0 + 8 * k;
+    *(u32x4 *)dst = v;
   }
 }
 
@@ -284,7 +381,7 @@ __global__ __launch_bounds__(gemm::THREADS, (BM * BN >= 256 * 256) ? 1 : 2) void
   // W rows f*32 + 8j + 4*(lane/32) + 0..3 of token t*32 + lane%32
   const int h4 = 4 * (lane >> 5);
   if constexpr (EPI == EPI_QKV) {
-    store_qkv_wave<TS, FS>(g, m0 + wm * WT, tn * BN + wn * WF, acc, lane);
+    qkv_epilogue<BM, THREADS, TS, FS>(g, m0, tn * BN, wm * WT, tn * BN + wn * WF, acc, tid, &sA[0][0], &sW[0][0]);
     return;
   }
 #pragma unroll
@@ -474,7 +571,7 @@ __global__ __launch_bounds__(64 * WMN * WNN, 1) void gemm_bf16_large_kernel(cons
 
   const int h4 = 4 * half;
   if constexpr (EPI == EPI_QKV) {
-    store_qkv_wave<TS, FS>(g, m0 + wm * WT, tn * BN + wn * WF, acc, lane);
+    qkv_epilogue<BM, THREADS, TS, FS>(g, m0, tn * BN, wm * WT, tn * BN + wn * WF, acc, tid, &sA[0][0], &sW[0][0]);
     return;
   }
 #pragma unroll
