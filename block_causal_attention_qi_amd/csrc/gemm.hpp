@@ -115,18 +115,31 @@ QI_DEV void store4(const GemmArgs &g, int m, int n, f32x4 v) {
   }
 }
 
+// The LDS a workgroup tile leaves free once its K loop is done, as NOBJ
+// objects of 32 KB (2048 16-byte slots) each, addressed by object so that the
+// kernels can keep their operand stages in separate LDS objects.
+template <int NOBJ>
+struct LdsObjs {
+  static_assert(NOBJ == 2 || NOBJ == 4, "two or four objects");
+  u32x4 *p0, *p1, *p2, *p3;
+  QI_DEV u32x4 *o(int i) const { return i == 0 ? p0 : i == 1 ? p1 : i == 2 ? p2 : p3; }
+};
+
 // RoPE rows of a QKV tile, staged in LDS once the K loop is done (the operand
 // buffers are free then).  Each lane rotates 32 pairs of each of its tokens,
 // and 32 lanes hold 32 different tokens: read straight from the tables, every
 // load instruction would touch 32 rows, which the vector cache serves one row
 // at a time.  Staged, the tables are read in whole contiguous rows instead.
-// Layout: the float2 (pairs 2q, 2q+1) of tile row r sits at slot
-// r * 32 + (q ^ (r & 31)), so the 32 rows one half-wave reads at a fixed q hit
-// 32 distinct bank pairs.  A 16-byte chunk k (q = 2k, 2k + 1) of the table row
-// lands at the even slot (2k) ^ (r & 30), its halves swapped when r is odd.
-template <int BM, int THREADS>
-QI_DEV void stage_rope_rows(const GemmArgs &g, int m0, u32x4 *cl, u32x4 *sl, int tid) {
+// Layout: tile rows come in blocks of 128 (one 32 KB object per block and
+// table: cos in objects 0 .. BM/128 - 1, sin in the next BM/128); the float2
+// (pairs 2q, 2q+1) of row r sits at slot (r % 128) * 32 + (q ^ (r & 31)) of
+// its object, so the 32 rows one half-wave reads at a fixed q hit 32 distinct
+// bank pairs.  A 16-byte chunk k (q = 2k, 2k + 1) of the table row lands at
+// the even slot (2k) ^ (r & 30), its halves swapped when r is odd.
+template <int BM, int THREADS, int NOBJ>
+QI_DEV void stage_rope_rows(const GemmArgs &g, int m0, const LdsObjs<NOBJ> lo, int tid) {
   static_assert((BM * 16) % THREADS == 0, "whole passes over the tile's rows");
+  static_assert(NOBJ >= 2 * (BM / 128), "a cos and a sin object per 128 rows");
 #pragma unroll
   for (int it = 0; it < BM * 16 / THREADS; ++it) {
     const int i = tid + THREADS * it;
@@ -141,9 +154,9 @@ QI_DEV void stage_rope_rows(const GemmArgs &g, int m0, u32x4 *cl, u32x4 *sl, int
       c = u32x4{c[2], c[3], c[0], c[1]};
       sn = u32x4{sn[2], sn[3], sn[0], sn[1]};
     }
-    const int chunk = r * 16 + (k ^ ((r & 30) >> 1));
-    cl[chunk] = c;
-    sl[chunk] = sn;
+    const int chunk = (r & 127) * 16 + (k ^ ((r & 30) >> 1));
+    lo.o(r >> 7)[chunk] = c;
+    lo.o(BM / 128 + (r >> 7))[chunk] = sn;
   }
 }
 
@@ -191,12 +204,14 @@ QI_DEV void store_v_wave(const GemmArgs &g, int mbase, int n0, const f32x16 (&ac
 // at rr * 16 + (s ^ ((rr >> 1) & 15)): the 32 rows a half-wave writes at a
 // fixed s cover all 64 banks, and a 16-byte read of slots 2k, 2k + 1 stays
 // one aligned chunk (halves swapped when the XOR term is odd).
-template <int BM, int THREADS, int TS, int FS>
+template <int BM, int THREADS, int TS, int FS, int NOBJ>
 QI_DEV void qkv_epilogue(const GemmArgs &g, int m0, int n_tile, int wrow, int n0, const f32x16 (&acc)[FS][TS],
-                         int tid, u32x4 *cl, u32x4 *sl) {
+                         int tid, const LdsObjs<NOBJ> lo) {
   static_assert(FS == 2, "a wave tile is half a head: 64 W rows");
   constexpr int WT = 32 * TS;
-  static_assert((THREADS / 64) * WT * 8 <= 2 * BM * 16, "the waves' regions fit in the staged-table space");
+  constexpr int RS = WT * 8;          // 16-byte slots of one wave's region
+  constexpr int RPO = 2048 / RS;      // regions per 32 KB object
+  static_assert(RPO >= 1 && (THREADS / 64) <= RPO * NOBJ, "the waves' regions fit in the objects");
   const int lane = tid & 63, wave = tid >> 6;
   const int fr = lane & 31, hf = lane >> 5;
   if (n_tile / g.H >= 2) {
@@ -207,21 +222,21 @@ QI_DEV void qkv_epilogue(const GemmArgs &g, int m0, int n_tile, int wrow, int n0
   const int w0 = n0 - sec * g.H;
   const int head = w0 >> 7, dh0 = w0 & 127;
   __syncthreads();
-  stage_rope_rows<BM, THREADS>(g, m0, cl, sl, tid);
+  stage_rope_rows<BM, THREADS>(g, m0, lo, tid);
   __syncthreads();
   // outputs dh0 + 32 f + 8 j + 4 hf + 0..3 are RoPE pairs 2q, 2q + 1 with
   // q = dh0 / 4 + hf + 8 f + 2 j
-  const u32x2 *cl2 = (const u32x2 *)cl, *sl2 = (const u32x2 *)sl;
   const int q0 = (dh0 >> 2) + hf;
   u32x2 y[TS][FS][4];
 #pragma unroll
   for (int t = 0; t < TS; ++t) {
     const int r = wrow + 32 * t + fr;
+    const u32x2 *cl2 = (const u32x2 *)lo.o(r >> 7), *sl2 = (const u32x2 *)lo.o(BM / 128 + (r >> 7));
 #pragma unroll
     for (int f = 0; f < FS; ++f)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const int slot = r * 32 + ((q0 + 8 * f + 2 * j) ^ (r & 31));
+        const int slot = (r & 127) * 32 + ((q0 + 8 * f + 2 * j) ^ (r & 31));
         const float2 cs = __builtin_bit_cast(float2, cl2[slot]);
         const float2 sn = __builtin_bit_cast(float2, sl2[slot]);
         const f32x4 v = quad(acc[f][t], j);
@@ -231,8 +246,7 @@ QI_DEV void qkv_epilogue(const GemmArgs &g, int m0, int n_tile, int wrow, int n0
       }
   }
   __syncthreads();  // every wave is done with the staged tables
-  const int roff = wave * WT * 8;
-  u32x4 *reg = roff < BM * 16 ? cl + roff : sl + (roff - BM * 16);
+  u32x4 *reg = lo.o(wave / RPO) + (wave % RPO) * RS;
   u32x2 *reg2 = (u32x2 *)reg;
 #pragma unroll
   for (int t = 0; t < TS; ++t) {
@@ -381,7 +395,9 @@ __global__ __launch_bounds__(gemm::THREADS, (BM * BN >= 256 * 256) ? 1 : 2) void
   // W rows f*32 + 8j + 4*(lane/32) + 0..3 of token t*32 + lane%32
   const int h4 = 4 * (lane >> 5);
   if constexpr (EPI == EPI_QKV) {
-    qkv_epilogue<BM, THREADS, TS, FS>(g, m0, tn * BN, wm * WT, tn * BN + wn * WF, acc, tid, &sA[0][0], &sW[0][0]);
+    static_assert(BM == 128 && BN == 128, "the epilogue's LDS objects are the two operand arrays");
+    qkv_epilogue<BM, THREADS, TS, FS>(g, m0, tn * BN, wm * WT, tn * BN + wn * WF, acc, tid,
+                                      LdsObjs<2>{&sA[0][0], &sW[0][0], nullptr, nullptr});
     return;
   }
 #pragma unroll
@@ -405,34 +421,47 @@ __global__ __launch_bounds__(gemm::THREADS, (BM * BN >= 256 * 256) ? 1 : 2) void
 }
 
 // ---------------------------------------------------------------- 256 x 256 tiles
-// Large-M shape: one 256 x 256 tile per workgroup of WMN x WNN waves (wave
-// tile (256/WMN) tokens x (256/WNN) W rows, MFMA 32x32x16), one workgroup per
-// CU.  A 256-row operand tile costs 4x fewer fetched bytes per FLOP than the
-// 128 x 128 tile.  Operands come in through buffer loads (32-bit VGPR offset
-// + per-chunk SGPR offset; rows past M read as zero), are staged in registers
-// during one K step and written into the second LDS buffer; MFMA fragments
-// are read one 16-deep step ahead into a second register set.  With 8 waves
-// each SIMD holds two, so one wave's LDS and barrier waits overlap the
-// other's MFMAs.
+// Large-M shape: one 256 x 256 tile per workgroup of 8 waves (2 along tokens
+// x 4 along W rows; wave tile 128 tokens x 64 W rows, MFMA 32x32x16), one
+// workgroup per CU.  A 256-row operand tile costs 4x fewer fetched bytes per
+// FLOP than the 128 x 128 tile.
+//
+// Operands go from global memory straight into LDS (buffer loads with the LDS
+// flag: lane l of a copy instruction lands 16 bytes at slot base + l), so no
+// register staging and no LDS store instructions: measured on gfx950, a
+// ds_write_b128 costs the LDS about 2.3x a ds_read_b128 per byte, and with
+// register staging the stores alone held the K loop to ~75% of MFMA rate.
+// Each K step of 64 moves a 32 KB A slice and a 32 KB W slice.  The A
+// slices (activations, just written by the previous kernel, mostly cache
+// hits) are double-buffered and copied one step ahead; the W slices (weights,
+// streamed from HBM) are triple-buffered and copied two steps ahead, so a W
+// copy has two steps of MFMA work to land.  The five stages are separate LDS
+// objects indexed by compile-time constants (the K loop is unrolled by 6), so
+// the compiler's wait for a copy covers exactly the stage it fills, and the
+// barrier that ends a step waits only for the copies that the next step
+// reads, leaving the newest W copy in flight.
+//
+// LDS layout of a slice: row r (64 bf16 = 8 chunks of 16 bytes), chunk c at
+// slot r * 8 + (c ^ ((r >> 1) & 7)) (see lds_slot).  Copy instruction j of
+// wave w fills slots (8 j + w) * 64 .. + 63: rows 64 j + 8 w + lane / 8, slot
+// lane % 8 holding chunk (lane % 8) ^ ((row >> 1) & 7) -- which does not
+// depend on j -- so each lane's source offset is fixed and j only adds a
+// uniform 64-row step.  Rows past M read as zero (buffer range check).
 namespace gemmL {
-constexpr int BM = 256, BN = 256, BK = 64;
+constexpr int BM = 256, BN = 256, BK = 64, THREADS = 512;
+constexpr int TS = 4, FS = 2;           // wave tile: 4 x 32 tokens, 2 x 32 W rows
+constexpr int NCP = BM * 8 / THREADS;   // copy instructions per operand slice per thread (4)
 constexpr int RSRC_FLAGS = 0x00020000;  // raw buffer, 32-bit dwords
 }  // namespace gemmL
 
 template <int EPI, int WMN, int WNN>
-__global__ __launch_bounds__(64 * WMN * WNN, 1) void gemm_bf16_large_kernel(const GemmArgs g) {
+__global__ __launch_bounds__(gemmL::THREADS, 1) void gemm_bf16_large_kernel(const GemmArgs g) {
   using namespace gemmL;
+  static_assert(WMN == 2 && WNN == 4, "8 waves as 2 x 4");
   if (g.skip && *g.skip) return;
-  constexpr int THREADS = 64 * WMN * WNN;
-  constexpr int WT = BM / WMN, WF = BN / WNN;  // wave tile
-  constexpr int TS = WT / 32, FS = WF / 32;
-  constexpr int RPP = THREADS / 8;             // rows per fetch pass
-  constexpr int NJ = BM / RPP;                 // fetch passes per operand
-  static_assert(FS % 2 == 0, "SwiGLU pairs gate/up slices inside a wave");
-  static_assert(RPP % 32 == 0, "fetch pass covers whole 32-row slices");
-  static_assert(RPP == 32 || RPP == 64, "fetch pass of 32 or 64 rows");
-  __shared__ u32x4 sA[2][BM * 8];
-  __shared__ u32x4 sW[2][BN * 8];
+  constexpr int WT = BM / WMN, WF = BN / WNN;
+  __shared__ u32x4 sA0[BM * 8], sA1[BM * 8];
+  __shared__ u32x4 sW0[BN * 8], sW1[BN * 8], sW2[BN * 8];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave % WMN, wn = wave / WMN;
@@ -442,53 +471,38 @@ __global__ __launch_bounds__(64 * WMN * WNN, 1) void gemm_bf16_large_kernel(cons
   tile_of(blockIdx.x, nTM, nTN, tm, tn);
   const int m0 = tm * BM;
 
-  // operand fetch: thread t moves chunk (t & 7) of rows (t >> 3) + RPP j
-  const int lrow = tid >> 3, lc = tid & 7;
+  // copy sources: tile row r0 + 64 j, chunk cch
+  const int r0 = 8 * wave + (lane >> 3);
+  const int cch = (lane & 7) ^ ((r0 >> 1) & 7);
   const __amdgpu_buffer_rsrc_t ra =
       __builtin_amdgcn_make_buffer_rsrc((void *)g.A, (short)0, (int)((size_t)g.M * g.lda * 2), RSRC_FLAGS);
   const int wrows = EPI == EPI_SWIGLU ? 2 * g.F : g.N;
   const __amdgpu_buffer_rsrc_t rw =
       __builtin_amdgcn_make_buffer_rsrc((void *)g.W, (short)0, (int)((size_t)wrows * g.ldw * 2), RSRC_FLAGS);
-  const int voff_a = ((m0 + lrow) * g.lda + lc * 8) * 2;
+  const int voff_a = ((m0 + r0) * g.lda + cch * 8) * 2;
   // SwiGLU: W tile rows alternate 32-row gate / up slices for the same 32
-  // outputs, i.e. tile row r reads W row tn*128 + (r>>6)*32 + (r&31) (+F when
-  // bit 5 of r is set).  For r = lrow + RPP j the lrow part goes into the VGPR
-  // offset and the pass part (uniform) into the SGPR offset.
-  int wrow0;
-  if constexpr (EPI == EPI_SWIGLU)
-    wrow0 = tn * (BN / 2) + ((lrow >> 6) * 32) + (lrow & 31) + ((lrow >> 5) & 1) * g.F;
-  else
-    wrow0 = tn * BN + lrow;
-  const int voff_w = (wrow0 * g.ldw + lc * 8) * 2;
-  auto soff_w = [&](int j) {
-    if constexpr (EPI == EPI_SWIGLU) {
-      const int s32 = RPP * j / 32;  // 32-row slices before pass j
-      return ((s32 >> 1) * 32 + (s32 & 1) * g.F) * g.ldw * 2;
-    } else {
-      return RPP * j * g.ldw * 2;
-    }
+  // outputs: tile row r reads W row tn*128 + (r>>6)*32 + (r&31) (+F when bit
+  // 5 of r is set); for r = r0 + 64 j that is a per-lane part plus 32 j.
+  const int wrow0 = EPI == EPI_SWIGLU ? tn * (BN / 2) + (r0 & 31) + ((r0 >> 5) & 1) * g.F : tn * BN + r0;
+  const int voff_w = (wrow0 * g.ldw + cch * 8) * 2;
+  const int wstep = (EPI == EPI_SWIGLU ? 32 : 64) * g.ldw * 2;  // bytes per copy instruction j
+  const int astep = 64 * g.lda * 2;
+  auto lds_ptr = [](u32x4 *p) { return (__attribute__((address_space(3))) void *)p; };
+  auto copy_a = [&](int kt, u32x4 *dst) {
+#if __HIP_DEVICE_COMPILE__  // the host pass cannot resolve this builtin in a template
+#pragma unroll
+    for (int j = 0; j < NCP; ++j)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, lds_ptr(dst + (8 * j + wave) * 64), 16, voff_a,
+                                               astep * j + kt * BK * 2, 0, 0);
+#endif
   };
-  const int slot0 = lrow * 8 + (lc ^ ((lrow >> 1) & 7));  // row (lrow + RPP j) -> slot0 + 8 RPP j
-
-  // two register stages: slice kt+3 is fetched at the end of step kt and
-  // written to LDS at the end of step kt+2, so its latency is covered by two
-  // steps of MFMA work; the loop is unrolled by two to keep the stage index
-  // static
-  u32x4 stA[2][NJ], stW[2][NJ];
-  auto gload = [&](int st, int kt) {
-    const int kb = kt * BK * 2;
+  auto copy_w = [&](int kt, u32x4 *dst) {
+#if __HIP_DEVICE_COMPILE__
 #pragma unroll
-    for (int j = 0; j < NJ; ++j)
-      stA[st][j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(ra, voff_a, RPP * j * g.lda * 2 + kb, 0));
-#pragma unroll
-    for (int j = 0; j < NJ; ++j)
-      stW[st][j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rw, voff_w, soff_w(j) + kb, 0));
-  };
-  auto lstore = [&](int st, int b) {
-#pragma unroll
-    for (int j = 0; j < NJ; ++j) sA[b][slot0 + 8 * RPP * j] = stA[st][j];
-#pragma unroll
-    for (int j = 0; j < NJ; ++j) sW[b][slot0 + 8 * RPP * j] = stW[st][j];
+    for (int j = 0; j < NCP; ++j)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, lds_ptr(dst + (8 * j + wave) * 64), 16, voff_w,
+                                               wstep * j + kt * BK * 2, 0, 0);
+#endif
   };
 
   f32x16 acc[FS][TS];
@@ -503,12 +517,12 @@ __global__ __launch_bounds__(64 * WMN * WNN, 1) void gemm_bf16_large_kernel(cons
   const int fr = lane & 31, sw = (fr >> 1) & 7, half = lane >> 5;
   const int rowA = wm * WT + fr, rowW = wn * WF + fr;
   u32x4 fa[2][TS], fw[2][FS];
-  auto fload = [&](int b, int kk, int set) {
+  auto fload = [&](const u32x4 *sa, const u32x4 *sw_, int kk, int set) {
     const int ch = (kk * 2 + half) ^ sw;
 #pragma unroll
-    for (int t = 0; t < TS; ++t) fa[set][t] = sA[b][(rowA + 32 * t) * 8 + ch];
+    for (int t = 0; t < TS; ++t) fa[set][t] = sa[(rowA + 32 * t) * 8 + ch];
 #pragma unroll
-    for (int f = 0; f < FS; ++f) fw[set][f] = sW[b][(rowW + 32 * f) * 8 + ch];
+    for (int f = 0; f < FS; ++f) fw[set][f] = sw_[(rowW + 32 * f) * 8 + ch];
   };
   auto mfma_kk = [&](int set) {
 #pragma unroll
@@ -516,62 +530,97 @@ __global__ __launch_bounds__(64 * WMN * WNN, 1) void gemm_bf16_large_kernel(cons
 #pragma unroll
       for (int t = 0; t < TS; ++t) acc[f][t] = mfma32x32x16(fw[set][f], fa[set][t], acc[f][t]);
   };
-  // Interleave n MFMAs with the LDS traffic issued next to them in program
-  // order: reads (and writes) of the next operands ride in the shadow of the
-  // MFMA pipe instead of stalling the wave between sub-steps.
-  auto interleave = [&](auto n_mfma, auto n_rd, auto n_wr) {
-    constexpr int NM = decltype(n_mfma)::value, NR = decltype(n_rd)::value, NW = decltype(n_wr)::value;
+  // n MFMAs, each followed by up to one LDS read and one copy issued next to
+  // it in program order
+  auto interleave = [&](auto n_mfma, auto n_rd, auto n_cp) {
+    constexpr int NM = decltype(n_mfma)::value, NR = decltype(n_rd)::value, NC = decltype(n_cp)::value;
 #pragma unroll
     for (int i = 0; i < NM; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);          // one MFMA
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);              // one MFMA
       if (i < NR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
-      if (i < NW) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);  // one LDS write
+      if (i < NC) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // one copy
     }
   };
   using I0 = std::integral_constant<int, 0>;
   using I8 = std::integral_constant<int, FS * TS>;
   using IR = std::integral_constant<int, FS + TS>;
-  using IW = std::integral_constant<int, 2 * NJ>;
+  using IC = std::integral_constant<int, NCP>;
+  // stage objects by compile-time index
+  auto SA = [&](auto i) -> u32x4 * {
+    if constexpr (decltype(i)::value == 0) return sA0;
+    else return sA1;
+  };
+  auto SW = [&](auto i) -> u32x4 * {
+    if constexpr (decltype(i)::value == 0) return sW0;
+    else if constexpr (decltype(i)::value == 1) return sW1;
+    else return sW2;
+  };
+  using std::integral_constant;
 
   const int nk = g.K / BK;
-  // Step kt computes LDS buffer (kt & 1) whose 16-deep sub-step 0 fragments
-  // are already in register set 0.  During the MFMAs of sub-step kk the
-  // fragments of kk+1 are read; during sub-step 1 the staged slice kt+1 is
-  // written to the other LDS buffer.  After the barrier the freed register
-  // set receives slice kt+3 and sub-step 0 of the next buffer is read.  The
-  // body has no branches: past the last slice the loads repeat the last
-  // slice (in bounds, never used) and the stores fill a buffer never read.
-  auto step = [&](int kt, auto par) {
-    constexpr int P = decltype(par)::value;  // kt & 1
-    fload(P, 1, 1);
+  // Step kt reads A stage PA = kt % 2 and W stage PW = kt % 3 (sub-step 0's
+  // fragments already in register set 0).  It first copies A slice kt+1 into
+  // the other A stage, then (strictly after, in issue order) W slice kt+2
+  // into W stage (kt+2) % 3 -- both stages read by step kt-1 and released by
+  // its barrier; past the last slice the copies repeat slice nk-1 into a
+  // stage never read again.  The step ends with every copy but the NCP
+  // newest (W slice kt+2) landed -- vector-memory loads complete in issue
+  // order, so vmcnt(NCP) covers A slice kt+1 and W slice kt+1 -- and its own
+  // LDS reads done, then the barrier, then the next step's sub-step 0
+  // fragments.
+  auto step = [&](int kt, auto pa, auto pw) {
+    constexpr int PA = decltype(pa)::value, PW = decltype(pw)::value;
+    const u32x4 *a = SA(pa), *w = SW(pw);
+    copy_a(min(kt + 1, nk - 1), SA(integral_constant<int, PA ^ 1>{}));
+    __builtin_amdgcn_sched_barrier(0);  // the A copies are issued before the W copies
+    copy_w(min(kt + 2, nk - 1), SW(integral_constant<int, (PW + 2) % 3>{}));
+    fload(a, w, 1, 1);
+    mfma_kk(0);
+    interleave(I8{}, IR{}, IC{});
+    fload(a, w, 2, 0);
+    mfma_kk(1);
+    interleave(I8{}, IR{}, I0{});
+    fload(a, w, 3, 1);
     mfma_kk(0);
     interleave(I8{}, IR{}, I0{});
-    lstore(P ^ 1, P ^ 1);
-    fload(P, 2, 0);
     mfma_kk(1);
-    interleave(I8{}, IR{}, IW{});
-    fload(P, 3, 1);
-    mfma_kk(0);
-    interleave(I8{}, IR{}, I0{});
-    mfma_kk(1);
-    __syncthreads();
-    gload(P ^ 1, min(kt + 3, nk - 1));
-    fload(P ^ 1, 0, 0);
+    // s_waitcnt vmcnt(NCP) expcnt(7) lgkmcnt(0), then the barrier
+    __builtin_amdgcn_s_waitcnt((NCP & 15) | (7 << 4) | ((NCP >> 4) << 14));
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    fload(SA(integral_constant<int, PA ^ 1>{}), SW(integral_constant<int, (PW + 1) % 3>{}), 0, 0);
   };
-  gload(0, 0);
-  lstore(0, 0);
-  gload(1, min(1, nk - 1));
-  gload(0, min(2, nk - 1));
-  __syncthreads();
-  fload(0, 0, 0);
-  for (int kt = 0; kt < nk; kt += 2) {
-    step(kt, std::integral_constant<int, 0>{});
-    if (kt + 1 < nk) step(kt + 1, std::integral_constant<int, 1>{});
+  using C0 = std::integral_constant<int, 0>;
+  using C1 = std::integral_constant<int, 1>;
+  using C2 = std::integral_constant<int, 2>;
+  copy_a(0, sA0);
+  copy_w(0, sW0);
+  __builtin_amdgcn_sched_barrier(0);  // slice 0 is issued before W slice 1
+  copy_w(min(1, nk - 1), sW1);
+  __builtin_amdgcn_s_waitcnt((NCP & 15) | (7 << 4) | ((NCP >> 4) << 14));
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  fload(sA0, sW0, 0, 0);
+  int kt = 0;
+  for (; kt + 6 <= nk; kt += 6) {
+    step(kt, C0{}, C0{});
+    step(kt + 1, C1{}, C1{});
+    step(kt + 2, C0{}, C2{});
+    step(kt + 3, C1{}, C0{});
+    step(kt + 4, C0{}, C1{});
+    step(kt + 5, C1{}, C2{});
   }
+  if (kt < nk) step(kt, C0{}, C0{});
+  if (kt + 1 < nk) step(kt + 1, C1{}, C1{});
+  if (kt + 2 < nk) step(kt + 2, C0{}, C2{});
+  if (kt + 3 < nk) step(kt + 3, C1{}, C0{});
+  if (kt + 4 < nk) step(kt + 4, C0{}, C1{});
+  __syncthreads();  // every copy has landed and every fragment read is done
 
   const int h4 = 4 * half;
   if constexpr (EPI == EPI_QKV) {
-    qkv_epilogue<BM, THREADS, TS, FS>(g, m0, tn * BN, wm * WT, tn * BN + wn * WF, acc, tid, &sA[0][0], &sW[0][0]);
+    qkv_epilogue<BM, THREADS, TS, FS>(g, m0, tn * BN, wm * WT, tn * BN + wn * WF, acc, tid,
+                                      LdsObjs<4>{sA0, sA1, sW0, sW1});
     return;
   }
 #pragma unroll
