@@ -77,8 +77,9 @@ def calibrate_copy():
 
 def calibrate():
     """Sustained rates of the running part: the library's register-only MFMA
-    loops and copy kernel, and torch's (vendor library) bf16 GEMM on the four
-    projection shapes of the 1024^2 step."""
+    loops, copy kernel and LDS / MFMA instruction mixes (shader cycles per
+    iteration of 8 waves per CU), and torch's (vendor library) bf16 GEMM on
+    the four projection shapes of the 1024^2 step."""
     import ctypes
 
     import torch
@@ -98,6 +99,13 @@ def calibrate():
     _lib.check(lib.qi_calib_copy_gbs(a.data_ptr(), b.data_ptr(), n, 5, ctypes.byref(v)), "qi_calib_copy_gbs")
     res["copy_gbs_read_plus_write"] = round(v.value, 1)
     del a, b
+    lds = {}
+    for mode, name in ((0, "8_ds_read_b128"), (1, "8_ds_write_b128"), (2, "8_mfma"),
+                       (3, "8_mfma_6_reads_2_ds_writes"), (4, "8_mfma_6_reads_2_lds_copies")):
+        v = ctypes.c_double(0)
+        _lib.check(lib.qi_calib_lds_cycles(mode, 20000, ctypes.byref(v)), "qi_calib_lds_cycles")
+        lds[name] = round(v.value, 1)
+    res["lds_mix_cycles_per_iteration_per_cu"] = lds
     gemm = {}
     for (M, N, K) in [(4096, 24576, 4096), (4096, 12288, 4096), (4096, 4096, 12288), (4096, 4096, 4096)]:
         A = torch.randn(M, K, device="cuda", dtype=torch.bfloat16)

@@ -1,5 +1,6 @@
 // Calibration microbenchmarks (include/qi_calib.h): register-only MFMA
-// throughput and device copy bandwidth on the running MI355X.
+// throughput, device copy bandwidth, and the LDS cost of the GEMM's K-loop
+// instruction mixes on the running MI355X.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -43,6 +44,93 @@ __global__ __launch_bounds__(256) void mfma_loop_kernel(float *out, int iters) {
 
 __global__ __launch_bounds__(256) void copy_kernel(const u32x4 *__restrict__ a, u32x4 *__restrict__ b, int64_t n) {
   for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) b[i] = a[i];
+}
+
+// One 512-thread workgroup per CU (8 waves, two per SIMD), 128 KB of LDS;
+// each iteration every wave issues the MODE's mix (qi_calib.h), every fourth
+// iteration ends with a barrier.  Wave 0 of each workgroup adds its shader
+// cycles to clk[0] and 1 to clk[1].  Every LDS index stays below 8192 slots;
+// copy sources stay below 4096 slots of src.
+template <int MODE>
+__global__ __launch_bounds__(512, 1) void lds_mix_kernel(float *out, int iters, unsigned long long *clk,
+                                                         const u32x4 *src) {
+  __shared__ u32x4 s[8192];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  for (int i = tid; i < 8192; i += 512) s[i] = u32x4{(uint32_t)i, 1u, 2u, 3u};
+  __syncthreads();
+  const uint64_t t0 = __builtin_amdgcn_s_memtime();
+  // the GEMM's patterns: staging store slot of row tid/8, chunk tid%8; fragment
+  // read of row (wave&1)*128 + lane%32 at a swizzled chunk
+  const int lrow = tid >> 3, lc = tid & 7;
+  const int wslot = lrow * 8 + (lc ^ ((lrow >> 1) & 7));
+  const int fr = lane & 31, half = lane >> 5, sw = (fr >> 1) & 7;
+  const int rowA = (wave & 1) * 128 + fr;
+  u32x4 acc4 = {0, 0, 0, 0};
+  const u32x4 wv = {(uint32_t)tid, 7u, 9u, 11u};
+  f32x16 acc[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[j][e] = 0.f;
+  bf16x8 a, b;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    a[i] = (__bf16)(lane * 0.01f);
+    b[i] = (__bf16)0.5f;
+  }
+  constexpr bool kMfma = MODE >= 2, kReads = MODE == 0 || MODE >= 3;
+  constexpr int kNr = MODE == 0 ? 8 : 6;
+  for (int it = 0; it < iters; ++it) {
+    const int ch = ((it & 3) * 2 + half) ^ sw;
+    const int buf = (it & 1) * 4096;
+    if constexpr (kReads) {
+#pragma unroll
+      for (int r = 0; r < kNr; ++r) acc4 += s[buf + ((rowA + 32 * r) * 8) % 4096 + ch];
+    }
+    if constexpr (MODE == 1) {
+#pragma unroll
+      for (int r = 0; r < 8; ++r) s[buf + (wslot + 512 * r) % 4096] = wv + (uint32_t)(r + it);
+    }
+    if constexpr (MODE == 3) {
+#pragma unroll
+      for (int r = 0; r < 2; ++r)
+        s[(4096 - buf) + (wslot + 512 * (r + 2 * (it & 3))) % 4096] = wv + (uint32_t)(r + it);
+    }
+    if constexpr (MODE == 4) {
+#if __HIP_DEVICE_COMPILE__
+#pragma unroll
+      for (int r = 0; r < 2; ++r)
+        __builtin_amdgcn_global_load_lds((const void *)(src + ((wave * 64 + lane + 512 * r) & 4095)),
+                                         (__attribute__((address_space(3))) void *)&s[(4096 - buf) +
+                                             ((wave * 64 + 512 * (r + 2 * (it & 3))) % 4096)],
+                                         16, 0, 0);
+#endif
+    }
+    if constexpr (kMfma) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[j], 0, 0, 0);
+    }
+    if constexpr (MODE >= 3) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if (i < 6) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        if (i < 2) __builtin_amdgcn_sched_group_barrier(MODE == 3 ? 0x200 : 0x020, 1, 0);
+      }
+    }
+    if ((it & 3) == 3) __syncthreads();
+  }
+  const uint64_t t1 = __builtin_amdgcn_s_memtime();
+  __syncthreads();
+  float sum = (float)acc4[0] + (float)acc4[1] + (float)s[(tid * 3 + iters) & 8191][2];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) sum += acc[j][0];
+  // keeps the work alive: the compiler cannot decide this (practically never true)
+  if (__float_as_uint(sum) == (uint32_t)iters * 2654435761u) out[tid] = sum;
+  if (tid == 0) {
+    atomicAdd(&clk[0], (unsigned long long)(t1 - t0));
+    atomicAdd(&clk[1], 1ull);
+  }
 }
 
 }  // namespace
@@ -113,6 +201,50 @@ qi_status qi_calib_copy_gbs(const void *src, void *dst, int64_t bytes, int32_t r
   *gbs = rc == QI_OK ? 2.0 * (double)bytes / (best * 1e-3) / 1e9 : 0.0;
   (void)hipEventDestroy(e0);
   (void)hipEventDestroy(e1);
+  (void)hipStreamDestroy(st);
+  return rc;
+}
+
+qi_status qi_calib_lds_cycles(int32_t mode, int32_t iters, double *cycles) {
+  if (!cycles) return QI_ERR_NULL;
+  if (mode < 0 || mode > 4 || iters < 4 || iters > 10000000) return QI_ERR_RANGE;
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return QI_ERR_HIP;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return QI_ERR_HIP;
+  float *out = nullptr;
+  unsigned long long *clk = nullptr;
+  u32x4 *src = nullptr;
+  hipStream_t st;
+  if (hipStreamCreate(&st) != hipSuccess) return QI_ERR_HIP;
+  qi_status rc = QI_OK;
+  if (hipMalloc(&out, 512 * sizeof(float)) != hipSuccess || hipMalloc(&clk, 2 * sizeof(unsigned long long)) != hipSuccess ||
+      hipMalloc(&src, 4096 * sizeof(u32x4)) != hipSuccess)
+    rc = QI_ERR_HIP;
+  if (rc == QI_OK && hipMemsetAsync(src, 0, 4096 * sizeof(u32x4), st) != hipSuccess) rc = QI_ERR_HIP;
+  auto run = [&](int n) {
+    switch (mode) {
+      case 0: hipLaunchKernelGGL(lds_mix_kernel<0>, dim3(cus), dim3(512), 0, st, out, n, clk, src); break;
+      case 1: hipLaunchKernelGGL(lds_mix_kernel<1>, dim3(cus), dim3(512), 0, st, out, n, clk, src); break;
+      case 2: hipLaunchKernelGGL(lds_mix_kernel<2>, dim3(cus), dim3(512), 0, st, out, n, clk, src); break;
+      case 3: hipLaunchKernelGGL(lds_mix_kernel<3>, dim3(cus), dim3(512), 0, st, out, n, clk, src); break;
+      default: hipLaunchKernelGGL(lds_mix_kernel<4>, dim3(cus), dim3(512), 0, st, out, n, clk, src); break;
+    }
+  };
+  unsigned long long h[2] = {0, 0};
+  if (rc == QI_OK) {
+    run(100);  // warm-up
+    if (hipMemsetAsync(clk, 0, 2 * sizeof(unsigned long long), st) != hipSuccess) rc = QI_ERR_HIP;
+  }
+  if (rc == QI_OK) {
+    run(iters);
+    if (hipMemcpyAsync(h, clk, sizeof(h), hipMemcpyDeviceToHost, st) != hipSuccess ||
+        hipStreamSynchronize(st) != hipSuccess || hipGetLastError() != hipSuccess)
+      rc = QI_ERR_HIP;
+  }
+  *cycles = (rc == QI_OK && h[1]) ? (double)h[0] / (double)h[1] / iters : 0.0;
+  if (out) (void)hipFree(out);
+  if (clk) (void)hipFree(clk);
+  if (src) (void)hipFree(src);
   (void)hipStreamDestroy(st);
   return rc;
 }

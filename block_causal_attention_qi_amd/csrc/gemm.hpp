@@ -429,8 +429,8 @@ __global__ __launch_bounds__(gemm::THREADS, (BM * BN >= 256 * 256) ? 1 : 2) void
 // Operands go from global memory straight into LDS (buffer loads with the LDS
 // flag: lane l of a copy instruction lands 16 bytes at slot base + l), so no
 // register staging and no LDS store instructions: measured on gfx950, a
-// ds_write_b128 costs the LDS about 2.3x a ds_read_b128 per byte, and with
-// register staging the stores alone held the K loop to ~75% of MFMA rate.
+// ds_write_b128 costs the LDS about 2.5x a ds_read_b128 per byte, and with
+// register staging the stores held the K loop to ~70% of MFMA rate.
 // Each K step of 64 moves a 32 KB A slice and a 32 KB W slice.  The A
 // slices (activations, just written by the previous kernel, mostly cache
 // hits) are double-buffered and copied one step ahead; the W slices (weights,

@@ -30,6 +30,22 @@ qi_status qi_calib_mfma_tflops(int32_t shape, int32_t iters, double *tflops);
  * copies with HIP events; BLOCKS until done.  Errors: NULL, RANGE, ALIGN, HIP. */
 qi_status qi_calib_copy_gbs(const void *src, void *dst, int64_t bytes, int32_t reps, double *gbs);
 
+/* Shader cycles per iteration of a CU-wide LDS / MFMA instruction mix: one
+ * workgroup of 512 threads (8 waves, two per SIMD, 128 KB of LDS) per CU, each
+ * wave issuing per iteration
+ *   mode 0: 8 ds_read_b128 (the GEMM's swizzled fragment reads),
+ *   mode 1: 8 ds_write_b128 (the staging-store pattern),
+ *   mode 2: 8 v_mfma_f32_32x32x16_bf16,
+ *   mode 3: 8 MFMAs + 6 fragment reads + 2 staging stores (a register-staged
+ *           GEMM K loop),
+ *   mode 4: 8 MFMAs + 6 fragment reads + 2 16-byte-per-lane global -> LDS
+ *           copies from a 64 KB buffer (a K loop fed by LDS copies),
+ * with a barrier every fourth iteration, timed with the shader clock of wave
+ * 0 of every workgroup and averaged.  Data are synthetic (values not used).
+ * BLOCKS until done.  *cycles receives the cycles per iteration.  Errors:
+ * NULL, RANGE (mode not 0..4, iters < 4), HIP. */
+qi_status qi_calib_lds_cycles(int32_t mode, int32_t iters, double *cycles);
+
 #ifdef __cplusplus
 }
 #endif

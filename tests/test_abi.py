@@ -205,6 +205,9 @@ def test_capture_block_and_component_reject_bad_arguments():
     assert c(0, 10, None) == _lib.QI_ERR_NULL
     assert lib.qi_calib_copy_gbs(FAKE, FAKE, 15, 1, ctypes.byref(out)) == _lib.QI_ERR_RANGE
     assert lib.qi_calib_copy_gbs(FAKE_MIS, FAKE, 64, 1, ctypes.byref(out)) == _lib.QI_ERR_ALIGN
+    assert lib.qi_calib_lds_cycles(5, 100, ctypes.byref(out)) == _lib.QI_ERR_RANGE
+    assert lib.qi_calib_lds_cycles(0, 3, ctypes.byref(out)) == _lib.QI_ERR_RANGE
+    assert lib.qi_calib_lds_cycles(0, 100, None) == _lib.QI_ERR_NULL
     m = lib.qi_modulation
     assert m(ctypes.byref(d), FAKE, FAKE, 2.0, FAKE, None) == _lib.QI_ERR_RANGE
     assert m(ctypes.byref(d), None, FAKE, 0.5, FAKE, None) == _lib.QI_ERR_NULL
