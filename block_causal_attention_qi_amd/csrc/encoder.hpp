@@ -10,16 +10,22 @@
 // significant bits), and each product a_p * w of two bf16 values is exact in
 // the MFMA's fp32 accumulation.  So one 32x32x16 bf16 MFMA per plane gives the
 // fp32 product sum (up to the order of the fp32 additions) at three times the
-// bf16 MFMA count, far above the fp32 MFMA rate.  The attention (small: L <=
-// 512 tokens) runs on the fp32 MFMA 32x32x2 directly.
+// bf16 MFMA count, far above the fp32 MFMA rate.  The kernel that produces a
+// matmul input (the RMSNorms, attention, the SwiGLU epilogue) writes it as the
+// three planes [3][rows][cols] bf16 once, and the GEMMs copy the planes
+// straight into LDS.  The attention (small: L <= 512 tokens) runs on the fp32
+// MFMA 32x32x2 directly.
 #pragma once
 
 #include "common.hpp"
 #include "gemm.hpp"
 
 namespace enc {
-constexpr int BM = 128, BN = 128, BK = 64, THREADS = 256, NP = 3;
-constexpr int TS = 2, FS = 2;  // wave tile 64 tokens x 64 W rows
+constexpr int BM = 64, BN = 128, BK = 64, THREADS = 256, NP = 3;
+constexpr int FS = 2;                          // wave tile 32 tokens x 64 W rows
+constexpr int A_SLOTS = NP * BM * 8;           // 16-byte slots of an A stage (three planes)
+constexpr int W_SLOTS = BN * 8;                // of a W stage
+constexpr int CA = A_SLOTS / THREADS, CW = W_SLOTS / THREADS;  // copies per thread (6, 4)
 }  // namespace enc
 
 // exact split of 8 fp32 values into three planes of 8 bf16 (16 bytes each)
@@ -42,18 +48,34 @@ QI_DEV void split3(const f32x4 lo, const f32x4 hi, u32x4 &p0, u32x4 &p1, u32x4 &
   p2 = u32x4{c[0], c[1], c[2], c[3]};
 }
 
-// SwiGLU with an fp32 output: outf[m][o..o+3] = SiLU(gate) * up
-QI_DEV void store4_swiglu_f32(float *outf, int ldo, int m, int o, f32x4 gt, f32x4 up) {
-  f32x4 y;
+// the same split of 4 fp32 values, as three 8-byte plane entries
+QI_DEV void split3x4(const f32x4 v, u32x2 &p0, u32x2 &p1, u32x2 &p2) {
 #pragma unroll
-  for (int r = 0; r < 4; ++r) y[r] = gt[r] / (1.f + expf(-gt[r])) * up[r];
-  *(f32x4 *)(outf + (size_t)m * ldo + o) = y;
+  for (int e = 0; e < 4; e += 2) {
+    const uint32_t a = pack_bf16x2(v[e], v[e + 1]);
+    const float r0 = v[e] - bf16_to_f32((u16)(a & 0xFFFF)), r1 = v[e + 1] - bf16_to_f32((u16)(a >> 16));
+    const uint32_t b = pack_bf16x2(r0, r1);
+    const uint32_t c = pack_bf16x2(r0 - bf16_to_f32((u16)(b & 0xFFFF)), r1 - bf16_to_f32((u16)(b >> 16)));
+    p0[e / 2] = a;
+    p1[e / 2] = b;
+    p2[e / 2] = c;
+  }
+}
+
+// 4 consecutive fp32 values at [row][col] of a plane triple [3][rows][ld]
+QI_DEV void store4_planes(u16 *planes, size_t plane_elems, int ld, int row, int col, f32x4 v) {
+  u32x2 p0, p1, p2;
+  split3x4(v, p0, p1, p2);
+  u16 *q = planes + (size_t)row * ld + col;
+  *(u32x2 *)q = p0;
+  *(u32x2 *)(q + plane_elems) = p1;
+  *(u32x2 *)(q + 2 * plane_elems) = p2;
 }
 
 enum EncEpi { ENC_F32 = 0, ENC_RESID = 1, ENC_SWIGLU = 2 };
 
 struct EncGemmArgs {
-  const float *A;  // [M][lda] fp32
+  const u16 *A;    // [3][M][lda] bf16: the three planes of the fp32 input
   int lda;
   const u16 *W;    // [N][ldw] bf16 (SWIGLU: [2F][ldw], gate rows then up rows)
   int ldw;
@@ -62,18 +84,28 @@ struct EncGemmArgs {
   int ldc;
   float *X;        // ENC_RESID: X[m][n] += acc
   int ldx;
-  float *out;      // ENC_SWIGLU: out[m][o], o < F
+  u16 *out;        // ENC_SWIGLU: the planes [3][M][ldo] of out[m][o] = SiLU(gate) * up, o < F
   int ldo, F;
 };
 
-// 128 x 128 tile of C = A W^T with A in fp32, four waves (2 x 2), the three
-// A planes and the W tile double-buffered in LDS (2 x (3 x 16 + 16) KB), one
-// register stage of the next K slice.
+// 64 x 128 tile of C = A W^T with A fp32 given as its three bf16 planes:
+// four waves (2 x 2, wave tile 32 tokens x 64 W rows), two workgroups per CU.
+// A K step of 64 moves 24 KB of planes and a 16 KB W slice, copied global ->
+// LDS directly (buffer loads with the LDS flag; lane l of a copy lands 16
+// bytes at slot base + l) one step ahead into double buffers declared as four
+// LDS objects (80 KB).  Slot layout per 64-wide row as in gemm.hpp
+// (lds_slot): copy j of wave w fills slots (4 j + w) * 64 .. + 63, i.e. tile
+// row 8 (4 j + w) % 8 + lane / 8 of plane (4 j + w) / 8 (A; W: row
+// 8 (4 j + w) + lane / 8), chunk (lane % 8) ^ ((row >> 1) & 7), which depends
+// on the lane and the parity of w only.  Rows past M read as zero (plane 2)
+// or as other planes' rows (planes 0, 1): only outputs of rows past M see
+// them, and those are never stored.  Per 16-deep sub-step the MFMAs run the
+// planes from the smallest up, so the small terms add into small sums first.
 template <int EPI>
-__global__ __launch_bounds__(enc::THREADS, 1) void enc_gemm_kernel(const EncGemmArgs g) {
+__global__ __launch_bounds__(enc::THREADS, 2) void enc_gemm_kernel(const EncGemmArgs g) {
   using namespace enc;
-  __shared__ u32x4 sA[2][NP][BM * 8];
-  __shared__ u32x4 sW[2][BN * 8];
+  __shared__ u32x4 sA0[A_SLOTS], sA1[A_SLOTS];
+  __shared__ u32x4 sW0[W_SLOTS], sW1[W_SLOTS];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave & 1, wn = wave >> 1;
   const int nTM = (g.M + BM - 1) / BM;
@@ -82,114 +114,109 @@ __global__ __launch_bounds__(enc::THREADS, 1) void enc_gemm_kernel(const EncGemm
   tile_of(blockIdx.x, nTM, nTN, tm, tn);
   const int m0 = tm * BM;
 
-  // thread t moves chunk (i & 7) of tile row i >> 3, i = t + 256 j
-  constexpr int CJ = BM * 8 / THREADS;  // 4
-  const float *pa[CJ];
-  const u16 *pw[CJ];
-  int slot[CJ];
+  const size_t plane_elems = (size_t)g.M * g.lda;
+  const __amdgpu_buffer_rsrc_t ra =
+      __builtin_amdgcn_make_buffer_rsrc((void *)g.A, (short)0, (int)(3 * plane_elems * 2), 0x00020000);
+  const int wrows = EPI == ENC_SWIGLU ? 2 * g.F : g.N;
+  const __amdgpu_buffer_rsrc_t rw =
+      __builtin_amdgcn_make_buffer_rsrc((void *)g.W, (short)0, (int)((size_t)wrows * g.ldw * 2), 0x00020000);
+  const int lr = lane >> 3;
+  const int cch = (lane & 7) ^ (((wave & 1) * 4 + (lane >> 4)) & 7);
+  int voff_a[CA], voff_w[CW];
 #pragma unroll
-  for (int j = 0; j < CJ; ++j) {
-    const int i = tid + THREADS * j;
-    const int row = i >> 3, c = i & 7;
-    slot[j] = lds_slot(row, c);
-    pa[j] = g.A + (size_t)min(m0 + row, g.M - 1) * g.lda + c * 8;  // rows past M: valid, never stored
-    int wr;
-    if constexpr (EPI == ENC_SWIGLU) {
-      const int s = row >> 5;
-      wr = tn * (BN / 2) + (s >> 1) * 32 + (row & 31) + (s & 1) * g.F;
-    } else {
-      wr = tn * BN + row;
-    }
-    pw[j] = g.W + (size_t)wr * g.ldw + c * 8;
+  for (int j = 0; j < CA; ++j) {
+    const int blk = 4 * j + wave;  // 64-slot block: plane blk / 8, rows 8 (blk % 8) ..
+    const int row = 8 * (blk & 7) + lr;
+    voff_a[j] = (int)(((size_t)(blk >> 3) * plane_elems + (size_t)(m0 + row) * g.lda + cch * 8) * 2);
   }
-  f32x4 ra[CJ][2];
-  u32x4 rw[CJ];
-  auto gload = [&](int kt) {
-    const int k0 = kt * BK;
 #pragma unroll
-    for (int j = 0; j < CJ; ++j) {
-      ra[j][0] = *(const f32x4 *)(pa[j] + k0);
-      ra[j][1] = *(const f32x4 *)(pa[j] + k0 + 4);
-      rw[j] = *(const u32x4 *)(pw[j] + k0);
-    }
-  };
-  auto lstore = [&](int b) {
+  for (int j = 0; j < CW; ++j) {
+    const int r = 8 * (4 * j + wave) + lr;  // tile row
+    int wr;
+    if constexpr (EPI == ENC_SWIGLU)
+      wr = tn * (BN / 2) + (r >> 6) * 32 + (r & 31) + ((r >> 5) & 1) * g.F;
+    else
+      wr = tn * BN + r;
+    voff_w[j] = (wr * g.ldw + cch * 8) * 2;
+  }
+  auto lds_ptr = [](u32x4 *p) { return (__attribute__((address_space(3))) void *)p; };
+  auto copy = [&](int kt, u32x4 *sa, u32x4 *sw_) {
+#if __HIP_DEVICE_COMPILE__  // the host pass cannot resolve this builtin in a template
 #pragma unroll
-    for (int j = 0; j < CJ; ++j) {
-      u32x4 p0, p1, p2;
-      split3(ra[j][0], ra[j][1], p0, p1, p2);
-      sA[b][0][slot[j]] = p0;
-      sA[b][1][slot[j]] = p1;
-      sA[b][2][slot[j]] = p2;
-      sW[b][slot[j]] = rw[j];
-    }
+    for (int j = 0; j < CA; ++j)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, lds_ptr(sa + (4 * j + wave) * 64), 16, voff_a[j], kt * BK * 2, 0, 0);
+#pragma unroll
+    for (int j = 0; j < CW; ++j)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, lds_ptr(sw_ + (4 * j + wave) * 64), 16, voff_w[j], kt * BK * 2, 0,
+                                               0);
+#endif
   };
 
-  f32x16 acc[FS][TS];
+  f32x16 acc[FS];
 #pragma unroll
   for (int f = 0; f < FS; ++f)
 #pragma unroll
-    for (int t = 0; t < TS; ++t)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) acc[f][t][e] = 0.f;
+    for (int e = 0; e < 16; ++e) acc[f][e] = 0.f;
 
-  const int fr = lane & 31, half = lane >> 5;
-  const int nk = g.K / BK;
-  gload(0);
-  lstore(0);
-  __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    const int b = kt & 1;
-    if (kt + 1 < nk) gload(kt + 1);
+  const int fr = lane & 31, half = lane >> 5, sw = (fr >> 1) & 7;
+  const int rowA = wm * 32 + fr, rowW = wn * 64 + fr;
+  auto compute = [&](const u32x4 *sa, const u32x4 *sw_) {
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
-      const int ch = kk * 2 + half;
-      u32x4 fw[FS];
+      const int ch = (kk * 2 + half) ^ sw;
+      u32x4 fw[FS], fa[NP];
 #pragma unroll
-      for (int f = 0; f < FS; ++f) fw[f] = sW[b][lds_slot(wn * 64 + f * 32 + fr, ch)];
-      // planes from the smallest up, so the small terms add into small sums first
+      for (int f = 0; f < FS; ++f) fw[f] = sw_[(rowW + 32 * f) * 8 + ch];
 #pragma unroll
-      for (int p = NP - 1; p >= 0; --p) {
-        u32x4 fa[TS];
+      for (int p = 0; p < NP; ++p) fa[p] = sa[p * BM * 8 + rowA * 8 + ch];
 #pragma unroll
-        for (int t = 0; t < TS; ++t) fa[t] = sA[b][p][lds_slot(wm * 64 + t * 32 + fr, ch)];
+      for (int p = NP - 1; p >= 0; --p)
 #pragma unroll
-        for (int f = 0; f < FS; ++f)
-#pragma unroll
-          for (int t = 0; t < TS; ++t) acc[f][t] = mfma32x32x16(fw[f], fa[t], acc[f][t]);
-      }
+        for (int f = 0; f < FS; ++f) acc[f] = mfma32x32x16(fw[f], fa[p], acc[f]);
     }
-    if (kt + 1 < nk) lstore(b ^ 1);
+  };
+  const int nk = g.K / BK;
+  copy(0, sA0, sW0);
+  __syncthreads();
+  for (int kt = 0; kt < nk; kt += 2) {
+    if (kt + 1 < nk) copy(kt + 1, sA1, sW1);
+    compute(sA0, sW0);
     __syncthreads();
+    if (kt + 1 < nk) {
+      if (kt + 2 < nk) copy(kt + 2, sA0, sW0);
+      compute(sA1, sW1);
+      __syncthreads();
+    }
   }
 
-  // lane holds, for each (f, t) block and j, the 4 consecutive W rows
-  // f*32 + 8j + 4*half + 0..3 of token t*32 + lane%32
+  // lane holds, for each block f and j, the 4 consecutive W rows
+  // f*32 + 8j + 4*half + 0..3 of token rowA
   const int h4 = 4 * half;
+  const int m = m0 + rowA;
+  if (m >= g.M) return;
+  if constexpr (EPI == ENC_SWIGLU) {
 #pragma unroll
-  for (int t = 0; t < TS; ++t) {
-    const int m = m0 + wm * 64 + t * 32 + fr;
-    if (m >= g.M) continue;
-    if constexpr (EPI == ENC_SWIGLU) {
+    for (int j = 0; j < 4; ++j) {
+      const f32x4 gt = quad(acc[0], j), up = quad(acc[1], j);
+      f32x4 y;
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        store4_swiglu_f32(g.out, g.ldo, m, tn * (BN / 2) + wn * 32 + 8 * j + h4, quad(acc[0][t], j),
-                          quad(acc[1][t], j));
-    } else {
-#pragma unroll
-      for (int f = 0; f < FS; ++f)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int n = tn * BN + wn * 64 + f * 32 + 8 * j + h4;
-          const f32x4 v = quad(acc[f][t], j);
-          if constexpr (EPI == ENC_F32) {
-            *(f32x4 *)(g.C + (size_t)m * g.ldc + n) = v;
-          } else {
-            f32x4 *xp = (f32x4 *)(g.X + (size_t)m * g.ldx + n);
-            *xp = *xp + v;
-          }
-        }
+      for (int r = 0; r < 4; ++r) y[r] = gt[r] / (1.f + expf(-gt[r])) * up[r];
+      store4_planes(g.out, (size_t)g.M * g.ldo, g.ldo, m, tn * (BN / 2) + wn * 32 + 8 * j + h4, y);
     }
+  } else {
+#pragma unroll
+    for (int f = 0; f < FS; ++f)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int n = tn * BN + wn * 64 + f * 32 + 8 * j + h4;
+        const f32x4 v = quad(acc[f], j);
+        if constexpr (EPI == ENC_F32) {
+          *(f32x4 *)(g.C + (size_t)m * g.ldc + n) = v;
+        } else {
+          f32x4 *xp = (f32x4 *)(g.X + (size_t)m * g.ldx + n);
+          *xp = *xp + v;
+        }
+      }
   }
 }
 
@@ -206,10 +233,11 @@ __global__ __launch_bounds__(256) void enc_embed_kernel(const int *ids, int voca
   }
 }
 
-// out = x * rsqrt(mean(x^2) + eps) * w over rows of H (H % 256 == 0), fp32;
-// one wave per row, four rows per workgroup.
+// out = x * rsqrt(mean(x^2) + eps) * w over rows of H (H % 256 == 0), fp32,
+// written as its three bf16 planes [3][rows][H]; one wave per row, four rows
+// per workgroup.
 __global__ __launch_bounds__(256) void enc_rmsnorm_kernel(const float *x, const float *w, int rows, int H,
-                                                          float eps, float *out) {
+                                                          float eps, u16 *out) {
   const int lane = threadIdx.x & 63;
   const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (r >= rows) return;
@@ -224,7 +252,7 @@ __global__ __launch_bounds__(256) void enc_rmsnorm_kernel(const float *x, const 
   for (int c = lane * 4; c < H; c += 256) {
     const f32x4 v = *(const f32x4 *)(xr + c);
     const f32x4 gw = *(const f32x4 *)(w + c);
-    *(f32x4 *)(out + (size_t)r * H + c) = v * inv * gw;
+    store4_planes(out, (size_t)rows * H, H, r, c, v * inv * gw);
   }
 }
 
@@ -275,8 +303,9 @@ constexpr int WAVES = 4, BQ = 32 * WAVES, BKV = 32;
 // lane (query l % 32) is key kappa(i, h) = 8 (i / 4) + 4 h + i % 4 of the
 // tile, and step s of O^T = V^T P^T pairs key kappa(s, 0) (lanes of half 0)
 // with kappa(s, 1) (half 1), so the probabilities feed the MFMA straight from
-// the score registers.  Softmax in fp32 with expf; out O [L][heads * 128].
-__global__ __launch_bounds__(256) void enc_attention_kernel(const float *Q, const float *K, const float *V, float *O,
+// the score registers.  Softmax in fp32 with expf; out O [L][heads * 128] as
+// its three bf16 planes [3][L][heads * 128].
+__global__ __launch_bounds__(256) void enc_attention_kernel(const float *Q, const float *K, const float *V, u16 *O,
                                                             int L, int heads, int kvh) {
   using namespace enca;
   // rows padded to 132 floats: a column read by 32 lanes (32 rows) then hits
@@ -358,10 +387,11 @@ __global__ __launch_bounds__(256) void enc_attention_kernel(const float *Q, cons
   }
   const float inv = 1.f / (l_run + __shfl_xor(l_run, 32, 64));
   if (qrow < L) {
-    float *op = O + (size_t)qrow * heads * 128 + head * 128 + 4 * h;
+    const int ld = heads * 128;
 #pragma unroll
     for (int d = 0; d < 4; ++d)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) *(f32x4 *)(op + 32 * d + 8 * j) = quad(oacc[d], j) * inv;
+      for (int j = 0; j < 4; ++j)
+        store4_planes(O, (size_t)L * ld, ld, qrow, head * 128 + 4 * h + 32 * d + 8 * j, quad(oacc[d], j) * inv);
   }
 }

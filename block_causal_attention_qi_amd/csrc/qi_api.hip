@@ -374,6 +374,11 @@ bool enc_dims_ok(const qi_enc_dims *d) {
   if (d->ffn < 64 || d->ffn % 64 != 0 || d->ffn > 65536) return false;
   if (d->n_layers < 1 || d->n_layers > 256 || d->vocab < 1) return false;
   if ((size_t)d->heads * 128 > 65536) return false;
+  // every weight matrix addressed with 32-bit byte offsets
+  const size_t H = d->hidden, F = d->ffn, NQ = (size_t)d->heads * 128, NT = NQ + (size_t)2 * d->kv_heads * 128;
+  if (NT * H * 2 >= (1ull << 31) || H * NQ * 2 >= (1ull << 31) || 2 * F * H * 2 >= (1ull << 31) ||
+      H * F * 2 >= (1ull << 31))
+    return false;
   return true;
 }
 
@@ -389,13 +394,13 @@ EncLayout enc_layout(const qi_enc_dims &d, int L) {
     off += align256(bytes);
     return o;
   };
-  l.h = take((size_t)L * (H > F ? H : F) * 4);
+  l.h = take((size_t)3 * L * H * 2);  // bf16 planes of the normed rows
   l.qkv = take((size_t)L * (NQ + 2 * NKV) * 4);
   l.q = take((size_t)L * NQ * 4);
   l.k = take((size_t)L * NKV * 4);
   l.v = take((size_t)L * NKV * 4);
-  l.o = take((size_t)L * NQ * 4);
-  l.a = take((size_t)L * F * 4);
+  l.o = take((size_t)3 * L * NQ * 2);  // planes of the attention output
+  l.a = take((size_t)3 * L * F * 2);   // planes of the SwiGLU output
   l.total = off;
   return l;
 }
@@ -414,9 +419,9 @@ qi_status run_encoder(const qi_enc_dims &d, const qi_enc_model_w &w, const int32
                       const float *sin, float *x, char *ws, hipStream_t s) {
   const int H = d.hidden, F = d.ffn, NQ = d.heads * 128, NKV = d.kv_heads * 128, NT = NQ + 2 * NKV;
   const EncLayout lay = enc_layout(d, L);
-  float *h = (float *)(ws + lay.h), *qkv = (float *)(ws + lay.qkv), *Q = (float *)(ws + lay.q),
-        *K = (float *)(ws + lay.k), *V = (float *)(ws + lay.v), *O = (float *)(ws + lay.o),
-        *a = (float *)(ws + lay.a);
+  u16 *h = (u16 *)(ws + lay.h), *O = (u16 *)(ws + lay.o), *a = (u16 *)(ws + lay.a);
+  float *qkv = (float *)(ws + lay.qkv), *Q = (float *)(ws + lay.q), *K = (float *)(ws + lay.k),
+        *V = (float *)(ws + lay.v);
   {
     TimedLaunch tl(QI_KERNEL_ENC_MISC, s);
     hipLaunchKernelGGL(enc_embed_kernel, dim3(L), dim3(256), 0, s, ids, d.vocab, w.embed, H, x);
