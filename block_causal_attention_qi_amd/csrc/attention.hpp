@@ -120,52 +120,58 @@ __global__ __launch_bounds__(attn::THREADS, 1) void block_causal_attn_kernel(con
   // Tiles are copied global -> LDS directly (no register staging): lane l of
   // a wave-wide copy lands at 16 l past the wave's base, so the swizzle is
   // applied on the global side by choosing which chunk each lane fetches.
-  auto tile_src = [&](int t, const u16 *&K, const u16 *&Vt, int &key0, int &klen, int &ldv) {
-    const bool tx = t < nt_t;
-    K = tx ? Kt : Ki;
-    Vt = tx ? Vtt : Vti;
-    key0 = (tx ? t : t - nt_t) * BKV;
-    klen = tx ? a.L : a.N;
-    ldv = tx ? a.ldv_t : a.ldv_i;
-  };
+  // The copies are buffer loads over one resource per segment and operand
+  // (this head's K [len][128], V^T [128][ldv]): each lane's offset inside a
+  // tile is fixed and precomputed, the tile's first key enters as the uniform
+  // scalar offset, and K rows past the segment read as zeros (range check;
+  // masked below) -- no address arithmetic per tile.
+  constexpr int RSRC_FLAGS = 0x00020000;  // raw buffer, 32-bit dwords
+  const __amdgpu_buffer_rsrc_t rk_t = __builtin_amdgcn_make_buffer_rsrc((void *)Kt, (short)0, a.L * 256, RSRC_FLAGS);
+  const __amdgpu_buffer_rsrc_t rk_i = __builtin_amdgcn_make_buffer_rsrc((void *)Ki, (short)0, a.N * 256, RSRC_FLAGS);
+  const __amdgpu_buffer_rsrc_t rv_t =
+      __builtin_amdgcn_make_buffer_rsrc((void *)Vtt, (short)0, 256 * a.ldv_t, RSRC_FLAGS);
+  const __amdgpu_buffer_rsrc_t rv_i =
+      __builtin_amdgcn_make_buffer_rsrc((void *)Vti, (short)0, 256 * a.ldv_i, RSRC_FLAGS);
+  int koff[NLD], voff_t[NLD], voff_i[NLD];
+#pragma unroll
+  for (int j = 0; j < NLD; ++j) {
+    const int i = (j * WAVES + wave) * 64 + lane;
+    const int kr = i >> 4, kc = (i & 15) ^ (kr & 15);  // K row kr of the tile, chunk kc
+    koff[j] = (kr * 128 + kc * 8) * 2;
+    const int vr = i >> 3, vc = (i & 7) ^ ((vr >> 1) & 7);  // V^T row vr, chunk vc
+    voff_t[j] = (vr * a.ldv_t + vc * 8) * 2;
+    voff_i[j] = (vr * a.ldv_i + vc * 8) * 2;
+  }
+  auto lds_ptr = [](u32x4 *p) { return (__attribute__((address_space(3))) void *)p; };
   auto copy_k = [&](int t, auto B) {
     u32x4 *sk = B.value ? sK1 : sK0;
-    const u16 *K, *Vt;
-    int key0, klen, ldv;
-    tile_src(t, K, Vt, key0, klen, ldv);
+    const bool tx = t < nt_t;
+    const int key0 = (tx ? t : t - nt_t) * BKV;
+#if __HIP_DEVICE_COMPILE__  // the host pass cannot resolve this builtin in a template
 #pragma unroll
-    for (int j = 0; j < NLD; ++j) {
-      const int slot0 = (j * WAVES + wave) * 64;
-      const int i = slot0 + lane;
-      const int kr = i >> 4, kc = (i & 15) ^ (kr & 15);
-      const int key = min(key0 + kr, klen - 1);  // rows past the segment: masked below
-      __builtin_amdgcn_global_load_lds((const void *)(K + (size_t)key * 128 + kc * 8),
-                                       (__attribute__((address_space(3))) void *)&sk[slot0], 16, 0, 0);
-    }
+    for (int j = 0; j < NLD; ++j)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(tx ? rk_t : rk_i, lds_ptr(sk + (j * WAVES + wave) * 64), 16, koff[j],
+                                               key0 * 256, 0, 0);
+#endif
   };
   auto copy_v = [&](int t, auto B) {
     u32x4 *sv = B.value ? sV1 : sV0;
-    const u16 *K, *Vt;
-    int key0, klen, ldv;
-    tile_src(t, K, Vt, key0, klen, ldv);
+    const bool tx = t < nt_t;
+    const int key0 = (tx ? t : t - nt_t) * BKV;
+#if __HIP_DEVICE_COMPILE__
 #pragma unroll
-    for (int j = 0; j < NLD; ++j) {
-      const int slot0 = (j * WAVES + wave) * 64;
-      const int i = slot0 + lane;
-      const int vr = i >> 3, vc = (i & 7) ^ ((vr >> 1) & 7);
-      // in bounds: ldv >= key0 + 64
-      __builtin_amdgcn_global_load_lds((const void *)(Vt + (size_t)vr * ldv + key0 + vc * 8),
-                                       (__attribute__((address_space(3))) void *)&sv[slot0], 16, 0, 0);
-    }
+    for (int j = 0; j < NLD; ++j)  // in bounds: ldv >= key0 + 64
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(tx ? rv_t : rv_i, lds_ptr(sv + (j * WAVES + wave) * 64), 16,
+                                               tx ? voff_t[j] : voff_i[j], key0 * 2, 0, 0);
+#endif
   };
   // V^T columns past the segment's end (padding, any bit pattern) become exact
   // zeros, so that their zero probabilities contribute exact zeros.  Only the
   // segment's last tile has them; the caller brackets this with barriers.
   auto zero_v_tail = [&](int t, auto B) {
-    const u16 *K, *Vt;
-    int key0, klen, ldv;
-    tile_src(t, K, Vt, key0, klen, ldv);
-    const int valid = klen - key0;
+    const bool tx = t < nt_t;
+    const int key0 = (tx ? t : t - nt_t) * BKV;
+    const int valid = (tx ? a.L : a.N) - key0;
     if (valid >= BKV) return;
     const int npad = BKV - valid;
     u16 *sv = (u16 *)(B.value ? sV1 : sV0);
