@@ -20,8 +20,11 @@ def _dev(a):
     return torch.from_numpy(np.ascontiguousarray(a)).cuda()
 
 
+# (4096, 4096, 256), (4000, 4096, 192) and (4100, 4096, 832) run the 256 x 256
+# LDS-copy kernel: K steps only in its unrolled tail (4, 3), and 13 = 2 x 6 + 1
+# steps with a ragged last row tile
 @pytest.mark.parametrize("M,N,K", [(1, 128, 64), (200, 256, 192), (278, 384, 512), (1070, 512, 4096),
-                                   (4096, 4096, 256), (4000, 4096, 192)])
+                                   (4096, 4096, 256), (4000, 4096, 192), (4100, 4096, 832)])
 def test_linear_bf16_matches_fp64_matmul(M, N, K):
     import torch
     log(f"linear M={M} N={N} K={K}")
