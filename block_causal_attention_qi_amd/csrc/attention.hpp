@@ -57,6 +57,15 @@ QI_DEV void interleave_reads_mfma() {
   __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
 }
 
+// max of x over lanes l and l ^ 32: v_permlane32_swap of x with itself leaves
+// x[l % 32] in one result and x[l % 32 + 32] in the other, in every lane (a
+// VALU op; a shuffle through ds_bpermute would also wait for every LDS read
+// in flight)
+QI_DEV float max_over_halves(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
 // sum += lo + hi of a packed bf16 pair, in fp32
 QI_DEV float add_bf16x2(uint32_t pair, float sum) {
   const bf16x2 one = {(__bf16)1.f, (__bf16)1.f};
@@ -254,11 +263,18 @@ __global__ __launch_bounds__(attn::THREADS, 1) void block_causal_attn_kernel(con
         for (int e = 0; e < 16; ++e)
           if (32 * kb + 16 * (e >> 3) + (e & 7) >= lim) s_cur[kb][e] = -INFINITY;
     }
-    // tile max over this lane's 32 scores (three-way max) and the partner lane's
-    float mx = fmaxf(s_cur[0][0], s_cur[0][1]);
+    // tile max over this lane's 32 scores (three-way maxes in a shallow tree)
+    // and the partner lane's
+    float m4[4];
 #pragma unroll
-    for (int e = 2; e < 32; e += 2) mx = fmaxf(fmaxf(mx, s_cur[e >> 4][e & 15]), s_cur[e >> 4][(e & 15) + 1]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * c;
+    for (int q = 0; q < 4; ++q) {
+      const f32x16 &sv = s_cur[q >> 1];
+      const int e0 = 8 * (q & 1);
+      m4[q] = fmaxf(fmaxf(fmaxf(sv[e0], sv[e0 + 1]), sv[e0 + 2]), fmaxf(fmaxf(sv[e0 + 3], sv[e0 + 4]), sv[e0 + 5]));
+      m4[q] = fmaxf(fmaxf(m4[q], sv[e0 + 6]), sv[e0 + 7]);
+    }
+    float mx = fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3]));
+    mx = max_over_halves(mx) * c;
     // raise the running max only past the slack; only a raised max costs
     // a rescale of the accumulators
     const bool raise = mx > m_run + RESCALE_SLACK;
@@ -279,7 +295,7 @@ __global__ __launch_bounds__(attn::THREADS, 1) void block_causal_attn_kernel(con
     scores(NB, s_next);
 
     u32x4 pb[4];  // B operand per 16-key step c4 = 2 kb + cc: keys 16 c4 + 8 h .. +8
-    float psum = 0.f;
+    float psum[2] = {0.f, 0.f};  // two independent chains of dot2 additions
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -290,11 +306,11 @@ __global__ __launch_bounds__(attn::THREADS, 1) void block_causal_attn_kernel(con
           const int e = 8 * cc + 2 * k;
           w[k] = pack_bf16x2(__builtin_amdgcn_exp2f(__builtin_fmaf(s_cur[kb][e], c, nbase)),
                              __builtin_amdgcn_exp2f(__builtin_fmaf(s_cur[kb][e + 1], c, nbase)));
-          psum = add_bf16x2(w[k], psum);
+          psum[k & 1] = add_bf16x2(w[k], psum[k & 1]);
         }
         pb[2 * kb + cc] = w;
       }
-    l_run = l_run * alpha + psum;
+    l_run = l_run * alpha + (psum[0] + psum[1]);
     // interleave: the 16 score MFMAs of tile t+1 with their K reads and the
     // exponentials of tile t
     __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
