@@ -26,8 +26,7 @@ HIP_FLAGS = [
     "-munsafe-fp-atomics", "-Wno-unused-result",
 ]
 # The attention kernel's translation unit keeps MFMA accumulators in VGPRs
-# (two waves per SIMD share the VGPR file with the softmax state); the GEMM
-# kernels keep the default AGPR accumulators (256 per lane in the 4-wave tile).
+# (two waves per SIMD share the VGPR file with the softmax state).
 ATTN_FLAGS = ["-mllvm", "-amdgpu-mfma-vgpr-form"]
 
 
