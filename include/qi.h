@@ -356,8 +356,9 @@ size_t qi_enc_workspace_bytes(const qi_enc_dims *d, int32_t L);
  * a NaN row); cos, sin: device fp32 [L][64] from qi_enc_rope_table; hidden:
  * device fp32 [L][hidden] out.  Causal: the first L' outputs do not depend on
  * later tokens (bit for bit).  Ranges: 1 <= L <= 512; head_dim 128; hidden %
- * 256 == 0; heads % kv_heads == 0; ffn % 64 == 0.  Errors: NULL, SHAPE, RANGE,
- * ALIGN, WORKSPACE, HIP. */
+ * 256 == 0; heads % kv_heads == 0; ffn % 64 == 0; every weight matrix under
+ * 2 GiB (it is addressed with 32-bit byte offsets).  Errors: NULL, SHAPE,
+ * RANGE, ALIGN, WORKSPACE, HIP. */
 qi_status qi_text_encoder_fwd(const qi_enc_dims *d, const qi_enc_model_w *w, const int32_t *ids,
                               int32_t L, const float *cos, const float *sin, float *hidden, void *ws,
                               size_t ws_bytes, void *stream);
