@@ -21,11 +21,13 @@
 #include "gemm.hpp"
 
 namespace enc {
-constexpr int BM = 64, BN = 128, BK = 64, THREADS = 256, NP = 3;
+constexpr int BM = 64, BN = 128, BK = 32, THREADS = 256, NP = 3;
 constexpr int FS = 2;                          // wave tile 32 tokens x 64 W rows
-constexpr int A_SLOTS = NP * BM * 8;           // 16-byte slots of an A stage (three planes)
-constexpr int W_SLOTS = BN * 8;                // of a W stage
-constexpr int CA = A_SLOTS / THREADS, CW = W_SLOTS / THREADS;  // copies per thread (6, 4)
+constexpr int NST = 4;                         // stages in the LDS ring
+constexpr int A_SLOTS = NP * BM * 4;           // 16-byte slots of a stage's three A planes
+constexpr int W_SLOTS = BN * 4;                // of its W slice
+constexpr int ST_SLOTS = A_SLOTS + W_SLOTS;    // 20 KB per stage
+constexpr int CA = A_SLOTS / THREADS, CW = W_SLOTS / THREADS;  // copies per thread and stage (3, 2)
 }  // namespace enc
 
 // exact split of 8 fp32 values into three planes of 8 bf16 (16 bytes each)
@@ -90,22 +92,29 @@ struct EncGemmArgs {
 
 // 64 x 128 tile of C = A W^T with A fp32 given as its three bf16 planes:
 // four waves (2 x 2, wave tile 32 tokens x 64 W rows), two workgroups per CU.
-// A K step of 64 moves 24 KB of planes and a 16 KB W slice, copied global ->
+// A K step of 32 moves 12 KB of planes and an 8 KB W slice, copied global ->
 // LDS directly (buffer loads with the LDS flag; lane l of a copy lands 16
-// bytes at slot base + l) one step ahead into double buffers declared as four
-// LDS objects (80 KB).  Slot layout per 64-wide row as in gemm.hpp
-// (lds_slot): copy j of wave w fills slots (4 j + w) * 64 .. + 63, i.e. tile
-// row 8 (4 j + w) % 8 + lane / 8 of plane (4 j + w) / 8 (A; W: row
-// 8 (4 j + w) + lane / 8), chunk (lane % 8) ^ ((row >> 1) & 7), which depends
-// on the lane and the parity of w only.  Rows past M read as zero (plane 2)
-// or as other planes' rows (planes 0, 1): only outputs of rows past M see
-// them, and those are never stored.  Per 16-deep sub-step the MFMAs run the
-// planes from the smallest up, so the small terms add into small sums first.
+// bytes at slot base + l) three steps ahead into a ring of four stages, four
+// LDS objects of 20 KB indexed by compile-time constants (the K loop is
+// unrolled by 4).  The weights stream from HBM, and with only 421 rows per
+// forward each W slice feeds few MFMAs: the copies need the deep ring to hide
+// their latency.  A step ends with every copy but the two newest slices'
+// landed (vmcnt: loads complete in issue order) and its LDS reads done, then
+// the barrier.
+// Slot layout per 32-wide row (64 bytes = 4 chunks of 16): chunk c of row r at
+// slot r * 4 + (c ^ ((r >> 2) & 3)), so the 16 rows one ds_read_b128 pass
+// reads at a fixed chunk land on 16 distinct bank groups.  Copy j of wave w
+// fills slots (4 j + w) * 64 .. + 63 of its part: 16 rows (A: plane
+// (4 j + w) / 4, rows 16 ((4 j + w) % 4) + lane / 4; W: rows 16 (4 j + w) +
+// lane / 4), chunk (lane % 4) ^ ((lane / 16) % 4).  Rows past M read as zero
+// (plane 2) or as other planes' rows (planes 0, 1): only outputs of rows past
+// M see them, and those are never stored.  Per 16-deep sub-step the MFMAs run
+// the planes from the smallest up, so the small terms add into small sums
+// first.
 template <int EPI>
 __global__ __launch_bounds__(enc::THREADS, 2) void enc_gemm_kernel(const EncGemmArgs g) {
   using namespace enc;
-  __shared__ u32x4 sA0[A_SLOTS], sA1[A_SLOTS];
-  __shared__ u32x4 sW0[W_SLOTS], sW1[W_SLOTS];
+  __shared__ u32x4 sS0[ST_SLOTS], sS1[ST_SLOTS], sS2[ST_SLOTS], sS3[ST_SLOTS];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave & 1, wn = wave >> 1;
   const int nTM = (g.M + BM - 1) / BM;
@@ -120,18 +129,18 @@ __global__ __launch_bounds__(enc::THREADS, 2) void enc_gemm_kernel(const EncGemm
   const int wrows = EPI == ENC_SWIGLU ? 2 * g.F : g.N;
   const __amdgpu_buffer_rsrc_t rw =
       __builtin_amdgcn_make_buffer_rsrc((void *)g.W, (short)0, (int)((size_t)wrows * g.ldw * 2), 0x00020000);
-  const int lr = lane >> 3;
-  const int cch = (lane & 7) ^ (((wave & 1) * 4 + (lane >> 4)) & 7);
+  const int lr = lane >> 2;
+  const int cch = (lane & 3) ^ ((lane >> 4) & 3);
   int voff_a[CA], voff_w[CW];
 #pragma unroll
   for (int j = 0; j < CA; ++j) {
-    const int blk = 4 * j + wave;  // 64-slot block: plane blk / 8, rows 8 (blk % 8) ..
-    const int row = 8 * (blk & 7) + lr;
-    voff_a[j] = (int)(((size_t)(blk >> 3) * plane_elems + (size_t)(m0 + row) * g.lda + cch * 8) * 2);
+    const int blk = 4 * j + wave;  // 64-slot block: plane blk / 4, rows 16 (blk % 4) ..
+    const int row = 16 * (blk & 3) + lr;
+    voff_a[j] = (int)(((size_t)(blk >> 2) * plane_elems + (size_t)(m0 + row) * g.lda + cch * 8) * 2);
   }
 #pragma unroll
   for (int j = 0; j < CW; ++j) {
-    const int r = 8 * (4 * j + wave) + lr;  // tile row
+    const int r = 16 * (4 * j + wave) + lr;  // tile row
     int wr;
     if constexpr (EPI == ENC_SWIGLU)
       wr = tn * (BN / 2) + (r >> 6) * 32 + (r & 31) + ((r >> 5) & 1) * g.F;
@@ -140,16 +149,22 @@ __global__ __launch_bounds__(enc::THREADS, 2) void enc_gemm_kernel(const EncGemm
     voff_w[j] = (wr * g.ldw + cch * 8) * 2;
   }
   auto lds_ptr = [](u32x4 *p) { return (__attribute__((address_space(3))) void *)p; };
-  auto copy = [&](int kt, u32x4 *sa, u32x4 *sw_) {
+  auto copy = [&](int kt, u32x4 *st) {
 #if __HIP_DEVICE_COMPILE__  // the host pass cannot resolve this builtin in a template
 #pragma unroll
     for (int j = 0; j < CA; ++j)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, lds_ptr(sa + (4 * j + wave) * 64), 16, voff_a[j], kt * BK * 2, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, lds_ptr(st + (4 * j + wave) * 64), 16, voff_a[j], kt * BK * 2, 0, 0);
 #pragma unroll
     for (int j = 0; j < CW; ++j)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, lds_ptr(sw_ + (4 * j + wave) * 64), 16, voff_w[j], kt * BK * 2, 0,
-                                               0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, lds_ptr(st + A_SLOTS + (4 * j + wave) * 64), 16, voff_w[j],
+                                               kt * BK * 2, 0, 0);
 #endif
+  };
+  auto stage = [&](auto i) -> u32x4 * {
+    if constexpr (decltype(i)::value == 0) return sS0;
+    else if constexpr (decltype(i)::value == 1) return sS1;
+    else if constexpr (decltype(i)::value == 2) return sS2;
+    else return sS3;
   };
 
   f32x16 acc[FS];
@@ -158,36 +173,56 @@ __global__ __launch_bounds__(enc::THREADS, 2) void enc_gemm_kernel(const EncGemm
 #pragma unroll
     for (int e = 0; e < 16; ++e) acc[f][e] = 0.f;
 
-  const int fr = lane & 31, half = lane >> 5, sw = (fr >> 1) & 7;
+  const int fr = lane & 31, half = lane >> 5;
   const int rowA = wm * 32 + fr, rowW = wn * 64 + fr;
-  auto compute = [&](const u32x4 *sa, const u32x4 *sw_) {
+  auto compute = [&](const u32x4 *st) {
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      const int ch = (kk * 2 + half) ^ sw;
+    for (int kk = 0; kk < 2; ++kk) {
       u32x4 fw[FS], fa[NP];
 #pragma unroll
-      for (int f = 0; f < FS; ++f) fw[f] = sw_[(rowW + 32 * f) * 8 + ch];
+      for (int f = 0; f < FS; ++f) {
+        const int r = rowW + 32 * f;
+        fw[f] = st[A_SLOTS + r * 4 + ((kk * 2 + half) ^ ((r >> 2) & 3))];
+      }
 #pragma unroll
-      for (int p = 0; p < NP; ++p) fa[p] = sa[p * BM * 8 + rowA * 8 + ch];
+      for (int p = 0; p < NP; ++p) fa[p] = st[p * BM * 4 + rowA * 4 + ((kk * 2 + half) ^ ((rowA >> 2) & 3))];
 #pragma unroll
       for (int p = NP - 1; p >= 0; --p)
 #pragma unroll
         for (int f = 0; f < FS; ++f) acc[f] = mfma32x32x16(fw[f], fa[p], acc[f]);
     }
   };
+  constexpr int CPS = CA + CW;  // copies per thread and stage
+  auto wait_barrier = [&]() {   // s_waitcnt vmcnt(2 CPS) expcnt(7) lgkmcnt(0), then the barrier
+    __builtin_amdgcn_s_waitcnt(((2 * CPS) & 15) | (7 << 4) | (((2 * CPS) >> 4) << 14));
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  };
   const int nk = g.K / BK;
-  copy(0, sA0, sW0);
-  __syncthreads();
-  for (int kt = 0; kt < nk; kt += 2) {
-    if (kt + 1 < nk) copy(kt + 1, sA1, sW1);
-    compute(sA0, sW0);
-    __syncthreads();
-    if (kt + 1 < nk) {
-      if (kt + 2 < nk) copy(kt + 2, sA0, sW0);
-      compute(sA1, sW1);
-      __syncthreads();
-    }
+  // step kt computes stage kt % 4 after copying slice kt+3 into stage
+  // (kt+3) % 4, which step kt-1 read (past the last slice the copies repeat
+  // slice nk-1 into a stage never read again)
+  auto step = [&](int kt, auto S) {
+    constexpr int s4 = decltype(S)::value;
+    copy(min(kt + 3, nk - 1), stage(std::integral_constant<int, (s4 + 3) % NST>{}));
+    compute(stage(S));
+    wait_barrier();
+  };
+  copy(0, sS0);
+  copy(min(1, nk - 1), sS1);
+  copy(min(2, nk - 1), sS2);
+  wait_barrier();
+  int kt = 0;
+  for (; kt + 4 <= nk; kt += 4) {
+    step(kt, std::integral_constant<int, 0>{});
+    step(kt + 1, std::integral_constant<int, 1>{});
+    step(kt + 2, std::integral_constant<int, 2>{});
+    step(kt + 3, std::integral_constant<int, 3>{});
   }
+  if (kt < nk) step(kt, std::integral_constant<int, 0>{});
+  if (kt + 1 < nk) step(kt + 1, std::integral_constant<int, 1>{});
+  if (kt + 2 < nk) step(kt + 2, std::integral_constant<int, 2>{});
+  __syncthreads();  // every copy has landed before the workgroup ends
 
   // lane holds, for each block f and j, the 4 consecutive W rows
   // f*32 + 8j + 4*half + 0..3 of token rowA
