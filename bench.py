@@ -130,11 +130,21 @@ def cpu_baseline(wl):
     with perf_counter and scaled to one step of n_blocks blocks."""
     import qi_synth as qs
     from oracle import dit
+    blas = "unknown"
     try:
         from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+        info = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        cores = max([i.get("num_threads", 1) for i in info] or [1])
+        if info:
+            blas = f"{info[0].get('internal_api', '?')} {info[0].get('version', '')}".strip()
     except Exception:  # pragma: no cover
         cores = os.cpu_count()
+    cpu_model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            cpu_model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), "unknown")
+    except OSError:  # pragma: no cover
+        pass
     bw = qs.weights_as_f32(qs.block_weights(wl, 0, threads=8))
     H, N, L = wl.hidden, wl.N, wl.L
     x = qs.normal_array((N, H), seed=31).astype(np.float64)
@@ -147,6 +157,7 @@ def cpu_baseline(wl):
     dt = time.perf_counter() - t0
     step_s = dt * wl.n_blocks
     return {"value": 1.0 / step_s, "unit": "steps/s", "cores": int(cores), "kind": "oracle",
+            "cpu_model": cpu_model, "nproc": os.cpu_count(), "blas": blas,
             "sample": f"1 of {wl.n_blocks} blocks, image-only pass (T={N}, L={L} cached), float64 numpy; "
                       f"{dt:.2f} s per block scaled x{wl.n_blocks}"}
 
