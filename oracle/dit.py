@@ -49,13 +49,13 @@ Readings of points the pages leave open (each is stated where it is used):
   S15 sampler constants base_shift 0.5 at 256 tokens, max_shift 0.9 at 8192
       tokens, mu linear in N with no clamp, 1000 train timesteps; each array
       operation in fp32 as the host contract states, mu and e^mu in float64.
-  S16 true CFG: noise = neg + g * (pos - neg) exactly as [MLX] "Optional
+  S20 true CFG: noise = neg + g * (pos - neg) exactly as [MLX] "Optional
       modes" writes it (no rescaling of the combined prediction), evaluated
       in fp32 as written -- difference, product, sum, each rounded once -- and
       fed to the S14 Euler update; each branch is an ordinary step on its own
       prompt (its own text K/V and its own image RoPE rows, which depend on
       its L).
-  S17 first-block cache (Fast mode): block 0 always runs; its residual
+  S21 first-block cache (Fast mode): block 0 always runs; its residual
       r0 = x1 - x0 (after the embed, after block 0) is compared with the r0
       cached at the last step that ran every block, change = sum|r0 - r0c| /
       sum|r0c| over all image rows and features; below the threshold blocks
@@ -66,7 +66,7 @@ Readings of points the pages leave open (each is stated where it is used):
       full step rather than the previous step keeps slow drift from adding up
       unchecked, and reusing the last full step's residual is the plainest
       value for the skipped work.)
-  S18 DPM++ 2M sampler: the page only names it.  Read as DPM-Solver++(2M)
+  S22 DPM++ 2M sampler: the page only names it.  Read as DPM-Solver++(2M)
       (Lu et al., "DPM-Solver++: Fast Solver for Guided Sampling of
       Diffusion Probabilistic Models", 2022, the multistep second-order
       data-prediction solver) written for the flow x = (1 - sigma) x0 +
@@ -448,7 +448,7 @@ def euler_update(x: np.ndarray, vel: np.ndarray, sigma_cur, sigma_next) -> np.nd
 
 def dpmpp_2m_coeffs(sigma_prev, sigma_cur, sigma_next):
     """Float64 coefficients (a, b, c1, c2, order) of one DPM++ 2M step
-    sigma_cur -> sigma_next (reading S18): x_next = a x - b D, D = c1 x0 -
+    sigma_cur -> sigma_next (reading S22): x_next = a x - b D, D = c1 x0 -
     c2 x0_prev.  sigma_prev None: no previous data prediction (first step)."""
     def lam(sg):
         sg = float(sg)
@@ -472,7 +472,7 @@ def dpmpp_2m_coeffs(sigma_prev, sigma_cur, sigma_next):
 
 
 def dpmpp_2m_step(x, vel, x0_prev, sigma_prev, sigma_cur, sigma_next):
-    """One DPM++ 2M update in fp32 (reading S18).  Returns (x_next, x0), x0
+    """One DPM++ 2M update in fp32 (reading S22).  Returns (x_next, x0), x0
     being the data prediction to pass as x0_prev to the next step."""
     a, b, c1, c2, order = dpmpp_2m_coeffs(sigma_prev, sigma_cur, sigma_next)
     x = x.astype(F32)
@@ -503,14 +503,14 @@ def dpmpp_2m_sample(vel_fn, x, sigmas):
 
 
 def fbc_new_state() -> dict:
-    """Empty first-block-cache state (reading S17)."""
+    """Empty first-block-cache state (reading S21)."""
     return {"valid": False, "r0": None, "rem": None, "steps": 0, "skipped": 0, "last_change": math.inf}
 
 
 def first_block_cache_step(sw: dict, blocks, img_tokens, t: float, img_cos, img_sin, heads: int,
                            kv_cache, state: dict, threshold: float, dtype=np.float64):
     """An image-only step with the first-block cache ([MLX] "Optional
-    modes", Fast mode), reading S17.  blocks: a list of block weights;
+    modes", Fast mode), reading S21.  blocks: a list of block weights;
     kv_cache: the captured text K/V per block; state: fbc_new_state(),
     updated in place.  Returns vel [N, 64]."""
     H = sw["w_img"].shape[0]
@@ -538,7 +538,7 @@ def first_block_cache_step(sw: dict, blocks, img_tokens, t: float, img_cos, img_
 
 
 def cfg_combine(pos: np.ndarray, neg: np.ndarray, g) -> np.ndarray:
-    """True-CFG prediction ([MLX] "Optional modes"), reading S16:
+    """True-CFG prediction ([MLX] "Optional modes"), reading S20:
     neg + g * (pos - neg), each operation rounded to fp32 in that order."""
     pos = pos.astype(F32)
     neg = neg.astype(F32)
@@ -548,7 +548,7 @@ def cfg_combine(pos: np.ndarray, neg: np.ndarray, g) -> np.ndarray:
 
 
 def euler_update_cfg(x: np.ndarray, pos: np.ndarray, neg: np.ndarray, g, sigma_cur, sigma_next) -> np.ndarray:
-    """The S14 Euler update on the S16 guided prediction."""
+    """The S14 Euler update on the S20 guided prediction."""
     return euler_update(x, cfg_combine(pos, neg, g), sigma_cur, sigma_next)
 
 

@@ -1,4 +1,4 @@
-"""GPU parity of the DPM++ 2M update (reading S18; the sampler [MLX]
+"""GPU parity of the DPM++ 2M update (reading S22; the sampler [MLX]
 "Optional modes" names): the fused fp32 kernel equals the oracle's fp32 step
 bit for bit on random inputs at the first, second-order, middle and final
 steps of the 40-step schedule, x and the carried data prediction alike; and a

@@ -1,5 +1,5 @@
 """GPU parity of the first-block cache (Fast mode of [MLX] "Optional modes";
-reading S17: block 0 always runs, blocks 1.. are skipped while block 0's
+reading S21: block 0 always runs, blocks 1.. are skipped while block 0's
 residual changes less than the threshold against the last full step, a
 skipped step adding that step's residual of blocks 1..):
 

@@ -2,7 +2,7 @@
 
 What fixes them: the formula the MLX page gives for true CFG ("Optional
 modes": noise = neg + g * (pos - neg)) read as fp32 operations in the written
-order (reading S16), checked against exact rational arithmetic; special cases
+order (reading S20), checked against exact rational arithmetic; special cases
 the formula reduces to (g = 0 gives the negative branch, equal branches give
 that branch for any g); and the S14 Euler update it feeds."""
 from fractions import Fraction

@@ -1,4 +1,4 @@
-"""Pins of the oracle's DPM++ 2M sampler (reading S18), CPU only.
+"""Pins of the oracle's DPM++ 2M sampler (reading S22), CPU only.
 
 What fixes them, beyond the oracle's own formulas:
   - exactness on a straight path: with the exact velocity of a single data

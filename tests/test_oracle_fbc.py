@@ -1,4 +1,4 @@
-"""Pins of the oracle's first-block cache (Fast mode, reading S17), CPU only.
+"""Pins of the oracle's first-block cache (Fast mode, reading S21), CPU only.
 
 What fixes them: the special cases the definition reduces to -- threshold 0
 never skips, so every step is the ordinary cached step (oracle.dit_step); a
