@@ -15,8 +15,9 @@
 // 64 copied global -> LDS directly and double buffered.  A single wave issues
 // VALU work at about half rate and hides only a few VALU instructions behind
 // each of its own MFMAs (measured on MI355X), so each wave is software
-// pipelined (the exponentials of tile t run between the score MFMAs of tile
-// t+1) and the second wave on each SIMD fills the rest.  MFMA 32x32x16 bf16
+// pipelined over three tiles (the softmax of tile t runs between the score
+// MFMAs of tile t+1 and the PV MFMAs of tile t-1, a few VALU instructions per
+// MFMA) and the second wave on each SIMD fills the rest.  MFMA 32x32x16 bf16
 // (the full-rate shape on gfx950).
 // S^T = K Q^T: the A operand takes the tile's K rows in the order
 // kappa(i) = 16*(i/16) + 8*((i/4)&1) + 4*((i/8)&1) + (i&3), which leaves each
@@ -224,29 +225,45 @@ __global__ __launch_bounds__(attn::THREADS, 1) void block_causal_attn_kernel(con
 #pragma unroll
     for (int e = 0; e < 16; ++e) oacc[d][e] = 0.f;
 
-  // Software pipeline: iteration t exponentiates the scores of tile t while
-  // the MFMAs of tile t+1's scores run, then accumulates tile t's P V.  K runs
-  // two tiles ahead in LDS and V one: iteration t copies K(t+2) into sK[t&1]
-  // and V(t+1) into sV[(t+1)&1], both freed by the previous iteration.
+  // Software pipeline over three tiles: iteration t exponentiates the scores
+  // of tile t between the score MFMAs of tile t+1 and the PV MFMAs of tile
+  // t-1, so the softmax's VALU work is spread over all 32 MFMAs of an
+  // iteration.  K runs two tiles ahead in LDS: iteration t copies K(t+2) into
+  // sK[t&1], whose K(t) was consumed in iteration t-1.  V(t) is copied in
+  // iteration t into sV[t&1] (its V(t-2) was consumed in iteration t-1) and
+  // consumed in iteration t+1.  The accumulators take tile t-1's PV product
+  // in tile t-1's base and are rescaled to tile t's base after it, so the
+  // arithmetic is the same sequence as rescale-then-accumulate per tile.
   constexpr std::integral_constant<int, 0> B0{};
   constexpr std::integral_constant<int, 1> B1{};
+  constexpr std::false_type NO_PV{};
+  constexpr std::true_type PV{};
   copy_k(0, B0);
-  copy_v(0, B0);
   if (ntiles > 1) copy_k(1, B1);
   __syncthreads();
-  if (v_tail(0)) {
-    zero_v_tail(0, B0);
-    __syncthreads();
-  }
   f32x16 s_cur[2];
   scores(B0, s_cur);
   __syncthreads();  // sK0 is overwritten next
+  u32x4 pb_prev[4];  // bf16 probabilities of the previous tile (B operand)
 
-  // one iteration; B = t & 1 as a constant
-  auto iteration = [&](int t, auto B) {
+  // O^T[d][q] += V^T[d][16 c4 + 8h .. +8] P^T with V from sV[B]
+  auto pv = [&](auto B, const u32x4 *pb) {
+#pragma unroll
+    for (int c4 = 0; c4 < 4; ++c4) {
+#pragma unroll
+      for (int db = 0; db < 4; ++db) {
+        const int vr = db * 32 + l32;
+        const u32x4 va = (B.value ? sV1 : sV0)[vr * 8 + ((2 * c4 + h) ^ vsw)];
+        oacc[db] = mfma32x32x16(va, pb[c4], oacc[db]);
+      }
+    }
+  };
+
+  // one iteration; B = t & 1 as a constant; HAS_PV: tile t-1 exists
+  auto iteration = [&](int t, auto B, auto HAS_PV) {
     constexpr std::integral_constant<int, 1 - B.value> NB{};
     if (t + 2 < ntiles) copy_k(t + 2, B);
-    if (t + 1 < ntiles) copy_v(t + 1, NB);
+    copy_v(t, B);
 
     // element e of block kb holds key key0 + 32 kb + 16 (e >> 3) + 8 h + (e & 7)
     const bool tx = t < nt_t;
@@ -263,88 +280,114 @@ __global__ __launch_bounds__(attn::THREADS, 1) void block_causal_attn_kernel(con
         for (int e = 0; e < 16; ++e)
           if (32 * kb + 16 * (e >> 3) + (e & 7) >= lim) s_cur[kb][e] = -INFINITY;
     }
-    // tile max over this lane's 32 scores (three-way maxes in a shallow tree)
-    // and the partner lane's
-    float m4[4];
+
+    // 32 MFMA slots: even slots run the score MFMAs of tile t+1 (from
+    // sK[b^1]), odd slots the PV MFMAs of tile t-1 (from sV[b^1]); each slot's
+    // LDS fragment is read two slots ahead.  The softmax of tile t is cut into
+    // pieces placed between the slots, and sched_barrier keeps each slot's
+    // instructions together.
+    const u32x4 *sk = NB.value ? sK1 : sK0;
+    const u32x4 *sv = NB.value ? sV1 : sV0;
+    auto frag = [&](int i) -> u32x4 {
+      const int j = i >> 1;
+      if ((i & 1) == 0) {
+        const int ds = j >> 1, kr = (j & 1) * 32 + krow_l;
+        return sk[kr * 16 + ((2 * ds + h) ^ (kr & 15))];
+      }
+      const int c4 = j >> 2, vr = (j & 3) * 32 + l32;
+      return sv[vr * 8 + ((2 * c4 + h) ^ vsw)];
+    };
+    f32x16 s_next[2];
+    u32x4 fr[3];
+    fr[0] = frag(0);
+    if constexpr (HAS_PV.value) fr[1] = frag(1);
+    float m4[4], mx = 0.f, alpha = 1.f, nbase = 0.f;
+    bool raise = false;
+    u32x4 pb[4];
+    float psum[2] = {0.f, 0.f};
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const f32x16 &sv = s_cur[q >> 1];
-      const int e0 = 8 * (q & 1);
-      m4[q] = fmaxf(fmaxf(fmaxf(sv[e0], sv[e0 + 1]), sv[e0 + 2]), fmaxf(fmaxf(sv[e0 + 3], sv[e0 + 4]), sv[e0 + 5]));
-      m4[q] = fmaxf(fmaxf(m4[q], sv[e0 + 6]), sv[e0 + 7]);
+    for (int i = 0; i < 32; ++i) {
+      const bool slot = HAS_PV.value || (i & 1) == 0;
+      if (i + 2 < 32 && (HAS_PV.value || ((i + 2) & 1) == 0)) fr[(i + 2) % 3] = frag(i + 2);
+      if (slot) {
+        const int j = i >> 1;
+        if ((i & 1) == 0) {
+          const int kb = j & 1;
+          if (j < 2)
+            s_next[kb] = mfma32x32x16(fr[i % 3], qreg[j >> 1], f32x16{});
+          else
+            s_next[kb] = mfma32x32x16(fr[i % 3], qreg[j >> 1], s_next[kb]);
+        } else {
+          oacc[j & 3] = mfma32x32x16(fr[i % 3], pb_prev[j >> 2], oacc[j & 3]);
+        }
+      }
+      // softmax pieces
+      if (i < 4) {
+        // tile max over this lane's 32 scores: a shallow tree of 3-way maxes
+        const f32x16 &s4 = s_cur[i >> 1];
+        const int e0 = 8 * (i & 1);
+        m4[i] = fmaxf(fmaxf(fmaxf(s4[e0], s4[e0 + 1]), s4[e0 + 2]), fmaxf(fmaxf(s4[e0 + 3], s4[e0 + 4]), s4[e0 + 5]));
+        m4[i] = fmaxf(fmaxf(m4[i], s4[e0 + 6]), s4[e0 + 7]);
+      } else if (i == 4) {
+        mx = fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3]));
+        mx = max_over_halves(mx) * c;  // with the partner lane's
+      } else if (i == 5) {
+        // raise the running max only past the slack; only a raised max
+        // costs a rescale of the accumulators
+        raise = mx > m_run + RESCALE_SLACK;
+        if (raise) {
+          alpha = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - mx);
+          m_run = mx;
+        }
+        nbase = m_run == -INFINITY ? 0.f : -m_run;
+      } else {
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+          if (6 + (u * 26) / 16 != i) continue;
+          // probabilities of keys 16 c4 + 8 h + 2 k, +1 (c4 = 2 kb + cc)
+          const int kb = u >> 3, cc = (u >> 2) & 1, k = u & 3, e = 8 * cc + 2 * k;
+          const uint32_t w = pack_bf16x2(__builtin_amdgcn_exp2f(__builtin_fmaf(s_cur[kb][e], c, nbase)),
+                                         __builtin_amdgcn_exp2f(__builtin_fmaf(s_cur[kb][e + 1], c, nbase)));
+          pb[2 * kb + cc][k] = w;
+          psum[k & 1] = add_bf16x2(w, psum[k & 1]);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
-    float mx = fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3]));
-    mx = max_over_halves(mx) * c;
-    // raise the running max only past the slack; only a raised max costs
-    // a rescale of the accumulators
-    const bool raise = mx > m_run + RESCALE_SLACK;
-    float alpha = 1.f;
-    if (raise) {
-      alpha = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - mx);
-      m_run = mx;
-    }
+    l_run = l_run * alpha + (psum[0] + psum[1]);
+    // keep the exponentials between the MFMAs (the compiler would otherwise
+    // sink them past the barrier to their use in the next iteration)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) asm volatile("" : "+v"(pb[i]));
+    asm volatile("" : "+v"(l_run));
+
+    // tile t-1 is in the accumulators: move them to tile t's base
     if (__any(raise)) {
 #pragma unroll
       for (int d = 0; d < 4; ++d) oacc[d] *= alpha;
     }
-    const float nbase = m_run == -INFINITY ? 0.f : -m_run;
-
-    // scores of tile t+1 (discarded past the last tile: sK[b^1] then holds
-    // stale or uninitialised data, never used)
-    f32x16 s_next[2];
-    scores(NB, s_next);
-
-    u32x4 pb[4];  // B operand per 16-key step c4 = 2 kb + cc: keys 16 c4 + 8 h .. +8
-    float psum[2] = {0.f, 0.f};  // two independent chains of dot2 additions
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int cc = 0; cc < 2; ++cc) {
-        u32x4 w;
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const int e = 8 * cc + 2 * k;
-          w[k] = pack_bf16x2(__builtin_amdgcn_exp2f(__builtin_fmaf(s_cur[kb][e], c, nbase)),
-                             __builtin_amdgcn_exp2f(__builtin_fmaf(s_cur[kb][e + 1], c, nbase)));
-          psum[k & 1] = add_bf16x2(w[k], psum[k & 1]);
-        }
-        pb[2 * kb + cc] = w;
-      }
-    l_run = l_run * alpha + (psum[0] + psum[1]);
-    // interleave: the 16 score MFMAs of tile t+1 with their K reads and the
-    // exponentials of tile t
-    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-#pragma unroll
-    for (int i = 0; i < 14; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
-    }
-    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-
-    // O^T[d][q] += V^T[d][16 c4 + 8h .. +8] P^T
-#pragma unroll
-    for (int c4 = 0; c4 < 4; ++c4) {
-#pragma unroll
-      for (int db = 0; db < 4; ++db) {
-        const int vr = db * 32 + l32;
-        const u32x4 va = (B.value ? sV1 : sV0)[vr * 8 + ((2 * c4 + h) ^ vsw)];
-        oacc[db] = mfma32x32x16(va, pb[c4], oacc[db]);
-      }
-    }
-    interleave_reads_mfma();
-
+    for (int i = 0; i < 4; ++i) pb_prev[i] = pb[i];
     s_cur[0] = s_next[0];
     s_cur[1] = s_next[1];
     __syncthreads();
-    if (t + 1 < ntiles && v_tail(t + 1)) {
-      zero_v_tail(t + 1, NB);
+    if (v_tail(t)) {
+      zero_v_tail(t, B);
       __syncthreads();
     }
   };
-  for (int t = 0; t < ntiles; t += 2) {
-    iteration(t, B0);
-    if (t + 1 < ntiles) iteration(t + 1, B1);
+  iteration(0, B0, NO_PV);
+  for (int t = 1; t < ntiles; t += 2) {
+    iteration(t, B1, PV);
+    if (t + 1 < ntiles) iteration(t + 1, B0, PV);
+  }
+  // the last tile's PV product
+  if ((ntiles - 1) & 1) {
+    pv(B1, pb_prev);
+    interleave_reads_mfma();
+  } else {
+    pv(B0, pb_prev);
+    interleave_reads_mfma();
   }
 
   const float l = l_run + __shfl_xor(l_run, 32, 64);
