@@ -84,6 +84,53 @@ def test_block_causal_attention_matches_oracle(heads, L, N):
     assert_bits_equal(host(o2), host(o)[L:], "image-only attention rows")
 
 
+def test_attention_lazy_rescale_path():
+    """Keys scaled up tile by tile along the kernel's walk (text key tiles, then
+    image key tiles) make each query's running max rise past its slack of 2^8
+    on most tiles, so the accumulators are rescaled while they hold earlier
+    tiles' products (random unit-scale inputs never get there after the first
+    tile).  The result must still match the oracle's exact softmax."""
+    import torch
+    heads, L, N = 2, 200, 300
+    log(f"attention lazy rescale heads={heads} L={L} N={N}")
+    qa = qs.normal_array((heads, L + N, 128), seed=70) * 3.0
+    ka = qs.normal_array((heads, L + N, 128), seed=71)
+    va = qs.normal_array((heads, L + N, 128), seed=72)
+    nt_t = (L + 63) // 64
+    tile = np.concatenate([np.arange(L) // 64, nt_t + np.arange(N) // 64])  # position in the walk
+    ka = ka * (1.0 + tile)[None, :, None]
+    q, k, v = bf16_bits(qa), bf16_bits(ka), bf16_bits(va)
+    qv, kv, vv = bf16_vals(q), bf16_vals(k), bf16_vals(v)
+    # the construction does what it claims: count, per image query, the tiles
+    # whose max exceeds the running max by more than 8 (log2 units)
+    s = np.einsum("hqd,hkd->hqk", qv[:, L:], kv) / np.sqrt(128.0) * np.log2(np.e)
+    tmax = np.stack([s[:, :, tile == j].max(axis=2) for j in range(int(tile.max()) + 1)], axis=2)
+    run = tmax[:, :, 0].copy()
+    raises = np.zeros(run.shape, int)
+    for j in range(1, tmax.shape[2]):
+        up = tmax[:, :, j] > run + 8.0
+        raises += up
+        run = np.where(up, tmax[:, :, j], run)
+    log(f"  rescales after the first tile per image query: mean {raises.mean():.2f}, min {raises.min()}")
+    assert raises.mean() >= 3 and raises.min() >= 1
+    Lp, Np = (L + 63) // 64 * 64, (N + 63) // 64 * 64
+    q_t, k_t, q_i, k_i = (_dev(np.ascontiguousarray(a)) for a in (q[:, :L], k[:, :L], q[:, L:], k[:, L:]))
+    vt_t, vt_i = _dev(_vt(v[:, :L], Lp)), _dev(_vt(v[:, L:], Np))
+    o = torch.empty((L + N, heads * 128), dtype=torch.int16, device="cuda")
+    qi.block_causal_attention(heads, L, N, qi.QI_MODE_JOINT, q_t, k_t, vt_t, q_i, k_i, vt_i, o)
+    got = bf16_vals(host(o).view(np.uint16)).reshape(L + N, heads, 128).transpose(1, 0, 2)
+    o_t, o_i = dit.block_causal_attention(qv[:, :L], kv[:, :L], vv[:, :L], qv[:, L:], kv[:, L:], vv[:, L:])
+    ref = np.concatenate([o_t, o_i], axis=1)
+    assert np.all(np.isfinite(got))
+    rel = dit.rel_l2(got, ref)
+    mx = np.max(np.abs(got - ref))
+    log(f"  rel_l2={rel:.3e} max_abs={mx:.3e}")
+    assert rel < 1e-2 and mx < 5e-2
+    o2 = torch.empty((N, heads * 128), dtype=torch.int16, device="cuda")
+    qi.block_causal_attention(heads, L, N, qi.QI_MODE_IMAGE_ONLY, None, k_t, vt_t, q_i, k_i, vt_i, o2)
+    assert_bits_equal(host(o2), host(o)[L:], "image-only attention rows")
+
+
 def test_attention_text_rows_ignore_image_keys():
     import torch
     heads, L, N = 2, 70, 90
