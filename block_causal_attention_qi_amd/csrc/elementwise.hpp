@@ -145,76 +145,79 @@ __global__ __launch_bounds__(256) void img_embed_kernel(const float *X, int N, c
 
 // ----------------------------------------------------------------- head
 // vel[i][c] = sum_n (x[i][n] rsqrt(mean(x[i]^2) + eps) gamma[n]) W[c][n] + b[c],
-// c < 64, fp32 (proj_out on the image rows).  16 tokens per workgroup; the
-// normalised rows are staged through LDS in chunks of 256 features, each wave
-// covers a quarter of a chunk for all 16 tokens and 64 channels (lane =
-// channel), and the four partial sums are added at the end.  H % 256 == 0.
+// c < 64, fp32 (proj_out on the image rows), evaluated as
+// b[c] + r_i sum_n (x[i][n] gamma[n]) W[c][n] with r_i the row's rsqrt factor.
+// 16 tokens per workgroup; the contraction runs on the fp32 matrix cores
+// (v_mfma_f32_16x16x4_f32: A = 16 tokens x 4 features, B = 4 features x 16
+// channels) and is split over the four waves along the features; each wave
+// also accumulates the rows' sums of squares from the same loads, so x is
+// read once.  Within a 16-feature chunk, lane l (row l % 16, group g = l / 16)
+// feeds features 4 g .. 4 g + 3 to the four MFMA steps (any fixed assignment of
+// features to steps gives the same sum; this one makes each lane's operands
+// one float4 of x and four consecutive bf16 of W).  The loads of U chunks are
+// issued before their MFMAs (one wave per SIMD: nothing else hides the HBM
+// latency).  H % (64 U) == 0.
+template <int U>
 __global__ __launch_bounds__(256) void head_kernel(const float *x, int ldx, int N, const float *gamma,
                                                    const u16 *W, const float *b, int H, float eps,
                                                    float *vel) {
-  constexpr int TOK = 16, KC = 256;
-  __shared__ float sX[TOK][KC];
-  __shared__ float sInv[TOK];
-  __shared__ float sRed[4][TOK][64];
+  __shared__ float sRed[4][16][64];  // per wave: [token][channel] partial sums
+  __shared__ float sSq[4][4][16];    // per wave and lane group: [token] partial sums of squares
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int t0 = blockIdx.x * TOK;
-  for (int tt = 0; tt < 4; ++tt) {
-    const int tok = wave * 4 + tt;
-    const int ti = min(t0 + tok, N - 1);
-    const float *row = x + (size_t)ti * ldx;
-    float ss = 0.f;
-    for (int k = lane * 4; k < H; k += 256) {
-      const f32x4 v = *(const f32x4 *)(row + k);
-      ss += v[0] * v[0] + v[1] * v[1] + v[2] * v[2] + v[3] * v[3];
+  const int r = lane & 15, g = lane >> 4;
+  const int t0 = blockIdx.x * 16;
+  const float *row = x + (size_t)min(t0 + r, N - 1) * ldx;
+  const int nch = H >> 6;                       // 16-feature chunks per wave
+  const int kbase = wave * (H >> 2) + 4 * g;    // this lane's first feature
+  f32x4 acc[4];
+#pragma unroll
+  for (int cb = 0; cb < 4; ++cb) acc[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float ss = 0.f;
+  for (int c = 0; c < nch; c += U) {
+    f32x4 xv[U], gv[U];
+    u32x2 wv[U][4];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int k = kbase + 16 * (c + u);
+      xv[u] = *(const f32x4 *)(row + k);
+      gv[u] = *(const f32x4 *)(gamma + k);
+#pragma unroll
+      for (int cb = 0; cb < 4; ++cb) wv[u][cb] = *(const u32x2 *)(W + (size_t)(cb * 16 + r) * H + k);
     }
-    ss = wave_sum(ss);
-    if (lane == 0) sInv[tok] = rsqrtf(ss / (float)H + eps);
-  }
-  __syncthreads();
-  float acc[TOK];
 #pragma unroll
-  for (int i = 0; i < TOK; ++i) acc[i] = 0.f;
-  for (int kc = 0; kc < H; kc += KC) {
+    for (int u = 0; u < U; ++u) {
+      const f32x4 a = xv[u] * gv[u];
+      ss += xv[u][0] * xv[u][0] + xv[u][1] * xv[u][1] + xv[u][2] * xv[u][2] + xv[u][3] * xv[u][3];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int i = tid + 256 * j;        // float4 index in the [TOK][KC] chunk
-      const int tok = i / (KC / 4), k4 = i % (KC / 4);
-      const int ti = min(t0 + tok, N - 1);
-      const f32x4 v = *(const f32x4 *)(x + (size_t)ti * ldx + kc + k4 * 4);
-      const f32x4 gm = *(const f32x4 *)(gamma + kc + k4 * 4);
-      *(f32x4 *)&sX[tok][k4 * 4] = v * sInv[tok] * gm;
-    }
-    __syncthreads();
-    const u16 *wr = W + (size_t)lane * H + kc + wave * 64;
-#pragma unroll 2
-    for (int kk = 0; kk < 64; kk += 8) {
-      const u32x4 w8 = *(const u32x4 *)(wr + kk);
-      float wf[8];
+      for (int cb = 0; cb < 4; ++cb) {
+        const u32x2 w4 = wv[u][cb];
+        const float wf[4] = {__uint_as_float(w4[0] << 16), __uint_as_float(w4[0] & 0xFFFF0000u),
+                             __uint_as_float(w4[1] << 16), __uint_as_float(w4[1] & 0xFFFF0000u)};
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        wf[2 * e] = __uint_as_float(w8[e] << 16);
-        wf[2 * e + 1] = __uint_as_float(w8[e] & 0xFFFF0000u);
-      }
-#pragma unroll
-      for (int tok = 0; tok < TOK; ++tok) {
-        const f32x4 xa = *(const f32x4 *)&sX[tok][wave * 64 + kk];
-        const f32x4 xb = *(const f32x4 *)&sX[tok][wave * 64 + kk + 4];
-        acc[tok] += xa[0] * wf[0] + xa[1] * wf[1] + xa[2] * wf[2] + xa[3] * wf[3] + xb[0] * wf[4] +
-                    xb[1] * wf[5] + xb[2] * wf[6] + xb[3] * wf[7];
+        for (int s = 0; s < 4; ++s) acc[cb] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[s], wf[s], acc[cb], 0, 0, 0);
       }
     }
-    __syncthreads();
   }
+  // D element j of lane l: token 4 (l / 16) + j, channel 16 cb + l % 16
 #pragma unroll
-  for (int tok = 0; tok < TOK; ++tok) sRed[wave][tok][lane] = acc[tok];
+  for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) sRed[wave][4 * g + j][cb * 16 + r] = acc[cb][j];
+  sSq[wave][g][r] = ss;
   __syncthreads();
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int i = tid + 256 * j;
     const int tok = i >> 6, ch = i & 63;
+    float q = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w)
+#pragma unroll
+      for (int gg = 0; gg < 4; ++gg) q += sSq[w][gg][tok];
+    const float rinv = rsqrtf(q / (float)H + eps);
     if (t0 + tok < N)
       vel[(size_t)(t0 + tok) * 64 + ch] =
-          b[ch] + sRed[0][tok][ch] + sRed[1][tok][ch] + sRed[2][tok][ch] + sRed[3][tok][ch];
+          b[ch] + rinv * (sRed[0][tok][ch] + sRed[1][tok][ch] + sRed[2][tok][ch] + sRed[3][tok][ch]);
   }
 }
 

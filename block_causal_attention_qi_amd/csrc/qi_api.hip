@@ -174,6 +174,17 @@ qi_status launch_gemm(const GemmArgs &g, int kind, hipStream_t s) {
   return last_launch();
 }
 
+// The output head over `rows` rows of x [rows][H]; H % 256 == 0 (checked with
+// the model dimensions).
+void launch_head(const float *x, int H, int rows, const qi_model_w &w, float eps, float *vel, hipStream_t s) {
+  if ((H / 64) % 8 == 0)
+    hipLaunchKernelGGL(head_kernel<8>, dim3((rows + 15) / 16), dim3(256), 0, s, x, H, rows, w.norm_out, w.w_out,
+                       w.b_out, H, eps, vel);
+  else
+    hipLaunchKernelGGL(head_kernel<4>, dim3((rows + 15) / 16), dim3(256), 0, s, x, H, rows, w.norm_out, w.w_out,
+                       w.b_out, H, eps, vel);
+}
+
 qi_status launch_norm(const float *x, int ldx, const float *gamma, int zc, const float *mod,
                       int mod_img_off, int L_rows, int rows, int H, u16 *out, int ldo, hipStream_t s,
                       const int *skip = nullptr) {
@@ -359,8 +370,7 @@ qi_status run_step(const qi_dims &d, const qi_model_w &w, int L, int N, const fl
   }
   if (vel) {
     TimedLaunch tl(QI_KERNEL_HEAD, s);
-    hipLaunchKernelGGL(head_kernel, dim3((N + 15) / 16), dim3(256), 0, s, x + (size_t)L_rows * H, H, N,
-                       w.norm_out, w.w_out, w.b_out, H, kRmsEps, vel);
+    launch_head(x + (size_t)L_rows * H, H, N, w, kRmsEps, vel, s);
     QI_TRY(last_launch());
   }
   return QI_OK;
@@ -537,8 +547,7 @@ qi_status run_step_fbc(const qi_dims &d, const qi_model_w &w, int L, int N, cons
   hipLaunchKernelGGL(fbc_finish_kernel, dim3(eblocks), dim3(256), 0, s, x, x1s, rem, n4, st);
   QI_TRY(last_launch());
   TimedLaunch tl(QI_KERNEL_HEAD, s);
-  hipLaunchKernelGGL(head_kernel, dim3((N + 15) / 16), dim3(256), 0, s, x, H, N, w.norm_out, w.w_out, w.b_out, H,
-                     kRmsEps, vel);
+  launch_head(x, H, N, w, kRmsEps, vel, s);
   return last_launch();
 }
 
@@ -563,8 +572,7 @@ qi_status run_step_cfg(const qi_dims &d, const qi_model_w &w, int N, const float
     QI_TRY(run_block(d, w.blocks[b], L_pos, N, false, x, mod, nullptr, nullptr, img_cos, img_sin,
                      kv_pos + (size_t)b * slot_p, ws, lay, s, 2, kv_neg + (size_t)b * slot_n, L_neg));
   TimedLaunch tl(QI_KERNEL_HEAD, s);
-  hipLaunchKernelGGL(head_kernel, dim3((2 * N + 15) / 16), dim3(256), 0, s, x, H, 2 * N, w.norm_out, w.w_out,
-                     w.b_out, H, kRmsEps, vel);
+  launch_head(x, H, 2 * N, w, kRmsEps, vel, s);
   return last_launch();
 }
 
