@@ -276,11 +276,13 @@ QI_DEV void qkv_epilogue(const GemmArgs &g, int m0, int n_tile, int wrow, int n0
   }
 }
 
-// SwiGLU outputs o..o+3 of token m from the gate and up accumulators.
+// SwiGLU outputs o..o+3 of token m from the gate and up accumulators.  The
+// sigmoid's reciprocal is v_rcp_f32 (within 1 ulp; the output is rounded to
+// bf16 next), not the ten-instruction IEEE division sequence.
 QI_DEV void store4_swiglu(const GemmArgs &g, int m, int o, f32x4 gt, f32x4 up) {
   float y[4];
 #pragma unroll
-  for (int r = 0; r < 4; ++r) y[r] = gt[r] / (1.f + __expf(-gt[r])) * up[r];
+  for (int r = 0; r < 4; ++r) y[r] = gt[r] * __builtin_amdgcn_rcpf(1.f + __expf(-gt[r])) * up[r];
   *(u32x2 *)(g.out + (size_t)m * g.ldo + o) = u32x2{pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3])};
 }
 
