@@ -37,7 +37,9 @@ def _dev(a):
     return torch.from_numpy(np.ascontiguousarray(a)).cuda()
 
 
-@pytest.mark.parametrize("wl_id,L,h,w", [(1, 8, 8, 8), (1, 37, 9, 7), (2, 22, 16, 16)])
+# (1, 1, 1, 1) and (1, 1, 8, 8): the degenerate sizes the API accepts, one
+# text token and a 1 x 1 image grid (every tile of every kernel ragged)
+@pytest.mark.parametrize("wl_id,L,h,w", [(1, 8, 8, 8), (1, 37, 9, 7), (2, 22, 16, 16), (1, 1, 1, 1), (1, 1, 8, 8)])
 def test_block_matches_oracle_joint_and_image_only(wl_id, L, h, w):
     import torch
     wl = qs.workload(wl_id, L=L, h=h, w=w)
@@ -90,7 +92,8 @@ def _oracle_step(wl, sw, blocks, t, img=None, txt=None, **kw):
     return dit.dit_step(sw, blocks, wl.L, img, txt, t, tc, ts, ic, is_, wl.heads, **kw)
 
 
-@pytest.mark.parametrize("wl_id,over", [(1, {}), (1, dict(L=37, h=9, w=7)), (1, dict(n_blocks=3)), (2, {})])
+@pytest.mark.parametrize("wl_id,over", [(1, {}), (1, dict(L=37, h=9, w=7)), (1, dict(n_blocks=3)), (2, {}),
+                                         (1, dict(L=1, h=1, w=1, n_blocks=2))])
 def test_step_matches_oracle(wl_id, over):
     wl = qs.workload(wl_id, **over)
     log(f"step wl={wl_id} {over} L={wl.L} N={wl.N} blocks={wl.n_blocks}")
@@ -108,7 +111,8 @@ def test_step_matches_oracle(wl_id, over):
         assert rel16 <= dit.rel_l2(vel, ref)
 
 
-@pytest.mark.parametrize("wl_id,over", [(1, {}), (1, dict(L=37, h=9, w=7, n_blocks=2)), (2, {})])
+@pytest.mark.parametrize("wl_id,over", [(1, {}), (1, dict(L=37, h=9, w=7, n_blocks=2)), (2, {}),
+                                         (1, dict(L=1, h=1, w=1, n_blocks=2))])
 def test_cached_step_bit_equals_full_recompute(wl_id, over):
     import torch
     wl = qs.workload(wl_id, **over)
