@@ -92,8 +92,11 @@ def _oracle_step(wl, sw, blocks, t, img=None, txt=None, **kw):
     return dit.dit_step(sw, blocks, wl.L, img, txt, t, tc, ts, ic, is_, wl.heads, **kw)
 
 
+# hidden 768 (6 heads): every GEMM on the 128 x 128 kernel, and the head's
+# feature loop in batches of 4 chunks (H / 64 = 12)
 @pytest.mark.parametrize("wl_id,over", [(1, {}), (1, dict(L=37, h=9, w=7)), (1, dict(n_blocks=3)), (2, {}),
-                                         (1, dict(L=1, h=1, w=1, n_blocks=2))])
+                                         (1, dict(L=1, h=1, w=1, n_blocks=2)),
+                                         (1, dict(hidden=768, ffn=2304, txt_dim=768))])
 def test_step_matches_oracle(wl_id, over):
     wl = qs.workload(wl_id, **over)
     log(f"step wl={wl_id} {over} L={wl.L} N={wl.N} blocks={wl.n_blocks}")
