@@ -44,11 +44,15 @@ Readings of points the pages leave open (each is stated where it is used):
       accumulation, residual stream, norm statistics and softmax sums.
   S12 RoPE tables: each step of the printed formula rounded to fp32, pow and
       cos/sin correctly rounded (evaluated in float64, rounded once).
+  S13 metrics: rel L2 over all of vel; per-token Pearson correlation over the
+      64 channels, minimum over tokens.
   S14 Euler: the sigma difference in fp32, then a fp32 multiply and a fp32
       add, no fused multiply-add.
   S15 sampler constants base_shift 0.5 at 256 tokens, max_shift 0.9 at 8192
       tokens, mu linear in N with no clamp, 1000 train timesteps; each array
       operation in fp32 as the host contract states, mu and e^mu in float64.
+  S16 image frame position: the first position axis of every image token is
+      L, the text length, as the host contract prints it.
   S20 true CFG: noise = neg + g * (pos - neg) exactly as [MLX] "Optional
       modes" writes it (no rescaling of the combined prediction), evaluated
       in fp32 as written -- difference, product, sum, each rounded once -- and
