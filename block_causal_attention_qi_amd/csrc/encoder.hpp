@@ -372,23 +372,38 @@ __global__ __launch_bounds__(256) void enc_attention_kernel(const float *Q, cons
 #pragma unroll
     for (int e = 0; e < 16; ++e) oacc[d][e] = 0.f;
   const int kend = min(q0 + BQ, L);  // keys 0 .. kend-1 reach this workgroup's queries
+  // K/V tiles go through registers one tile ahead: the loads of tile t+1 are
+  // in flight while tile t is computed, and land in LDS at the next step
+  constexpr int PER = BKV * 32 / 256;  // float4 of K (and of V) per thread per tile
+  f32x4 kr[PER], vr[PER];
+  auto load_tile = [&](int key0) {
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const int i = tid + 256 * j, r = i >> 5, c = (i & 31) * 4;
+      const int key = min(key0 + r, L - 1);
+      kr[j] = *(const f32x4 *)(Kh + (size_t)key * 128 + c);
+      vr[j] = *(const f32x4 *)(Vh + (size_t)key * 128 + c);
+    }
+  };
+  load_tile(0);
   for (int key0 = 0; key0 < kend; key0 += BKV) {
     __syncthreads();
-    for (int i = tid; i < BKV * 32; i += 256) {  // 32 float4 per row
-      const int r = i >> 5, c = (i & 31) * 4;
-      const int key = min(key0 + r, L - 1);
-      *(f32x4 *)&sK[r][c] = *(const f32x4 *)(Kh + (size_t)key * 128 + c);
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {  // 32 float4 per row
+      const int i = tid + 256 * j, r = i >> 5, c = (i & 31) * 4;
+      *(f32x4 *)&sK[r][c] = kr[j];
       // a key masked by causality meets probability 0, and 0 * v must stay 0:
       // non-finite values (only an invalid input makes them) enter as 0
-      f32x4 v = *(const f32x4 *)(Vh + (size_t)key * 128 + c);
+      f32x4 v = vr[j];
 #pragma unroll
       for (int e = 0; e < 4; ++e) v[e] = __builtin_isfinite(v[e]) ? v[e] : 0.f;
       *(f32x4 *)&sV[r][c] = v;
     }
     __syncthreads();
+    if (key0 + BKV < kend) load_tile(key0 + BKV);
     if (key0 > wq0 + 31) continue;  // every key of the tile is after every query of this wave
     f32x16 s = {};
-#pragma unroll 16
+#pragma unroll
     for (int j = 0; j < 64; ++j) s = mfma32x32x2f32(sK[l32][64 * h + j], qreg[j], s);
     float mx = -INFINITY;
 #pragma unroll
