@@ -14,6 +14,10 @@
 // ZeroCenterRMSNorm for the text projection.  One wave per row (4 rows per
 // workgroup): each lane keeps VPL float4 of the row in registers, so the whole
 // row is in flight at once and the reduction is a pure wavefront reduction.
+// The row-invariant factors w and 1 + scale are read from global memory once
+// per workgroup into LDS (while the rows' loads are in flight) instead of once
+// per row; a workgroup whose rows straddle L_rows (two scale vectors) reads
+// them per row as before.  Same operations in the same order either way.
 // H % 256 == 0, H <= 256 * VPL.
 template <int VPL>
 __global__ __launch_bounds__(256) void rmsnorm_mod_kernel(const float *x, int ldx, const float *gamma,
@@ -21,20 +25,36 @@ __global__ __launch_bounds__(256) void rmsnorm_mod_kernel(const float *x, int ld
                                                           int mod_img_off, int L_rows, int rows, int H,
                                                           float eps, u16 *out, int ldo, const int *skip) {
   if (skip && *skip) return;  // first-block cache: this block is skipped this step
+  __shared__ f32x4 sW[VPL * 64], sS[VPL * 64];
   const int lane = threadIdx.x & 63;
-  const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (r >= rows) return;
-  const f32x4 *xr = (const f32x4 *)(x + (size_t)r * ldx);
+  const int r0 = blockIdx.x * 4;
+  const int r = r0 + (threadIdx.x >> 6);
+  const bool live = r < rows;
   const int nv = H >> 8;  // float4 per lane
   f32x4 v[VPL];
-  float ss = 0.f;
+  if (live) {
+    const f32x4 *xr = (const f32x4 *)(x + (size_t)r * ldx);
 #pragma unroll
-  for (int i = 0; i < VPL; ++i) {
-    if (i < nv) {
-      v[i] = xr[lane + 64 * i];
-      ss += v[i][0] * v[i][0] + v[i][1] * v[i][1] + v[i][2] * v[i][2] + v[i][3] * v[i][3];
+    for (int i = 0; i < VPL; ++i)
+      if (i < nv) v[i] = xr[lane + 64 * i];
+  }
+  // one scale vector for the whole workgroup (uniform over the workgroup)
+  const bool staged = !mod || ((r0 < L_rows) == (min(r0 + 3, rows - 1) < L_rows));
+  const float *sc0 = mod ? mod + (r0 < L_rows ? 0 : mod_img_off) : nullptr;
+  if (staged) {
+    for (int i = threadIdx.x; i < nv * 64; i += 256) {
+      f32x4 w = ((const f32x4 *)gamma)[i];
+      if (zero_centred) w += 1.f;
+      sW[i] = w;
+      if (sc0) sS[i] = ((const f32x4 *)sc0)[i] + 1.f;
     }
   }
+  __syncthreads();
+  if (!live) return;
+  float ss = 0.f;
+#pragma unroll
+  for (int i = 0; i < VPL; ++i)
+    if (i < nv) ss += v[i][0] * v[i][0] + v[i][1] * v[i][1] + v[i][2] * v[i][2] + v[i][3] * v[i][3];
   ss = wave_sum(ss);
   const float inv = rsqrtf(ss / (float)H + eps);
   const float *sc = mod ? mod + (r < L_rows ? 0 : mod_img_off) : nullptr;
@@ -43,10 +63,15 @@ __global__ __launch_bounds__(256) void rmsnorm_mod_kernel(const float *x, int ld
   for (int i = 0; i < VPL; ++i) {
     if (i < nv) {
       const int idx = lane + 64 * i;
-      f32x4 w = ((const f32x4 *)gamma)[idx];
-      if (zero_centred) w += 1.f;
+      f32x4 w;
+      if (staged) {
+        w = sW[idx];
+      } else {
+        w = ((const f32x4 *)gamma)[idx];
+        if (zero_centred) w += 1.f;
+      }
       f32x4 y = v[i] * inv * w;
-      if (sc) y *= ((const f32x4 *)sc)[idx] + 1.f;
+      if (sc) y *= staged ? sS[idx] : ((const f32x4 *)sc)[idx] + 1.f;
       *(u32x2 *)(orow + idx * 4) = u32x2{pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3])};
     }
   }
