@@ -241,10 +241,13 @@ __global__ __launch_bounds__(attn::THREADS, 1) void block_causal_attn_kernel(con
   copy_k(0, B0);
   if (ntiles > 1) copy_k(1, B1);
   __syncthreads();
-  f32x16 s_cur[2];
-  scores(B0, s_cur);
+  // Scores and bf16 probabilities of consecutive tiles alternate between two
+  // register sets chosen by the tile's parity (a constant in each unrolled
+  // iteration), so no iteration copies one tile's state into the other's.
+  f32x16 sA[2], sB[2];  // scores of even / odd tiles
+  u32x4 pA[4], pB[4];   // bf16 probabilities of even / odd tiles (PV's B operand)
+  scores(B0, sA);
   __syncthreads();  // sK0 is overwritten next
-  u32x4 pb_prev[4];  // bf16 probabilities of the previous tile (B operand)
 
   // O^T[d][q] += V^T[d][16 c4 + 8h .. +8] P^T with V from sV[B]
   auto pv = [&](auto B, const u32x4 *pb) {
@@ -262,6 +265,10 @@ __global__ __launch_bounds__(attn::THREADS, 1) void block_causal_attn_kernel(con
   // one iteration; B = t & 1 as a constant; HAS_PV: tile t-1 exists
   auto iteration = [&](int t, auto B, auto HAS_PV) {
     constexpr std::integral_constant<int, 1 - B.value> NB{};
+    f32x16(&s_cur)[2] = B.value ? sB : sA;
+    f32x16(&s_next)[2] = B.value ? sA : sB;
+    u32x4(&pb)[4] = B.value ? pB : pA;
+    const u32x4(&pb_prev)[4] = B.value ? pA : pB;
     if (t + 2 < ntiles) copy_k(t + 2, B);
     copy_v(t, B);
 
@@ -297,13 +304,11 @@ __global__ __launch_bounds__(attn::THREADS, 1) void block_causal_attn_kernel(con
       const int c4 = j >> 2, vr = (j & 3) * 32 + l32;
       return sv[vr * 8 + ((2 * c4 + h) ^ vsw)];
     };
-    f32x16 s_next[2];
     u32x4 fr[3];
     fr[0] = frag(0);
     if constexpr (HAS_PV.value) fr[1] = frag(1);
     float m4[4], mx = 0.f, alpha = 1.f, nbase = 0.f;
     bool raise = false;
-    u32x4 pb[4];
     float psum[2] = {0.f, 0.f};
 #pragma unroll
     for (int i = 0; i < 32; ++i) {
@@ -371,10 +376,6 @@ __global__ __launch_bounds__(attn::THREADS, 1) void block_causal_attn_kernel(con
 #pragma unroll
       for (int d = 0; d < 4; ++d) oacc[d] *= alpha;
     }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) pb_prev[i] = pb[i];
-    s_cur[0] = s_next[0];
-    s_cur[1] = s_next[1];
     __syncthreads();
     if (v_tail(t)) {
       zero_v_tail(t, B);
@@ -388,10 +389,10 @@ __global__ __launch_bounds__(attn::THREADS, 1) void block_causal_attn_kernel(con
   }
   // the last tile's PV product
   if ((ntiles - 1) & 1) {
-    pv(B1, pb_prev);
+    pv(B1, pB);
     interleave_reads_mfma();
   } else {
-    pv(B0, pb_prev);
+    pv(B0, pA);
     interleave_reads_mfma();
   }
 
