@@ -86,7 +86,7 @@ def calibrate():
     import torch.nn.functional as F
 
     from block_causal_attention_qi_amd import _lib
-    lib = _lib.load()
+    lib = _lib.load_calib()
     res = {}
     for shape, name in ((0, "mfma_32x32x16_bf16_tflops"), (1, "mfma_16x16x32_bf16_tflops")):
         v = ctypes.c_double(0)

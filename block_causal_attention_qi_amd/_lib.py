@@ -105,6 +105,10 @@ SIGNATURES = {
     "qi_kernel_kind_name": (c_char_p, [c_int32]),
     "qi_timing_begin": (c_int32, [c_int32]),
     "qi_timing_end": (c_int32, [c_void_p, c_void_p, c_void_p]),
+}
+# the bench-only calibration library (include/qi_calib.h, lib/libqi_calib.so)
+CALIB_PATH = os.path.join(PKG, "lib", "libqi_calib.so")
+CALIB_SIGNATURES = {
     "qi_calib_mfma_tflops": (c_int32, [c_int32, c_int32, c_void_p]),
     "qi_calib_copy_gbs": (c_int32, [c_void_p, c_void_p, c_int64, c_int32, c_void_p]),
     "qi_calib_lds_cycles": (c_int32, [c_int32, c_int32, c_void_p]),
@@ -112,6 +116,7 @@ SIGNATURES = {
 QI_KERNEL_KINDS = 15
 
 _lib = None
+_calib = None
 
 
 class QiError(RuntimeError):
@@ -137,6 +142,23 @@ def load(path: str | None = None):
         fn.argtypes = args
     if path is None:
         _lib = lib
+    return lib
+
+
+def load_calib():
+    """Load the bench-only calibration library libqi_calib.so (once)."""
+    global _calib
+    if _calib is not None:
+        return _calib
+    if not os.path.exists(CALIB_PATH):
+        raise RuntimeError(f"calibration library {CALIB_PATH} is not built; run "
+                           "`python -m block_causal_attention_qi_amd.build`")
+    lib = ctypes.CDLL(CALIB_PATH)
+    for name, (res, args) in CALIB_SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _calib = lib
     return lib
 
 

@@ -4,7 +4,11 @@
 
 Kernels and the C ABI are compiled with hipcc for gfx950 only; the host tables
 are compiled with g++ and -ffp-contract=off (each fp32 operation rounded on its
-own).  The library lands in block_causal_attention_qi_amd/lib/libqi.so."""
+own).  The library lands in block_causal_attention_qi_amd/lib/libqi.so.
+
+The calibration microbenchmarks (include/qi_calib.h) are a separate,
+bench-only library, lib/libqi_calib.so: they allocate, create a stream and
+block, which the product library never does."""
 from __future__ import annotations
 
 import os
@@ -17,6 +21,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OUT_DIR = os.path.join(PKG, "lib")
 LIB = os.path.join(OUT_DIR, "libqi.so")
+CALIB_LIB = os.path.join(OUT_DIR, "libqi_calib.so")
 ARCH = "gfx950"
 
 HIP_FLAGS = [
@@ -65,13 +70,24 @@ def build(verbose: bool = False) -> str:
         print(out)
     objs.append(api_obj)
     objs.append(attn_obj)
-    calib_obj = os.path.join(obj_dir, "calib.o")
-    _run([hipcc, *HIP_FLAGS, "-c", os.path.join(CSRC, "calib.hip"), "-o", calib_obj])
-    objs.append(calib_obj)
     tmp = LIB + ".tmp"
     _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp])
     os.replace(tmp, LIB)
+    build_calib(hipcc, obj_dir)
     return LIB
+
+
+def build_calib(hipcc: str, obj_dir: str) -> str:
+    """The bench-only calibration library (its own .so, not linked into
+    libqi.so)."""
+    if os.path.exists(CALIB_LIB):
+        os.remove(CALIB_LIB)
+    calib_obj = os.path.join(obj_dir, "calib.o")
+    _run([hipcc, *HIP_FLAGS, "-c", os.path.join(CSRC, "calib.hip"), "-o", calib_obj])
+    tmp = CALIB_LIB + ".tmp"
+    _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", calib_obj, "-o", tmp])
+    os.replace(tmp, CALIB_LIB)
+    return CALIB_LIB
 
 
 if __name__ == "__main__":

@@ -307,10 +307,11 @@ __global__ __launch_bounds__(256) void euler_cfg_kernel(float *x, const float *v
 }
 
 // ---------------------------------------------------------------- first-block cache
-// [MLX] "Optional modes": "Fast mode" runs block 0 every step and skips blocks
-// 1..n-1 while block 0's residual changes less than a threshold; a skipped
-// step adds the residual that blocks 1..n-1 produced at the last step that ran
-// them.  State on the device (so the loop needs no host sync): the flag every
+// First-block cache ([MLX] "Optional modes", Fast mode): the first block is
+// always computed, and the rest of the stack is reused from the last step
+// that computed it for as long as the first block's residual stays within a
+// relative threshold of the residual cached at that step; a reused step adds
+// the residual the later blocks produced then.  State on the device (so the loop needs no host sync): the flag every
 // kernel of blocks 1..n-1 reads, the validity of the cached residuals, counts,
 // and the change the last decision saw.
 struct FbcState {

@@ -10,11 +10,13 @@
 namespace {
 constexpr int kPosMin = -1024, kPosMax = 8191, kRows = kPosMax - kPosMin + 1;  // 9216 rows
 
-// Host contract -- RGBA-Image-2.1, s.4: table = polar(1, outer(pos,
-// 1/10000^(arange(0,d,2)/d))).  Every printed step is one fp32 operation:
-// the exponent 2k/d, 10000^exponent (evaluated in double, rounded once), the
-// reciprocal, and the product with the position; cos and sin of the fp32
-// angle are evaluated in double and rounded once.
+// One axis of the RoPE tables (Host contract -- RGBA-Image-2.1, s.4): entry
+// (p, k) is the unit complex number at angle p * w_k, with the inverse
+// frequency w_k = 1 / 10000^(2k/d), for positions p = -1024..8191.  The
+// contract requires these tables bit-exact, so each arithmetic step is one
+// fp32 operation: the exponent 2k/d, the power (evaluated in double and
+// rounded once), its reciprocal, and the product with the position; cos and
+// sin of the fp32 angle are evaluated in double and rounded once.
 void axis_table(int d, float *c, float *s) {
   const int P = d / 2;
   for (int k = 0; k < P; ++k) {
@@ -77,15 +79,17 @@ qi_status qi_rope_tables(int32_t L, int32_t h, int32_t w, float *txt_cos, float 
   return QI_OK;
 }
 
-// Host contract s.6 (FlowMatch Euler): sigmas = linspace(1, 1/steps, steps);
-// mu = N m + b with m = (max_shift - base_shift)/(max_seq - base_seq), b =
-// base_shift - m base_seq; sigmas = e^mu / (e^mu + (1/sigmas - 1));
-// sigmas = 1 - (1 - sigmas)/((1 - sigmas[-1])/(1 - shift_terminal));
-// timesteps = sigmas * 1000; sigmas ++ [0].  base_shift 0.5 at 256 tokens and
-// max_shift 0.9 at 8192 tokens reproduce the printed mu values.  linspace
-// follows the usual start + i*step with the last point set to the end value,
-// in double, rounded once to fp32; mu and e^mu in double rounded once; every
-// array operation after that in fp32.
+// The FlowMatch Euler schedule (Host contract -- RGBA-Image-2.1, s.6).  The
+// schedule is a uniform grid from 1 down to 1/steps, bent by the exponential
+// time shift s -> e^mu / (e^mu + 1/s - 1) whose strength mu grows linearly
+// with the image token count (0.5 at 256 tokens, 0.9 at 8192: the constants
+// that give the contract's printed mu values), then stretched affinely in
+// 1 - s so that the last value lands on 0.02; timesteps are the sigmas times
+// 1000, and a final sigma 0 is appended.  The contract gates sigmas bit for
+// bit, so the fp32 operation order is fixed: the grid points are computed in
+// double as start + i * step (the last one set to the end value) and rounded
+// once, mu and e^mu in double rounded once, and every later array operation
+// is one fp32 operation.
 qi_status qi_flow_sigmas(int32_t steps, int32_t n_img_tokens, float *sigmas, float *timesteps) {
   if (!sigmas || !timesteps) return QI_ERR_NULL;
   if (steps < 2 || steps > 100000 || n_img_tokens < 1) return QI_ERR_RANGE;

@@ -3,7 +3,10 @@
  *
  * Roofline fractions are quoted against the vendor peaks and against what this
  * part measurably sustains: register-only MFMA throughput and a device copy.
- * These calls are diagnostics for the benchmark, not part of the DiT step.
+ * These calls are diagnostics for the benchmark, not part of the DiT step: they
+ * are exported by a separate, bench-only library, libqi_calib.so, and not by
+ * libqi.so.  Unlike libqi, they allocate device memory, create a stream and
+ * block until their measurement ends.
  */
 #ifndef QI_CALIB_H_
 #define QI_CALIB_H_

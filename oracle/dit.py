@@ -114,9 +114,10 @@ def round_bf16(a: np.ndarray) -> np.ndarray:
 # ------------------------------------------------------------------ RoPE
 
 def rope_axis_table(d: int):
-    """fp32 cos/sin table of one axis: rows for positions -1024..8191, column
-    k holds angle pos * 1/10000^(2k/d)  ([HOST] s.4: polar(1, outer(pos,
-    1/10000^(arange(0,d,2)/d)))).  Reading S12 for the rounding."""
+    """fp32 cos/sin table of one axis ([HOST] s.4): row p + 1024 for each
+    position p in -1024..8191; column k is the unit complex number at angle
+    p * w_k with inverse frequency w_k = 1 / 10000^(2k/d).  Reading S12 for
+    the rounding."""
     pos = np.arange(ROPE_POS_MIN, ROPE_POS_MAX + 1, dtype=np.int64)
     expo = np.arange(0, d, 2, dtype=np.int64).astype(F32) / F32(d)          # fp32 quotient
     powv = np.power(np.float64(10000.0), expo.astype(np.float64)).astype(F32)  # pow, rounded once
@@ -422,13 +423,14 @@ def flow_mu(n_tokens: int) -> float:
 
 
 def flow_sigmas(steps: int, n_tokens: int):
-    """FlowMatch Euler schedule ([HOST] s.6; all arrays fp32):
-    sigmas = linspace(1, 1/steps, steps); exponential shift
-    e^mu / (e^mu + (1/sigma - 1)); terminal stretch
-    1 - (1 - sigma) / ((1 - sigma[-1]) / (1 - 0.02)); timesteps = sigmas * 1000;
-    sigmas ++ [0].  Every array operation is one fp32 operation; mu and e^mu
-    are computed in float64 and rounded once.  Returns (sigmas fp32
-    [steps+1], timesteps fp32 [steps])."""
+    """FlowMatch Euler schedule ([HOST] s.6): a uniform grid from 1 down to
+    1/steps; the exponential time shift s -> e^mu / (e^mu + 1/s - 1) with mu
+    from flow_mu; an affine stretch of 1 - s that puts the last value at the
+    terminal 0.02; timesteps = 1000 s; a final sigma 0 appended.  The host
+    contract keeps these arrays in fp32 and gates them bit for bit, so each
+    array operation here is one fp32 operation, and mu and e^mu are computed
+    in float64 and rounded once.  Returns (sigmas fp32 [steps+1], timesteps
+    fp32 [steps])."""
     s = np.linspace(1.0, 1.0 / steps, steps).astype(F32)
     em = F32(math.exp(flow_mu(n_tokens)))
     one = F32(1.0)

@@ -18,9 +18,8 @@ from oracle import dit
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
-def _declared_symbols():
-    inc = os.path.join(ROOT, "include")
-    src = "".join(open(os.path.join(inc, f)).read() for f in sorted(os.listdir(inc)) if f.endswith(".h"))
+def _declared_symbols(header="qi.h"):
+    src = open(os.path.join(ROOT, "include", header)).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
     return sorted(set(re.findall(r"\b(qi_[a-z0-9_]+)\s*\(", src)))
 
@@ -38,12 +37,29 @@ no_gpu_only = pytest.mark.skipif(_gpu_visible(), reason="fake-pointer validation
 
 def test_library_loads_and_exports_every_declared_symbol():
     lib = _lib.load()
-    decl = _declared_symbols()
-    assert len(decl) >= 20 and "qi_calib_mfma_tflops" in decl
+    decl = _declared_symbols("qi.h")
+    assert len(decl) >= 20 and "qi_dit_step" in decl
     for name in decl:
         assert hasattr(lib, name), name
         assert name in _lib.SIGNATURES, f"binding misses {name}"
     assert lib.qi_version().decode().startswith("qi-dit-gfx950")
+    headers = sorted(f for f in os.listdir(os.path.join(ROOT, "include")) if f.endswith(".h"))
+    assert headers == ["qi.h", "qi_calib.h"], headers
+
+
+def test_calibration_library_is_separate():
+    """The calibration microbenchmarks (which allocate, create a stream and
+    block) live in their own bench-only library, not in libqi."""
+    lib = _lib.load()
+    cal = _lib.load_calib()
+    decl = _declared_symbols("qi_calib.h")
+    assert len(decl) == 3
+    for name in decl:
+        assert hasattr(cal, name), name
+        assert name in _lib.CALIB_SIGNATURES, f"binding misses {name}"
+    import subprocess
+    syms = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True, text=True).stdout
+    assert "qi_dit_step" in syms and "qi_calib" not in syms
 
 
 def test_status_strings():
@@ -199,15 +215,16 @@ def test_capture_block_and_component_reject_bad_arguments():
     assert g(64, 100, 64, FAKE, FAKE, None, FAKE, None) == _lib.QI_ERR_RANGE
     assert g(64, 128, 96, FAKE, FAKE, None, FAKE, None) == _lib.QI_ERR_RANGE
     assert g(64, 128, 64, None, FAKE, None, FAKE, None) == _lib.QI_ERR_NULL
-    c = lib.qi_calib_mfma_tflops
+    cal = _lib.load_calib()
+    c = cal.qi_calib_mfma_tflops
     out = ctypes.c_double(0)
     assert c(2, 10, ctypes.byref(out)) == _lib.QI_ERR_RANGE
     assert c(0, 10, None) == _lib.QI_ERR_NULL
-    assert lib.qi_calib_copy_gbs(FAKE, FAKE, 15, 1, ctypes.byref(out)) == _lib.QI_ERR_RANGE
-    assert lib.qi_calib_copy_gbs(FAKE_MIS, FAKE, 64, 1, ctypes.byref(out)) == _lib.QI_ERR_ALIGN
-    assert lib.qi_calib_lds_cycles(5, 100, ctypes.byref(out)) == _lib.QI_ERR_RANGE
-    assert lib.qi_calib_lds_cycles(0, 3, ctypes.byref(out)) == _lib.QI_ERR_RANGE
-    assert lib.qi_calib_lds_cycles(0, 100, None) == _lib.QI_ERR_NULL
+    assert cal.qi_calib_copy_gbs(FAKE, FAKE, 15, 1, ctypes.byref(out)) == _lib.QI_ERR_RANGE
+    assert cal.qi_calib_copy_gbs(FAKE_MIS, FAKE, 64, 1, ctypes.byref(out)) == _lib.QI_ERR_ALIGN
+    assert cal.qi_calib_lds_cycles(5, 100, ctypes.byref(out)) == _lib.QI_ERR_RANGE
+    assert cal.qi_calib_lds_cycles(0, 3, ctypes.byref(out)) == _lib.QI_ERR_RANGE
+    assert cal.qi_calib_lds_cycles(0, 100, None) == _lib.QI_ERR_NULL
     m = lib.qi_modulation
     assert m(ctypes.byref(d), FAKE, FAKE, 2.0, FAKE, None) == _lib.QI_ERR_RANGE
     assert m(ctypes.byref(d), None, FAKE, 0.5, FAKE, None) == _lib.QI_ERR_NULL

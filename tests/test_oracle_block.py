@@ -268,3 +268,117 @@ def test_bf16_mode_stays_within_the_rounding_envelope():
     b16 = dit.dit_step(sw, [bw], WL.L, X, E, 0.7, tc, ts, ic, is_, WL.heads, bf16=True)
     rel = dit.rel_l2(b16, exact)
     assert 1e-4 < rel < 1e-2, rel
+
+
+def _structured_shared(wl=WL):
+    """Shared weights whose projections are selections with a known product:
+    W_txt a cyclic shift (row j reads feature j - 1: not symmetric, so a
+    transposed W_txt lands every value two features off), W_img and W_out
+    scatter / gather matrices, and distinct biases and norm weights (so a
+    dropped bias or norm weight changes the result)."""
+    sw, bw = _weights(wl)
+    H, D = wl.hidden, wl.txt_dim
+    sw = dict(sw)
+    w_txt = np.zeros((H, D), np.float32)
+    w_txt[(np.arange(D) + 1) % H, np.arange(D)] = 1.0
+    w_img = np.zeros((H, 64), np.float32)
+    w_img[5 * np.arange(64) + 2, np.arange(64)] = 1.0
+    w_out = np.zeros((64, H), np.float32)
+    w_out[np.arange(64), 7 * np.arange(64) + 3] = 1.0
+    sw.update(w_txt=w_txt, b_txt=(100.0 + np.arange(H)).astype(np.float32),
+              txt_norm=(0.25 + 0.5 * (np.arange(D) % 3)).astype(np.float32),
+              w_img=w_img, b_img=(-50.0 - np.arange(H)).astype(np.float32),
+              w_out=w_out, b_out=(1000.0 + np.arange(64)).astype(np.float32),
+              norm_out=(1.0 + 0.01 * np.arange(H)).astype(np.float32))
+    return sw, bw
+
+
+def test_text_projection_and_img_in_closed_form():
+    """embed() on one-hot text rows c * e_i: the zero-centred norm gives
+    c / sqrt(c^2/D + eps) * (1 + w_i) at feature i, the cyclic-shift W_txt
+    moves it to feature i + 1, and b_txt adds its own value everywhere; the
+    image rows are X scattered to features 5c + 2 plus b_img.  Fails for a
+    transposed W_txt, a dropped b_txt or norm weight, or a transposed W_img."""
+    sw, _ = _structured_shared()
+    H, D = WL.hidden, WL.txt_dim
+    idx = np.array([0, 3, 100, D - 1, 257, 31, 64, 9])[:WL.L]
+    c = np.array([1.0, -2.0, 0.5, 3.0, -1.5, 10.0, 0.25, -4.0])[:WL.L]
+    E = np.zeros((WL.L, D), np.float32)
+    E[np.arange(WL.L), idx] = c
+    X = qs.img_tokens(WL)
+    x = dit.embed(sw, X, E)
+    ref_txt = np.tile(100.0 + np.arange(H), (WL.L, 1))
+    wn = 0.25 + 0.5 * (idx % 3)
+    ref_txt[np.arange(WL.L), (idx + 1) % H] += c / np.sqrt(c * c / D + 1e-6) * (1.0 + wn)
+    ref_img = np.tile(-50.0 - np.arange(H), (WL.N, 1))
+    ref_img[:, 5 * np.arange(64) + 2] += X
+    assert x.shape == (WL.L + WL.N, H)
+    assert np.max(np.abs(x[:WL.L] - ref_txt)) < 1e-9
+    assert np.max(np.abs(x[WL.L:] - ref_img)) < 1e-9
+
+
+def test_head_closed_form_on_the_image_rows():
+    """A step whose gates are zero leaves x = embed(); the gather W_out then
+    reads feature 7c + 3 of each IMAGE row, divided by the row's RMS (over all
+    H features, eps 1e-6), times norm_out at that feature, plus b_out[c].  The
+    reference below is that closed form written from X alone: it fails if
+    the head reads the text rows, drops norm_out or b_out, or normalises
+    over the wrong axis."""
+    sw, bw = _structured_shared()
+    H = WL.hidden
+    for chunk in (1, 3):                        # zero gates (reading S2)
+        sw["w_mod"] = sw["w_mod"].copy(); sw["b_mod"] = sw["b_mod"].copy()
+        sw["w_mod"][chunk * H:(chunk + 1) * H] = 0
+        sw["b_mod"][chunk * H:(chunk + 1) * H] = 0
+    X = qs.img_tokens(WL).astype(np.float64)
+    E = qs.txt_feats(WL)
+    tc, ts, ic, is_ = _rows()
+    vel = dit.dit_step(sw, [bw], WL.L, X.astype(np.float32), E, 0.7, tc, ts, ic, is_, WL.heads)
+    # image row r of x: b_img = -50 - j everywhere, plus X[r, c] at feature 5c + 2
+    j = np.arange(H)
+    x_img = np.tile(-50.0 - j, (WL.N, 1))
+    x_img[:, 5 * np.arange(64) + 2] += X
+    inv_rms = 1.0 / np.sqrt(np.mean(x_img * x_img, axis=1) + 1e-6)
+    f = 7 * np.arange(64) + 3
+    g = (1.0 + 0.01 * f).astype(np.float32).astype(np.float64)       # norm_out as stored (fp32)
+    ref = x_img[:, f] * inv_rms[:, None] * g[None, :] + (1000.0 + np.arange(64))[None, :]
+    assert np.max(np.abs(vel - ref)) < 1e-9
+
+
+@pytest.mark.parametrize("old,new", [
+    ('sw["w_txt"].astype(dtype).T', 'sw["w_txt"].astype(dtype)'),                 # transposed W_txt
+    (' + sw["b_txt"].astype(dtype)', ''),                                          # dropped b_txt
+    ('zero_center_rms_norm(txt_feats.astype(dtype), sw["txt_norm"])',
+     'rms_norm(txt_feats.astype(dtype), sw["txt_norm"])'),                         # weight not zero-centred
+    ('sw["w_img"].astype(dtype).T', 'sw["w_img"].astype(dtype).T[:, ::-1]'),       # features reversed
+])
+def test_negative_controls_break_the_text_projection_pin(old, new):
+    bad = planted(dit.embed, old, new)
+    sw, _ = _structured_shared()
+    D = WL.txt_dim
+    E = np.zeros((WL.L, D), np.float32)
+    E[np.arange(WL.L), np.arange(WL.L) * 3] = 2.0
+    X = qs.img_tokens(WL)
+    good = dit.embed(sw, X, E)
+    assert np.max(np.abs(bad(sw, X, E) - good)) > 1e-3
+
+
+@pytest.mark.parametrize("plant", ["text rows", "no norm_out", "no b_out"])
+def test_negative_controls_break_the_head_pin(plant):
+    sw, bw = _structured_shared()
+    H = WL.hidden
+    for chunk in (1, 3):
+        sw["w_mod"] = sw["w_mod"].copy(); sw["b_mod"] = sw["b_mod"].copy()
+        sw["w_mod"][chunk * H:(chunk + 1) * H] = 0
+        sw["b_mod"][chunk * H:(chunk + 1) * H] = 0
+    X, E = qs.img_tokens(WL), qs.txt_feats(WL)
+    tc, ts, ic, is_ = _rows()
+    args = (sw, [bw], WL.L, X, E, 0.7, tc, ts, ic, is_, WL.heads)
+    good = dit.dit_step(*args)
+    if plant == "text rows":
+        step = planted(dit.dit_step, "vel = head(sw, x[L_rows:])", "vel = head(sw, x[:x.shape[0] - L_rows])")
+    else:
+        old = 'rms_norm(x_img, sw["norm_out"])' if plant == "no norm_out" else ' + sw["b_out"].astype(dt)'
+        new = 'rms_norm(x_img, np.ones_like(sw["norm_out"]))' if plant == "no norm_out" else ''
+        step = step_with(head=planted(dit.head, old, new))
+    assert np.max(np.abs(step(*args) - good)) > 1e-3
