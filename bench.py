@@ -18,8 +18,13 @@ roofline fraction of the dominant kernel, the CPU oracle's throughput on a
 bounded sample (one image-only block, scaled to a step), and, as an extra,
 true CFG on the same workload (a negative prompt of half the length in a
 second K/V slot, both branches through every block at once), the
-first-block cache (Fast mode) and the 36-layer text encoder on the 1024^2
-prompt."""
+first-block cache (Fast mode), the 36-layer text encoder on the 1024^2
+prompt, and the other workloads on the same weights: one full-width block
+(L 22, N 256: HBM-bound, reported against the HBM peak), the 384^2 step
+(L 494, N 576: where text is 46% of the joint sequence and reuse matters
+most) and the 2048^2 step (L 512, N 16384: attention over 16896 tokens).
+The CPU baseline is the oracle in fp32 numpy on a bounded sample of every
+workload (block 0 of a joint and of an image-only step, scaled)."""
 from __future__ import annotations
 
 import argparse
@@ -53,6 +58,8 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-cfg", action="store_true", help="skip the true-CFG and first-block-cache extras")
     p.add_argument("--no-encoder", action="store_true", help="skip the text-encoder extra")
+    p.add_argument("--no-workloads", action="store_true",
+                   help="skip the other workloads (one full-width block, 384^2, 2048^2)")
     p.add_argument("--only-encoder", action="store_true",
                    help="run only the text-encoder measurement and print its JSON (for profiling)")
     p.add_argument("--threads", type=int, default=16, help="host threads for weight generation")
@@ -124,19 +131,9 @@ def calibrate():
     print(json.dumps({"calibration": "MI355X", **res}))
 
 
-CPU_SAMPLE_S = 10.0   # seconds of oracle work the CPU baseline times at least
-CPU_SAMPLE_MAX_BLOCKS = 4
-
-
-def cpu_baseline(wl):
-    """The oracle as it stands (numpy, float64) on image-only blocks of the
-    workload (text K/V of the right shape from the seeded generator): blocks
-    0, 1, ... with their own weights, each timed with perf_counter, until at
-    least CPU_SAMPLE_S seconds are timed (at most CPU_SAMPLE_MAX_BLOCKS), and
-    the mean scaled to one step of n_blocks blocks."""
-    import qi_synth as qs
-    from oracle import dit
-    blas = "unknown"
+def host_info():
+    """CPU model, core count and the BLAS numpy uses (threads it runs)."""
+    blas, cores = "unknown", os.cpu_count()
     try:
         from threadpoolctl import threadpool_info
         info = [i for i in threadpool_info() if i.get("user_api") == "blas"]
@@ -144,61 +141,281 @@ def cpu_baseline(wl):
         if info:
             blas = f"{info[0].get('internal_api', '?')} {info[0].get('version', '')}".strip()
     except Exception:  # pragma: no cover
-        cores = os.cpu_count()
+        pass
     cpu_model = "unknown"
     try:
         with open("/proc/cpuinfo") as f:
             cpu_model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), "unknown")
     except OSError:  # pragma: no cover
         pass
-    H, N, L = wl.hidden, wl.N, wl.L
-    x = qs.normal_array((N, H), seed=31).astype(np.float64)
-    mod = qs.normal_array((2, 4 * H), seed=32, scale=0.5).astype(np.float64)
-    k_txt = qs.normal_array((wl.heads, L, 128), seed=33).astype(np.float64)
-    v_txt = qs.normal_array((wl.heads, L, 128), seed=34).astype(np.float64)
-    _, _, ic, is_ = dit.rope_rows(L, wl.h, wl.w)
-    dt, nb = 0.0, 0
-    while nb < min(CPU_SAMPLE_MAX_BLOCKS, wl.n_blocks) and (nb == 0 or dt < CPU_SAMPLE_S):
-        bw = qs.weights_as_f32(qs.block_weights(wl, nb, threads=8))
+    return {"cpu_model": cpu_model, "nproc": os.cpu_count(), "blas": blas, "cores": int(cores)}
+
+
+def cpu_oracle_config(wl, joint_block=True):
+    """The oracle as it stands, in fp32 numpy, on one workload: the shared
+    part of a step (modulation rows, embed, head) and block 0 on the step's
+    real input -- a joint pass over [text | image] and an image-only pass on
+    the text K/V the joint pass captured -- each timed once with
+    perf_counter; a step is the shared part plus n_blocks blocks (every block
+    has the same shape and work).  joint_block=False skips the joint block
+    (its time is then not reported)."""
+    import qi_synth as qs
+    from oracle import dit
+    f32 = np.float32
+    H, L, N = wl.hidden, wl.L, wl.N
+    sw = qs.weights_as_f32(qs.shared_weights(wl, as_bf16=wl.bf16_weights, threads=8))
+    bw = qs.weights_as_f32(qs.block_weights(wl, 0, as_bf16=wl.bf16_weights, threads=8))
+    X, E = qs.img_tokens(wl), qs.txt_feats(wl)
+    tc, ts, ic, is_ = dit.rope_rows(L, wl.h, wl.w)
+    t = f32(0.7)
+    t0 = time.perf_counter()
+    m_txt, m_img = dit.modulation_rows(sw["w_mod"], sw["b_mod"], t, H, f32)
+    x = dit.embed(sw, X, E, f32)
+    dit.head(sw, x[L:])
+    t_shared = time.perf_counter() - t0
+    out = {"shared_s": round(t_shared, 3)}
+    if joint_block:
+        cos, sin = np.concatenate([tc, ic]), np.concatenate([ts, is_])
         t0 = time.perf_counter()
-        dit.dit_block(x, 0, bw, mod[0], mod[1], ic, is_, wl.heads, kv_text=(k_txt, v_txt))
-        dt += time.perf_counter() - t0
-        nb += 1
-    step_s = dt / nb * wl.n_blocks
-    return {"value": 1.0 / step_s, "unit": "steps/s", "cores": int(cores), "kind": "oracle",
-            "cpu_model": cpu_model, "nproc": os.cpu_count(), "blas": blas,
-            "sample": f"{nb} of {wl.n_blocks} blocks, image-only pass (T={N}, L={L} cached), float64 numpy; "
-                      f"{dt:.1f} s timed, {dt / nb:.2f} s per block, scaled x{wl.n_blocks}"}
+        _, kv = dit.dit_block(x, L, bw, m_txt, m_img, cos, sin, wl.heads)
+        out["joint_block_s"] = round(time.perf_counter() - t0, 3)
+    else:
+        kv = tuple(qs.normal_array((wl.heads, L, 128), seed=33 + i) for i in range(2))
+    t0 = time.perf_counter()
+    dit.dit_block(x[L:], 0, bw, m_txt, m_img, ic, is_, wl.heads, kv_text=kv)
+    out["image_only_block_s"] = round(time.perf_counter() - t0, 3)
+    nb = wl.n_blocks
+    out["image_only_step_s"] = round(t_shared + nb * out["image_only_block_s"], 2)
+    if joint_block:
+        out["joint_step_s"] = round(t_shared + nb * out["joint_block_s"], 2)
+    return out
 
 
-def kernel_code_text(src: str) -> str:
-    """The kernel sources without comments and with whitespace runs collapsed:
-    what the counters' validity depends on (a comment edit changes no kernel)."""
-    import re
-    src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
-    src = re.sub(r"//[^\n]*", " ", src)
-    return " ".join(src.split())
+def cpu_baseline(wl4, extra_workloads=(2, 3, 5)):
+    """The CPU oracle's throughput on the benchmark's workload (1024^2) as
+    the same 40-step loop the GPU runs (1 joint + 39 image-only steps), from
+    the bounded sample of cpu_oracle_config, plus the same figures for the
+    other workloads (the 2048^2 one image-only only: its joint block would
+    materialise 35 GB of fp32 scores)."""
+    import qi_synth as qs
+    info = host_info()
+    per = {}
+    c4 = cpu_oracle_config(wl4)
+    per[wl4.name] = c4
+    for k in extra_workloads:
+        wl = qs.workload(k)
+        per[wl.name] = cpu_oracle_config(wl, joint_block=(k != 5))
+    loop_s = (c4["joint_step_s"] + 39 * c4["image_only_step_s"]) / 40
+    log(f"cpu oracle (fp32): {loop_s:.1f} s per loop step at {wl4.name}")
+    return {"value": 1.0 / loop_s, "unit": "steps/s", "cores": info["cores"], "kind": "oracle",
+            "cpu_model": info["cpu_model"], "nproc": info["nproc"], "blas": info["blas"],
+            "sample": f"oracle in fp32 numpy: the shared part and block 0 of a joint and of an image-only step of "
+                      f"{wl4.name}, each timed once; step = shared + {wl4.n_blocks} blocks; value = 40 / (joint step "
+                      f"+ 39 image-only steps)", "per_workload": per}
 
 
 def measured_traffic(kind: str):
     """HBM bytes per image-only launch of `kind` from the committed rocprofv3
     counter summary (FETCH_SIZE / WRITE_SIZE scaled by a 1 GiB copy), or None
     when the kernel sources have changed since the counters were taken."""
-    import hashlib
+    from block_causal_attention_qi_amd.profile_summary import kernel_source_sha256
     path = os.path.join(ROOT, "profiles", "dit32_1024px_hbm_traffic.json")
     try:
         rec = json.load(open(path))
     except (OSError, ValueError):
         return None, "no counter summary"
-    csrc = os.path.join(ROOT, "block_causal_attention_qi_amd", "csrc")
-    src = "".join(open(os.path.join(csrc, f)).read()
-                  for f in ("common.hpp", "gemm.hpp", "attention_args.hpp", "attention.hpp", "elementwise.hpp"))
-    if hashlib.sha256(kernel_code_text(src).encode()).hexdigest() != rec.get("kernel_source_sha256"):
+    if kernel_source_sha256() != rec.get("kernel_source_sha256"):
         return None, "kernels changed since the counters were taken"
     ent = rec.get("kernels", {}).get(kind, {}).get("image-only")
     if not ent:
         return None, "kernel not in the counter summary"
     return int(ent["hbm_bytes"]), "profiles/dit32_1024px_hbm_traffic.json"
+
+
+def measure_workload(qi, qs, wl, model, loop_steps, n_img, n_joint=3):
+    """One workload on the device model (a reported extra): a denoising loop
+    of loop_steps steps (step 1 joint with capture, then image-only steps on
+    the cache, each followed by the Euler update) timed with events; the
+    first call; the median of n_joint warm joint steps and of n_img warm
+    image-only steps, each timed alone; per-kernel durations over n_img
+    image-only steps with the library's event timer; FLOP and byte rates from
+    the FLOP model."""
+    import torch
+
+    from block_causal_attention_qi_amd import flops
+    dev = "cuda"
+    H, N, L, nb = wl.hidden, wl.N, wl.L, wl.n_blocks
+    dims = model.dims
+    x0 = torch.from_numpy(qs.img_tokens(wl)).to(dev)
+    txt = torch.from_numpy(qs.txt_feats(wl)).to(dev)
+    rope = [torch.from_numpy(a).to(dev) for a in qi.rope_tables(L, wl.h, wl.w)]
+    sig, ts = qi.flow_sigmas(40, N)
+    tin = [np.float32(ts[i]) / np.float32(1000) for i in range(40)]
+    ws = qi.Workspace(dims, L, N, dev)
+    cache = qi.KVCache(dims, L, dev)
+    vel = torch.empty((N, 64), dtype=torch.float32, device=dev)
+    x = torch.empty_like(x0)
+
+    def step(i):
+        k = i % 40
+        if k == 0:
+            qi.text_kv_capture(model, L, N, x, txt, tin[k], *rope, cache, vel, ws)
+        else:
+            qi.dit_step(model, L, N, x, None, tin[k], None, None, rope[2], rope[3], vel, ws, cache)
+        qi.euler_update(x, vel, sig[k], sig[k + 1])
+
+    def timed(fn):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1)
+
+    x.copy_(x0)
+    torch.cuda.synchronize()
+    first_ms = timed(lambda: step(0))
+
+    def loop():
+        x.copy_(x0)
+        for i in range(loop_steps):
+            step(i)
+    loop()                                     # warm
+    loop_ms = timed(loop)
+    joint_ms = float(np.median([timed(lambda: (x.copy_(x0), step(0))) for _ in range(n_joint)]))
+    img_ms = float(np.median([timed(lambda i=i: step(i)) for i in range(1, 1 + n_img)]))
+    qi.timing_begin(4096 * 4)
+    for i in range(1, 1 + n_img):
+        step(i)
+    timing = qi.timing_end()
+    if not torch.isfinite(vel).all():
+        raise RuntimeError(f"non-finite vel at {wl.name}")
+    sh_img = flops.Shape(H, wl.ffn, L, N, nb, wl.txt_dim, joint=False)
+    sh_joint = flops.Shape(H, wl.ffn, L, N, nb, wl.txt_dim, joint=True)
+    work = flops.kernel_work(sh_img)
+    kern = {}
+    for kind, (ms, cnt) in timing.items():
+        if cnt == 0 or kind not in work:
+            continue
+        ent = {"avg_us": round(ms / cnt * 1e3, 2)}
+        f, b = work[kind]
+        if f and kind.startswith(("gemm", "attention")):
+            tf = f / (ms / cnt * 1e-3) / 1e12
+            ent.update(tflops=round(tf, 1), frac_bf16_peak=round(tf / flops.PEAK_BF16_TFLOPS, 4))
+        elif b:
+            ent.update(gbs=round(b / (ms / cnt * 1e-3) / 1e9, 1))
+        kern[kind] = ent
+    gemm_ms = sum(timing[k][0] for k in timing if k.startswith("gemm")) / n_img
+    gemm_f = sum(work[k][0] * timing[k][1] for k in work if k.startswith("gemm") and k in timing) / n_img
+    attn_ms = timing["attention"][0] / n_img
+    attn_f = work["attention"][0] * nb
+    out = {"workload": wl.name, "blocks": nb, "L": L, "N": N,
+           "loop": f"{loop_steps} steps: 1 joint + {loop_steps - 1} image-only, Euler update each",
+           "loop_steps_per_s": round(loop_steps / (loop_ms * 1e-3), 3),
+           "first_call_joint_step_ms": round(first_ms, 3),
+           f"joint_step_ms_median_of_{n_joint}": round(joint_ms, 3),
+           f"image_only_step_ms_median_of_{n_img}": round(img_ms, 3),
+           "reuse_speedup_joint_over_image_only": round(joint_ms / img_ms, 3),
+           "ms_per_block_image_only": round(img_ms / nb, 4),
+           "step_tflops_image_only": round(flops.step_flops(sh_img) / (img_ms * 1e-3) / 1e12, 1),
+           "step_tflops_joint": round(flops.step_flops(sh_joint) / (joint_ms * 1e-3) / 1e12, 1),
+           "gemm_tflops_image_only": round(gemm_f / (gemm_ms * 1e-3) / 1e12, 1),
+           "gemm_mfma_frac": round(gemm_f / (gemm_ms * 1e-3) / 1e12 / flops.PEAK_BF16_TFLOPS, 4),
+           "attention_tflops_image_only": round(attn_f / (attn_ms * 1e-3) / 1e12, 1),
+           "attention_mfma_frac": round(attn_f / (attn_ms * 1e-3) / 1e12 / flops.PEAK_BF16_TFLOPS, 4),
+           "kernels_image_only": kern}
+    # attention over the joint pass's L + N keys (text rows causal), one launch per block
+    qi.timing_begin(4096)
+    x.copy_(x0)
+    step(0)
+    tj = qi.timing_end()
+    aj = flops.kernel_work(sh_joint)["attention"][0] * nb / (tj["attention"][0] * 1e-3) / 1e12
+    out["attention_tflops_joint"] = round(aj, 1)
+    out["attention_joint_tokens"] = L + N
+    # the joint step's algorithmic bytes against the HBM peak (what bounds a
+    # one-block step at small T)
+    jb = flops.step_bytes(sh_joint)
+    out["joint_step_bytes"] = jb
+    out["joint_step_gbs"] = round(jb / (joint_ms * 1e-3) / 1e9, 1)
+    out["joint_step_frac_hbm_peak"] = round(jb / (joint_ms * 1e-3) / 1e9 / flops.PEAK_HBM_GBS, 4)
+    log(f"{wl.name}: {out['loop_steps_per_s']} steps/s over the loop, joint {joint_ms:.3f} ms, "
+        f"image-only {img_ms:.3f} ms")
+    return out
+
+
+def profiled_duration(kind: str):
+    """Average duration (us) of `kind`'s image-only launches in the committed
+    rocprofv3 kernel trace (profiles/dit32_1024px_kernel_trace.json), or None
+    when the kernel sources have changed since the trace was taken."""
+    from block_causal_attention_qi_amd.profile_summary import kernel_source_sha256
+    path = os.path.join(ROOT, "profiles", "dit32_1024px_kernel_trace.json")
+    try:
+        rec = json.load(open(path))
+    except (OSError, ValueError):
+        return None, "no kernel-trace summary"
+    if kernel_source_sha256() != rec.get("kernel_source_sha256"):
+        return None, "kernels changed since the trace was taken"
+    ent = rec.get("kinds", {}).get(kind, {}).get("image-only")
+    if not ent:
+        return None, "kernel not in the trace summary"
+    return float(ent["avg_us"]), "profiles/dit32_1024px_kernel_trace.json"
+
+
+class ClockSampler:
+    """Samples the GPU's current shader clock (the level marked '*' in the
+    driver's pp_dpm_sclk file) from a host thread while running; the mean of
+    the samples is the clock the timed region ran at.  Reports None where the
+    file is not readable."""
+
+    def __init__(self, period_s: float = 0.005):
+        import glob
+        self.period = period_s
+        self.path = next((p for p in sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk"))
+                          if self._read(p) is not None), None)
+        self.samples = []
+        self._stop = None
+        self._thread = None
+
+    @staticmethod
+    def _read(path):
+        try:
+            with open(path) as f:
+                for ln in f:
+                    if "*" in ln:
+                        v = ln.split(":", 1)[1].strip().rstrip("*").strip().lower()
+                        return float(v.replace("mhz", "").strip())
+        except (OSError, ValueError, IndexError):
+            return None
+        return None
+
+    def __enter__(self):
+        import threading
+        if self.path is None:
+            return self
+        self._stop = threading.Event()
+
+        def run():
+            while not self._stop.is_set():
+                v = self._read(self.path)
+                if v is not None:
+                    self.samples.append(v)
+                self._stop.wait(self.period)
+        self._thread = threading.Thread(target=run, daemon=True)
+        self._thread.start()
+        return self
+
+    def __exit__(self, *exc):
+        if self._thread is not None:
+            self._stop.set()
+            self._thread.join()
+
+    def summary(self):
+        if not self.samples:
+            return None
+        a = np.asarray(self.samples)
+        return {"mean_mhz": round(float(a.mean()), 1), "median_mhz": round(float(np.median(a)), 1),
+                "min_mhz": round(float(a.min()), 1), "max_mhz": round(float(a.max()), 1), "samples": int(a.size),
+                "source": self.path}
 
 
 def measure_cfg(qi, qs, wl, model, dims, x0, rope, sig, tin, img_step_ms):
@@ -424,11 +641,12 @@ def main():
     n_img = max(3, min(K - 1, 10))
     qi.timing_begin(4096 * 4)
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    ev0.record()
-    for i in range(1, 1 + n_img):
-        step(i)
-    ev1.record()
-    timing = qi.timing_end()
+    with ClockSampler() as clock:
+        ev0.record()
+        for i in range(1, 1 + n_img):
+            step(i)
+        ev1.record()
+        timing = qi.timing_end()
     img_step_ms = ev0.elapsed_time(ev1) / n_img
     # warm calls, each timed on its own: 10 image-only steps and the joint step
     x.copy_(x0)
@@ -482,6 +700,14 @@ def main():
                 "unit": "GB/s", "frac": round(ach / flops.PEAK_HBM_GBS, 4), "traffic": None,
                 "bytes_per_launch": db, "avg_launch_us": round(dms * 1e3, 2)}
     roof["traffic"], roof["traffic_source"] = measured_traffic(dom)
+    prof_us, roof["profile_source"] = profiled_duration(dom)
+    roof["profile_avg_launch_us"] = prof_us
+    if prof_us:
+        pa = (df / (prof_us * 1e-6) / 1e12) if roof["bound"] == "mfma" else (db / (prof_us * 1e-6) / 1e9)
+        roof["frac_from_profile"] = round(pa / roof["peak"], 4)
+    else:
+        roof["frac_from_profile"] = None
+    roof["sclk_during_kernel_timing"] = clock.summary()
     gemm_ms = sum(timing[k][0] for k in timing if k.startswith("gemm")) / n_img
     gemm_f = sum(work[k][0] * timing[k][1] for k in work if k.startswith("gemm") and k in timing) / n_img
     attn_ms = timing["attention"][0] / n_img
@@ -489,7 +715,15 @@ def main():
     cfg = None if args.no_cfg else measure_cfg(qi, qs, wl, model, dims, x0, rope, sig, tin, img_step_ms)
     fbc = None if args.no_cfg else measure_fbc(qi, qs, wl, model, dims, x0, rope, sig, tin, img_step_ms)
     enc = None if args.no_encoder else measure_encoder(qi, qs, args.threads)
-    cpu = None if args.no_cpu_baseline else cpu_baseline(wl)
+    others = None
+    if not args.no_workloads and args.workload == 4:
+        others = {}
+        for k, view, loop_steps, n_img, n_joint in ((2, model.prefix(1), 40, 10, 5), (3, model, 40, 10, 5),
+                                                     (5, model, 6, 3, 2)):
+            w2 = qs.workload(k)
+            assert view.dims.n_blocks == w2.n_blocks and w2.hidden == H
+            others[w2.name] = measure_workload(qi, qs, w2, view, loop_steps, n_img, n_joint)
+    cpu = None if args.no_cpu_baseline else cpu_baseline(wl, (2, 3, 5) if args.workload == 4 else ())
 
     out = {
         "metric": METRIC,
@@ -523,6 +757,7 @@ def main():
         "cfg": cfg,
         "first_block_cache": fbc,
         "text_encoder": enc,
+        "workloads": others,
     }
     print(json.dumps(out))
 

@@ -80,6 +80,22 @@ def step_flops(s: Shape, include_shared: bool = False) -> int:
     return f
 
 
+def launches_per_step(s: Shape) -> dict:
+    """Launches of each kernel kind in one step (two norms per block)."""
+    n = {k: s.n_blocks for k in ("gemm_qkv", "attention", "gemm_o", "gemm_gate_up", "gemm_down")}
+    n.update(norm_mod=2 * s.n_blocks, modulation=1, img_embed=1, head=1)
+    if s.joint:
+        n.update(txt_norm=1, gemm_txt=1)
+    return n
+
+
+def step_bytes(s: Shape) -> int:
+    """Algorithmic HBM bytes of one step: every kernel's minimum traffic
+    (kernel_work) times its launches per step, the Euler update excluded."""
+    kw = kernel_work(s)
+    return sum(kw[k][1] * n for k, n in launches_per_step(s).items())
+
+
 def encoder_flops(hidden: int, heads: int, kv_heads: int, ffn: int, n_layers: int, L: int,
                   head_dim: int = 128) -> dict:
     """Algorithmic FLOPs of one causal forward of the text encoder over L

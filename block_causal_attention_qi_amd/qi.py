@@ -127,6 +127,29 @@ class DeviceModel:
     def block_struct(self, b: int) -> QiBlockW:
         return self._bw[b]
 
+    def prefix(self, n_blocks: int) -> "DeviceModel":
+        """The model made of this one's first n_blocks blocks (all device
+        weights shared; a one-block workload of the same width and seeds is
+        block 0 of the deeper ones)."""
+        if not 1 <= n_blocks <= self.dims.n_blocks:
+            raise ValueError(f"n_blocks {n_blocks} outside 1..{self.dims.n_blocks}")
+        m = DeviceModel.__new__(DeviceModel)
+        d = self.dims
+        m.dims = QiDims(d.hidden, d.heads, d.head_dim, d.ffn, n_blocks, d.txt_dim)
+        m.device, m.shared, m.blocks, m._bw, m.w = self.device, self.shared, self.blocks[:n_blocks], self._bw, self.w
+        return m
+
+    def with_shared(self, shared: dict) -> "DeviceModel":
+        """A model that shares this one's device block weights and has its own
+        copies of the shared weights (modulation, embed, text projection,
+        head)."""
+        m = DeviceModel.__new__(DeviceModel)
+        m.dims, m.device, m.blocks, m._bw = self.dims, self.device, self.blocks, self._bw
+        m.shared = {k: to_device(_as_dev(k, shared[k]), self.device) for k in self.SHARED_KEYS}
+        sh = m.shared
+        m.w = QiModelW(ctypes.cast(m._bw, ctypes.POINTER(QiBlockW)), *(_ptr(sh[k]) for k in self.SHARED_KEYS))
+        return m
+
 
 def _as_dev(name: str, a: np.ndarray) -> np.ndarray:
     """Linear weights go to the device as bf16 bits; fp32 arrays given for a

@@ -27,3 +27,24 @@ def pytest_collection_modifyitems(config, items):
     for it in items:
         if "gpu" in it.keywords:
             it.add_marker(skip)
+
+
+@pytest.fixture(scope="session")
+def model32():
+    """The 32-block, hidden-4096 model shared by the 384^2, 1024^2 and 2048^2
+    workloads (same widths, depth and seeds), uploaded once per session:
+    {"dims", "model" (device), "blocks" (host bf16 bits per block), "shared"}."""
+    import concurrent.futures as cf
+
+    import block_causal_attention_qi_amd as qi
+    import qi_synth as qs
+    from tests.gpu_util import log
+    wl = qs.workload(4)
+    log("generating 32 blocks of bf16 weights")
+    with cf.ThreadPoolExecutor(16) as ex:
+        blocks = list(ex.map(lambda b: qs.block_weights(wl, b, as_bf16=True, threads=1), range(wl.n_blocks)))
+    shared = qs.shared_weights(wl, as_bf16=True)
+    dims = qi.make_dims(wl.hidden, wl.ffn, wl.n_blocks, wl.txt_dim)
+    model = qi.DeviceModel(dims, shared, blocks)
+    log("weights on device")
+    return {"dims": dims, "model": model, "blocks": blocks, "shared": shared}

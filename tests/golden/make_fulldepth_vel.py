@@ -1,0 +1,103 @@
+"""Writes the oracle's whole-step velocities of the 32-block workloads, the
+stored expected values of tests/test_gpu_fulldepth.py.
+
+    python tests/golden/make_fulldepth_vel.py [--only NAME]
+
+Calls only the oracle (oracle/dit.py) and the seeded input generators
+(qi_synth); nothing here touches the HIP library.  For each case it runs one
+joint DiT step (the DiT graph of the host contract, s.1) three times:
+  exact     -- the definition in float64 (the oracle's default);
+  bf16_f64  -- the bf16-compute reading (every matmul operand rounded once to
+               bf16), float64 accumulation;
+  bf16_f32  -- the same rounding points, float32 accumulation: a second
+               legitimate order of the same bf16 arithmetic, whose distance to
+               bf16_f64 is the cross-order spread that bf16 rounding alone
+               produces through the stack.
+Cases: the 384^2 workload (L 494, N 576) at sampler steps 0, 20 and 39, the
+1024^2 workload (L 407, N 4096) at step 20, and the 384^2 workload at step 20
+with the shared modulation Linear (weight and bias) scaled by 1/4 and 1/8
+(powers of two, so the scaled bf16 weights stay exact; the same weights
+otherwise: a modulation closer to the identity, as in a trained DiT).  Step i
+uses the timestep of the workload's 40-step schedule and the latent drawn
+with seed 1234 + i, the other inputs the workload's own.
+
+Output: tests/golden/vel_<case>.npz with arrays exact, bf16_f64, bf16_f32
+([N, 64] float32) and a JSON string `meta`."""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(os.path.dirname(HERE))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import qi_synth as qs  # noqa: E402
+from oracle import dit  # noqa: E402
+
+CASES = [
+    # name, workload id, sampler step, modulation scale
+    ("dit32-384px-step0", 3, 0, 1.0),
+    ("dit32-384px-step20", 3, 20, 1.0),
+    ("dit32-384px-step39", 3, 39, 1.0),
+    ("dit32-384px-step20-mod0.25", 3, 20, 0.25),
+    ("dit32-384px-step20-mod0.125", 3, 20, 0.125),
+    ("dit32-1024px-step20", 4, 20, 1.0),
+]
+
+
+def case_inputs(wl_id: int, step: int, mod_scale: float):
+    """The case's workload, shared weights (fp32 values), inputs and t."""
+    wl = qs.workload(wl_id)
+    sw = qs.weights_as_f32(qs.shared_weights(wl, as_bf16=True))
+    if mod_scale != 1.0:
+        assert mod_scale in (0.5, 0.25, 0.125), "a power of two keeps the bf16 weights exact"
+        sw = dict(sw)
+        sw["w_mod"] = (sw["w_mod"].astype(np.float64) * mod_scale).astype(np.float32)
+        sw["b_mod"] = (sw["b_mod"].astype(np.float64) * mod_scale).astype(np.float32)
+    _, ts = dit.flow_sigmas(40, wl.N)
+    t = dit.timestep_input(ts, step)
+    return wl, sw, qs.img_tokens(wl, seed=qs.NOISE_SEED + step), qs.txt_feats(wl), t
+
+
+def run_case(name, wl_id, step, mod_scale):
+    wl, sw, X, E, t = case_inputs(wl_id, step, mod_scale)
+    tc, tsn, ic, is_ = dit.rope_rows(wl.L, wl.h, wl.w)
+
+    def blocks():
+        for b in range(wl.n_blocks):
+            yield qs.weights_as_f32(qs.block_weights(wl, b, as_bf16=True, threads=8))
+
+    out = {}
+    for mode, dtype, bf16 in (("exact", np.float64, False), ("bf16_f64", np.float64, True),
+                              ("bf16_f32", np.float32, True)):
+        t0 = time.time()
+        vel = dit.dit_step(sw, blocks, wl.L, X, E, t, tc, tsn, ic, is_, wl.heads, dtype=dtype, bf16=bf16)
+        out[mode] = vel.astype(np.float32)
+        print(f"{name} {mode}: {time.time() - t0:.0f} s", flush=True)
+    meta = {"case": name, "workload": wl.name, "sampler_step": step, "t": float(t), "mod_scale": mod_scale,
+            "img_seed": qs.NOISE_SEED + step, "script": "tests/golden/make_fulldepth_vel.py",
+            "drift_bf16_vs_exact": dit.rel_l2(out["bf16_f64"], out["exact"]),
+            "spread_bf16_f32_vs_f64": dit.rel_l2(out["bf16_f32"], out["bf16_f64"])}
+    np.savez_compressed(os.path.join(HERE, f"vel_{name}.npz"), meta=json.dumps(meta), **out)
+    print(json.dumps(meta), flush=True)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--only", default=None)
+    args = ap.parse_args()
+    for c in CASES:
+        if args.only and c[0] != args.only:
+            continue
+        run_case(*c)
+
+
+if __name__ == "__main__":
+    main()

@@ -5,7 +5,8 @@ import os
 import subprocess
 import sys
 
-import bench
+import bench  # noqa: F401  (importable without a GPU)
+from block_causal_attention_qi_amd.profile_summary import _pass_of, kernel_code_text, kind_of
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
@@ -22,9 +23,9 @@ def test_kernel_fingerprint_ignores_comments_and_layout_only():
     src = "int f(int a) {\n  // scale\n  return a * 2; /* twice */\n}\n"
     same = "int f(int a) { /* other words */ return a * 2;   // changed comment\n}"
     other = "int f(int a) {\n  // scale\n  return a * 3; /* twice */\n}\n"
-    assert bench.kernel_code_text(src) == bench.kernel_code_text(same)
-    assert bench.kernel_code_text(src) != bench.kernel_code_text(other)
-    assert "scale" not in bench.kernel_code_text(src)  # the comments are gone
+    assert kernel_code_text(src) == kernel_code_text(same)
+    assert kernel_code_text(src) != kernel_code_text(other)
+    assert "scale" not in kernel_code_text(src)  # the comments are gone
 
 
 def test_committed_counter_summary_names_its_fingerprint_and_kernels():
@@ -34,3 +35,15 @@ def test_committed_counter_summary_names_its_fingerprint_and_kernels():
     for kind in ("gemm_gate_up", "gemm_qkv", "gemm_down", "gemm_o", "attention"):
         ent = rec["kernels"][kind]["image-only"]
         assert int(ent["hbm_bytes"]) > 0
+
+
+def test_profile_summary_classifies_launches_by_name_order_and_grid():
+    assert kind_of("void gemm_bf16_large_kernel<1, 2, 4>(GemmArgs)", "attention") == "gemm_o"
+    assert kind_of("void gemm_bf16_large_kernel<1, 2, 4>(GemmArgs)", "gemm_gate_up") == "gemm_down"
+    assert kind_of("block_causal_attn_kernel(AttnBatch)", None) == "attention"
+    assert kind_of("void rmsnorm_mod_kernel<16>(float const*)", None) == "norm_mod"
+    grids = {26112, 262144, 288256}               # text norm, image-only, joint
+    assert _pass_of("norm_mod", 262144, grids) == "image-only"
+    assert _pass_of("norm_mod", 288256, grids) == "joint"
+    assert _pass_of("norm_mod", 26112, grids) == "joint (text)"
+    assert _pass_of("head", 65536, {65536}) == "both"
