@@ -21,6 +21,7 @@ QI_ERR_HIP = -7
 QI_ERR_UNSUPPORTED = -8
 QI_MODE_JOINT = 0
 QI_MODE_IMAGE_ONLY = 1
+QI_NOALLOC_SCRATCH_BYTES = 96 * 1024 * 1024
 
 
 class QiDims(Structure):
@@ -76,6 +77,8 @@ SIGNATURES = {
     "qi_dit_step": (c_int32, [_P(QiDims), _P(QiModelW), c_int32, c_int32, c_void_p, c_void_p, c_float,
                               c_void_p, c_void_p, c_void_p, c_void_p, _P(QiKvCache), c_void_p,
                               c_void_p, c_size_t, c_void_p]),
+    "qi_dit_step_noalloc": (c_int32, [_P(QiDims), _P(QiModelW), c_int32, c_int32, c_void_p, c_void_p, c_float,
+                                      c_void_p, c_void_p, c_void_p, c_void_p, _P(QiKvCache), c_void_p, c_void_p]),
     "qi_text_kv_capture": (c_int32, [_P(QiDims), _P(QiModelW), c_int32, c_int32, c_void_p, c_void_p,
                                      c_float, c_void_p, c_void_p, c_void_p, c_void_p, _P(QiKvCache),
                                      c_void_p, c_void_p, c_size_t, c_void_p]),

@@ -16,7 +16,7 @@ from ._lib import (QI_MODE_IMAGE_ONLY, QI_MODE_JOINT, QiBlockW, QiDims, QiEncDim
 
 __all__ = ["QI_MODE_JOINT", "QI_MODE_IMAGE_ONLY", "QiError", "make_dims", "rope_axis_table",
            "rope_tables", "flow_sigmas", "workspace_bytes", "kv_cache_bytes", "kv_slot_elems",
-           "DeviceModel", "KVCache", "Workspace", "dit_step", "text_kv_capture", "dit_block_fwd",
+           "DeviceModel", "KVCache", "Workspace", "dit_step", "dit_step_noalloc", "text_kv_capture", "dit_block_fwd",
            "euler_update", "modulation", "block_causal_attention", "linear_bf16", "stream_handle",
            "timing_begin", "timing_end", "KERNEL_KINDS", "cfg_workspace_bytes", "CfgWorkspace", "dit_step_cfg",
            "euler_update_cfg", "fbc_bytes", "FirstBlockCache", "dit_step_fbc", "dpmpp_2m_coeffs",
@@ -318,6 +318,17 @@ def dit_step(model: DeviceModel, L: int, N: int, img_tokens, txt_feats, t: float
                          _ptr(img_sin), ctypes.byref(cache.c) if cache is not None else None,
                          _ptr(vel), ws.ptr, ws.nbytes, stream_handle(stream))
     check(st, "qi_dit_step")
+
+
+def dit_step_noalloc(model: DeviceModel, L: int, N: int, img_tokens, txt_feats, t: float, txt_cos, txt_sin,
+                     img_cos, img_sin, vel, cache: KVCache | None = None, stream=None):
+    """qi_dit_step on the library's static per-GPU scratch (no workspace)."""
+    lib = _lib.load()
+    st = lib.qi_dit_step_noalloc(ctypes.byref(model.dims), ctypes.byref(model.w), L, N, _ptr(img_tokens),
+                                 _ptr(txt_feats), float(t), _ptr(txt_cos), _ptr(txt_sin), _ptr(img_cos),
+                                 _ptr(img_sin), ctypes.byref(cache.c) if cache is not None else None,
+                                 _ptr(vel), stream_handle(stream))
+    check(st, "qi_dit_step_noalloc")
 
 
 def text_kv_capture(model: DeviceModel, L: int, N: int, img_tokens, txt_feats, t: float, txt_cos,

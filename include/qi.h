@@ -19,7 +19,8 @@
  *   - "device" pointers are HIP device memory of the current device; "host"
  *     pointers are ordinary host memory.  The caller owns every buffer; the
  *     library allocates nothing per call and keeps no mutable global state
- *     beyond the optional kernel-timing facility at the end of this header.
+ *     beyond the optional kernel-timing facility at the end of this header
+ *     and the static per-GPU scratch of qi_dit_step_noalloc.
  *   - Linear weights use the [out, in] row-major layout, so each projection is
  *     y = x W^T.  Device pointers must be 16-byte aligned.
  *   - `stream` is a hipStream_t (NULL = the default stream).  Work is enqueued
@@ -188,6 +189,29 @@ qi_status qi_dit_step(const qi_dims *d, const qi_model_w *w, int32_t L, int32_t 
                       const float *txt_cos, const float *txt_sin, const float *img_cos,
                       const float *img_sin, const qi_kv_cache *cache, float *vel, void *ws,
                       size_t ws_bytes, void *stream);
+
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): qi_dit_step
+ * with its workspace taken from a static scratch array inside the library
+ * instead of a caller buffer.  Same arguments, same kernels and bit-identical
+ * results as qi_dit_step, minus ws / ws_bytes.  The scratch is one
+ * QI_NOALLOC_SCRATCH_BYTES (96 MiB) array per GPU, held from the library's
+ * first use on that GPU until the process ends; its device address is looked
+ * up once per device (hipGetSymbolAddress, the calling thread's current
+ * device).  The call allocates nothing and clears nothing (no kernel of the
+ * step reads workspace it has not written in the same call).  Every call on
+ * one GPU uses the same scratch: calls that may overlap on one GPU (two
+ * streams, two threads) race and must be serialised by the caller.
+ * Limit: qi_workspace_bytes(d, L, N) <= QI_NOALLOC_SCRATCH_BYTES, e.g. the
+ * 384^2 step (hidden 4096, L 494, N 576, 92 MB) fits, the 1024^2 step does
+ * not.  Errors: as qi_dit_step; QI_ERR_WORKSPACE when the request needs more
+ * scratch than that (checked before anything else is done), QI_ERR_HIP if the
+ * scratch address cannot be obtained. */
+#define QI_NOALLOC_SCRATCH_BYTES (96u * 1024u * 1024u)
+qi_status qi_dit_step_noalloc(const qi_dims *d, const qi_model_w *w, int32_t L, int32_t N,
+                              const float *img_tokens, const float *txt_feats, float timestep,
+                              const float *txt_cos, const float *txt_sin, const float *img_cos,
+                              const float *img_sin, const qi_kv_cache *cache, float *vel, void *stream);
 
 /* Step 1 of a render with reuse ([MLX] "Text K/V reuse"): the joint pass of
  * qi_dit_step that also writes every block's text K/V into cache->kv, then sets
