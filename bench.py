@@ -204,6 +204,7 @@ def cpu_baseline(wl4, extra_workloads=(2, 3, 5)):
     per[wl4.name] = c4
     for k in extra_workloads:
         wl = qs.workload(k)
+        log(f"cpu oracle (fp32) on {wl.name}")
         per[wl.name] = cpu_oracle_config(wl, joint_block=(k != 5))
     loop_s = (c4["joint_step_s"] + 39 * c4["image_only_step_s"]) / 40
     log(f"cpu oracle (fp32): {loop_s:.1f} s per loop step at {wl4.name}")

@@ -46,6 +46,30 @@ QI_DEV f32x16 mfma32x32x16(u32x4 a, u32x4 b, f32x16 c) {
 // The 4 accumulators 4j .. 4j+3 of a 32x32 MFMA result (rows 8j + 4*(l/32) + 0..3).
 QI_DEV f32x4 quad(const f32x16 &a, int j) { return f32x4{a[4 * j], a[4 * j + 1], a[4 * j + 2], a[4 * j + 3]}; }
 
+// Exact split of 8 fp32 values into three planes of 8 bf16 (16 bytes each):
+// a = a0 + a1 + a2 with a0 = bf16(a), a1 = bf16(a - a0), a2 = a - a0 - a1 (each
+// remainder exact in fp32, the last with at most 8 significant bits), so three
+// bf16 MFMAs against an exact bf16 operand give the fp32 product sum up to the
+// order of the fp32 additions.
+QI_DEV void split3(const f32x4 lo, const f32x4 hi, u32x4 &p0, u32x4 &p1, u32x4 &p2) {
+  float v[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  float r1[8], r2[8];
+  uint32_t a[4], b[4], c[4];
+#pragma unroll
+  for (int e = 0; e < 8; e += 2) {
+    a[e / 2] = pack_bf16x2(v[e], v[e + 1]);
+    r1[e] = v[e] - bf16_to_f32((u16)(a[e / 2] & 0xFFFF));
+    r1[e + 1] = v[e + 1] - bf16_to_f32((u16)(a[e / 2] >> 16));
+    b[e / 2] = pack_bf16x2(r1[e], r1[e + 1]);
+    r2[e] = r1[e] - bf16_to_f32((u16)(b[e / 2] & 0xFFFF));
+    r2[e + 1] = r1[e + 1] - bf16_to_f32((u16)(b[e / 2] >> 16));
+    c[e / 2] = pack_bf16x2(r2[e], r2[e + 1]);
+  }
+  p0 = u32x4{a[0], a[1], a[2], a[3]};
+  p1 = u32x4{b[0], b[1], b[2], b[3]};
+  p2 = u32x4{c[0], c[1], c[2], c[3]};
+}
+
 QI_DEV float wave_sum(float v) {
 #pragma unroll
   for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);

@@ -81,14 +81,75 @@ __global__ __launch_bounds__(256) void rmsnorm_mod_kernel(const float *x, int ld
 // The one modulation Linear shared by all blocks, evaluated for tau = 0 (text
 // rows) and the sampled t (image rows):  mod[s][n] = sum_k W[n][k] e_s[k] + b[n]
 // with the time embedding e(tau)[j] = cos(1000 tau f_j), e(tau)[H/2 + j] =
-// sin(1000 tau f_j), f_j = 10000^(-j/(H/2)).  Each workgroup builds both
-// embeddings in LDS (float64 internally, rounded once to fp32), then streams
-// 16 rows of W [rows][H] bf16 from HBM, 4 per wave.
-__global__ __launch_bounds__(256) void mod_gemv_kernel(const u16 *W, const float *b, float t, int H,
-                                                       int rows, float *mod) {
+// sin(1000 tau f_j), f_j = 10000^(-j/(H/2)).  An HBM-bound GEMV over the
+// 4H x H bf16 weight (134 MB at H = 4096): one 8-wave workgroup per block of
+// `rows_per_wg` rows (one per CU at H = 4096), so the float64 embedding --
+// built in LDS, rounded once to fp32 -- is computed once per CU.  Each wave
+// streams pairs of rows with every lane loading its NC 16-byte chunks of both
+// rows at once, and keeps the next pair's loads in flight while it sums the
+// current one; the first pair's loads are issued before the embedding is
+// built, so the float64 work hides memory latency instead of adding to it.
+// Each row's sum runs over k in the same order for any NC split.  NC =
+// ceil(H / 512); H % 256 == 0, so only the last chunk can be half covered
+// (its upper lanes load nothing and add nothing).
+template <int NC>
+QI_DEV void mod_load_pair(const u16 *W, int H, int n, int n_end, int lane, u32x4 (&w8)[2][NC]) {
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    const int k = c * 512 + lane * 8;
+    const bool in = k < H && n < n_end;
+    const int n1 = n + 1 < n_end ? n + 1 : n;
+    w8[0][c] = in ? *(const u32x4 *)(W + (size_t)n * H + k) : u32x4{0u, 0u, 0u, 0u};
+    w8[1][c] = in ? *(const u32x4 *)(W + (size_t)n1 * H + k) : u32x4{0u, 0u, 0u, 0u};
+  }
+}
+
+template <int NC>
+QI_DEV void mod_sum_pair(const u32x4 (&w8)[2][NC], const float *se, int H, int rows, int n, int n_end, int lane,
+                         const float *b, float *mod) {
+  float a[2][2] = {{0.f, 0.f}, {0.f, 0.f}};
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    const int k = c * 512 + lane * 8;
+    if (k >= H) continue;
+    const f32x4 e0a = *(const f32x4 *)(se + k), e0b = *(const f32x4 *)(se + k + 4);
+    const f32x4 e1a = *(const f32x4 *)(se + H + k), e1b = *(const f32x4 *)(se + H + k + 4);
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      float wf[8];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        wf[2 * q] = __uint_as_float(w8[r][c][q] << 16);
+        wf[2 * q + 1] = __uint_as_float(w8[r][c][q] & 0xFFFF0000u);
+      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        a[r][0] += wf[q] * e0a[q] + wf[q + 4] * e0b[q];
+        a[r][1] += wf[q] * e1a[q] + wf[q + 4] * e1b[q];
+      }
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+    const float s0 = wave_sum(a[r][0]), s1 = wave_sum(a[r][1]);
+    if (lane == 0 && n + r < n_end) {
+      mod[n + r] = s0 + b[n + r];
+      mod[rows + n + r] = s1 + b[n + r];
+    }
+  }
+}
+
+template <int NC>
+__global__ __launch_bounds__(512) void mod_gemv_kernel(const u16 *W, const float *b, float t, int H, int rows,
+                                                       int rows_per_wg, float *mod) {
   extern __shared__ float se[];  // [2][H]
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int n_end = min(rows, (blockIdx.x + 1) * rows_per_wg);
+  int n = blockIdx.x * rows_per_wg + 2 * wave;  // pairs n, n + 16, ...
+  u32x4 wa[2][NC], wb[2][NC];
+  mod_load_pair<NC>(W, H, n, n_end, lane, wa);
   const int half = H >> 1;
-  for (int j = threadIdx.x; j < half; j += 256) {
+  for (int j = threadIdx.x; j < half; j += 512) {
     const double f = pow(10000.0, -(double)j / (double)half);
     const double arg = 1000.0 * (double)t * f;
     se[j] = 1.f;
@@ -97,74 +158,61 @@ __global__ __launch_bounds__(256) void mod_gemv_kernel(const u16 *W, const float
     se[H + half + j] = (float)sin(arg);
   }
   __syncthreads();
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll 1
-  for (int rr = 0; rr < 4; ++rr) {
-    const int n = blockIdx.x * 16 + wave * 4 + rr;
-    if (n >= rows) break;
-    const u16 *wr = W + (size_t)n * H;
-    float a0 = 0.f, a1 = 0.f;
-    for (int k = lane * 8; k < H; k += 512) {
-      const u32x4 w8 = *(const u32x4 *)(wr + k);
-      const f32x4 e0a = *(const f32x4 *)(se + k), e0b = *(const f32x4 *)(se + k + 4);
-      const f32x4 e1a = *(const f32x4 *)(se + H + k), e1b = *(const f32x4 *)(se + H + k + 4);
-      float wf[8];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        wf[2 * q] = __uint_as_float(w8[q] << 16);
-        wf[2 * q + 1] = __uint_as_float(w8[q] & 0xFFFF0000u);
-      }
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        a0 += wf[q] * e0a[q] + wf[q + 4] * e0b[q];
-        a1 += wf[q] * e1a[q] + wf[q + 4] * e1b[q];
-      }
-    }
-    a0 = wave_sum(a0);
-    a1 = wave_sum(a1);
-    if (lane == 0) {
-      mod[n] = a0 + b[n];
-      mod[rows + n] = a1 + b[n];
-    }
+  for (; n < n_end; n += 32) {
+    mod_load_pair<NC>(W, H, n + 16, n_end, lane, wb);
+    mod_sum_pair<NC>(wa, se, H, rows, n, n_end, lane, b, mod);
+    if (n + 16 >= n_end) break;
+    mod_load_pair<NC>(W, H, n + 32, n_end, lane, wa);
+    mod_sum_pair<NC>(wb, se, H, rows, n + 16, n_end, lane, b, mod);
   }
 }
 
 // ----------------------------------------------------------------- embed
 // x[row0 + i][n] = sum_c X[i][c] W[n][c] + b[n]  (img-in Linear 64 -> H, fp32).
-// 16 tokens per workgroup, one output feature per thread.
+// A workgroup computes 32 tokens x 256 features, each wave 32 tokens x 64
+// features as two 32 x 32 blocks, on the bf16 matrix cores at fp32 accuracy:
+// X (fp32) is split exactly into three bf16 planes, each plane goes through
+// v_mfma_f32_32x32x16_bf16 (A = 32 tokens x 16 channels, B = 16 channels x 32
+// features of the exactly-bf16 W), so every partial product is exact and the
+// sums are fp32.  A lane's results are 32 consecutive features of the block
+// across the half-wave for each token row: 128-byte coalesced stores.
+// H % 256 == 0.
 __global__ __launch_bounds__(256) void img_embed_kernel(const float *X, int N, const u16 *W,
                                                         const float *b, int H, float *x, int ldx,
                                                         int row0) {
-  __shared__ f32x4 sX[16][16];
-  const int t0 = blockIdx.x * 16;
-  {
-    const int tok = threadIdx.x >> 4, c4 = threadIdx.x & 15;
-    const int ti = min(t0 + tok, N - 1);
-    sX[tok][c4] = ((const f32x4 *)(X + (size_t)ti * 64))[c4];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int l32 = lane & 31, hf = lane >> 5;
+  const int t0 = blockIdx.x * 32;
+  const int n0 = blockIdx.y * 256 + wave * 64;
+  // this lane's token row and its 4 x 8 channels (k steps of 16, 8 channels per half-wave)
+  const float *xr = X + (size_t)min(t0 + l32, N - 1) * 64;
+  u32x4 pa[4][3];
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    const f32x4 lo = *(const f32x4 *)(xr + 16 * ks + 8 * hf), hi = *(const f32x4 *)(xr + 16 * ks + 8 * hf + 4);
+    split3(lo, hi, pa[ks][0], pa[ks][1], pa[ks][2]);
   }
-  __syncthreads();
-  const int n = blockIdx.y * 256 + threadIdx.x;
-  if (n >= H) return;
-  float w[64];
 #pragma unroll
-  for (int q = 0; q < 8; ++q) {
-    const u32x4 w8 = *(const u32x4 *)(W + (size_t)n * 64 + q * 8);
+  for (int nb = 0; nb < 2; ++nb) {
+    const int n = n0 + 32 * nb + l32;
+    u32x4 wv[4];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      w[q * 8 + 2 * e] = __uint_as_float(w8[e] << 16);
-      w[q * 8 + 2 * e + 1] = __uint_as_float(w8[e] & 0xFFFF0000u);
+    for (int ks = 0; ks < 4; ++ks) wv[ks] = *(const u32x4 *)(W + (size_t)n * 64 + 16 * ks + 8 * hf);
+    f32x16 acc;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[e] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+      for (int p = 0; p < 3; ++p) acc = mfma32x32x16(pa[ks][p], wv[ks], acc);
+    const float bn = b[n];
+    // element i: token 8 (i / 4) + 4 hf + i % 4 of the tile, feature n
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int tok = t0 + 8 * (i >> 2) + 4 * hf + (i & 3);
+      if (tok < N) x[(size_t)(row0 + tok) * ldx + n] = acc[i] + bn;
     }
-  }
-  const float bn = b[n];
-  for (int tok = 0; tok < 16; ++tok) {
-    if (t0 + tok >= N) break;
-    float acc = 0.f;
-#pragma unroll
-    for (int c4 = 0; c4 < 16; ++c4) {
-      const f32x4 xv = sX[tok][c4];
-      acc += xv[0] * w[4 * c4] + xv[1] * w[4 * c4 + 1] + xv[2] * w[4 * c4 + 2] + xv[3] * w[4 * c4 + 3];
-    }
-    x[(size_t)(row0 + t0 + tok) * ldx + n] = acc + bn;
   }
 }
 
@@ -172,56 +220,79 @@ __global__ __launch_bounds__(256) void img_embed_kernel(const float *X, int N, c
 // vel[i][c] = sum_n (x[i][n] rsqrt(mean(x[i]^2) + eps) gamma[n]) W[c][n] + b[c],
 // c < 64, fp32 (proj_out on the image rows), evaluated as
 // b[c] + r_i sum_n (x[i][n] gamma[n]) W[c][n] with r_i the row's rsqrt factor.
-// 16 tokens per workgroup; the contraction runs on the fp32 matrix cores
-// (v_mfma_f32_16x16x4_f32: A = 16 tokens x 4 features, B = 4 features x 16
-// channels) and is split over the four waves along the features; each wave
-// also accumulates the rows' sums of squares from the same loads, so x is
-// read once.  Within a 16-feature chunk, lane l (row l % 16, group g = l / 16)
-// feeds features 4 g .. 4 g + 3 to the four MFMA steps (any fixed assignment of
-// features to steps gives the same sum; this one makes each lane's operands
-// one float4 of x and four consecutive bf16 of W).  The loads of U chunks are
-// issued before their MFMAs (one wave per SIMD: nothing else hides the HBM
-// latency).  H % (64 U) == 0.
+// 16 tokens per workgroup, the features split over its eight waves.  The
+// contraction runs on the bf16 matrix cores at fp32 accuracy: each product
+// a = x gamma (fp32) is split exactly into three bf16 planes and each plane
+// goes through v_mfma_f32_16x16x32_bf16 against the (exactly bf16) weight, so
+// every partial product is exact and the sums are fp32 -- at 16x the fp32
+// MFMA's rate.  MFMA operands: A = 16 tokens x 32 features (lane l: token
+// l % 16, features 8 (l / 16) .. +8 of the chunk), B = 32 features x 16
+// channels (lane l: channel l % 16 of the block); each wave's sums of
+// squares come from the same loads, so x is read once.  Loads run one group
+// of U chunks ahead of the MFMAs (two register sets).  H % 256 == 0.
 template <int U>
-__global__ __launch_bounds__(256) void head_kernel(const float *x, int ldx, int N, const float *gamma,
+QI_DEV void head_load(const float *row, const float *gamma, const u16 *W, int H, int k0, int nch, int c, int r,
+                      f32x4 (&xv)[U][2], f32x4 (&gv)[U][2], u32x4 (&wv)[U][4]) {
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int k = k0 + 32 * min(c + u, nch - 1);
+    xv[u][0] = *(const f32x4 *)(row + k);
+    xv[u][1] = *(const f32x4 *)(row + k + 4);
+    gv[u][0] = *(const f32x4 *)(gamma + k);
+    gv[u][1] = *(const f32x4 *)(gamma + k + 4);
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb) wv[u][cb] = *(const u32x4 *)(W + (size_t)(cb * 16 + r) * H + k);
+  }
+}
+
+template <int U>
+QI_DEV void head_mfma(int nch, int c, const f32x4 (&xv)[U][2], const f32x4 (&gv)[U][2], const u32x4 (&wv)[U][4],
+                      f32x4 (&acc)[4], float &ss) {
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    if (c + u >= nch) break;
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+      ss += xv[u][h][0] * xv[u][h][0] + xv[u][h][1] * xv[u][h][1] + xv[u][h][2] * xv[u][h][2] +
+            xv[u][h][3] * xv[u][h][3];
+    u32x4 p0, p1, p2;
+    split3(xv[u][0] * gv[u][0], xv[u][1] * gv[u][1], p0, p1, p2);
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb) {
+      acc[cb] = mfma16x16x32(p0, wv[u][cb], acc[cb]);
+      acc[cb] = mfma16x16x32(p1, wv[u][cb], acc[cb]);
+      acc[cb] = mfma16x16x32(p2, wv[u][cb], acc[cb]);
+    }
+  }
+}
+
+template <int U>
+__global__ __launch_bounds__(512) void head_kernel(const float *x, int ldx, int N, const float *gamma,
                                                    const u16 *W, const float *b, int H, float eps,
                                                    float *vel) {
-  __shared__ float sRed[4][16][64];  // per wave: [token][channel] partial sums
-  __shared__ float sSq[4][4][16];    // per wave and lane group: [token] partial sums of squares
+  constexpr int NW = 8;
+  __shared__ float sRed[NW][16][64];  // per wave: [token][channel] partial sums
+  __shared__ float sSq[NW][4][16];    // per wave and lane group: [token] partial sums of squares
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r = lane & 15, g = lane >> 4;
   const int t0 = blockIdx.x * 16;
   const float *row = x + (size_t)min(t0 + r, N - 1) * ldx;
-  const int nch = H >> 6;                       // 16-feature chunks per wave
-  const int kbase = wave * (H >> 2) + 4 * g;    // this lane's first feature
+  const int per_wave = H / NW;
+  const int nch = per_wave >> 5;                 // 32-feature chunks per wave
+  const int k0 = wave * per_wave + 8 * g;        // this lane's first feature
   f32x4 acc[4];
 #pragma unroll
   for (int cb = 0; cb < 4; ++cb) acc[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
   float ss = 0.f;
-  for (int c = 0; c < nch; c += U) {
-    f32x4 xv[U], gv[U];
-    u32x2 wv[U][4];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int k = kbase + 16 * (c + u);
-      xv[u] = *(const f32x4 *)(row + k);
-      gv[u] = *(const f32x4 *)(gamma + k);
-#pragma unroll
-      for (int cb = 0; cb < 4; ++cb) wv[u][cb] = *(const u32x2 *)(W + (size_t)(cb * 16 + r) * H + k);
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const f32x4 a = xv[u] * gv[u];
-      ss += xv[u][0] * xv[u][0] + xv[u][1] * xv[u][1] + xv[u][2] * xv[u][2] + xv[u][3] * xv[u][3];
-#pragma unroll
-      for (int cb = 0; cb < 4; ++cb) {
-        const u32x2 w4 = wv[u][cb];
-        const float wf[4] = {__uint_as_float(w4[0] << 16), __uint_as_float(w4[0] & 0xFFFF0000u),
-                             __uint_as_float(w4[1] << 16), __uint_as_float(w4[1] & 0xFFFF0000u)};
-#pragma unroll
-        for (int s = 0; s < 4; ++s) acc[cb] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[s], wf[s], acc[cb], 0, 0, 0);
-      }
-    }
+  f32x4 xa[U][2], ga[U][2], xb[U][2], gb[U][2];
+  u32x4 wa[U][4], wb[U][4];
+  head_load<U>(row, gamma, W, H, k0, nch, 0, r, xa, ga, wa);
+  for (int c = 0; c < nch; c += 2 * U) {
+    if (c + U < nch) head_load<U>(row, gamma, W, H, k0, nch, c + U, r, xb, gb, wb);
+    head_mfma<U>(nch, c, xa, ga, wa, acc, ss);
+    if (c + U >= nch) break;
+    if (c + 2 * U < nch) head_load<U>(row, gamma, W, H, k0, nch, c + 2 * U, r, xa, ga, wa);
+    head_mfma<U>(nch, c + U, xb, gb, wb, acc, ss);
   }
   // D element j of lane l: token 4 (l / 16) + j, channel 16 cb + l % 16
 #pragma unroll
@@ -231,18 +302,19 @@ __global__ __launch_bounds__(256) void head_kernel(const float *x, int ldx, int 
   sSq[wave][g][r] = ss;
   __syncthreads();
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int i = tid + 256 * j;
+  for (int j = 0; j < 2; ++j) {
+    const int i = tid + 512 * j;
     const int tok = i >> 6, ch = i & 63;
     float q = 0.f;
 #pragma unroll
-    for (int w = 0; w < 4; ++w)
+    for (int w = 0; w < NW; ++w)
 #pragma unroll
       for (int gg = 0; gg < 4; ++gg) q += sSq[w][gg][tok];
     const float rinv = rsqrtf(q / (float)H + eps);
-    if (t0 + tok < N)
-      vel[(size_t)(t0 + tok) * 64 + ch] =
-          b[ch] + rinv * (sRed[0][tok][ch] + sRed[1][tok][ch] + sRed[2][tok][ch] + sRed[3][tok][ch]);
+    float sum = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) sum += sRed[w][tok][ch];
+    if (t0 + tok < N) vel[(size_t)(t0 + tok) * 64 + ch] = b[ch] + rinv * sum;
   }
 }
 

@@ -30,26 +30,6 @@ constexpr int ST_SLOTS = A_SLOTS + W_SLOTS;    // 20 KB per stage
 constexpr int CA = A_SLOTS / THREADS, CW = W_SLOTS / THREADS;  // copies per thread and stage (3, 2)
 }  // namespace enc
 
-// exact split of 8 fp32 values into three planes of 8 bf16 (16 bytes each)
-QI_DEV void split3(const f32x4 lo, const f32x4 hi, u32x4 &p0, u32x4 &p1, u32x4 &p2) {
-  float v[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-  float r1[8], r2[8];
-  uint32_t a[4], b[4], c[4];
-#pragma unroll
-  for (int e = 0; e < 8; e += 2) {
-    a[e / 2] = pack_bf16x2(v[e], v[e + 1]);
-    r1[e] = v[e] - bf16_to_f32((u16)(a[e / 2] & 0xFFFF));
-    r1[e + 1] = v[e + 1] - bf16_to_f32((u16)(a[e / 2] >> 16));
-    b[e / 2] = pack_bf16x2(r1[e], r1[e + 1]);
-    r2[e] = r1[e] - bf16_to_f32((u16)(b[e / 2] & 0xFFFF));
-    r2[e + 1] = r1[e + 1] - bf16_to_f32((u16)(b[e / 2] >> 16));
-    c[e / 2] = pack_bf16x2(r2[e], r2[e + 1]);
-  }
-  p0 = u32x4{a[0], a[1], a[2], a[3]};
-  p1 = u32x4{b[0], b[1], b[2], b[3]};
-  p2 = u32x4{c[0], c[1], c[2], c[3]};
-}
-
 // the same split of 4 fp32 values, as three 8-byte plane entries
 QI_DEV void split3x4(const f32x4 v, u32x2 &p0, u32x2 &p1, u32x2 &p2) {
 #pragma unroll

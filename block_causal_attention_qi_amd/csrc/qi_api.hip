@@ -207,12 +207,8 @@ qi_status launch_gemm(const GemmArgs &g, int kind, hipStream_t s) {
 // The output head over `rows` rows of x [rows][H]; H % 256 == 0 (checked with
 // the model dimensions).
 void launch_head(const float *x, int H, int rows, const qi_model_w &w, float eps, float *vel, hipStream_t s) {
-  if ((H / 64) % 8 == 0)
-    hipLaunchKernelGGL(head_kernel<8>, dim3((rows + 15) / 16), dim3(256), 0, s, x, H, rows, w.norm_out, w.w_out,
-                       w.b_out, H, eps, vel);
-  else
-    hipLaunchKernelGGL(head_kernel<4>, dim3((rows + 15) / 16), dim3(256), 0, s, x, H, rows, w.norm_out, w.w_out,
-                       w.b_out, H, eps, vel);
+  hipLaunchKernelGGL(head_kernel<2>, dim3((rows + 15) / 16), dim3(512), 0, s, x, H, rows, w.norm_out, w.w_out, w.b_out,
+                     H, eps, vel);
 }
 
 qi_status launch_norm(const float *x, int ldx, const float *gamma, int zc, const float *mod,
@@ -229,10 +225,38 @@ qi_status launch_norm(const float *x, int ldx, const float *gamma, int zc, const
   return last_launch();
 }
 
+// The modulation GEMV (H % 256 == 0 and H <= 8192 are checked with the model
+// dimensions): 4H rows over 256 workgroups (one per CU), at least 16 rows
+// each (8 waves, one pair of rows per wave at a time).
+template <int NC>
+void launch_mod_gemv(int H, const u16 *w_mod, const float *b_mod, float t, float *mod, hipStream_t s) {
+  const int rows = 4 * H;
+  const int per = max(16, (rows + 255) / 256 + 15) & ~15;
+  hipLaunchKernelGGL(mod_gemv_kernel<NC>, dim3((rows + per - 1) / per), dim3(512), 2 * H * sizeof(float), s, w_mod,
+                     b_mod, t, H, rows, per, mod);
+}
+
 qi_status launch_modulation(int H, const u16 *w_mod, const float *b_mod, float t, float *mod, hipStream_t s) {
   TimedLaunch tl(QI_KERNEL_MODULATION, s);
-  hipLaunchKernelGGL(mod_gemv_kernel, dim3((4 * H + 15) / 16), dim3(256), 2 * H * sizeof(float), s, w_mod, b_mod,
-                     t, H, 4 * H, mod);
+  switch ((H + 511) / 512) {
+    case 1: launch_mod_gemv<1>(H, w_mod, b_mod, t, mod, s); break;
+    case 2: launch_mod_gemv<2>(H, w_mod, b_mod, t, mod, s); break;
+    case 3: launch_mod_gemv<3>(H, w_mod, b_mod, t, mod, s); break;
+    case 4: launch_mod_gemv<4>(H, w_mod, b_mod, t, mod, s); break;
+    case 5: launch_mod_gemv<5>(H, w_mod, b_mod, t, mod, s); break;
+    case 6: launch_mod_gemv<6>(H, w_mod, b_mod, t, mod, s); break;
+    case 7: launch_mod_gemv<7>(H, w_mod, b_mod, t, mod, s); break;
+    case 8: launch_mod_gemv<8>(H, w_mod, b_mod, t, mod, s); break;
+    case 9: launch_mod_gemv<9>(H, w_mod, b_mod, t, mod, s); break;
+    case 10: launch_mod_gemv<10>(H, w_mod, b_mod, t, mod, s); break;
+    case 11: launch_mod_gemv<11>(H, w_mod, b_mod, t, mod, s); break;
+    case 12: launch_mod_gemv<12>(H, w_mod, b_mod, t, mod, s); break;
+    case 13: launch_mod_gemv<13>(H, w_mod, b_mod, t, mod, s); break;
+    case 14: launch_mod_gemv<14>(H, w_mod, b_mod, t, mod, s); break;
+    case 15: launch_mod_gemv<15>(H, w_mod, b_mod, t, mod, s); break;
+    case 16: launch_mod_gemv<16>(H, w_mod, b_mod, t, mod, s); break;
+    default: return QI_ERR_SHAPE;
+  }
   return last_launch();
 }
 
@@ -387,7 +411,7 @@ qi_status run_step(const qi_dims &d, const qi_model_w &w, int L, int N, const fl
   }
   {
     TimedLaunch tl(QI_KERNEL_IMG_EMBED, s);
-    hipLaunchKernelGGL(img_embed_kernel, dim3((N + 15) / 16, (H + 255) / 256), dim3(256), 0, s, img_tokens, N,
+    hipLaunchKernelGGL(img_embed_kernel, dim3((N + 31) / 32, H / 256), dim3(256), 0, s, img_tokens, N,
                        w.w_img, w.b_img, H, x, H, L_rows);
   }
   QI_TRY(last_launch());
@@ -557,7 +581,7 @@ qi_status run_step_fbc(const qi_dims &d, const qi_model_w &w, int L, int N, cons
   QI_TRY(launch_modulation(H, w.w_mod, w.b_mod, t, mod, s));
   {
     TimedLaunch tl(QI_KERNEL_IMG_EMBED, s);
-    hipLaunchKernelGGL(img_embed_kernel, dim3((N + 15) / 16, (H + 255) / 256), dim3(256), 0, s, img_tokens, N,
+    hipLaunchKernelGGL(img_embed_kernel, dim3((N + 31) / 32, H / 256), dim3(256), 0, s, img_tokens, N,
                        w.w_img, w.b_img, H, x, H, 0);
   }
   QI_TRY(last_launch());
@@ -593,7 +617,7 @@ qi_status run_step_cfg(const qi_dims &d, const qi_model_w &w, int N, const float
   QI_TRY(launch_modulation(H, w.w_mod, w.b_mod, t, mod, s));
   for (int b = 0; b < 2; ++b) {
     TimedLaunch tl(QI_KERNEL_IMG_EMBED, s);
-    hipLaunchKernelGGL(img_embed_kernel, dim3((N + 15) / 16, (H + 255) / 256), dim3(256), 0, s, img_tokens, N,
+    hipLaunchKernelGGL(img_embed_kernel, dim3((N + 31) / 32, H / 256), dim3(256), 0, s, img_tokens, N,
                        w.w_img, w.b_img, H, x, H, b * N);
     QI_TRY(last_launch());
   }
