@@ -21,7 +21,7 @@ QI_ERR_HIP = -7
 QI_ERR_UNSUPPORTED = -8
 QI_MODE_JOINT = 0
 QI_MODE_IMAGE_ONLY = 1
-QI_NOALLOC_SCRATCH_BYTES = 96 * 1024 * 1024
+QI_NOALLOC_SCRATCH_BYTES = 160 * 1024 * 1024
 
 
 class QiDims(Structure):
@@ -116,7 +116,7 @@ CALIB_SIGNATURES = {
     "qi_calib_copy_gbs": (c_int32, [c_void_p, c_void_p, c_int64, c_int32, c_void_p]),
     "qi_calib_lds_cycles": (c_int32, [c_int32, c_int32, c_void_p]),
 }
-QI_KERNEL_KINDS = 15
+QI_KERNEL_KINDS = 16
 
 _lib = None
 _calib = None

@@ -2,7 +2,10 @@
 // operands K-contiguous (A [M,K] token rows, W [N,K] in the [out, in] Linear
 // layout), fp32 accumulation, and fused epilogues:
 //   EPI_F32    C[m][n] = acc (+ bias[n])                      (text projection)
-//   EPI_RESID  x[m][n] += gate[row kind][n] * acc             (O-proj, down)
+//   EPI_RESID  x[m][n] += gate[row kind][n] * acc             (O-proj, down);
+//              split over K (128 x 128 kernel only): chunk s of K writes
+//              its fp32 partial sums, and resid_reduce_kernel adds the
+//              chunks in order into x
 //   EPI_SWIGLU a[m][o] = bf16(SiLU(acc_gate) * acc_up)        (gate/up)
 //   EPI_QKV    RoPE on q, k from the row's cos/sin, one bf16 rounding, and a
 //              scatter into per-segment Q, K [heads][T][128] and V^T
@@ -18,7 +21,11 @@
 // Row-count invariance (the MLX page's row-count hazard in "Text K/V reuse"):
 // every output element is produced by the same MFMA instruction over the same
 // K order whatever M is and wherever the row sits in its tile, so a row's
-// result does not depend on how many rows the pass has.  No split-K, no atomics.
+// result does not depend on how many rows the pass has.  No atomics.  The
+// residual GEMMs of a small image (few rows, too few tiles for the chip) are
+// split over K; the split is chosen from the image's token count N alone, so
+// the joint and the image-only passes of one render (and both CFG branches)
+// take the same chunks and reduce them in the same order.
 #pragma once
 
 #include <type_traits>
@@ -56,6 +63,11 @@ struct GemmArgs {
   int batch;         // image rows form `batch` branches of seg_i rows each (true CFG: 2),
                      // each with its own Q, K [heads][seg_i][128] and V^T [heads][128][ldv_i]
   const int *skip;   // first-block cache: when non-NULL and *skip, the launch does nothing
+  // EPI_RESID split over K (ksplit > 1; 128 x 128 kernel): grid = tiles x
+  // ksplit; chunk s covers K columns [s K/ksplit, (s+1) K/ksplit) and writes
+  // its fp32 partial sums to part + s * M * N ([M][N] row-major)
+  int ksplit;
+  float *part;
 };
 
 namespace gemm {
@@ -301,8 +313,13 @@ __global__ __launch_bounds__(gemm::THREADS, (BM * BN >= 256 * 256) ? 1 : 2) void
   const int wm = wave & 1, wn = wave >> 1;
   const int nTM = (g.M + BM - 1) / BM;
   const int nTN = (EPI == EPI_SWIGLU ? g.F / (BN / 2) : g.N / BN);
+  // split over K (EPI_RESID only): the workgroup's chunk and its K columns
+  const bool split = EPI == EPI_RESID && g.ksplit > 1;
+  const int ntile = nTM * nTN;
+  const int kchunk = split ? (int)(blockIdx.x / ntile) : 0;
+  const int kc = split ? g.K / g.ksplit : g.K;
   int tm, tn;
-  tile_of(blockIdx.x, nTM, nTN, tm, tn);
+  tile_of(split ? (int)(blockIdx.x % ntile) : (int)blockIdx.x, nTM, nTN, tm, tn);
   const int m0 = tm * BM;
 
   const u16 *pa[CA], *pw[CW];
@@ -313,7 +330,7 @@ __global__ __launch_bounds__(gemm::THREADS, (BM * BN >= 256 * 256) ? 1 : 2) void
     const int row = i >> 3, c = i & 7;
     slot_a[j] = lds_slot(row, c);
     const int am = min(m0 + row, g.M - 1);  // rows past M load a valid row; never stored
-    pa[j] = g.A + (size_t)am * g.lda + c * 8;
+    pa[j] = g.A + (size_t)am * g.lda + c * 8 + (size_t)kchunk * kc;
   }
 #pragma unroll
   for (int j = 0; j < CW; ++j) {
@@ -328,7 +345,7 @@ __global__ __launch_bounds__(gemm::THREADS, (BM * BN >= 256 * 256) ? 1 : 2) void
     } else {
       wr = tn * BN + row;
     }
-    pw[j] = g.W + (size_t)wr * g.ldw + c * 8;
+    pw[j] = g.W + (size_t)wr * g.ldw + c * 8 + (size_t)kchunk * kc;
   }
 
   f32x16 acc[FS][TS];
@@ -344,7 +361,7 @@ __global__ __launch_bounds__(gemm::THREADS, (BM * BN >= 256 * 256) ? 1 : 2) void
   // so its latency is covered by two steps of MFMA work (the K loop is
   // unrolled by two to keep the stage registers static).
   u32x4 ra[2][CA], rw[2][CW];
-  const int nk = g.K / BK;
+  const int nk = kc / BK;
 
   auto gload = [&](int st, int kt) {
     const int k0 = kt * BK;
@@ -413,6 +430,12 @@ __global__ __launch_bounds__(gemm::THREADS, (BM * BN >= 256 * 256) ? 1 : 2) void
         for (int j = 0; j < 4; ++j)
           store4_swiglu(g, m, tn * (BN / 2) + wn * (WF / 2) + p * 32 + 8 * j + h4, quad(acc[2 * p][t], j),
                         quad(acc[2 * p + 1][t], j));
+    } else if (split) {
+      float *prow = g.part + ((size_t)kchunk * g.M + m) * g.N;
+#pragma unroll
+      for (int f = 0; f < FS; ++f)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) *(f32x4 *)(prow + tn * BN + wn * WF + f * 32 + 8 * j + h4) = quad(acc[f][t], j);
     } else {
 #pragma unroll
       for (int f = 0; f < FS; ++f)
@@ -420,6 +443,24 @@ __global__ __launch_bounds__(gemm::THREADS, (BM * BN >= 256 * 256) ? 1 : 2) void
         for (int j = 0; j < 4; ++j) store4<EPI>(g, m, tn * BN + wn * WF + f * 32 + 8 * j + h4, quad(acc[f][t], j));
     }
   }
+}
+
+// The residual update of a K-split GEMM: x[m][n] += gate[row kind][n] *
+// (((P_0 + P_1) + P_2) + ...)[m][n], the chunks summed in order in fp32.
+// One thread per 4 consecutive outputs.
+__global__ __launch_bounds__(256) void resid_reduce_kernel(const GemmArgs g) {
+  if (g.skip && *g.skip) return;
+  const int n4 = g.N >> 2;
+  const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= (size_t)g.M * n4) return;
+  const int m = (int)(i / n4), n = (int)(i % n4) * 4;
+  const size_t mn = (size_t)g.M * g.N;
+  const float *p = g.part + (size_t)m * g.N + n;
+  f32x4 v = *(const f32x4 *)p;
+  for (int s = 1; s < g.ksplit; ++s) v += *(const f32x4 *)(p + s * mn);
+  const float *gp = g.gate + (m < g.L_rows ? 0 : g.gate_img_off) + n;
+  f32x4 *xp = (f32x4 *)(g.X + (size_t)m * g.ldx + n);
+  *xp = *xp + *(const f32x4 *)gp * v;
 }
 
 // ---------------------------------------------------------------- 256 x 256 tiles

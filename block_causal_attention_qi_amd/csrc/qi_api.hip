@@ -7,6 +7,7 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <algorithm>
 #include <mutex>
 #include <vector>
 
@@ -46,8 +47,27 @@ bool dims_ok(const qi_dims *d) {
 // Workspace of one joint pass over T = L + N rows (an image-only pass uses a
 // prefix of each buffer).
 struct Layout {
-  size_t x, mod, tn, h, q_t, k_t, vt_t, q_i, k_i, vt_i, o, a, total;
+  size_t x, mod, tn, h, q_t, k_t, vt_t, q_i, k_i, vt_i, o, a, part, total;
 };
+
+// K-split of the residual GEMMs (O-proj, K = H; down, K = F) for a render of N
+// image tokens.  A small image gives the whole-K 128 x 128 tiles too few
+// workgroups for 256 CUs (160 at N = 576), so their K is cut into chunks
+// whose partial sums resid_reduce_kernel adds in order.  The choice depends
+// on N only, so both passes of a render and both CFG branches split alike.
+constexpr int kSplitMaxN = 1024;
+int ksplit_for(int N, int K, int want) {
+  if (N > kSplitMaxN) return 1;
+  int s = want;
+  while (s > 1 && K % (s * gemm::BK) != 0) --s;
+  return s;
+}
+int ksplit_o(const qi_dims &d, int N) { return ksplit_for(N, d.hidden, 2); }
+int ksplit_down(const qi_dims &d, int N) { return ksplit_for(N, d.ffn, 3); }
+size_t part_bytes(const qi_dims &d, int N, size_t rows) {
+  const int s = std::max(ksplit_o(d, N), ksplit_down(d, N));
+  return s > 1 ? (size_t)s * rows * d.hidden * 4 : 0;
+}
 
 Layout layout(const qi_dims &d, int L, int N) {
   const size_t H = d.hidden, F = d.ffn, D = d.txt_dim, T = (size_t)L + N;
@@ -71,6 +91,7 @@ Layout layout(const qi_dims &d, int L, int N) {
   l.vt_i = take(H * Np * 2);
   l.o = take(T * H * 2);
   l.a = take(T * F * 2);
+  l.part = take(part_bytes(d, N, T));
   l.total = off;
   return l;
 }
@@ -95,6 +116,7 @@ Layout layout_cfg(const qi_dims &d, int N) {
   l.vt_i = take(2 * H * Np * 2);
   l.o = take(R * H * 2);
   l.a = take(R * F * 2);
+  l.part = take(part_bytes(d, N, R));
   l.total = off;
   return l;
 }
@@ -193,15 +215,34 @@ qi_status launch_gemm(const GemmArgs &g, int kind, hipStream_t s) {
   const int per_tile_big = EPI == EPI_SWIGLU ? 128 : 256;
   const int nTM_big = (g.M + 255) / 256;
   const int tiles_big = n_out % per_tile_big == 0 ? nTM_big * (n_out / per_tile_big) : 0;
+  const int tiles_small = ((g.M + 127) / 128) * (EPI == EPI_SWIGLU ? g.F / 64 : g.N / 128);
   const bool fits32 = (size_t)g.M * g.lda * 2 < (1ull << 31) &&
                       (size_t)(EPI == EPI_SWIGLU ? 2 * g.F : g.N) * g.ldw * 2 < (1ull << 31);
-  TimedLaunch tl(kind, s);
-  if (fits32 && tiles_big >= 256)
-    hipLaunchKernelGGL((gemm_bf16_large_kernel<EPI, QI_GEMM_WM, QI_GEMM_WN>), dim3(tiles_big),
-                       dim3(64 * QI_GEMM_WM * QI_GEMM_WN), 0, s, g);
-  else
-    launch_gemm_tile<EPI, 128, 128>(g, s);
-  return last_launch();
+  // Rounds of workgroups over the 256 CUs: one 256 x 256 tile per CU, two
+  // 128 x 128 tiles per CU (each about 0.85 of a large round per round,
+  // measured).  The large tile when it needs no more time.
+  const int rounds_big = (tiles_big + 255) / 256, rounds_small = (tiles_small + 511) / 512;
+  const bool big = g.ksplit <= 1 && fits32 && tiles_big >= 256 && 100 * rounds_big <= 85 * rounds_small;
+  {
+    TimedLaunch tl(kind, s);
+    if (big) {
+      hipLaunchKernelGGL((gemm_bf16_large_kernel<EPI, QI_GEMM_WM, QI_GEMM_WN>), dim3(tiles_big),
+                         dim3(64 * QI_GEMM_WM * QI_GEMM_WN), 0, s, g);
+    } else if (EPI == EPI_RESID && g.ksplit > 1) {
+      hipLaunchKernelGGL((gemm_bf16_kernel<EPI, 128, 128>), dim3(tiles_small * g.ksplit), dim3(gemm::THREADS), 0,
+                         s, g);
+    } else {
+      launch_gemm_tile<EPI, 128, 128>(g, s);
+    }
+  }
+  QI_TRY(last_launch());
+  if (EPI == EPI_RESID && g.ksplit > 1) {
+    TimedLaunch tl(QI_KERNEL_SPLITK_REDUCE, s);
+    const size_t n4 = (size_t)g.M * (g.N / 4);
+    hipLaunchKernelGGL(resid_reduce_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, s, g);
+    QI_TRY(last_launch());
+  }
+  return QI_OK;
 }
 
 // The output head over `rows` rows of x [rows][H]; H % 256 == 0 (checked with
@@ -346,6 +387,8 @@ qi_status run_block(const qi_dims &d, const qi_block_w &w, int L, int N, bool jo
   r.A = o; r.lda = H; r.W = w.w_o; r.ldw = H; r.M = T; r.N = H; r.K = H; r.L_rows = L_rows;
   r.X = x; r.ldx = H; r.gate = mod + H; r.gate_img_off = img_off;
   r.skip = skip;
+  r.ksplit = ksplit_o(d, N);
+  r.part = (float *)(ws + lay.part);
   QI_TRY(launch_gemm<EPI_RESID>(r, QI_KERNEL_GEMM_O, s));
 
   // norm 2 + modulation (scale2 = chunk 2)
@@ -363,6 +406,8 @@ qi_status run_block(const qi_dims &d, const qi_block_w &w, int L, int N, bool jo
   dn.A = a; dn.lda = F; dn.W = w.w_down; dn.ldw = F; dn.M = T; dn.N = H; dn.K = F; dn.L_rows = L_rows;
   dn.X = x; dn.ldx = H; dn.gate = mod + 3 * H; dn.gate_img_off = img_off;
   dn.skip = skip;
+  dn.ksplit = ksplit_down(d, N);
+  dn.part = (float *)(ws + lay.part);
   QI_TRY(launch_gemm<EPI_RESID>(dn, QI_KERNEL_GEMM_DOWN, s));
   return QI_OK;
 }
@@ -940,7 +985,7 @@ const char *qi_kernel_kind_name(int32_t kind) {
   static const char *names[QI_KERNEL_KINDS] = {"modulation", "txt_norm",   "gemm_txt",  "img_embed",
                                                "norm_mod",   "gemm_qkv",   "attention", "gemm_o",
                                                "gemm_gate_up", "gemm_down", "head",     "euler",
-                                               "enc_gemm",   "enc_attention", "enc_misc"};
+                                               "enc_gemm",   "enc_attention", "enc_misc", "splitk_reduce"};
   return (kind >= 0 && kind < QI_KERNEL_KINDS) ? names[kind] : "?";
 }
 

@@ -439,7 +439,7 @@ def linear_bf16(A, W, bias, C, stream=None):
 # ------------------------------------------------------------------ kernel timing
 
 KERNEL_KINDS = ["modulation", "txt_norm", "gemm_txt", "img_embed", "norm_mod", "gemm_qkv", "attention",
-                "gemm_o", "gemm_gate_up", "gemm_down", "head", "euler", "enc_gemm", "enc_attention", "enc_misc"]
+                "gemm_o", "gemm_gate_up", "gemm_down", "head", "euler", "enc_gemm", "enc_attention", "enc_misc", "splitk_reduce"]
 
 
 def timing_begin(max_launches: int = 65536):

@@ -195,7 +195,7 @@ qi_status qi_dit_step(const qi_dims *d, const qi_model_w *w, int32_t L, int32_t 
  * with its workspace taken from a static scratch array inside the library
  * instead of a caller buffer.  Same arguments, same kernels and bit-identical
  * results as qi_dit_step, minus ws / ws_bytes.  The scratch is one
- * QI_NOALLOC_SCRATCH_BYTES (96 MiB) array per GPU, held from the library's
+ * QI_NOALLOC_SCRATCH_BYTES (160 MiB) array per GPU, held from the library's
  * first use on that GPU until the process ends; its device address is looked
  * up once per device (hipGetSymbolAddress, the calling thread's current
  * device).  The call allocates nothing and clears nothing (no kernel of the
@@ -203,11 +203,11 @@ qi_status qi_dit_step(const qi_dims *d, const qi_model_w *w, int32_t L, int32_t 
  * one GPU uses the same scratch: calls that may overlap on one GPU (two
  * streams, two threads) race and must be serialised by the caller.
  * Limit: qi_workspace_bytes(d, L, N) <= QI_NOALLOC_SCRATCH_BYTES, e.g. the
- * 384^2 step (hidden 4096, L 494, N 576, 92 MB) fits, the 1024^2 step does
+ * 384^2 step (hidden 4096, L 494, N 576, 138 MiB) fits, the 1024^2 step does
  * not.  Errors: as qi_dit_step; QI_ERR_WORKSPACE when the request needs more
  * scratch than that (checked before anything else is done), QI_ERR_HIP if the
  * scratch address cannot be obtained. */
-#define QI_NOALLOC_SCRATCH_BYTES (96u * 1024u * 1024u)
+#define QI_NOALLOC_SCRATCH_BYTES (160u * 1024u * 1024u)
 qi_status qi_dit_step_noalloc(const qi_dims *d, const qi_model_w *w, int32_t L, int32_t N,
                               const float *img_tokens, const float *txt_feats, float timestep,
                               const float *txt_cos, const float *txt_sin, const float *img_cos,
@@ -436,7 +436,8 @@ qi_status qi_linear_bf16(int32_t M, int32_t N, int32_t K, const uint16_t *A, con
 #define QI_KERNEL_ENC_GEMM 12    /* text encoder: fp32-activation GEMMs */
 #define QI_KERNEL_ENC_ATTN 13    /* text encoder: fp32 attention */
 #define QI_KERNEL_ENC_MISC 14    /* text encoder: embed, norms, q/k prep */
-#define QI_KERNEL_KINDS 15
+#define QI_KERNEL_SPLITK_REDUCE 15 /* residual update of a K-split O-proj / down GEMM */
+#define QI_KERNEL_KINDS 16
 
 /* Name of a kernel kind (static string, "?" if out of range). */
 const char *qi_kernel_kind_name(int32_t kind);
