@@ -70,6 +70,9 @@ def build(verbose: bool = False) -> str:
         print(out)
     objs.append(api_obj)
     objs.append(attn_obj)
+    na_obj = os.path.join(obj_dir, "noalloc.o")
+    _run([hipcc, *HIP_FLAGS, "-c", os.path.join(CSRC, "noalloc.hip"), "-o", na_obj])
+    objs.append(na_obj)
     tmp = LIB + ".tmp"
     _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp])
     os.replace(tmp, LIB)

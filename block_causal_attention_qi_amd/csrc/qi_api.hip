@@ -127,36 +127,6 @@ size_t slot_elems(const qi_dims &d, int L) {
 
 qi_status last_launch() { return hipGetLastError() == hipSuccess ? QI_OK : QI_ERR_HIP; }
 
-// ---------------------------------------------------------------- allocation-free scratch
-// The workspace of qi_dit_step_noalloc: a file-scope device array, one copy
-// per GPU, held from the code object's load until the process ends.  In host
-// code `scratch` names a host-side stand-in, never the device memory: its
-// device address is looked up once per device with hipGetSymbolAddress (with
-// that device current) and only that address is handed to kernels.
-static __device__ __align__(256) char scratch[QI_NOALLOC_SCRATCH_BYTES];
-
-constexpr int kMaxDevices = 64;
-struct ScratchAddr {
-  std::mutex mu;
-  void *ptr[kMaxDevices] = {};
-};
-ScratchAddr g_scratch;
-
-// Device address of the current device's scratch array.
-qi_status scratch_address(void **out) {
-  int dev = -1;
-  if (hipGetDevice(&dev) != hipSuccess) return QI_ERR_HIP;
-  if (dev < 0 || dev >= kMaxDevices) return QI_ERR_UNSUPPORTED;
-  std::lock_guard<std::mutex> g(g_scratch.mu);
-  if (!g_scratch.ptr[dev]) {
-    void *p = nullptr;
-    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return QI_ERR_HIP;
-    g_scratch.ptr[dev] = p;
-  }
-  *out = g_scratch.ptr[dev];
-  return QI_OK;
-}
-
 // ---------------------------------------------------------------- kernel timing
 // Optional per-kernel timing: while enabled, every launch is bracketed by two
 // events from a pool created by qi_timing_begin, on the launch's own stream.
@@ -767,23 +737,6 @@ qi_status qi_dit_step(const qi_dims *d, const qi_model_w *w, int32_t L, int32_t 
   }
   return run_step(*d, *w, L, N, img_tokens, txt_feats, timestep, txt_cos, txt_sin, img_cos, img_sin,
                   cache ? cache->kv : nullptr, joint, vel, (char *)ws, (hipStream_t)stream);
-}
-
-qi_status qi_dit_step_noalloc(const qi_dims *d, const qi_model_w *w, int32_t L, int32_t N,
-                              const float *img_tokens, const float *txt_feats, float timestep,
-                              const float *txt_cos, const float *txt_sin, const float *img_cos,
-                              const float *img_sin, const qi_kv_cache *cache, float *vel, void *stream) {
-  // the size check comes first: nothing is looked up or enqueued for a
-  // request the scratch cannot hold
-  if (!d) return QI_ERR_NULL;
-  if (!dims_ok(d)) return QI_ERR_SHAPE;
-  if (L < 1 || L > kMaxL || N < 1 || N > kMaxN) return QI_ERR_RANGE;
-  const size_t need = layout(*d, L, N).total;
-  if (need > (size_t)QI_NOALLOC_SCRATCH_BYTES) return QI_ERR_WORKSPACE;
-  void *ws = nullptr;
-  QI_TRY(scratch_address(&ws));
-  return qi_dit_step(d, w, L, N, img_tokens, txt_feats, timestep, txt_cos, txt_sin, img_cos, img_sin, cache, vel,
-                     ws, QI_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 qi_status qi_text_kv_capture(const qi_dims *d, const qi_model_w *w, int32_t L, int32_t N,
