@@ -26,3 +26,61 @@ def record(kind: str, **fields) -> dict:
     print(line, flush=True)
     sys.stdout.flush()
     return rec
+
+
+def summarize(path: str) -> str:
+    """Markdown tables of a records.jsonl: per-workload teacher-forced worst
+    blocks, sampled-row blocks and whole-step velocities (the latest record of
+    each kind and key wins)."""
+    recs = [json.loads(line) for line in open(path) if line.strip()]
+    out = [f"Parity records from `{os.path.basename(path)}` ({len(recs)} records).", ""]
+    tf = {}
+    for r in recs:
+        if r["kind"] == "teacher_forced_block":
+            tf[(r["workload"], r["sampler_step"], r["block"])] = r
+    if tf:
+        out += ["## Teacher-forced blocks (all rows; bar rel <= 1e-2, corr_min >= 0.999)", "",
+                "| workload | sampler step | blocks | worst rel (block) | median rel | worst corr_min (block) "
+                "| worst text rel | worst image rel |", "|---|---|---|---|---|---|---|---|"]
+        for wl, st in sorted({(k[0], k[1]) for k in tf}):
+            rs = [tf[k] for k in sorted(tf) if k[0] == wl and k[1] == st]
+            wr = max(rs, key=lambda r: r["rel"])
+            wc = min(rs, key=lambda r: r["corr_min"])
+            rels = sorted(r["rel"] for r in rs)
+            txt = [r["rel_text"] for r in rs if r.get("rel_text") is not None]
+            out.append(f"| {wl} | {st} | {len(rs)} | {wr['rel']:.3e} ({wr['block']}) | {rels[len(rels) // 2]:.3e} "
+                       f"| {wc['corr_min']:.6f} ({wc['block']}) | {max(txt) if txt else float('nan'):.3e} "
+                       f"| {max(r['rel_image'] for r in rs):.3e} |")
+        out.append("")
+    sr = {(r["workload"], r["block"]): r for r in recs if r["kind"] == "sampled_rows_block"}
+    if sr:
+        out += ["## Sampled-row blocks on the oracle's embed output", "",
+                "| workload | block | rows | rel | corr_min |", "|---|---|---|---|---|"]
+        for k in sorted(sr):
+            r = sr[k]
+            out.append(f"| {k[0]} | {k[1]} | {r['rows']} | {r['rel']:.3e} | {r['corr_min']:.6f} |")
+        out.append("")
+    ws = {r["case"]: r for r in recs if r["kind"] == "whole_step_vel"}
+    if ws:
+        out += ["## Whole-step vel against the stored oracle velocities", "",
+                "| case | rel vs exact | corr vs exact | rel vs bf16 oracle | bf16 oracle rel vs exact "
+                "| bf16 cross-order spread |", "|---|---|---|---|---|---|"]
+        for k in sorted(ws):
+            r = ws[k]
+            out.append(f"| {k} | {r['rel_vs_exact']:.3e} | {r['corr_vs_exact']:.6f} | {r['rel_vs_bf16']:.3e} "
+                       f"| {r['bf16_oracle_rel_vs_exact']:.3e} | {r['bf16_cross_order_spread']:.3e} |")
+        out.append("")
+    tr = {(r["workload"], r["sampler_step"]): r for r in recs if r["kind"] == "whole_step_vs_exact_oracle_trajectory"}
+    if tr:
+        out += ["## Whole-step vel of the teacher-forced runs against the exact oracle's own trajectory", "",
+                "| workload | sampler step | rel | corr_min |", "|---|---|---|---|"]
+        for k in sorted(tr):
+            r = tr[k]
+            out.append(f"| {k[0]} | {k[1]} | {r['rel']:.3e} | {r['corr_min']:.6f} |")
+        out.append("")
+    return "\n".join(out)
+
+
+if __name__ == "__main__":
+    # python tests/parity_record.py RECORDS.jsonl > SUMMARY.md
+    print(summarize(sys.argv[1]))
