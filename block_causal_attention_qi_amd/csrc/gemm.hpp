@@ -128,11 +128,14 @@ QI_DEV void store4(const GemmArgs &g, int m, int n, f32x4 v) {
 }
 
 // The LDS a workgroup tile leaves free once its K loop is done, as NOBJ
-// objects of 32 KB (2048 16-byte slots) each, addressed by object so that the
-// kernels can keep their operand stages in separate LDS objects.
-template <int NOBJ>
+// objects of SLOTS 16-byte slots each (32 KB or 16 KB), addressed by object so
+// that the kernels can keep their operand stages in separate LDS objects.
+template <int NOBJ, int SLOTS = 2048>
 struct LdsObjs {
   static_assert(NOBJ == 2 || NOBJ == 4, "two or four objects");
+  static_assert(SLOTS == 2048 || SLOTS == 1024, "32 KB or 16 KB objects");
+  static constexpr int kSlots = SLOTS;
+  static constexpr int kRows = SLOTS / 16;  // staged RoPE table rows per object
   u32x4 *p0, *p1, *p2, *p3;
   QI_DEV u32x4 *o(int i) const { return i == 0 ? p0 : i == 1 ? p1 : i == 2 ? p2 : p3; }
 };
@@ -142,16 +145,18 @@ struct LdsObjs {
 // and 32 lanes hold 32 different tokens: read straight from the tables, every
 // load instruction would touch 32 rows, which the vector cache serves one row
 // at a time.  Staged, the tables are read in whole contiguous rows instead.
-// Layout: tile rows come in blocks of 128 (one 32 KB object per block and
-// table: cos in objects 0 .. BM/128 - 1, sin in the next BM/128); the float2
-// (pairs 2q, 2q+1) of row r sits at slot (r % 128) * 32 + (q ^ (r & 31)) of
-// its object, so the 32 rows one half-wave reads at a fixed q hit 32 distinct
-// bank pairs.  A 16-byte chunk k (q = 2k, 2k + 1) of the table row lands at
-// the even slot (2k) ^ (r & 30), its halves swapped when r is odd.
-template <int BM, int THREADS, int NOBJ>
-QI_DEV void stage_rope_rows(const GemmArgs &g, int m0, const LdsObjs<NOBJ> lo, int tid) {
+// Layout: tile rows come in blocks of R = kRows (128 rows per 32 KB object,
+// 64 per 16 KB object; one object per block and table: cos in objects
+// 0 .. BM/R - 1, sin in the next BM/R); the float2 (pairs 2q, 2q+1) of row r
+// sits at slot (r % R) * 32 + (q ^ (r & 31)) of its object, so the 32 rows
+// one half-wave reads at a fixed q hit 32 distinct bank pairs.  A 16-byte
+// chunk k (q = 2k, 2k + 1) of the table row lands at the even slot
+// (2k) ^ (r & 30), its halves swapped when r is odd.
+template <int BM, int THREADS, int NOBJ, int SLOTS>
+QI_DEV void stage_rope_rows(const GemmArgs &g, int m0, const LdsObjs<NOBJ, SLOTS> lo, int tid) {
+  constexpr int R = LdsObjs<NOBJ, SLOTS>::kRows;
   static_assert((BM * 16) % THREADS == 0, "whole passes over the tile's rows");
-  static_assert(NOBJ >= 2 * (BM / 128), "a cos and a sin object per 128 rows");
+  static_assert(NOBJ >= 2 * (BM / R) && BM % R == 0, "a cos and a sin object per R rows");
 #pragma unroll
   for (int it = 0; it < BM * 16 / THREADS; ++it) {
     const int i = tid + THREADS * it;
@@ -166,9 +171,9 @@ QI_DEV void stage_rope_rows(const GemmArgs &g, int m0, const LdsObjs<NOBJ> lo, i
       c = u32x4{c[2], c[3], c[0], c[1]};
       sn = u32x4{sn[2], sn[3], sn[0], sn[1]};
     }
-    const int chunk = (r & 127) * 16 + (k ^ ((r & 30) >> 1));
-    lo.o(r >> 7)[chunk] = c;
-    lo.o(BM / 128 + (r >> 7))[chunk] = sn;
+    const int chunk = (r % R) * 16 + (k ^ ((r & 30) >> 1));
+    lo.o(r / R)[chunk] = c;
+    lo.o(BM / R + r / R)[chunk] = sn;
   }
 }
 
@@ -216,13 +221,14 @@ QI_DEV void store_v_wave(const GemmArgs &g, int mbase, int n0, const f32x16 (&ac
 // at rr * 16 + (s ^ ((rr >> 1) & 15)): the 32 rows a half-wave writes at a
 // fixed s cover all 64 banks, and a 16-byte read of slots 2k, 2k + 1 stays
 // one aligned chunk (halves swapped when the XOR term is odd).
-template <int BM, int THREADS, int TS, int FS, int NOBJ>
+template <int BM, int THREADS, int TS, int FS, int NOBJ, int SLOTS>
 QI_DEV void qkv_epilogue(const GemmArgs &g, int m0, int n_tile, int wrow, int n0, const f32x16 (&acc)[FS][TS],
-                         int tid, const LdsObjs<NOBJ> lo) {
+                         int tid, const LdsObjs<NOBJ, SLOTS> lo) {
   static_assert(FS == 2, "a wave tile is half a head: 64 W rows");
+  constexpr int R = LdsObjs<NOBJ, SLOTS>::kRows;
   constexpr int WT = 32 * TS;
   constexpr int RS = WT * 8;          // 16-byte slots of one wave's region
-  constexpr int RPO = 2048 / RS;      // regions per 32 KB object
+  constexpr int RPO = SLOTS / RS;     // regions per object
   static_assert(RPO >= 1 && (THREADS / 64) <= RPO * NOBJ, "the waves' regions fit in the objects");
   const int lane = tid & 63, wave = tid >> 6;
   const int fr = lane & 31, hf = lane >> 5;
@@ -243,12 +249,12 @@ QI_DEV void qkv_epilogue(const GemmArgs &g, int m0, int n_tile, int wrow, int n0
 #pragma unroll
   for (int t = 0; t < TS; ++t) {
     const int r = wrow + 32 * t + fr;
-    const u32x2 *cl2 = (const u32x2 *)lo.o(r >> 7), *sl2 = (const u32x2 *)lo.o(BM / 128 + (r >> 7));
+    const u32x2 *cl2 = (const u32x2 *)lo.o(r / R), *sl2 = (const u32x2 *)lo.o(BM / R + r / R);
 #pragma unroll
     for (int f = 0; f < FS; ++f)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const int slot = (r & 127) * 32 + ((q0 + 8 * f + 2 * j) ^ (r & 31));
+        const int slot = (r % R) * 32 + ((q0 + 8 * f + 2 * j) ^ (r & 31));
         const float2 cs = __builtin_bit_cast(float2, cl2[slot]);
         const float2 sn = __builtin_bit_cast(float2, sl2[slot]);
         const f32x4 v = quad(acc[f][t], j);
@@ -677,6 +683,224 @@ __global__ __launch_bounds__(gemmL::THREADS, 1) void gemm_bf16_large_kernel(cons
         for (int j = 0; j < 4; ++j)
           store4_swiglu(g, m, tn * (BN / 2) + wn * (WF / 2) + p * 32 + 8 * j + h4, quad(acc[2 * p][t], j),
                         quad(acc[2 * p + 1][t], j));
+    } else {
+#pragma unroll
+      for (int f = 0; f < FS; ++f)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) store4<EPI>(g, m, tn * BN + wn * WF + f * 32 + 8 * j + h4, quad(acc[f][t], j));
+    }
+  }
+}
+
+// ---------------------------------------------------------------- 128 x 128 tiles, LDS copies
+// Small-M shape with the large kernel's operand path.  A few hundred token
+// rows give too few 256 x 256 tiles for 256 CUs, so the tile stays 128 x 128
+// (4 waves as 2 x 2, wave tile 64 tokens x 64 W rows, two workgroups per CU):
+// exactly the MFMA sequence of gemm_bf16_kernel<EPI, 128, 128>, hence the
+// same bits.  What changes is how the operands reach LDS.  With register
+// staging each K step writes its 32 KB of slices with ds_write, which the
+// LDS serves at about 2.5x the cost of a read per byte; together with one
+// fragment read per MFMA (a 64 x 64 wave tile reads 4 fragments for 4
+// MFMAs) that held the small kernel to about 45% of the MFMA rate.  Here the
+// slices are copied global -> LDS directly, A double-buffered one step ahead
+// and W triple-buffered two steps ahead, five 16 KB LDS objects (80 KB per
+// workgroup, two workgroups fill the 160 KB), with the large kernel's copy
+// order and waits.  Copy instruction j of wave w fills slots (4 j + w) * 64
+// .. + 63: tile rows 32 j + 8 w + lane / 8, chunk (lane % 8) ^ ((row >> 1) & 7)
+// -- independent of j.  Token rows past M are clamped to row M - 1 (loaded,
+// never stored), so every copy stays inside the operands.
+namespace gemmM {
+constexpr int BM = 128, BN = 128, BK = 64, THREADS = 256;
+constexpr int TS = 2, FS = 2;           // wave tile: 2 x 32 tokens, 2 x 32 W rows
+constexpr int NCP = BM * 8 / THREADS;   // copy instructions per operand slice per thread (4)
+constexpr int RSRC_FLAGS = 0x00020000;  // raw buffer, 32-bit dwords
+}  // namespace gemmM
+
+template <int EPI>
+__global__ __launch_bounds__(gemmM::THREADS, 2) void gemm_bf16_mid_kernel(const GemmArgs g) {
+  using namespace gemmM;
+  if (g.skip && *g.skip) return;
+  constexpr int WT = BM / 2, WF = BN / 2;
+  __shared__ u32x4 sA0[BM * 8], sA1[BM * 8];
+  __shared__ u32x4 sW0[BN * 8], sW1[BN * 8], sW2[BN * 8];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave & 1, wn = wave >> 1;
+  const int nTM = (g.M + BM - 1) / BM;
+  const int nTN = EPI == EPI_SWIGLU ? g.F / (BN / 2) : g.N / BN;
+  // split over K (EPI_RESID only): the workgroup's chunk and its K columns
+  const bool split = EPI == EPI_RESID && g.ksplit > 1;
+  const int ntile = nTM * nTN;
+  const int kchunk = split ? (int)(blockIdx.x / ntile) : 0;
+  const int kc = split ? g.K / g.ksplit : g.K;
+  int tm, tn;
+  tile_of(split ? (int)(blockIdx.x % ntile) : (int)blockIdx.x, nTM, nTN, tm, tn);
+  const int m0 = tm * BM;
+
+  // copy sources: tile row r0 + 32 j, chunk cch
+  const int r0 = 8 * wave + (lane >> 3);
+  const int cch = (lane & 7) ^ ((r0 >> 1) & 7);
+  const __amdgpu_buffer_rsrc_t ra =
+      __builtin_amdgcn_make_buffer_rsrc((void *)g.A, (short)0, (int)((size_t)g.M * g.lda * 2), RSRC_FLAGS);
+  const int wrows = EPI == EPI_SWIGLU ? 2 * g.F : g.N;
+  const __amdgpu_buffer_rsrc_t rw =
+      __builtin_amdgcn_make_buffer_rsrc((void *)g.W, (short)0, (int)((size_t)wrows * g.ldw * 2), RSRC_FLAGS);
+  int voff_a[NCP];
+#pragma unroll
+  for (int j = 0; j < NCP; ++j) voff_a[j] = (min(m0 + r0 + 32 * j, g.M - 1) * g.lda + cch * 8) * 2;
+  // SwiGLU: 32-row W slices alternate gate / up for the same 32 outputs; tile
+  // row 32 j + r0 (r0 < 32) reads W row tn*64 + (j>>1)*32 + r0 (+F for odd j)
+  const int wrow0 = EPI == EPI_SWIGLU ? tn * (BN / 2) + r0 : tn * BN + r0;
+  const int voff_w = (wrow0 * g.ldw + cch * 8) * 2;
+  auto wrow_step = [&](int j) {
+    return EPI == EPI_SWIGLU ? ((j >> 1) * 32 + (j & 1) * g.F) * g.ldw * 2 : 32 * j * g.ldw * 2;
+  };
+  const int kbase = kchunk * kc * 2;  // byte offset of the chunk's first K column
+  auto lds_ptr = [](u32x4 *p) { return (__attribute__((address_space(3))) void *)p; };
+  auto copy_a = [&](int kt, u32x4 *dst) {
+#if __HIP_DEVICE_COMPILE__  // the host pass cannot resolve this builtin in a template
+#pragma unroll
+    for (int j = 0; j < NCP; ++j)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, lds_ptr(dst + (4 * j + wave) * 64), 16, voff_a[j],
+                                               kbase + kt * BK * 2, 0, 0);
+#endif
+  };
+  auto copy_w = [&](int kt, u32x4 *dst) {
+#if __HIP_DEVICE_COMPILE__
+#pragma unroll
+    for (int j = 0; j < NCP; ++j)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, lds_ptr(dst + (4 * j + wave) * 64), 16, voff_w,
+                                               wrow_step(j) + kbase + kt * BK * 2, 0, 0);
+#endif
+  };
+
+  f32x16 acc[FS][TS];
+#pragma unroll
+  for (int a = 0; a < FS; ++a)
+#pragma unroll
+    for (int b = 0; b < TS; ++b)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[a][b][e] = 0.f;
+
+  const int fr = lane & 31, sw = (fr >> 1) & 7, half = lane >> 5;
+  const int rowA = wm * WT + fr, rowW = wn * WF + fr;
+  u32x4 fa[2][TS], fw[2][FS];
+  auto fload = [&](const u32x4 *sa, const u32x4 *sw_, int kk, int set) {
+    const int ch = (kk * 2 + half) ^ sw;
+#pragma unroll
+    for (int f = 0; f < FS; ++f) fw[set][f] = sw_[(rowW + 32 * f) * 8 + ch];
+#pragma unroll
+    for (int t = 0; t < TS; ++t) fa[set][t] = sa[(rowA + 32 * t) * 8 + ch];
+  };
+  auto mfma_kk = [&](int set) {
+#pragma unroll
+    for (int f = 0; f < FS; ++f)
+#pragma unroll
+      for (int t = 0; t < TS; ++t) acc[f][t] = mfma32x32x16(fw[set][f], fa[set][t], acc[f][t]);
+  };
+  auto interleave = [&](auto n_mfma, auto n_rd, auto n_cp) {
+    constexpr int NM = decltype(n_mfma)::value, NR = decltype(n_rd)::value, NC = decltype(n_cp)::value;
+#pragma unroll
+    for (int i = 0; i < NM; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);              // one MFMA
+      if (i < NR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+      if (i < NC) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // one copy
+    }
+  };
+  using I0 = std::integral_constant<int, 0>;
+  using I4 = std::integral_constant<int, FS * TS>;
+  using IR = std::integral_constant<int, FS + TS>;
+  using IC = std::integral_constant<int, NCP>;
+  auto SA = [&](auto i) -> u32x4 * {
+    if constexpr (decltype(i)::value == 0) return sA0;
+    else return sA1;
+  };
+  auto SW = [&](auto i) -> u32x4 * {
+    if constexpr (decltype(i)::value == 0) return sW0;
+    else if constexpr (decltype(i)::value == 1) return sW1;
+    else return sW2;
+  };
+  using std::integral_constant;
+
+  const int nk = kc / BK;
+  // Step kt: the large kernel's step (A slice kt+1 and W slice kt+2 copied
+  // into the stages step kt-1 released, the barrier waits for all but the
+  // newest W copy).
+  auto step = [&](int kt, auto pa, auto pw) {
+    constexpr int PA = decltype(pa)::value, PW = decltype(pw)::value;
+    const u32x4 *a = SA(pa), *w = SW(pw);
+    copy_a(min(kt + 1, nk - 1), SA(integral_constant<int, PA ^ 1>{}));
+    __builtin_amdgcn_sched_barrier(0);  // the A copies are issued before the W copies
+    copy_w(min(kt + 2, nk - 1), SW(integral_constant<int, (PW + 2) % 3>{}));
+    fload(a, w, 1, 1);
+    mfma_kk(0);
+    interleave(I4{}, IR{}, IC{});
+    fload(a, w, 2, 0);
+    mfma_kk(1);
+    interleave(I4{}, IR{}, I0{});
+    fload(a, w, 3, 1);
+    mfma_kk(0);
+    interleave(I4{}, IR{}, I0{});
+    mfma_kk(1);
+    // s_waitcnt vmcnt(NCP) expcnt(7) lgkmcnt(0), then the barrier
+    __builtin_amdgcn_s_waitcnt((NCP & 15) | (7 << 4) | ((NCP >> 4) << 14));
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    fload(SA(integral_constant<int, PA ^ 1>{}), SW(integral_constant<int, (PW + 1) % 3>{}), 0, 0);
+  };
+  using C0 = std::integral_constant<int, 0>;
+  using C1 = std::integral_constant<int, 1>;
+  using C2 = std::integral_constant<int, 2>;
+  copy_a(0, sA0);
+  copy_w(0, sW0);
+  __builtin_amdgcn_sched_barrier(0);  // slice 0 is issued before W slice 1
+  copy_w(min(1, nk - 1), sW1);
+  __builtin_amdgcn_s_waitcnt((NCP & 15) | (7 << 4) | ((NCP >> 4) << 14));
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  fload(sA0, sW0, 0, 0);
+  int kt = 0;
+  for (; kt + 6 <= nk; kt += 6) {
+    step(kt, C0{}, C0{});
+    step(kt + 1, C1{}, C1{});
+    step(kt + 2, C0{}, C2{});
+    step(kt + 3, C1{}, C0{});
+    step(kt + 4, C0{}, C1{});
+    step(kt + 5, C1{}, C2{});
+  }
+  if (kt < nk) step(kt, C0{}, C0{});
+  if (kt + 1 < nk) step(kt + 1, C1{}, C1{});
+  if (kt + 2 < nk) step(kt + 2, C0{}, C2{});
+  if (kt + 3 < nk) step(kt + 3, C1{}, C0{});
+  if (kt + 4 < nk) step(kt + 4, C0{}, C1{});
+  // every copy has landed (vmcnt(0) expcnt(7) lgkmcnt(0)) and every fragment
+  // read is done before the epilogue reuses the stages
+  __builtin_amdgcn_s_waitcnt(7 << 4);
+  __syncthreads();
+
+  const int h4 = 4 * half;
+  if constexpr (EPI == EPI_QKV) {
+    qkv_epilogue<BM, THREADS, TS, FS>(g, m0, tn * BN, wm * WT, tn * BN + wn * WF, acc, tid,
+                                      LdsObjs<4, BM * 8>{sA0, sA1, sW0, sW1});
+    return;
+  }
+#pragma unroll
+  for (int t = 0; t < TS; ++t) {
+    const int m = m0 + wm * WT + t * 32 + fr;
+    if (m >= g.M) continue;
+    if constexpr (EPI == EPI_SWIGLU) {
+#pragma unroll
+      for (int p = 0; p < FS / 2; ++p)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          store4_swiglu(g, m, tn * (BN / 2) + wn * (WF / 2) + p * 32 + 8 * j + h4, quad(acc[2 * p][t], j),
+                        quad(acc[2 * p + 1][t], j));
+    } else if (split) {
+      float *prow = g.part + ((size_t)kchunk * g.M + m) * g.N;
+#pragma unroll
+      for (int f = 0; f < FS; ++f)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) *(f32x4 *)(prow + tn * BN + wn * WF + f * 32 + 8 * j + h4) = quad(acc[f][t], j);
     } else {
 #pragma unroll
       for (int f = 0; f < FS; ++f)

@@ -198,6 +198,9 @@ qi_status launch_gemm(const GemmArgs &g, int kind, hipStream_t s) {
     if (big) {
       hipLaunchKernelGGL((gemm_bf16_large_kernel<EPI, QI_GEMM_WM, QI_GEMM_WN>), dim3(tiles_big),
                          dim3(64 * QI_GEMM_WM * QI_GEMM_WN), 0, s, g);
+    } else if (fits32) {
+      hipLaunchKernelGGL((gemm_bf16_mid_kernel<EPI>), dim3(tiles_small * (g.ksplit > 1 ? g.ksplit : 1)),
+                         dim3(gemmM::THREADS), 0, s, g);
     } else if (EPI == EPI_RESID && g.ksplit > 1) {
       hipLaunchKernelGGL((gemm_bf16_kernel<EPI, 128, 128>), dim3(tiles_small * g.ksplit), dim3(gemm::THREADS), 0,
                          s, g);
