@@ -469,18 +469,21 @@ __global__ __launch_bounds__(256) void resid_reduce_kernel(const GemmArgs g) {
   *xp = *xp + *(const f32x4 *)gp * v;
 }
 
-// ---------------------------------------------------------------- 256 x 256 tiles
+// ---------------------------------------------------------------- 256-row W tiles, 8 waves
 // Large-M shape: one 256 x 256 tile per workgroup of 8 waves (2 along tokens
 // x 4 along W rows; wave tile 128 tokens x 64 W rows, MFMA 32x32x16), one
 // workgroup per CU.  A 256-row operand tile costs 4x fewer fetched bytes per
-// FLOP than the 128 x 128 tile.
+// FLOP than the 128 x 128 tile.  The same kernel with BMT = 128 token rows
+// (wave tile 64 x 64, the 128 x 128 kernels' MFMA sequence) serves a few
+// hundred rows: one workgroup per CU still, and 3/4 of the copied bytes per
+// FLOP of two 128 x 128 workgroups.
 //
 // Operands go from global memory straight into LDS (buffer loads with the LDS
 // flag: lane l of a copy instruction lands 16 bytes at slot base + l), so no
 // register staging and no LDS store instructions: measured on gfx950, a
 // ds_write_b128 costs the LDS about 2.5x a ds_read_b128 per byte, and with
 // register staging the stores held the K loop to ~70% of MFMA rate.
-// Each K step of 64 moves a 32 KB A slice and a 32 KB W slice.  The A
+// Each K step of 64 moves a BMT-row A slice and a 32 KB W slice.  The A
 // slices (activations, just written by the previous kernel, mostly cache
 // hits) are double-buffered and copied one step ahead; the W slices (weights,
 // streamed from HBM) are triple-buffered and copied two steps ahead, so a W
@@ -494,20 +497,28 @@ __global__ __launch_bounds__(256) void resid_reduce_kernel(const GemmArgs g) {
 // slot r * 8 + (c ^ ((r >> 1) & 7)) (see lds_slot).  Copy instruction j of
 // wave w fills slots (8 j + w) * 64 .. + 63: rows 64 j + 8 w + lane / 8, slot
 // lane % 8 holding chunk (lane % 8) ^ ((row >> 1) & 7) -- which does not
-// depend on j -- so each lane's source offset is fixed and j only adds a
-// uniform 64-row step.  Rows past M read as zero (buffer range check).
+// depend on j -- so each lane's W source offset is fixed and j only adds a
+// uniform 64-row step.  Token rows past M are clamped to row M - 1 (loaded,
+// never stored), so every copy stays inside the operands.
+//
+// EPI_RESID may split K (BMT = 128 only in practice): as in the 128 x 128
+// kernels, chunk s of K writes fp32 partial sums and resid_reduce_kernel adds
+// them in order.
 namespace gemmL {
-constexpr int BM = 256, BN = 256, BK = 64, THREADS = 512;
-constexpr int TS = 4, FS = 2;           // wave tile: 4 x 32 tokens, 2 x 32 W rows
-constexpr int NCP = BM * 8 / THREADS;   // copy instructions per operand slice per thread (4)
+constexpr int BN = 256, BK = 64, THREADS = 512;
+constexpr int FS = 2;                   // wave tile: 2 x 32 W rows
+constexpr int NCP = BN * 8 / THREADS;   // W copy instructions per slice per thread (4)
 constexpr int RSRC_FLAGS = 0x00020000;  // raw buffer, 32-bit dwords
 }  // namespace gemmL
 
-template <int EPI, int WMN, int WNN>
+template <int EPI, int WMN, int WNN, int BMT = 256>
 __global__ __launch_bounds__(gemmL::THREADS, 1) void gemm_bf16_large_kernel(const GemmArgs g) {
   using namespace gemmL;
   static_assert(WMN == 2 && WNN == 4, "8 waves as 2 x 4");
+  static_assert(BMT == 256 || BMT == 128, "256 or 128 token rows");
   if (g.skip && *g.skip) return;
+  constexpr int BM = BMT, TS = BM / (WMN * 32);
+  constexpr int NCPA = BM * 8 / THREADS;  // A copy instructions per slice per thread (4 or 2)
   constexpr int WT = BM / WMN, WF = BN / WNN;
   __shared__ u32x4 sA0[BM * 8], sA1[BM * 8];
   __shared__ u32x4 sW0[BN * 8], sW1[BN * 8], sW2[BN * 8];
@@ -516,8 +527,12 @@ __global__ __launch_bounds__(gemmL::THREADS, 1) void gemm_bf16_large_kernel(cons
   const int wm = wave % WMN, wn = wave / WMN;
   const int nTM = (g.M + BM - 1) / BM;
   const int nTN = EPI == EPI_SWIGLU ? g.F / (BN / 2) : g.N / BN;
+  const bool split = EPI == EPI_RESID && g.ksplit > 1;
+  const int ntile = nTM * nTN;
+  const int kchunk = split ? (int)(blockIdx.x / ntile) : 0;
+  const int kc = split ? g.K / g.ksplit : g.K;
   int tm, tn;
-  tile_of(blockIdx.x, nTM, nTN, tm, tn);
+  tile_of(split ? (int)(blockIdx.x % ntile) : (int)blockIdx.x, nTM, nTN, tm, tn);
   const int m0 = tm * BM;
 
   // copy sources: tile row r0 + 64 j, chunk cch
@@ -528,21 +543,23 @@ __global__ __launch_bounds__(gemmL::THREADS, 1) void gemm_bf16_large_kernel(cons
   const int wrows = EPI == EPI_SWIGLU ? 2 * g.F : g.N;
   const __amdgpu_buffer_rsrc_t rw =
       __builtin_amdgcn_make_buffer_rsrc((void *)g.W, (short)0, (int)((size_t)wrows * g.ldw * 2), RSRC_FLAGS);
-  const int voff_a = ((m0 + r0) * g.lda + cch * 8) * 2;
+  int voff_a[NCPA];
+#pragma unroll
+  for (int j = 0; j < NCPA; ++j) voff_a[j] = (min(m0 + r0 + 64 * j, g.M - 1) * g.lda + cch * 8) * 2;
   // SwiGLU: W tile rows alternate 32-row gate / up slices for the same 32
   // outputs: tile row r reads W row tn*128 + (r>>6)*32 + (r&31) (+F when bit
   // 5 of r is set); for r = r0 + 64 j that is a per-lane part plus 32 j.
   const int wrow0 = EPI == EPI_SWIGLU ? tn * (BN / 2) + (r0 & 31) + ((r0 >> 5) & 1) * g.F : tn * BN + r0;
   const int voff_w = (wrow0 * g.ldw + cch * 8) * 2;
   const int wstep = (EPI == EPI_SWIGLU ? 32 : 64) * g.ldw * 2;  // bytes per copy instruction j
-  const int astep = 64 * g.lda * 2;
+  const int kbase = kchunk * kc * 2;                            // the chunk's first K column, bytes
   auto lds_ptr = [](u32x4 *p) { return (__attribute__((address_space(3))) void *)p; };
   auto copy_a = [&](int kt, u32x4 *dst) {
 #if __HIP_DEVICE_COMPILE__  // the host pass cannot resolve this builtin in a template
 #pragma unroll
-    for (int j = 0; j < NCP; ++j)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, lds_ptr(dst + (8 * j + wave) * 64), 16, voff_a,
-                                               astep * j + kt * BK * 2, 0, 0);
+    for (int j = 0; j < NCPA; ++j)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, lds_ptr(dst + (8 * j + wave) * 64), 16, voff_a[j],
+                                               kbase + kt * BK * 2, 0, 0);
 #endif
   };
   auto copy_w = [&](int kt, u32x4 *dst) {
@@ -550,7 +567,7 @@ __global__ __launch_bounds__(gemmL::THREADS, 1) void gemm_bf16_large_kernel(cons
 #pragma unroll
     for (int j = 0; j < NCP; ++j)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, lds_ptr(dst + (8 * j + wave) * 64), 16, voff_w,
-                                               wstep * j + kt * BK * 2, 0, 0);
+                                               wstep * j + kbase + kt * BK * 2, 0, 0);
 #endif
   };
 
@@ -591,7 +608,7 @@ __global__ __launch_bounds__(gemmL::THREADS, 1) void gemm_bf16_large_kernel(cons
     }
   };
   using I0 = std::integral_constant<int, 0>;
-  using I8 = std::integral_constant<int, FS * TS>;
+  using IM = std::integral_constant<int, FS * TS>;
   using IR = std::integral_constant<int, FS + TS>;
   using IC = std::integral_constant<int, NCP>;
   // stage objects by compile-time index
@@ -606,7 +623,7 @@ __global__ __launch_bounds__(gemmL::THREADS, 1) void gemm_bf16_large_kernel(cons
   };
   using std::integral_constant;
 
-  const int nk = g.K / BK;
+  const int nk = kc / BK;
   // Step kt reads A stage PA = kt % 2 and W stage PW = kt % 3 (sub-step 0's
   // fragments already in register set 0).  It first copies A slice kt+1 into
   // the other A stage, then (strictly after, in issue order) W slice kt+2
@@ -625,13 +642,13 @@ __global__ __launch_bounds__(gemmL::THREADS, 1) void gemm_bf16_large_kernel(cons
     copy_w(min(kt + 2, nk - 1), SW(integral_constant<int, (PW + 2) % 3>{}));
     fload(a, w, 1, 1);
     mfma_kk(0);
-    interleave(I8{}, IR{}, IC{});
+    interleave(IM{}, IR{}, IC{});
     fload(a, w, 2, 0);
     mfma_kk(1);
-    interleave(I8{}, IR{}, I0{});
+    interleave(IM{}, IR{}, I0{});
     fload(a, w, 3, 1);
     mfma_kk(0);
-    interleave(I8{}, IR{}, I0{});
+    interleave(IM{}, IR{}, I0{});
     mfma_kk(1);
     // s_waitcnt vmcnt(NCP) expcnt(7) lgkmcnt(0), then the barrier
     __builtin_amdgcn_s_waitcnt((NCP & 15) | (7 << 4) | ((NCP >> 4) << 14));
@@ -664,12 +681,19 @@ __global__ __launch_bounds__(gemmL::THREADS, 1) void gemm_bf16_large_kernel(cons
   if (kt + 2 < nk) step(kt + 2, C0{}, C2{});
   if (kt + 3 < nk) step(kt + 3, C1{}, C0{});
   if (kt + 4 < nk) step(kt + 4, C0{}, C1{});
-  __syncthreads();  // every copy has landed and every fragment read is done
+  // every copy has landed (vmcnt(0) expcnt(7) lgkmcnt(0)) and every fragment
+  // read is done before the epilogue reuses the stages
+  __builtin_amdgcn_s_waitcnt(7 << 4);
+  __syncthreads();
 
   const int h4 = 4 * half;
   if constexpr (EPI == EPI_QKV) {
-    qkv_epilogue<BM, THREADS, TS, FS>(g, m0, tn * BN, wm * WT, tn * BN + wn * WF, acc, tid,
-                                      LdsObjs<4>{sA0, sA1, sW0, sW1});
+    if constexpr (BM == 256)
+      qkv_epilogue<BM, THREADS, TS, FS>(g, m0, tn * BN, wm * WT, tn * BN + wn * WF, acc, tid,
+                                        LdsObjs<4>{sA0, sA1, sW0, sW1});
+    else
+      qkv_epilogue<BM, THREADS, TS, FS>(g, m0, tn * BN, wm * WT, tn * BN + wn * WF, acc, tid,
+                                        LdsObjs<4, BM * 8>{sA0, sA1, sW0, sW1});
     return;
   }
 #pragma unroll
@@ -683,6 +707,12 @@ __global__ __launch_bounds__(gemmL::THREADS, 1) void gemm_bf16_large_kernel(cons
         for (int j = 0; j < 4; ++j)
           store4_swiglu(g, m, tn * (BN / 2) + wn * (WF / 2) + p * 32 + 8 * j + h4, quad(acc[2 * p][t], j),
                         quad(acc[2 * p + 1][t], j));
+    } else if (split) {
+      float *prow = g.part + ((size_t)kchunk * g.M + m) * g.N;
+#pragma unroll
+      for (int f = 0; f < FS; ++f)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) *(f32x4 *)(prow + tn * BN + wn * WF + f * 32 + 8 * j + h4) = quad(acc[f][t], j);
     } else {
 #pragma unroll
       for (int f = 0; f < FS; ++f)

@@ -168,10 +168,7 @@ struct TimedLaunch {
     if (s__ != QI_OK) return s__;  \
   } while (0)
 
-// Tile shape per launch: 256 x 256 (the large-tile kernel) when that still
-// gives at least one full wave of workgroups over the 256 CUs, else 128 x 128.
-// Both issue the same MFMA over the same K order for every output element, so
-// the choice never changes a result bit.
+// The register-staged 128 x 128 kernel, for operands past 32-bit buffer offsets.
 template <int EPI, int BM, int BN>
 void launch_gemm_tile(const GemmArgs &g, hipStream_t s) {
   const int nTM = (g.M + BM - 1) / BM;
@@ -179,33 +176,63 @@ void launch_gemm_tile(const GemmArgs &g, hipStream_t s) {
   hipLaunchKernelGGL((gemm_bf16_kernel<EPI, BM, BN>), dim3(nTM * nTN), dim3(gemm::THREADS), 0, s, g);
 }
 
+// Tile shape per launch, from the number of rounds of workgroups each shape
+// needs over the 256 CUs and a per-round time relative to a round of
+// 256 x 256 tiles (one per CU), measured on MI355X at K = 4096: a round of
+// 128 x 256 tiles (8 waves, one per CU) takes 0.59 of it; a full round of
+// 128 x 128 tiles (4 waves, two per CU) 0.65, and 0.45 when no CU gets a
+// second one.  All three issue the same MFMA over the same K order for every
+// output element, so the choice never changes a result bit.
+enum GemmShape { SHAPE_256x256, SHAPE_128x256, SHAPE_128x128 };
+
+template <int EPI>
+GemmShape gemm_shape(const GemmArgs &g, int &grid) {
+  const int n_out = EPI == EPI_SWIGLU ? g.F : g.N;
+  const int per_tile_w = EPI == EPI_SWIGLU ? 128 : 256;  // outputs of a 256-row W tile
+  const int ks = g.ksplit > 1 ? g.ksplit : 1;
+  const int cols_w = n_out % per_tile_w == 0 ? n_out / per_tile_w : 0;
+  const int tiles_256 = ((g.M + 255) / 256) * cols_w * ks;
+  const int tiles_128w = ((g.M + 127) / 128) * cols_w * ks;
+  const int tiles_128 = ((g.M + 127) / 128) * (EPI == EPI_SWIGLU ? g.F / 64 : g.N / 128) * ks;
+  auto rounds = [](int tiles, int per_round) { return (tiles + per_round - 1) / per_round; };
+  const int c256 = cols_w ? 100 * rounds(tiles_256, 256) : INT32_MAX;
+  const int c128w = cols_w ? 59 * rounds(tiles_128w, 256) : INT32_MAX;
+  const int c128 = tiles_128 <= 256 ? 45 : 65 * rounds(tiles_128, 512);
+  if (c256 <= c128w && c256 <= c128) {
+    grid = tiles_256;
+    return SHAPE_256x256;
+  }
+  if (c128w <= c128) {
+    grid = tiles_128w;
+    return SHAPE_128x256;
+  }
+  grid = tiles_128;
+  return SHAPE_128x128;
+}
+
 template <int EPI>
 qi_status launch_gemm(const GemmArgs &g, int kind, hipStream_t s) {
-  const int n_out = EPI == EPI_SWIGLU ? g.F : g.N;
-  const int per_tile_big = EPI == EPI_SWIGLU ? 128 : 256;
-  const int nTM_big = (g.M + 255) / 256;
-  const int tiles_big = n_out % per_tile_big == 0 ? nTM_big * (n_out / per_tile_big) : 0;
-  const int tiles_small = ((g.M + 127) / 128) * (EPI == EPI_SWIGLU ? g.F / 64 : g.N / 128);
+  // the LDS-copy kernels address each operand with a 32-bit buffer offset
   const bool fits32 = (size_t)g.M * g.lda * 2 < (1ull << 31) &&
                       (size_t)(EPI == EPI_SWIGLU ? 2 * g.F : g.N) * g.ldw * 2 < (1ull << 31);
-  // Rounds of workgroups over the 256 CUs: one 256 x 256 tile per CU, two
-  // 128 x 128 tiles per CU (each about 0.85 of a large round per round,
-  // measured).  The large tile when it needs no more time.
-  const int rounds_big = (tiles_big + 255) / 256, rounds_small = (tiles_small + 511) / 512;
-  const bool big = g.ksplit <= 1 && fits32 && tiles_big >= 256 && 100 * rounds_big <= 85 * rounds_small;
   {
     TimedLaunch tl(kind, s);
-    if (big) {
-      hipLaunchKernelGGL((gemm_bf16_large_kernel<EPI, QI_GEMM_WM, QI_GEMM_WN>), dim3(tiles_big),
-                         dim3(64 * QI_GEMM_WM * QI_GEMM_WN), 0, s, g);
-    } else if (fits32) {
-      hipLaunchKernelGGL((gemm_bf16_mid_kernel<EPI>), dim3(tiles_small * (g.ksplit > 1 ? g.ksplit : 1)),
-                         dim3(gemmM::THREADS), 0, s, g);
-    } else if (EPI == EPI_RESID && g.ksplit > 1) {
-      hipLaunchKernelGGL((gemm_bf16_kernel<EPI, 128, 128>), dim3(tiles_small * g.ksplit), dim3(gemm::THREADS), 0,
-                         s, g);
+    int grid = 0;
+    const GemmShape shape = fits32 ? gemm_shape<EPI>(g, grid) : SHAPE_128x128;
+    if (!fits32) {
+      const int tiles = ((g.M + 127) / 128) * (EPI == EPI_SWIGLU ? g.F / 64 : g.N / 128);
+      if (EPI == EPI_RESID && g.ksplit > 1)
+        hipLaunchKernelGGL((gemm_bf16_kernel<EPI, 128, 128>), dim3(tiles * g.ksplit), dim3(gemm::THREADS), 0, s, g);
+      else
+        launch_gemm_tile<EPI, 128, 128>(g, s);
+    } else if (shape == SHAPE_256x256) {
+      hipLaunchKernelGGL((gemm_bf16_large_kernel<EPI, QI_GEMM_WM, QI_GEMM_WN, 256>), dim3(grid),
+                         dim3(gemmL::THREADS), 0, s, g);
+    } else if (shape == SHAPE_128x256) {
+      hipLaunchKernelGGL((gemm_bf16_large_kernel<EPI, QI_GEMM_WM, QI_GEMM_WN, 128>), dim3(grid),
+                         dim3(gemmL::THREADS), 0, s, g);
     } else {
-      launch_gemm_tile<EPI, 128, 128>(g, s);
+      hipLaunchKernelGGL((gemm_bf16_mid_kernel<EPI>), dim3(grid), dim3(gemmM::THREADS), 0, s, g);
     }
   }
   QI_TRY(last_launch());
