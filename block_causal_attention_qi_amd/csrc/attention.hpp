@@ -132,9 +132,11 @@ __global__ __launch_bounds__(attn::THREADS, 1) void block_causal_attn_kernel(con
   // applied on the global side by choosing which chunk each lane fetches.
   // The copies are buffer loads over one resource per segment and operand
   // (this head's K [len][128], V^T [128][ldv]): each lane's offset inside a
-  // tile is fixed and precomputed, the tile's first key enters as the uniform
-  // scalar offset, and K rows past the segment read as zeros (range check;
-  // masked below) -- no address arithmetic per tile.
+  // tile is fixed and precomputed.  For K the tile's first key is added to
+  // that per-lane offset, which the buffer's range check covers, so K rows
+  // past the segment read as zeros and never past the caller's buffer
+  // (masked below in any case); a V^T tile is always inside its row
+  // (ldv >= key0 + 64), so its first key enters as the uniform scalar offset.
   constexpr int RSRC_FLAGS = 0x00020000;  // raw buffer, 32-bit dwords
   const __amdgpu_buffer_rsrc_t rk_t = __builtin_amdgcn_make_buffer_rsrc((void *)Kt, (short)0, a.L * 256, RSRC_FLAGS);
   const __amdgpu_buffer_rsrc_t rk_i = __builtin_amdgcn_make_buffer_rsrc((void *)Ki, (short)0, a.N * 256, RSRC_FLAGS);
@@ -160,8 +162,8 @@ __global__ __launch_bounds__(attn::THREADS, 1) void block_causal_attn_kernel(con
 #if __HIP_DEVICE_COMPILE__  // the host pass cannot resolve this builtin in a template
 #pragma unroll
     for (int j = 0; j < NLD; ++j)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(tx ? rk_t : rk_i, lds_ptr(sk + (j * WAVES + wave) * 64), 16, koff[j],
-                                               key0 * 256, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(tx ? rk_t : rk_i, lds_ptr(sk + (j * WAVES + wave) * 64), 16,
+                                               koff[j] + key0 * 256, 0, 0, 0);
 #endif
   };
   auto copy_v = [&](int t, auto B) {
