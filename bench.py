@@ -84,8 +84,8 @@ def calibrate_copy():
 
 def calibrate():
     """Sustained rates of the running part: the library's register-only MFMA
-    loops, copy kernel and LDS / MFMA instruction mixes (shader cycles per
-    iteration of 8 waves per CU), and torch's (vendor library) bf16 GEMM on
+    loops, copy kernel, LDS / MFMA and VALU / MFMA instruction mixes (shader
+    cycles per iteration of 8 waves per CU), and torch's (vendor library) bf16 GEMM on
     the four projection shapes of the 1024^2 step."""
     import ctypes
 
@@ -113,6 +113,12 @@ def calibrate():
         _lib.check(lib.qi_calib_lds_cycles(mode, 20000, ctypes.byref(v)), "qi_calib_lds_cycles")
         lds[name] = round(v.value, 1)
     res["lds_mix_cycles_per_iteration_per_cu"] = lds
+    valu = {}
+    for mode, name in ((0, "32_exp"), (1, "32_fma"), (2, "8_mfma_32_exp"), (3, "8_mfma_32_fma"), (4, "8_mfma")):
+        v = ctypes.c_double(0)
+        _lib.check(lib.qi_calib_valu_cycles(mode, 20000, ctypes.byref(v)), "qi_calib_valu_cycles")
+        valu[name] = round(v.value, 1)
+    res["valu_mix_cycles_per_iteration_per_wave_two_waves_per_simd"] = valu
     gemm = {}
     for (M, N, K) in [(4096, 24576, 4096), (4096, 12288, 4096), (4096, 4096, 12288), (4096, 4096, 4096)]:
         A = torch.randn(M, K, device="cuda", dtype=torch.bfloat16)

@@ -133,6 +133,60 @@ __global__ __launch_bounds__(512, 1) void lds_mix_kernel(float *out, int iters, 
   }
 }
 
+// One 512-thread workgroup per CU (8 waves, two per SIMD); each iteration
+// every wave issues the MODE's mix (qi_calib.h) on 8 independent chains;
+// wave 0 of each workgroup adds its shader cycles to clk[0] and 1 to clk[1].
+template <int MODE>
+__global__ __launch_bounds__(512, 1) void valu_mix_kernel(float *out, int iters, unsigned long long *clk) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  float v[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) v[j] = -1.f - 0.01f * (float)(lane + j);
+  f32x16 acc[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[j][e] = 0.f;
+  bf16x8 a, b;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    a[i] = (__bf16)(lane * 0.01f);
+    b[i] = (__bf16)0.5f;
+  }
+  constexpr bool kMfma = MODE >= 2, kExp = MODE == 0 || MODE == 2, kFma = MODE == 1 || MODE == 3;
+  const uint64_t t0 = __builtin_amdgcn_s_memtime();
+  for (int it = 0; it < iters; ++it) {
+    if constexpr (kMfma) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[j], 0, 0, 0);
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        if constexpr (kExp) v[j] = __builtin_amdgcn_exp2f(v[j]);
+        if constexpr (kFma) v[j] = __builtin_fmaf(v[j], 0.999f, 0.001f);
+      }
+    if constexpr (kMfma && MODE != 4) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+        __builtin_amdgcn_sched_group_barrier(0x402, 4, 0);  // four VALU / transcendental
+      }
+    }
+  }
+  const uint64_t t1 = __builtin_amdgcn_s_memtime();
+  float sum = 0.f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) sum += v[j] + acc[j][0];
+  // keeps the work alive: the compiler cannot decide this (practically never true)
+  if (__float_as_uint(sum) == (uint32_t)iters * 2654435761u) out[tid] = sum;
+  if (tid == 0) {
+    atomicAdd(&clk[0], (unsigned long long)(t1 - t0));
+    atomicAdd(&clk[1], 1ull);
+  }
+}
+
 }  // namespace
 
 extern "C" {
@@ -245,6 +299,46 @@ qi_status qi_calib_lds_cycles(int32_t mode, int32_t iters, double *cycles) {
   if (out) (void)hipFree(out);
   if (clk) (void)hipFree(clk);
   if (src) (void)hipFree(src);
+  (void)hipStreamDestroy(st);
+  return rc;
+}
+
+qi_status qi_calib_valu_cycles(int32_t mode, int32_t iters, double *cycles) {
+  if (!cycles) return QI_ERR_NULL;
+  if (mode < 0 || mode > 4 || iters < 4 || iters > 10000000) return QI_ERR_RANGE;
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return QI_ERR_HIP;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return QI_ERR_HIP;
+  float *out = nullptr;
+  unsigned long long *clk = nullptr;
+  hipStream_t st;
+  if (hipStreamCreate(&st) != hipSuccess) return QI_ERR_HIP;
+  qi_status rc = QI_OK;
+  if (hipMalloc(&out, 512 * sizeof(float)) != hipSuccess || hipMalloc(&clk, 2 * sizeof(unsigned long long)) != hipSuccess)
+    rc = QI_ERR_HIP;
+  auto run = [&](int n) {
+    switch (mode) {
+      case 0: hipLaunchKernelGGL(valu_mix_kernel<0>, dim3(cus), dim3(512), 0, st, out, n, clk); break;
+      case 1: hipLaunchKernelGGL(valu_mix_kernel<1>, dim3(cus), dim3(512), 0, st, out, n, clk); break;
+      case 2: hipLaunchKernelGGL(valu_mix_kernel<2>, dim3(cus), dim3(512), 0, st, out, n, clk); break;
+      case 3: hipLaunchKernelGGL(valu_mix_kernel<3>, dim3(cus), dim3(512), 0, st, out, n, clk); break;
+      default: hipLaunchKernelGGL(valu_mix_kernel<4>, dim3(cus), dim3(512), 0, st, out, n, clk); break;
+    }
+  };
+  unsigned long long h[2] = {0, 0};
+  if (rc == QI_OK) {
+    run(100);  // warm-up
+    if (hipMemsetAsync(clk, 0, 2 * sizeof(unsigned long long), st) != hipSuccess) rc = QI_ERR_HIP;
+  }
+  if (rc == QI_OK) {
+    run(iters);
+    if (hipMemcpyAsync(h, clk, sizeof(h), hipMemcpyDeviceToHost, st) != hipSuccess ||
+        hipStreamSynchronize(st) != hipSuccess || hipGetLastError() != hipSuccess)
+      rc = QI_ERR_HIP;
+  }
+  *cycles = (rc == QI_OK && h[1]) ? (double)h[0] / (double)h[1] / iters : 0.0;
+  if (out) (void)hipFree(out);
+  if (clk) (void)hipFree(clk);
   (void)hipStreamDestroy(st);
   return rc;
 }

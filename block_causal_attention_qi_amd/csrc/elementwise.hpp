@@ -170,48 +170,56 @@ __global__ __launch_bounds__(512) void mod_gemv_kernel(const u16 *W, const float
 
 // ----------------------------------------------------------------- embed
 // x[row0 + i][n] = sum_c X[i][c] W[n][c] + b[n]  (img-in Linear 64 -> H, fp32).
-// A workgroup computes 32 tokens x 256 features, each wave 32 tokens x 64
-// features as two 32 x 32 blocks, on the bf16 matrix cores at fp32 accuracy:
+// A workgroup computes TB blocks of 32 tokens x 256 features, each wave 32
+// tokens x 64 features per block as two 32 x 32 blocks (its W slice and bias
+// loaded once for the TB blocks), on the bf16 matrix cores at fp32 accuracy:
 // X (fp32) is split exactly into three bf16 planes, each plane goes through
 // v_mfma_f32_32x32x16_bf16 (A = 32 tokens x 16 channels, B = 16 channels x 32
 // features of the exactly-bf16 W), so every partial product is exact and the
 // sums are fp32.  A lane's results are 32 consecutive features of the block
 // across the half-wave for each token row: 128-byte coalesced stores.
 // H % 256 == 0.
+template <int TB>
 __global__ __launch_bounds__(256) void img_embed_kernel(const float *X, int N, const u16 *W,
                                                         const float *b, int H, float *x, int ldx,
                                                         int row0) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int l32 = lane & 31, hf = lane >> 5;
-  const int t0 = blockIdx.x * 32;
   const int n0 = blockIdx.y * 256 + wave * 64;
-  // this lane's token row and its 4 x 8 channels (k steps of 16, 8 channels per half-wave)
-  const float *xr = X + (size_t)min(t0 + l32, N - 1) * 64;
-  u32x4 pa[4][3];
-#pragma unroll
-  for (int ks = 0; ks < 4; ++ks) {
-    const f32x4 lo = *(const f32x4 *)(xr + 16 * ks + 8 * hf), hi = *(const f32x4 *)(xr + 16 * ks + 8 * hf + 4);
-    split3(lo, hi, pa[ks][0], pa[ks][1], pa[ks][2]);
-  }
+  u32x4 wv[2][4];
+  float bn[2];
 #pragma unroll
   for (int nb = 0; nb < 2; ++nb) {
     const int n = n0 + 32 * nb + l32;
-    u32x4 wv[4];
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) wv[ks] = *(const u32x4 *)(W + (size_t)n * 64 + 16 * ks + 8 * hf);
-    f32x16 acc;
+    for (int ks = 0; ks < 4; ++ks) wv[nb][ks] = *(const u32x4 *)(W + (size_t)n * 64 + 16 * ks + 8 * hf);
+    bn[nb] = b[n];
+  }
+  for (int tb = 0; tb < TB; ++tb) {
+    const int t0 = (blockIdx.x * TB + tb) * 32;
+    if (t0 >= N) break;
+    const float *xr = X + (size_t)min(t0 + l32, N - 1) * 64;
+    u32x4 pa[4][3];
 #pragma unroll
-    for (int e = 0; e < 16; ++e) acc[e] = 0.f;
+    for (int ks = 0; ks < 4; ++ks) {
+      const f32x4 lo = *(const f32x4 *)(xr + 16 * ks + 8 * hf), hi = *(const f32x4 *)(xr + 16 * ks + 8 * hf + 4);
+      split3(lo, hi, pa[ks][0], pa[ks][1], pa[ks][2]);
+    }
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
+    for (int nb = 0; nb < 2; ++nb) {
+      const int n = n0 + 32 * nb + l32;
+      f32x16 acc;
 #pragma unroll
-      for (int p = 0; p < 3; ++p) acc = mfma32x32x16(pa[ks][p], wv[ks], acc);
-    const float bn = b[n];
-    // element i: token 8 (i / 4) + 4 hf + i % 4 of the tile, feature n
+      for (int e = 0; e < 16; ++e) acc[e] = 0.f;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int tok = t0 + 8 * (i >> 2) + 4 * hf + (i & 3);
-      if (tok < N) x[(size_t)(row0 + tok) * ldx + n] = acc[i] + bn;
+      for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+        for (int p = 0; p < 3; ++p) acc = mfma32x32x16(pa[ks][p], wv[nb][ks], acc);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int tok = t0 + 8 * (i >> 2) + 4 * hf + (i & 3);
+        if (tok < N) x[(size_t)(row0 + tok) * ldx + n] = acc[i] + bn[nb];
+      }
     }
   }
 }

@@ -245,6 +245,20 @@ qi_status launch_gemm(const GemmArgs &g, int kind, hipStream_t s) {
   return QI_OK;
 }
 
+// img-in embed of N image tokens into x rows row0.. (ldx = H): four 32-token
+// blocks per workgroup from N = 4096 on (a W slice loaded once serves 128
+// tokens; 35 -> 24 us at N = 4096 on MI355X), one below, where four would
+// leave CUs idle (N = 256: 10 -> 14 us).
+void launch_img_embed(const float *img_tokens, int N, const qi_model_w &w, int H, float *x, int row0,
+                      hipStream_t s) {
+  if (N >= 4096)
+    hipLaunchKernelGGL(img_embed_kernel<4>, dim3((N + 127) / 128, H / 256), dim3(256), 0, s, img_tokens, N, w.w_img,
+                       w.b_img, H, x, H, row0);
+  else
+    hipLaunchKernelGGL(img_embed_kernel<1>, dim3((N + 31) / 32, H / 256), dim3(256), 0, s, img_tokens, N, w.w_img,
+                       w.b_img, H, x, H, row0);
+}
+
 // The output head over `rows` rows of x [rows][H]; H % 256 == 0 (checked with
 // the model dimensions).
 void launch_head(const float *x, int H, int rows, const qi_model_w &w, float eps, float *vel, hipStream_t s) {
@@ -456,8 +470,7 @@ qi_status run_step(const qi_dims &d, const qi_model_w &w, int L, int N, const fl
   }
   {
     TimedLaunch tl(QI_KERNEL_IMG_EMBED, s);
-    hipLaunchKernelGGL(img_embed_kernel, dim3((N + 31) / 32, H / 256), dim3(256), 0, s, img_tokens, N,
-                       w.w_img, w.b_img, H, x, H, L_rows);
+    launch_img_embed(img_tokens, N, w, H, x, L_rows, s);
   }
   QI_TRY(last_launch());
 
@@ -626,8 +639,7 @@ qi_status run_step_fbc(const qi_dims &d, const qi_model_w &w, int L, int N, cons
   QI_TRY(launch_modulation(H, w.w_mod, w.b_mod, t, mod, s));
   {
     TimedLaunch tl(QI_KERNEL_IMG_EMBED, s);
-    hipLaunchKernelGGL(img_embed_kernel, dim3((N + 31) / 32, H / 256), dim3(256), 0, s, img_tokens, N,
-                       w.w_img, w.b_img, H, x, H, 0);
+    launch_img_embed(img_tokens, N, w, H, x, 0, s);
   }
   QI_TRY(last_launch());
   hipLaunchKernelGGL(fbc_copy_kernel, dim3(eblocks), dim3(256), 0, s, x0, x, n4);
@@ -662,8 +674,7 @@ qi_status run_step_cfg(const qi_dims &d, const qi_model_w &w, int N, const float
   QI_TRY(launch_modulation(H, w.w_mod, w.b_mod, t, mod, s));
   for (int b = 0; b < 2; ++b) {
     TimedLaunch tl(QI_KERNEL_IMG_EMBED, s);
-    hipLaunchKernelGGL(img_embed_kernel, dim3((N + 31) / 32, H / 256), dim3(256), 0, s, img_tokens, N,
-                       w.w_img, w.b_img, H, x, H, b * N);
+    launch_img_embed(img_tokens, N, w, H, x, b * N, s);
     QI_TRY(last_launch());
   }
   const size_t slot_p = slot_elems(d, L_pos), slot_n = slot_elems(d, L_neg);

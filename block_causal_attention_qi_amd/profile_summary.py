@@ -58,13 +58,16 @@ def _rows(path):
 
 
 def kind_of(name: str, prev: str | None) -> str:
-    if "gemm_bf16_large_kernel<2" in name or "gemm_bf16_kernel<2" in name:
-        return "gemm_gate_up"
-    if "gemm_bf16_large_kernel<3" in name or "gemm_bf16_kernel<3" in name:
-        return "gemm_qkv"
-    if "gemm_bf16_large_kernel<1" in name or "gemm_bf16_kernel<1" in name:
-        return "gemm_o" if prev == "attention" else "gemm_down"
-    if "gemm_bf16" in name:
+    import re
+    m = re.search(r"gemm_bf16_(?:large_|mid_)?kernel<(\d)", name)
+    if m:
+        epi = int(m.group(1))  # the epilogue: 0 fp32 store, 1 residual, 2 SwiGLU, 3 QKV
+        if epi == 2:
+            return "gemm_gate_up"
+        if epi == 3:
+            return "gemm_qkv"
+        if epi == 1:
+            return "gemm_o" if prev == "attention" else "gemm_down"
         return "gemm_txt"
     for key, kind in (("attn", "attention"), ("rmsnorm", "norm_mod"), ("head_kernel", "head"),
                       ("mod_gemv", "modulation"), ("img_embed", "img_embed"), ("euler", "euler")):

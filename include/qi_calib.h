@@ -49,6 +49,22 @@ qi_status qi_calib_copy_gbs(const void *src, void *dst, int64_t bytes, int32_t r
  * NULL, RANGE (mode not 0..4, iters < 4), HIP. */
 qi_status qi_calib_lds_cycles(int32_t mode, int32_t iters, double *cycles);
 
+/* Shader cycles per iteration of a CU-wide VALU / MFMA instruction mix: one
+ * workgroup of 512 threads (8 waves, two per SIMD) per CU, each wave issuing
+ * per iteration, on 8 independent register chains,
+ *   mode 0: 32 v_exp_f32,
+ *   mode 1: 32 v_fma_f32,
+ *   mode 2: 8 v_mfma_f32_32x32x16_bf16 with the 32 v_exp_f32 of mode 0
+ *           interleaved (four after each MFMA),
+ *   mode 3: 8 MFMAs with the 32 v_fma_f32 of mode 1 interleaved,
+ *   mode 4: the 8 MFMAs alone,
+ * timed with the shader clock of wave 0 of every workgroup and averaged: the
+ * issue cost of the exponentials against plain FMAs, alone and beside the
+ * matrix cores.  Data are synthetic.  BLOCKS until done.  *cycles receives
+ * the cycles per iteration.  Errors: NULL, RANGE (mode not 0..4, iters < 4),
+ * HIP. */
+qi_status qi_calib_valu_cycles(int32_t mode, int32_t iters, double *cycles);
+
 #ifdef __cplusplus
 }
 #endif

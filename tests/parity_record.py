@@ -1,8 +1,9 @@
 """Measured parity figures of the GPU tests, kept as a record.
 
-Each call appends one JSON line to gpurun_out/parity/records.jsonl (under the
-repository root; the folder the GPU runs bring back) and prints it, so the
-figures a test gates on survive the run and the long tests show progress."""
+Each call appends one JSON line to gpurun_out/parity/records.jsonl under the
+repository root and prints it, so the figures a test gates on survive the run
+and the long tests show progress.  tests/records/ keeps the records of a full
+`python -m pytest tests -m gpu` run and their summary (summarize below)."""
 from __future__ import annotations
 
 import json
@@ -33,7 +34,9 @@ def summarize(path: str) -> str:
     blocks, sampled-row blocks and whole-step velocities (the latest record of
     each kind and key wins)."""
     recs = [json.loads(line) for line in open(path) if line.strip()]
-    out = [f"Parity records from `{os.path.basename(path)}` ({len(recs)} records).", ""]
+    out = [f"Parity records from `{os.path.basename(path)}` ({len(recs)} records), written by the GPU tests of",
+           "`python -m pytest tests -m gpu` (tests/parity_record.py) on one MI355X; this summary by",
+           f"`python tests/parity_record.py {os.path.basename(path)}`.", ""]
     tf = {}
     for r in recs:
         if r["kind"] == "teacher_forced_block":

@@ -53,7 +53,7 @@ def test_calibration_library_is_separate():
     lib = _lib.load()
     cal = _lib.load_calib()
     decl = _declared_symbols("qi_calib.h")
-    assert len(decl) == 3
+    assert len(decl) == 4
     for name in decl:
         assert hasattr(cal, name), name
         assert name in _lib.CALIB_SIGNATURES, f"binding misses {name}"
