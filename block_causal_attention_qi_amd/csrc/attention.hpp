@@ -11,8 +11,9 @@
 // image row computes bit-identical results in a joint pass and in an
 // image-only pass that reads the cached text K/V.
 //
-// Per workgroup: 256 queries (8 waves x 32, two waves per SIMD), key tiles of
-// 64 copied global -> LDS directly and double buffered.  A single wave issues
+// Per workgroup: 32 queries per wave, 8 waves (two per SIMD) or, for small
+// images, 4 (one per SIMD); key tiles of 64 copied global -> LDS directly and
+// double buffered.  A single wave issues
 // VALU work at about half rate and hides only a few VALU instructions behind
 // each of its own MFMAs (measured on MI355X), so each wave is software
 // pipelined over three tiles (the softmax of tile t runs between the score
@@ -73,8 +74,10 @@ QI_DEV float add_bf16x2(uint32_t pair, float sum) {
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pair), one, sum, false);
 }
 
-__global__ __launch_bounds__(attn::THREADS, 1) void block_causal_attn_kernel(const AttnBatch ab) {
+template <int WAVES>
+__global__ __launch_bounds__(attn::Shape<WAVES>::THREADS, 1) void block_causal_attn_kernel(const AttnBatch ab) {
   using namespace attn;
+  constexpr int BQ = Shape<WAVES>::BQ, THREADS = Shape<WAVES>::THREADS, NLD = Shape<WAVES>::NLD;
   // Double buffers as four separate objects, always indexed by a constant:
   // the compiler then knows that a copy into one buffer does not alias reads
   // of the other and does not make those reads wait for the copy.

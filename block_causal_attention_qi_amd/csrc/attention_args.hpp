@@ -14,19 +14,25 @@ struct AttnArgs {
   int ldo;                       // heads * 128
   int heads, L, N;
   int ldv_t, ldv_i;              // V^T row strides (>= segment length rounded up to 64)
-  int n_img_qt, n_txt_qt;        // query tiles of BQ per head
+  int joint;                     // 1: text query tiles too (causal over the text keys)
+  int n_img_qt, n_txt_qt;        // query tiles per head (set by launch_block_causal_attn)
   int o_img_row0;                // output row of image query 0 (L in a joint pass, else 0)
   float scale_log2;              // log2(e) / sqrt(128)
   const int *skip;               // first-block cache: when non-NULL and *skip, do nothing
 };
 
 namespace attn {
-constexpr int WAVES = 8;
-constexpr int BQ = WAVES * 32;           // queries per workgroup, 32 per wave
-constexpr int BKV = 64;
-constexpr int THREADS = 64 * WAVES;
-constexpr int NLD = BKV * 16 / THREADS;  // 16-byte K (and V^T) chunks per thread per tile
+constexpr int BKV = 64;                  // keys per tile
 constexpr float RESCALE_SLACK = 8.f;     // log2 units
+// A workgroup of WAVES waves takes 32 queries per wave: 8 waves (two per
+// SIMD) for the large images, 4 (one per SIMD) when the 8-wave grid would
+// leave CUs idle.
+template <int WAVES>
+struct Shape {
+  static constexpr int BQ = WAVES * 32;           // queries per workgroup
+  static constexpr int THREADS = 64 * WAVES;
+  static constexpr int NLD = BKV * 16 / THREADS;  // 16-byte K (and V^T) chunks per thread per tile
+};
 }  // namespace attn
 
 // One launch over up to two independent problems of the same shape apart from
@@ -39,5 +45,9 @@ struct AttnBatch {
 };
 
 // Launches the kernel (defined in attention.hip, which is compiled with MFMA
-// accumulators in VGPRs) over grid (n_img_qt + n_txt_qt, heads * nbranch).
+// accumulators in VGPRs) over grid (n_img_qt + n_txt_qt, heads * nbranch),
+// choosing the workgroup size and filling in the query-tile counts.  Every
+// query's arithmetic is the same in both shapes (one wave walks its 32
+// queries over all their keys in one fixed order), so the choice never
+// changes a result bit.
 void launch_block_causal_attn(const AttnBatch &ab, hipStream_t s);

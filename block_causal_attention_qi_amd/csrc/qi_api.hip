@@ -324,8 +324,7 @@ AttnArgs attn_args(int heads, int L, int N, bool joint, const u16 *q_t, const u1
   a.ldo = heads * 128;
   a.heads = heads; a.L = L; a.N = N;
   a.ldv_t = round64(L); a.ldv_i = round64(N);
-  a.n_img_qt = (N + attn::BQ - 1) / attn::BQ;
-  a.n_txt_qt = joint ? (L + attn::BQ - 1) / attn::BQ : 0;
+  a.joint = joint ? 1 : 0;
   a.o_img_row0 = joint ? L : 0;
   a.scale_log2 = (float)(1.4426950408889634 / sqrt(128.0));
   return a;
