@@ -3,7 +3,7 @@
 // layout), fp32 accumulation, and fused epilogues:
 //   EPI_F32    C[m][n] = acc (+ bias[n])                      (text projection)
 //   EPI_RESID  x[m][n] += gate[row kind][n] * acc             (O-proj, down);
-//              split over K (128 x 128 kernel only): chunk s of K writes
+//              split over K (small images): chunk s of K writes
 //              its fp32 partial sums, and resid_reduce_kernel adds the
 //              chunks in order into x
 //   EPI_SWIGLU a[m][o] = bf16(SiLU(acc_gate) * acc_up)        (gate/up)
@@ -63,7 +63,7 @@ struct GemmArgs {
   int batch;         // image rows form `batch` branches of seg_i rows each (true CFG: 2),
                      // each with its own Q, K [heads][seg_i][128] and V^T [heads][128][ldv_i]
   const int *skip;   // first-block cache: when non-NULL and *skip, the launch does nothing
-  // EPI_RESID split over K (ksplit > 1; 128 x 128 kernel): grid = tiles x
+  // EPI_RESID split over K (ksplit > 1): grid = tiles x
   // ksplit; chunk s covers K columns [s K/ksplit, (s+1) K/ksplit) and writes
   // its fp32 partial sums to part + s * M * N ([M][N] row-major)
   int ksplit;
