@@ -185,8 +185,9 @@ void launch_gemm_tile(const GemmArgs &g, hipStream_t s) {
 // output element, so the choice never changes a result bit.
 enum GemmShape { SHAPE_256x256, SHAPE_128x256, SHAPE_128x128 };
 
+// The cheapest shape for g and its cost (in hundredths of a 256 x 256 round).
 template <int EPI>
-GemmShape gemm_shape(const GemmArgs &g, int &grid) {
+GemmShape gemm_shape(const GemmArgs &g, int &grid, int &cost) {
   const int n_out = EPI == EPI_SWIGLU ? g.F : g.N;
   const int per_tile_w = EPI == EPI_SWIGLU ? 128 : 256;  // outputs of a 256-row W tile
   const int ks = g.ksplit > 1 ? g.ksplit : 1;
@@ -200,14 +201,48 @@ GemmShape gemm_shape(const GemmArgs &g, int &grid) {
   const int c128 = tiles_128 <= 256 ? 45 : 65 * rounds(tiles_128, 512);
   if (c256 <= c128w && c256 <= c128) {
     grid = tiles_256;
+    cost = c256;
     return SHAPE_256x256;
   }
   if (c128w <= c128) {
     grid = tiles_128w;
+    cost = c128w;
     return SHAPE_128x256;
   }
   grid = tiles_128;
+  cost = c128;
   return SHAPE_128x128;
+}
+
+template <int EPI>
+void launch_gemm_shape(const GemmArgs &g, GemmShape shape, int grid, hipStream_t s) {
+  if (shape == SHAPE_256x256)
+    hipLaunchKernelGGL((gemm_bf16_large_kernel<EPI, QI_GEMM_WM, QI_GEMM_WN, 256>), dim3(grid), dim3(gemmL::THREADS),
+                       0, s, g);
+  else if (shape == SHAPE_128x256)
+    hipLaunchKernelGGL((gemm_bf16_large_kernel<EPI, QI_GEMM_WM, QI_GEMM_WN, 128>), dim3(grid), dim3(gemmL::THREADS),
+                       0, s, g);
+  else
+    hipLaunchKernelGGL((gemm_bf16_mid_kernel<EPI>), dim3(grid), dim3(gemmM::THREADS), 0, s, g);
+}
+
+// The rows past the last multiple of 256 as a launch of their own: a pass
+// whose row count is a little over a multiple of 256 (the joint pass at
+// 1024^2: 4503 rows) would otherwise need a nearly empty extra round of
+// 256-row tiles.  The tail must hold image rows only (text rows index their
+// outputs from the pass's first row); its arguments see the same rows through
+// offset operands and a negative text-row count, so every output element
+// gets the same MFMA sequence as in one launch.
+template <int EPI>
+GemmArgs gemm_tail(const GemmArgs &g, int m_main) {
+  GemmArgs t = g;
+  t.M = g.M - m_main;
+  t.A = g.A + (size_t)m_main * g.lda;
+  t.L_rows = g.L_rows - m_main;
+  if (EPI == EPI_F32) t.C = g.C + (size_t)m_main * g.ldc;
+  if (EPI == EPI_RESID) t.X = g.X + (size_t)m_main * g.ldx;
+  if (EPI == EPI_SWIGLU) t.out = g.out + (size_t)m_main * g.ldo;
+  return t;
 }
 
 template <int EPI>
@@ -217,22 +252,43 @@ qi_status launch_gemm(const GemmArgs &g, int kind, hipStream_t s) {
                       (size_t)(EPI == EPI_SWIGLU ? 2 * g.F : g.N) * g.ldw * 2 < (1ull << 31);
   {
     TimedLaunch tl(kind, s);
-    int grid = 0;
-    const GemmShape shape = fits32 ? gemm_shape<EPI>(g, grid) : SHAPE_128x128;
     if (!fits32) {
       const int tiles = ((g.M + 127) / 128) * (EPI == EPI_SWIGLU ? g.F / 64 : g.N / 128);
       if (EPI == EPI_RESID && g.ksplit > 1)
         hipLaunchKernelGGL((gemm_bf16_kernel<EPI, 128, 128>), dim3(tiles * g.ksplit), dim3(gemm::THREADS), 0, s, g);
       else
         launch_gemm_tile<EPI, 128, 128>(g, s);
-    } else if (shape == SHAPE_256x256) {
-      hipLaunchKernelGGL((gemm_bf16_large_kernel<EPI, QI_GEMM_WM, QI_GEMM_WN, 256>), dim3(grid),
-                         dim3(gemmL::THREADS), 0, s, g);
-    } else if (shape == SHAPE_128x256) {
-      hipLaunchKernelGGL((gemm_bf16_large_kernel<EPI, QI_GEMM_WM, QI_GEMM_WN, 128>), dim3(grid),
-                         dim3(gemmL::THREADS), 0, s, g);
     } else {
-      hipLaunchKernelGGL((gemm_bf16_mid_kernel<EPI>), dim3(grid), dim3(gemmM::THREADS), 0, s, g);
+      int grid = 0, cost = 0;
+      const GemmShape shape = gemm_shape<EPI>(g, grid, cost);
+      // the cheapest split into a head of 256-row multiples (>= 2048 rows,
+      // holding every text row) and an image-row tail, if any beats one launch
+      bool two = false;
+      GemmArgs head = g, tail{};
+      int grid_h = 0, grid_t = 0;
+      GemmShape shape_h = shape, shape_t = shape;
+      if (g.ksplit <= 1) {
+        int best = cost - 10;  // a second launch costs about a tenth of a round
+        for (int m_main = g.M / 256 * 256; m_main >= 2048 && m_main >= g.L_rows; m_main -= 256) {
+          if (m_main == g.M) continue;
+          GemmArgs h = g;
+          h.M = m_main;
+          const GemmArgs t = gemm_tail<EPI>(g, m_main);
+          int gh = 0, gt = 0, ch = 0, ct = 0;
+          const GemmShape sh = gemm_shape<EPI>(h, gh, ch), st = gemm_shape<EPI>(t, gt, ct);
+          if (ch + ct < best) {
+            best = ch + ct;
+            two = true;
+            head = h, tail = t, grid_h = gh, grid_t = gt, shape_h = sh, shape_t = st;
+          }
+        }
+      }
+      if (two) {
+        launch_gemm_shape<EPI>(head, shape_h, grid_h, s);
+        launch_gemm_shape<EPI>(tail, shape_t, grid_t, s);
+      } else {
+        launch_gemm_shape<EPI>(g, shape, grid, s);
+      }
     }
   }
   QI_TRY(last_launch());
