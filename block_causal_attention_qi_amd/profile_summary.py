@@ -8,10 +8,10 @@ DIR holds the CSV output of the commands that each summary names (run from
 the repository root on one MI355X; see TRACE_CMD, TRAFFIC_CMDS, MFMA_CMD).
 Kernel launches are classified by name and launch order into the kinds of the
 library's own timer (the two residual-epilogue GEMMs share one instantiation:
-the one right after attention is the output projection), and by grid size
-into the image-only and joint passes.  The JSON sidecars carry the hash of
-the kernel sources they were measured on, so bench.py can tell when they no
-longer describe the current kernels."""
+the one right after attention is the output projection), and by the step they
+belong to into the image-only and joint passes (label_launches).  The JSON
+sidecars carry the hash of the kernel sources they were measured on, so
+bench.py can tell when they no longer describe the current kernels."""
 from __future__ import annotations
 
 import collections
@@ -66,8 +66,8 @@ def kind_of(name: str, prev: str | None) -> str:
             return "gemm_gate_up"
         if epi == 3:
             return "gemm_qkv"
-        if epi == 1:
-            return "gemm_o" if prev == "attention" else "gemm_down"
+        if epi == 1:  # the output projection follows attention (its row tail follows it)
+            return "gemm_o" if prev in ("attention", "gemm_o") else "gemm_down"
         return "gemm_txt"
     for key, kind in (("attn", "attention"), ("rmsnorm", "norm_mod"), ("head_kernel", "head"),
                       ("mod_gemv", "modulation"), ("img_embed", "img_embed"), ("euler", "euler")):
@@ -76,33 +76,41 @@ def kind_of(name: str, prev: str | None) -> str:
     return "other"
 
 
-def _pass_of(kind: str, grid: int, grids: set) -> str:
-    """Image-only launches have the smallest grid of their kind (T = N rows);
-    the text norm (T = L rows) is the smallest norm grid."""
-    gs = sorted(grids)
-    if kind == "gemm_txt":
-        return "joint (text)"
-    if kind == "norm_mod" and len(gs) > 2 and grid == gs[0]:
-        return "joint (text)"
-    rest = [g for g in gs if not (kind == "norm_mod" and len(gs) > 2 and g == gs[0])]
-    if len(rest) == 1:
-        return "both"
-    return "image-only" if grid == min(rest) else "joint"
+def label_launches(names):
+    """(kind, pass) of each launch of a bench run, in launch order.  Every DiT
+    step starts with its modulation kernel; a step that runs the text
+    projection is a joint pass (its text norm and text projection are the
+    "joint (text)" launches), every other step an image-only pass.  (A joint
+    pass may split a GEMM into a 256-row-tile head and a row tail, so launch
+    shapes alone do not tell the passes apart.)"""
+    kinds, prev = [], None
+    for n in names:
+        k = kind_of(n, prev)
+        kinds.append(k)
+        prev = k
+    starts = [i for i, k in enumerate(kinds) if k == "modulation"] + [len(kinds)]
+    passes = ["other"] * len(kinds)
+    for s0, s1 in zip(starts, starts[1:]):
+        step = kinds[s0:s1]
+        joint = "gemm_txt" in step
+        txt_end = s0 + step.index("gemm_txt") if joint else s0
+        for i in range(s0, s1):
+            if not joint:
+                passes[i] = "image-only"
+            elif kinds[i] == "gemm_txt" or (kinds[i] == "norm_mod" and i < txt_end):
+                passes[i] = "joint (text)"
+            else:
+                passes[i] = "joint"
+    return list(zip(kinds, passes))
 
 
 def summarize_trace(d: str):
     st = _rows(os.path.join(d, "trace", "bench_kernel_stats.csv"))
     tr = sorted(_rows(os.path.join(d, "trace", "bench_kernel_trace.csv")), key=lambda r: int(r["Start_Timestamp"]))
     agg = collections.defaultdict(list)
-    prev = None
-    for r in tr:
-        k = kind_of(r["Kernel_Name"], prev)
-        prev = k
+    for r, (k, p) in zip(tr, label_launches([r["Kernel_Name"] for r in tr])):
         g = int(r["Grid_Size_X"]) * int(r["Grid_Size_Y"]) * int(r.get("Grid_Size_Z", 1) or 1)
-        agg[(k, g)].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
-    grids = collections.defaultdict(set)
-    for (k, g) in agg:
-        grids[k].add(g)
+        agg[(k, p, g)].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
     cmd = TRACE_CMD.replace("DIR", "gpurun_out/prof")
     lines = ["# Kernel trace: 32-block DiT at 1024^2 (L 407, N 4096), bench loop", "",
              "Command (from the repository root, on one MI355X):", "", "    " + cmd, "",
@@ -116,15 +124,14 @@ def summarize_trace(d: str):
               "launches bench.py's `kernels` and `roofline` entries average:", "",
               "| kind | grid | launches | avg us | min us | max us | pass |", "|---|---|---|---|---|---|---|"]
     kinds = {}
-    for (k, g), v in sorted(agg.items(), key=lambda kv: -sum(kv[1])):
-        if k == "other":
+    for (k, p, g), v in sorted(agg.items(), key=lambda kv: -sum(kv[1])):
+        if k == "other" or p == "other":
             continue
-        p = _pass_of(k, g, grids[k])
         lines.append(f"| {k} | {g} | {len(v)} | {statistics.mean(v):.1f} | {min(v):.1f} | {max(v):.1f} | {p} |")
-        kinds.setdefault(k, {})[p] = {"grid": g, "launches": len(v), "avg_us": round(statistics.mean(v), 2),
-                                      "median_us": round(statistics.median(v), 2)}
-        if p == "both":
-            kinds[k]["image-only"] = kinds[k]["both"]
+        # the pass's main launch shape (a joint pass may add a row-tail launch)
+        if p not in kinds.setdefault(k, {}):
+            kinds[k][p] = {"grid": g, "launches": len(v), "avg_us": round(statistics.mean(v), 2),
+                           "median_us": round(statistics.median(v), 2)}
     os.makedirs(PROFILES, exist_ok=True)
     with open(os.path.join(PROFILES, "dit32_1024px_kernel_trace.md"), "w") as f:
         f.write("\n".join(lines) + "\n")
@@ -138,12 +145,11 @@ def summarize_trace(d: str):
 
 
 def _pmc(path):
+    """Counter values per (kind, pass, grid) of a one-counter rocprofv3 run."""
+    rows = sorted(_rows(path), key=lambda x: int(x["Dispatch_Id"]))
     vals = collections.defaultdict(list)
-    prev = None
-    for x in sorted(_rows(path), key=lambda x: int(x["Dispatch_Id"])):
-        k = kind_of(x["Kernel_Name"], prev)
-        prev = k
-        vals[(k, int(x["Grid_Size"]))].append(float(x["Counter_Value"]))
+    for x, (k, p) in zip(rows, label_launches([x["Kernel_Name"] for x in rows])):
+        vals[(k, p, int(x["Grid_Size"]))].append(float(x["Counter_Value"]))
     return vals
 
 
@@ -157,9 +163,6 @@ def summarize_traffic(d: str):
     cfv, cwv = copy_kib("FETCH_SIZE_copy"), copy_kib("WRITE_SIZE_copy")
     gib_kib = (1 << 30) / 1024
     sf, sw = gib_kib / cfv, gib_kib / cwv
-    grids = collections.defaultdict(set)
-    for (k, g) in fetch:
-        grids[k].add(g)
     out = {"what": "HBM bytes per launch from rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE (KiB per dispatch), "
                    "scaled by the same counters read on a 1 GiB device copy",
            "commands": [c.replace("DIR", "gpurun_out/prof") for c in TRAFFIC_CMDS],
@@ -168,11 +171,13 @@ def summarize_traffic(d: str):
            "kernel_source_sha256": kernel_source_sha256(),
            "kernel_source_sha256_of": " ".join(KERNEL_SOURCES) + ", comments removed and whitespace collapsed",
            "kernels": {}}
-    for (k, g), v in sorted(fetch.items(), key=lambda kv: -len(kv[1])):
-        if k == "other" or len(v) < 4:
+    for (k, p, g), v in sorted(fetch.items(), key=lambda kv: -len(kv[1]) * statistics.mean(kv[1])):
+        if k == "other" or p == "other" or len(v) < 4:
             continue
-        w = write.get((k, g), [0.0])
-        out["kernels"].setdefault(k, {})[_pass_of(k, g, grids[k])] = {
+        if p in out["kernels"].get(k, {}):  # the pass's main launch shape only
+            continue
+        w = write.get((k, p, g), [0.0])
+        out["kernels"].setdefault(k, {})[p] = {
             "grid": g, "launches": len(v), "fetch_kib": statistics.mean(v), "write_kib": statistics.mean(w),
             "hbm_bytes": statistics.mean(v) * 1024 * sf + statistics.mean(w) * 1024 * sw}
     with open(os.path.join(PROFILES, "dit32_1024px_hbm_traffic.json"), "w") as f:
@@ -183,12 +188,15 @@ def summarize_traffic(d: str):
 def summarize_mfma(d: str):
     path = os.path.join(d, "MFMA", "bench_counter_collection.csv")
     vals = collections.defaultdict(lambda: collections.defaultdict(list))
-    prev = None
-    for x in sorted(_rows(path), key=lambda x: (int(x["Dispatch_Id"]), x["Counter_Name"])):
-        k = kind_of(x["Kernel_Name"], prev)
-        vals[(k, int(x["Grid_Size"]))][x["Counter_Name"]].append(float(x["Counter_Value"]))
-        if x["Counter_Name"] == "SQ_WAVES":     # one per dispatch: advance the launch order
-            prev = k
+    rows = sorted(_rows(path), key=lambda x: (int(x["Dispatch_Id"]), x["Counter_Name"]))
+    ids = sorted({int(x["Dispatch_Id"]) for x in rows})
+    first = {}
+    for x in rows:
+        first.setdefault(int(x["Dispatch_Id"]), x["Kernel_Name"])
+    label = dict(zip(ids, label_launches([first[i] for i in ids])))
+    for x in rows:
+        k, p = label[int(x["Dispatch_Id"])]
+        vals[(k, p, int(x["Grid_Size"]))][x["Counter_Name"]].append(float(x["Counter_Value"]))
     cmd = MFMA_CMD.replace("DIR", "gpurun_out/prof")
     lines = ["# MFMA busy per kernel: 32-block DiT at 1024^2 (L 407, N 4096)", "",
              "Command (from the repository root, on one MI355X):", "", "    " + cmd, "",
@@ -197,15 +205,15 @@ def summarize_mfma(d: str):
              "cycles in which the CUs run the kernel that each SIMD's matrix core is busy, whatever the",
              "clock.  SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512 against the kernel's algorithmic FLOPs checks",
              "that no masked or padded MFMA work is counted as useful.", "",
-             "| kind | grid | launches | MFMA busy | MOPS x 512 / launch (TFLOP) |", "|---|---|---|---|---|"]
-    for (k, g), dd in sorted(vals.items(), key=lambda kv: -sum(kv[1].get("SQ_BUSY_CU_CYCLES", [0]))):
-        if k == "other" or not dd.get("SQ_VALU_MFMA_BUSY_CYCLES"):
+             "| kind | pass | grid | launches | MFMA busy | MOPS x 512 / launch (TFLOP) |", "|---|---|---|---|---|---|"]
+    for (k, p, g), dd in sorted(vals.items(), key=lambda kv: -sum(kv[1].get("SQ_BUSY_CU_CYCLES", [0]))):
+        if k == "other" or p == "other" or not dd.get("SQ_VALU_MFMA_BUSY_CYCLES"):
             continue
         busy = statistics.mean(dd["SQ_VALU_MFMA_BUSY_CYCLES"]) / (4 * statistics.mean(dd["SQ_BUSY_CU_CYCLES"]))
         mops = statistics.mean(dd.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", [0])) * 512 / 1e12
         if busy < 0.01:
             continue
-        lines.append(f"| {k} | {g} | {len(dd['SQ_WAVES'])} | {busy:.3f} | {mops:.3f} |")
+        lines.append(f"| {k} | {p} | {g} | {len(dd['SQ_WAVES'])} | {busy:.3f} | {mops:.3f} |")
     with open(os.path.join(PROFILES, "dit32_1024px_mfma_busy.md"), "w") as f:
         f.write("\n".join(lines) + "\n")
     print("\n".join(lines))
