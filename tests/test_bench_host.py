@@ -6,7 +6,7 @@ import subprocess
 import sys
 
 import bench  # noqa: F401  (importable without a GPU)
-from block_causal_attention_qi_amd.profile_summary import _pass_of, kernel_code_text, kind_of
+from block_causal_attention_qi_amd.profile_summary import kernel_code_text, kind_of, label_launches
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
@@ -37,13 +37,26 @@ def test_committed_counter_summary_names_its_fingerprint_and_kernels():
         assert int(ent["hbm_bytes"]) > 0
 
 
-def test_profile_summary_classifies_launches_by_name_order_and_grid():
-    assert kind_of("void gemm_bf16_large_kernel<1, 2, 4>(GemmArgs)", "attention") == "gemm_o"
-    assert kind_of("void gemm_bf16_large_kernel<1, 2, 4>(GemmArgs)", "gemm_gate_up") == "gemm_down"
-    assert kind_of("block_causal_attn_kernel(AttnBatch)", None) == "attention"
+def test_profile_summary_classifies_launches_by_name_and_step():
+    assert kind_of("void gemm_bf16_large_kernel<1, 2, 4, 256>(GemmArgs)", "attention") == "gemm_o"
+    assert kind_of("void gemm_bf16_mid_kernel<1>(GemmArgs)", "gemm_o") == "gemm_o"  # the O-proj's row tail
+    assert kind_of("void gemm_bf16_large_kernel<1, 2, 4, 256>(GemmArgs)", "gemm_gate_up") == "gemm_down"
+    assert kind_of("void gemm_bf16_large_kernel<3, 2, 4, 128>(GemmArgs)", None) == "gemm_qkv"
+    assert kind_of("void gemm_bf16_kernel<0, 128, 128>(GemmArgs)", None) == "gemm_txt"
+    assert kind_of("void block_causal_attn_kernel<8>(AttnBatch)", None) == "attention"
     assert kind_of("void rmsnorm_mod_kernel<16>(float const*)", None) == "norm_mod"
-    grids = {26112, 262144, 288256}               # text norm, image-only, joint
-    assert _pass_of("norm_mod", 262144, grids) == "image-only"
-    assert _pass_of("norm_mod", 288256, grids) == "joint"
-    assert _pass_of("norm_mod", 26112, grids) == "joint (text)"
-    assert _pass_of("head", 65536, {65536}) == "both"
+    # a joint step (it runs the text projection; its first norm is the text norm), then an
+    # image-only step; the joint pass splits the O-proj into a head and a row tail
+    joint = ["mod_gemv_kernel<8>", "rmsnorm_mod_kernel<16>", "gemm_bf16_kernel<0, 128, 128>", "img_embed_kernel<4>",
+             "rmsnorm_mod_kernel<16>", "gemm_bf16_large_kernel<3, 2, 4, 256>", "block_causal_attn_kernel<8>",
+             "gemm_bf16_large_kernel<1, 2, 4, 256>", "gemm_bf16_mid_kernel<1>", "head_kernel<2>", "euler_kernel"]
+    img = ["mod_gemv_kernel<8>", "img_embed_kernel<4>", "rmsnorm_mod_kernel<16>", "gemm_bf16_large_kernel<3, 2, 4, 256>",
+           "block_causal_attn_kernel<8>", "gemm_bf16_large_kernel<1, 2, 4, 256>", "head_kernel<2>", "euler_kernel"]
+    lab = label_launches(joint + img)
+    assert lab[1] == ("norm_mod", "joint (text)") and lab[2] == ("gemm_txt", "joint (text)")
+    assert lab[4] == ("norm_mod", "joint")
+    assert lab[7] == ("gemm_o", "joint") and lab[8] == ("gemm_o", "joint")
+    assert all(p == "image-only" for _, p in lab[len(joint):])
+    assert [k for k, _ in lab[len(joint):]] == ["modulation", "img_embed", "norm_mod", "gemm_qkv", "attention",
+                                                  "gemm_o", "head", "euler"]
+
