@@ -114,7 +114,10 @@ def calibrate():
         lds[name] = round(v.value, 1)
     res["lds_mix_cycles_per_iteration_per_cu"] = lds
     valu = {}
-    for mode, name in ((0, "32_exp"), (1, "32_fma"), (2, "8_mfma_32_exp"), (3, "8_mfma_32_fma"), (4, "8_mfma")):
+    for mode, name in ((0, "32_exp"), (1, "32_fma"), (2, "8_mfma_32_exp"), (3, "8_mfma_32_fma"), (4, "8_mfma"),
+                       (5, "8_mfma_beside_32_exp_other_wave"), (6, "8_mfma_beside_32_fma_other_wave"),
+                       (7, "8_mfma_one_wave_per_simd"), (8, "32_exp_one_wave_per_simd"),
+                       (9, "32_fma_one_wave_per_simd")):
         v = ctypes.c_double(0)
         _lib.check(lib.qi_calib_valu_cycles(mode, 20000, ctypes.byref(v)), "qi_calib_valu_cycles")
         valu[name] = round(v.value, 1)

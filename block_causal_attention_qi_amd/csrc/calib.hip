@@ -153,21 +153,32 @@ __global__ __launch_bounds__(512, 1) void valu_mix_kernel(float *out, int iters,
     a[i] = (__bf16)(lane * 0.01f);
     b[i] = (__bf16)0.5f;
   }
-  constexpr bool kMfma = MODE >= 2, kExp = MODE == 0 || MODE == 2, kFma = MODE == 1 || MODE == 3;
+  // modes 5..9: waves 0-3 (one per SIMD) issue only the MFMAs (modes 5-7),
+  // waves 4-7 (the other wave of each SIMD) only the exponentials (5, 8) or
+  // FMAs (6, 9); the rest of the waves run the empty loop
+  const int wave = tid >> 6;
+  const bool split = MODE >= 5;
+  const bool do_mfma = split ? (wave < 4 && MODE <= 7) : (MODE >= 2 && MODE <= 4);
+  const bool do_exp = split ? ((MODE == 5 || MODE == 8) && wave >= 4) : (MODE == 0 || MODE == 2);
+  const bool do_fma = split ? ((MODE == 6 || MODE == 9) && wave >= 4) : (MODE == 1 || MODE == 3);
+  constexpr bool kMfma = MODE >= 2 && MODE <= 7, kExp = MODE == 0 || MODE == 2 || MODE == 5 || MODE == 8,
+                 kFma = MODE == 1 || MODE == 3 || MODE == 6 || MODE == 9;
   const uint64_t t0 = __builtin_amdgcn_s_memtime();
   for (int it = 0; it < iters; ++it) {
-    if constexpr (kMfma) {
+    if (kMfma && do_mfma) {
 #pragma unroll
       for (int j = 0; j < 8; ++j) acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[j], 0, 0, 0);
     }
+    if ((kExp && do_exp) || (kFma && do_fma)) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r)
+      for (int r = 0; r < 4; ++r)
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        if constexpr (kExp) v[j] = __builtin_amdgcn_exp2f(v[j]);
-        if constexpr (kFma) v[j] = __builtin_fmaf(v[j], 0.999f, 0.001f);
-      }
-    if constexpr (kMfma && MODE != 4) {
+        for (int j = 0; j < 8; ++j) {
+          if constexpr (kExp) v[j] = __builtin_amdgcn_exp2f(v[j]);
+          if constexpr (kFma) v[j] = __builtin_fmaf(v[j], 0.999f, 0.001f);
+        }
+    }
+    if constexpr (kMfma && MODE >= 2 && MODE <= 3) {
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
@@ -181,9 +192,9 @@ __global__ __launch_bounds__(512, 1) void valu_mix_kernel(float *out, int iters,
   for (int j = 0; j < 8; ++j) sum += v[j] + acc[j][0];
   // keeps the work alive: the compiler cannot decide this (practically never true)
   if (__float_as_uint(sum) == (uint32_t)iters * 2654435761u) out[tid] = sum;
-  if (tid == 0) {
-    atomicAdd(&clk[0], (unsigned long long)(t1 - t0));
-    atomicAdd(&clk[1], 1ull);
+  if (tid == 0 || (split && tid == 256)) {  // modes 5..9 also time wave 4
+    atomicAdd(&clk[tid == 0 ? 0 : 2], (unsigned long long)(t1 - t0));
+    atomicAdd(&clk[tid == 0 ? 1 : 3], 1ull);
   }
 }
 
@@ -305,7 +316,7 @@ qi_status qi_calib_lds_cycles(int32_t mode, int32_t iters, double *cycles) {
 
 qi_status qi_calib_valu_cycles(int32_t mode, int32_t iters, double *cycles) {
   if (!cycles) return QI_ERR_NULL;
-  if (mode < 0 || mode > 4 || iters < 4 || iters > 10000000) return QI_ERR_RANGE;
+  if (mode < 0 || mode > 9 || iters < 4 || iters > 10000000) return QI_ERR_RANGE;
   int dev = 0, cus = 0;
   if (hipGetDevice(&dev) != hipSuccess) return QI_ERR_HIP;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return QI_ERR_HIP;
@@ -314,7 +325,7 @@ qi_status qi_calib_valu_cycles(int32_t mode, int32_t iters, double *cycles) {
   hipStream_t st;
   if (hipStreamCreate(&st) != hipSuccess) return QI_ERR_HIP;
   qi_status rc = QI_OK;
-  if (hipMalloc(&out, 512 * sizeof(float)) != hipSuccess || hipMalloc(&clk, 2 * sizeof(unsigned long long)) != hipSuccess)
+  if (hipMalloc(&out, 512 * sizeof(float)) != hipSuccess || hipMalloc(&clk, 4 * sizeof(unsigned long long)) != hipSuccess)
     rc = QI_ERR_HIP;
   auto run = [&](int n) {
     switch (mode) {
@@ -322,13 +333,18 @@ qi_status qi_calib_valu_cycles(int32_t mode, int32_t iters, double *cycles) {
       case 1: hipLaunchKernelGGL(valu_mix_kernel<1>, dim3(cus), dim3(512), 0, st, out, n, clk); break;
       case 2: hipLaunchKernelGGL(valu_mix_kernel<2>, dim3(cus), dim3(512), 0, st, out, n, clk); break;
       case 3: hipLaunchKernelGGL(valu_mix_kernel<3>, dim3(cus), dim3(512), 0, st, out, n, clk); break;
-      default: hipLaunchKernelGGL(valu_mix_kernel<4>, dim3(cus), dim3(512), 0, st, out, n, clk); break;
+      case 4: hipLaunchKernelGGL(valu_mix_kernel<4>, dim3(cus), dim3(512), 0, st, out, n, clk); break;
+      case 5: hipLaunchKernelGGL(valu_mix_kernel<5>, dim3(cus), dim3(512), 0, st, out, n, clk); break;
+      case 6: hipLaunchKernelGGL(valu_mix_kernel<6>, dim3(cus), dim3(512), 0, st, out, n, clk); break;
+      case 7: hipLaunchKernelGGL(valu_mix_kernel<7>, dim3(cus), dim3(512), 0, st, out, n, clk); break;
+      case 8: hipLaunchKernelGGL(valu_mix_kernel<8>, dim3(cus), dim3(512), 0, st, out, n, clk); break;
+      default: hipLaunchKernelGGL(valu_mix_kernel<9>, dim3(cus), dim3(512), 0, st, out, n, clk); break;
     }
   };
-  unsigned long long h[2] = {0, 0};
+  unsigned long long h[4] = {0, 0, 0, 0};
   if (rc == QI_OK) {
     run(100);  // warm-up
-    if (hipMemsetAsync(clk, 0, 2 * sizeof(unsigned long long), st) != hipSuccess) rc = QI_ERR_HIP;
+    if (hipMemsetAsync(clk, 0, 4 * sizeof(unsigned long long), st) != hipSuccess) rc = QI_ERR_HIP;
   }
   if (rc == QI_OK) {
     run(iters);
@@ -336,7 +352,10 @@ qi_status qi_calib_valu_cycles(int32_t mode, int32_t iters, double *cycles) {
         hipStreamSynchronize(st) != hipSuccess || hipGetLastError() != hipSuccess)
       rc = QI_ERR_HIP;
   }
-  *cycles = (rc == QI_OK && h[1]) ? (double)h[0] / (double)h[1] / iters : 0.0;
+  // the slower of the two timed waves (modes 5..9 time waves 0 and 4; in 7..9 one of them idles)
+  const double c0 = h[1] ? (double)h[0] / (double)h[1] / iters : 0.0;
+  const double c1 = h[3] ? (double)h[2] / (double)h[3] / iters : 0.0;
+  *cycles = rc == QI_OK ? (c0 > c1 ? c0 : c1) : 0.0;
   if (out) (void)hipFree(out);
   if (clk) (void)hipFree(clk);
   (void)hipStreamDestroy(st);

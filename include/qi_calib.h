@@ -58,11 +58,18 @@ qi_status qi_calib_lds_cycles(int32_t mode, int32_t iters, double *cycles);
  *           interleaved (four after each MFMA),
  *   mode 3: 8 MFMAs with the 32 v_fma_f32 of mode 1 interleaved,
  *   mode 4: the 8 MFMAs alone,
- * timed with the shader clock of wave 0 of every workgroup and averaged: the
- * issue cost of the exponentials against plain FMAs, alone and beside the
- * matrix cores.  Data are synthetic.  BLOCKS until done.  *cycles receives
- * the cycles per iteration.  Errors: NULL, RANGE (mode not 0..4, iters < 4),
- * HIP. */
+ *   mode 5: waves 0-3 (one on each SIMD) the 8 MFMAs, waves 4-7 (the other
+ *           wave of each SIMD) the 32 v_exp_f32,
+ *   mode 6: as mode 5 with the 32 v_fma_f32,
+ *   mode 7: waves 0-3 the 8 MFMAs, waves 4-7 idle (one MFMA wave per SIMD),
+ *   mode 8: waves 4-7 the 32 v_exp_f32, waves 0-3 idle,
+ *   mode 9: waves 4-7 the 32 v_fma_f32, waves 0-3 idle,
+ * timed with the shader clock of wave 0 of every workgroup (and in modes 5..9
+ * of wave 4, the slower of the two reported) and averaged: the issue cost of
+ * the exponentials against plain FMAs and of MFMAs, with one or two waves per
+ * SIMD, in the same wave or in the SIMD's other wave.  Data are synthetic.
+ * BLOCKS until done.  *cycles receives the cycles per iteration.  Errors:
+ * NULL, RANGE (mode not 0..9, iters < 4), HIP. */
 qi_status qi_calib_valu_cycles(int32_t mode, int32_t iters, double *cycles);
 
 #ifdef __cplusplus
