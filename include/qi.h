@@ -403,7 +403,7 @@ qi_status qi_modulation(const qi_dims *d, const uint16_t *w_mod, const float *b_
  *   L..) or N (IMAGE_ONLY: q_txt unused, may be NULL; image rows 0..N-1).
  * Text row i attends causally to text keys 0..i; image rows attend to all L
  * text keys then all N image keys; softmax in fp32 with scale 1/sqrt(128).
- * Errors: NULL, RANGE (heads < 1, L < 1 or > 512, N < 1 or > 16384), ALIGN,
+ * Errors: NULL, RANGE (heads < 1 or > 64, L < 1 or > 512, N < 1 or > 16384), ALIGN,
  * HIP. */
 qi_status qi_block_causal_attention(int32_t heads, int32_t L, int32_t N, int32_t mode,
                                     const uint16_t *q_txt, const uint16_t *k_txt,

@@ -43,6 +43,23 @@ def test_linear_bf16_matches_fp64_matmul(M, N, K):
     assert np.max(np.abs(got - (ref - b))) / np.max(np.abs(ref)) < 2e-5
 
 
+def test_linear_bf16_rows_do_not_depend_on_the_launch_split():
+    """4100 rows go out as a 4096-row launch of 256 x 256 tiles plus a 4-row
+    tail launch; inside an 8192-row product (one launch, no tail) the same rows
+    must come out bit for bit the same (every element sees one MFMA sequence
+    whatever the tile shape or launch)."""
+    import torch
+    M, N, K = 4100, 4096, 832
+    a = bf16_bits(qs.normal_array((8192, K), seed=11))
+    w = bf16_bits(qs.normal_array((N, K), seed=12, scale=0.02))
+    b = qs.normal_array((N,), seed=13, scale=0.1)
+    C1 = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    C2 = torch.empty((8192, N), dtype=torch.float32, device="cuda")
+    qi.linear_bf16(_dev(a[:M]), _dev(w), _dev(b), C1)
+    qi.linear_bf16(_dev(a), _dev(w), _dev(b), C2)
+    assert_bits_equal(host(C1), host(C2)[:M], "4100 rows (head + tail launches) vs inside 8192 rows")
+
+
 def _attn_inputs(heads, L, N, seed):
     q = bf16_bits(qs.normal_array((heads, L + N, 128), seed=seed))
     k = bf16_bits(qs.normal_array((heads, L + N, 128), seed=seed + 1))
@@ -82,6 +99,28 @@ def test_block_causal_attention_matches_oracle(heads, L, N):
     o2 = torch.empty((N, heads * 128), dtype=torch.int16, device="cuda")
     qi.block_causal_attention(heads, L, N, qi.QI_MODE_IMAGE_ONLY, None, k_t, vt_t, q_i, k_i, vt_i, o2)
     assert_bits_equal(host(o2), host(o)[L:], "image-only attention rows")
+
+
+def test_attention_workgroup_shape_changes_no_bit():
+    """2 heads at L 407, N 1100 launch 4-wave workgroups (too few 8-wave ones
+    for the CUs); 64 heads launch 8-wave ones, joint and image-only.  The
+    first two heads are the same inputs in both, and their output rows must be
+    the same bits."""
+    import torch
+    L, N, H2 = 407, 1100, 64
+    q, k, v = _attn_inputs(H2, L, N, seed=90)
+    Lp, Np = (L + 63) // 64 * 64, (N + 63) // 64 * 64
+    outs = {}
+    for heads in (2, H2):
+        q_t, k_t, q_i, k_i = (_dev(np.ascontiguousarray(a[:heads])) for a in (q[:, :L], k[:, :L], q[:, L:], k[:, L:]))
+        vt_t, vt_i = _dev(_vt(v[:heads, :L], Lp)), _dev(_vt(v[:heads, L:], Np))
+        o = torch.empty((L + N, heads * 128), dtype=torch.int16, device="cuda")
+        qi.block_causal_attention(heads, L, N, qi.QI_MODE_JOINT, q_t, k_t, vt_t, q_i, k_i, vt_i, o)
+        o2 = torch.empty((N, heads * 128), dtype=torch.int16, device="cuda")
+        qi.block_causal_attention(heads, L, N, qi.QI_MODE_IMAGE_ONLY, None, k_t, vt_t, q_i, k_i, vt_i, o2)
+        outs[heads] = (host(o)[:, :256].copy(), host(o2)[:, :256].copy())
+    assert_bits_equal(outs[2][0], outs[H2][0], "joint rows, 4-wave vs 8-wave workgroups")
+    assert_bits_equal(outs[2][1], outs[H2][1], "image-only rows, 4-wave vs 8-wave workgroups")
 
 
 def test_attention_lazy_rescale_path():
