@@ -111,10 +111,10 @@ def summarize_trace(d: str):
     for r, (k, p) in zip(tr, label_launches([r["Kernel_Name"] for r in tr])):
         g = int(r["Grid_Size_X"]) * int(r["Grid_Size_Y"]) * int(r.get("Grid_Size_Z", 1) or 1)
         agg[(k, p, g)].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
-    cmd = TRACE_CMD.replace("DIR", "gpurun_out/prof")
+    cmd = TRACE_CMD.replace("DIR", "OUT")
     lines = ["# Kernel trace: 32-block DiT at 1024^2 (L 407, N 4096), bench loop", "",
              "Command (from the repository root, on one MI355X):", "", "    " + cmd, "",
-             "Summary written by `python -m block_causal_attention_qi_amd.profile_summary trace gpurun_out/prof`.",
+             "Summary written by `python -m block_causal_attention_qi_amd.profile_summary trace OUT` (OUT: the runs' output directory).",
              "", "rocprofv3 kernel_stats (all launches of the run, joint and image-only steps):", "",
              "| kernel | calls | avg us | share % |", "|---|---|---|---|"]
     for r in st[:12]:
@@ -165,7 +165,7 @@ def summarize_traffic(d: str):
     sf, sw = gib_kib / cfv, gib_kib / cwv
     out = {"what": "HBM bytes per launch from rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE (KiB per dispatch), "
                    "scaled by the same counters read on a 1 GiB device copy",
-           "commands": [c.replace("DIR", "gpurun_out/prof") for c in TRAFFIC_CMDS],
+           "commands": [c.replace("DIR", "OUT") for c in TRAFFIC_CMDS],
            "copy_calibration": {"bytes_each_way": 1 << 30, "fetch_kib": cfv, "write_kib": cwv,
                                 "fetch_scale": sf, "write_scale": sw},
            "kernel_source_sha256": kernel_source_sha256(),
@@ -197,10 +197,10 @@ def summarize_mfma(d: str):
     for x in rows:
         k, p = label[int(x["Dispatch_Id"])]
         vals[(k, p, int(x["Grid_Size"]))][x["Counter_Name"]].append(float(x["Counter_Value"]))
-    cmd = MFMA_CMD.replace("DIR", "gpurun_out/prof")
+    cmd = MFMA_CMD.replace("DIR", "OUT")
     lines = ["# MFMA busy per kernel: 32-block DiT at 1024^2 (L 407, N 4096)", "",
              "Command (from the repository root, on one MI355X):", "", "    " + cmd, "",
-             "Summary written by `python -m block_causal_attention_qi_amd.profile_summary mfma gpurun_out/prof`.", "",
+             "Summary written by `python -m block_causal_attention_qi_amd.profile_summary mfma OUT` (OUT: the runs' output directory).", "",
              "MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (4 SIMDs x SQ_BUSY_CU_CYCLES): the share of the",
              "cycles in which the CUs run the kernel that each SIMD's matrix core is busy, whatever the",
              "clock.  SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512 against the kernel's algorithmic FLOPs checks",

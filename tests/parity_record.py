@@ -1,18 +1,20 @@
 """Measured parity figures of the GPU tests, kept as a record.
 
-Each call appends one JSON line to gpurun_out/parity/records.jsonl under the
-repository root and prints it, so the figures a test gates on survive the run
-and the long tests show progress.  tests/records/ keeps the records of a full
+Each call appends one JSON line to records.jsonl in the directory named by
+QI_PARITY_RECORD_DIR (default: qi_parity_records in the system's temporary
+directory) and prints it, so the figures a test gates on survive the run and
+the long tests show progress.  tests/records/ keeps the records of a full
 `python -m pytest tests -m gpu` run and their summary (summarize below)."""
 from __future__ import annotations
 
 import json
 import os
 import sys
+import tempfile
 import time
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-RECORD_DIR = os.path.join(ROOT, "gpurun_out", "parity")
+RECORD_DIR = os.environ.get("QI_PARITY_RECORD_DIR") or os.path.join(tempfile.gettempdir(), "qi_parity_records")
 
 
 def record(kind: str, **fields) -> dict:

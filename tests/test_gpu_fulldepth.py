@@ -30,7 +30,7 @@ trained DiT) the bf16-compute oracle's own distance to the exact one falls
 below the bar at 1/8, and there the exact-oracle 2e-2 / 0.999 bar itself is
 gated.
 
-Every figure goes to gpurun_out/parity/records.jsonl (tests/parity_record.py)."""
+Every figure is recorded by tests/parity_record.py."""
 import json
 import os
 
