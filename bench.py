@@ -114,14 +114,13 @@ def calibrate():
         lds[name] = round(v.value, 1)
     res["lds_mix_cycles_per_iteration_per_cu"] = lds
     valu = {}
-    for mode, name in ((0, "32_exp"), (1, "32_fma"), (2, "8_mfma_32_exp"), (3, "8_mfma_32_fma"), (4, "8_mfma"),
-                       (5, "8_mfma_beside_32_exp_other_wave"), (6, "8_mfma_beside_32_fma_other_wave"),
-                       (7, "8_mfma_one_wave_per_simd"), (8, "32_exp_one_wave_per_simd"),
-                       (9, "32_fma_one_wave_per_simd")):
+    for mode, name in ((0, "2w_32_exp"), (1, "2w_32_fma"), (2, "2w_8_mfma_32_exp_interleaved"),
+                       (3, "2w_8_mfma_32_fma_interleaved"), (4, "2w_8_mfma"), (5, "mfma_wave_beside_exp_wave"),
+                       (6, "mfma_wave_beside_fma_wave"), (7, "1w_8_mfma"), (8, "1w_32_exp"), (9, "1w_32_fma")):
         v = ctypes.c_double(0)
-        _lib.check(lib.qi_calib_valu_cycles(mode, 20000, ctypes.byref(v)), "qi_calib_valu_cycles")
+        _lib.check(lib.qi_calib_valu_ns(mode, 20000, ctypes.byref(v)), "qi_calib_valu_ns")
         valu[name] = round(v.value, 1)
-    res["valu_mix_cycles_per_iteration_per_wave_two_waves_per_simd"] = valu
+    res["valu_mix_ns_per_iteration"] = valu
     gemm = {}
     for (M, N, K) in [(4096, 24576, 4096), (4096, 12288, 4096), (4096, 4096, 12288), (4096, 4096, 4096)]:
         A = torch.randn(M, K, device="cuda", dtype=torch.bfloat16)

@@ -115,7 +115,7 @@ CALIB_SIGNATURES = {
     "qi_calib_mfma_tflops": (c_int32, [c_int32, c_int32, c_void_p]),
     "qi_calib_copy_gbs": (c_int32, [c_void_p, c_void_p, c_int64, c_int32, c_void_p]),
     "qi_calib_lds_cycles": (c_int32, [c_int32, c_int32, c_void_p]),
-    "qi_calib_valu_cycles": (c_int32, [c_int32, c_int32, c_void_p]),
+    "qi_calib_valu_ns": (c_int32, [c_int32, c_int32, c_void_p]),
 }
 QI_KERNEL_KINDS = 16
 

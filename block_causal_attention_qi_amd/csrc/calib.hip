@@ -133,18 +133,21 @@ __global__ __launch_bounds__(512, 1) void lds_mix_kernel(float *out, int iters, 
   }
 }
 
-// One 512-thread workgroup per CU (8 waves, two per SIMD); each iteration
-// every wave issues the MODE's mix (qi_calib.h) on 8 independent chains;
-// wave 0 of each workgroup adds its shader cycles to clk[0] and 1 to clk[1].
-template <int MODE>
-__global__ __launch_bounds__(512, 1) void valu_mix_kernel(float *out, int iters, unsigned long long *clk) {
-  const int tid = threadIdx.x, lane = tid & 63;
+// One workgroup per CU with W waves per SIMD (waves w and w + 4 share a SIMD
+// when W = 2).  ROLE of a wave: 1 = 8 MFMAs per iteration, 2 = 32 VALU
+// instructions (KIND 1: v_fma_f32, 2: v_exp_f32) on 8 independent chains,
+// 3 = both, four VALU instructions after each MFMA.  SPLIT: waves 0-3 take
+// role 1, waves 4-7 role 2.  Timed from the host with events (wall clock).
+template <int W, int KIND, int ROLE, int SPLIT>
+__global__ __launch_bounds__(256 * W, 1) void valu_mix_kernel(float *out, int iters) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int role = SPLIT ? (wave < 4 ? 1 : 2) : ROLE;
   float v[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) v[j] = -1.f - 0.01f * (float)(lane + j);
-  f32x16 acc[8];
+  f32x16 acc[4];
 #pragma unroll
-  for (int j = 0; j < 8; ++j)
+  for (int j = 0; j < 4; ++j)
 #pragma unroll
     for (int e = 0; e < 16; ++e) acc[j][e] = 0.f;
   bf16x8 a, b;
@@ -153,49 +156,37 @@ __global__ __launch_bounds__(512, 1) void valu_mix_kernel(float *out, int iters,
     a[i] = (__bf16)(lane * 0.01f);
     b[i] = (__bf16)0.5f;
   }
-  // modes 5..9: waves 0-3 (one per SIMD) issue only the MFMAs (modes 5-7),
-  // waves 4-7 (the other wave of each SIMD) only the exponentials (5, 8) or
-  // FMAs (6, 9); the rest of the waves run the empty loop
-  const int wave = tid >> 6;
-  const bool split = MODE >= 5;
-  const bool do_mfma = split ? (wave < 4 && MODE <= 7) : (MODE >= 2 && MODE <= 4);
-  const bool do_exp = split ? ((MODE == 5 || MODE == 8) && wave >= 4) : (MODE == 0 || MODE == 2);
-  const bool do_fma = split ? ((MODE == 6 || MODE == 9) && wave >= 4) : (MODE == 1 || MODE == 3);
-  constexpr bool kMfma = MODE >= 2 && MODE <= 7, kExp = MODE == 0 || MODE == 2 || MODE == 5 || MODE == 8,
-                 kFma = MODE == 1 || MODE == 3 || MODE == 6 || MODE == 9;
-  const uint64_t t0 = __builtin_amdgcn_s_memtime();
-  for (int it = 0; it < iters; ++it) {
-    if (kMfma && do_mfma) {
+  auto valu = [&](int j) {
+    if constexpr (KIND == 1) v[j] = __builtin_fmaf(v[j], 0.999f, 0.001f);
+    else v[j] = __builtin_amdgcn_exp2f(v[j]);
+  };
+  if (role == 1) {
+    for (int it = 0; it < iters; ++it)
 #pragma unroll
-      for (int j = 0; j < 8; ++j) acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[j], 0, 0, 0);
-    }
-    if ((kExp && do_exp) || (kFma && do_fma)) {
+      for (int m = 0; m < 8; ++m) acc[m & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[m & 3], 0, 0, 0);
+  } else if (role == 2) {
+    for (int it = 0; it < iters; ++it)
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
+      for (int r = 0; r < 32; ++r) valu(r & 7);
+  } else {
+    for (int it = 0; it < iters; ++it) {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          if constexpr (kExp) v[j] = __builtin_amdgcn_exp2f(v[j]);
-          if constexpr (kFma) v[j] = __builtin_fmaf(v[j], 0.999f, 0.001f);
-        }
-    }
-    if constexpr (kMfma && MODE >= 2 && MODE <= 3) {
+      for (int m = 0; m < 8; ++m) {
+        acc[m & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[m & 3], 0, 0, 0);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
+        for (int r = 0; r < 4; ++r) valu((4 * m + r) & 7);
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-        __builtin_amdgcn_sched_group_barrier(0x402, 4, 0);  // four VALU / transcendental
+        __builtin_amdgcn_sched_group_barrier(0x402, 4, 0);  // then four VALU / transcendental
       }
     }
   }
-  const uint64_t t1 = __builtin_amdgcn_s_memtime();
   float sum = 0.f;
 #pragma unroll
-  for (int j = 0; j < 8; ++j) sum += v[j] + acc[j][0];
+  for (int j = 0; j < 8; ++j) sum += v[j];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) sum += acc[j][0];
   // keeps the work alive: the compiler cannot decide this (practically never true)
   if (__float_as_uint(sum) == (uint32_t)iters * 2654435761u) out[tid] = sum;
-  if (tid == 0 || (split && tid == 256)) {  // modes 5..9 also time wave 4
-    atomicAdd(&clk[tid == 0 ? 0 : 2], (unsigned long long)(t1 - t0));
-    atomicAdd(&clk[tid == 0 ? 1 : 3], 1ull);
-  }
 }
 
 }  // namespace
@@ -314,50 +305,47 @@ qi_status qi_calib_lds_cycles(int32_t mode, int32_t iters, double *cycles) {
   return rc;
 }
 
-qi_status qi_calib_valu_cycles(int32_t mode, int32_t iters, double *cycles) {
-  if (!cycles) return QI_ERR_NULL;
+qi_status qi_calib_valu_ns(int32_t mode, int32_t iters, double *ns) {
+  if (!ns) return QI_ERR_NULL;
   if (mode < 0 || mode > 9 || iters < 4 || iters > 10000000) return QI_ERR_RANGE;
   int dev = 0, cus = 0;
   if (hipGetDevice(&dev) != hipSuccess) return QI_ERR_HIP;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return QI_ERR_HIP;
   float *out = nullptr;
-  unsigned long long *clk = nullptr;
   hipStream_t st;
+  hipEvent_t e0, e1;
   if (hipStreamCreate(&st) != hipSuccess) return QI_ERR_HIP;
   qi_status rc = QI_OK;
-  if (hipMalloc(&out, 512 * sizeof(float)) != hipSuccess || hipMalloc(&clk, 4 * sizeof(unsigned long long)) != hipSuccess)
-    rc = QI_ERR_HIP;
-  auto run = [&](int n) {
-    switch (mode) {
-      case 0: hipLaunchKernelGGL(valu_mix_kernel<0>, dim3(cus), dim3(512), 0, st, out, n, clk); break;
-      case 1: hipLaunchKernelGGL(valu_mix_kernel<1>, dim3(cus), dim3(512), 0, st, out, n, clk); break;
-      case 2: hipLaunchKernelGGL(valu_mix_kernel<2>, dim3(cus), dim3(512), 0, st, out, n, clk); break;
-      case 3: hipLaunchKernelGGL(valu_mix_kernel<3>, dim3(cus), dim3(512), 0, st, out, n, clk); break;
-      case 4: hipLaunchKernelGGL(valu_mix_kernel<4>, dim3(cus), dim3(512), 0, st, out, n, clk); break;
-      case 5: hipLaunchKernelGGL(valu_mix_kernel<5>, dim3(cus), dim3(512), 0, st, out, n, clk); break;
-      case 6: hipLaunchKernelGGL(valu_mix_kernel<6>, dim3(cus), dim3(512), 0, st, out, n, clk); break;
-      case 7: hipLaunchKernelGGL(valu_mix_kernel<7>, dim3(cus), dim3(512), 0, st, out, n, clk); break;
-      case 8: hipLaunchKernelGGL(valu_mix_kernel<8>, dim3(cus), dim3(512), 0, st, out, n, clk); break;
-      default: hipLaunchKernelGGL(valu_mix_kernel<9>, dim3(cus), dim3(512), 0, st, out, n, clk); break;
-    }
-  };
-  unsigned long long h[4] = {0, 0, 0, 0};
+  if (hipMalloc(&out, 1024 * sizeof(float)) != hipSuccess) rc = QI_ERR_HIP;
+  if (rc == QI_OK && (hipEventCreate(&e0) != hipSuccess || hipEventCreate(&e1) != hipSuccess)) rc = QI_ERR_HIP;
   if (rc == QI_OK) {
-    run(100);  // warm-up
-    if (hipMemsetAsync(clk, 0, 4 * sizeof(unsigned long long), st) != hipSuccess) rc = QI_ERR_HIP;
-  }
-  if (rc == QI_OK) {
+    auto run = [&](int n) {
+      switch (mode) {
+        case 0: hipLaunchKernelGGL((valu_mix_kernel<2, 2, 2, 0>), dim3(cus), dim3(512), 0, st, out, n); break;
+        case 1: hipLaunchKernelGGL((valu_mix_kernel<2, 1, 2, 0>), dim3(cus), dim3(512), 0, st, out, n); break;
+        case 2: hipLaunchKernelGGL((valu_mix_kernel<2, 2, 3, 0>), dim3(cus), dim3(512), 0, st, out, n); break;
+        case 3: hipLaunchKernelGGL((valu_mix_kernel<2, 1, 3, 0>), dim3(cus), dim3(512), 0, st, out, n); break;
+        case 4: hipLaunchKernelGGL((valu_mix_kernel<2, 1, 1, 0>), dim3(cus), dim3(512), 0, st, out, n); break;
+        case 5: hipLaunchKernelGGL((valu_mix_kernel<2, 2, 0, 1>), dim3(cus), dim3(512), 0, st, out, n); break;
+        case 6: hipLaunchKernelGGL((valu_mix_kernel<2, 1, 0, 1>), dim3(cus), dim3(512), 0, st, out, n); break;
+        case 7: hipLaunchKernelGGL((valu_mix_kernel<1, 1, 1, 0>), dim3(cus), dim3(256), 0, st, out, n); break;
+        case 8: hipLaunchKernelGGL((valu_mix_kernel<1, 2, 2, 0>), dim3(cus), dim3(256), 0, st, out, n); break;
+        default: hipLaunchKernelGGL((valu_mix_kernel<1, 1, 2, 0>), dim3(cus), dim3(256), 0, st, out, n); break;
+      }
+    };
+    run(200);  // warm-up
+    (void)hipEventRecord(e0, st);
     run(iters);
-    if (hipMemcpyAsync(h, clk, sizeof(h), hipMemcpyDeviceToHost, st) != hipSuccess ||
-        hipStreamSynchronize(st) != hipSuccess || hipGetLastError() != hipSuccess)
+    (void)hipEventRecord(e1, st);
+    float ms = 0.f;
+    if (hipEventSynchronize(e1) != hipSuccess || hipEventElapsedTime(&ms, e0, e1) != hipSuccess ||
+        hipGetLastError() != hipSuccess)
       rc = QI_ERR_HIP;
+    *ns = rc == QI_OK ? (double)ms * 1e6 / iters : 0.0;
+    (void)hipEventDestroy(e0);
+    (void)hipEventDestroy(e1);
   }
-  // the slower of the two timed waves (modes 5..9 time waves 0 and 4; in 7..9 one of them idles)
-  const double c0 = h[1] ? (double)h[0] / (double)h[1] / iters : 0.0;
-  const double c1 = h[3] ? (double)h[2] / (double)h[3] / iters : 0.0;
-  *cycles = rc == QI_OK ? (c0 > c1 ? c0 : c1) : 0.0;
   if (out) (void)hipFree(out);
-  if (clk) (void)hipFree(clk);
   (void)hipStreamDestroy(st);
   return rc;
 }

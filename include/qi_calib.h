@@ -49,28 +49,25 @@ qi_status qi_calib_copy_gbs(const void *src, void *dst, int64_t bytes, int32_t r
  * NULL, RANGE (mode not 0..4, iters < 4), HIP. */
 qi_status qi_calib_lds_cycles(int32_t mode, int32_t iters, double *cycles);
 
-/* Shader cycles per iteration of a CU-wide VALU / MFMA instruction mix: one
- * workgroup of 512 threads (8 waves, two per SIMD) per CU, each wave issuing
- * per iteration, on 8 independent register chains,
- *   mode 0: 32 v_exp_f32,
- *   mode 1: 32 v_fma_f32,
- *   mode 2: 8 v_mfma_f32_32x32x16_bf16 with the 32 v_exp_f32 of mode 0
+/* Wall-clock nanoseconds per iteration of a CU-wide VALU / MFMA instruction
+ * mix, timed with HIP events over `iters` iterations on every CU (one
+ * workgroup per CU); per iteration a wave issues 8 v_mfma_f32_32x32x16_bf16
+ * and/or 32 VALU instructions on 8 independent register chains:
+ *   mode 0: two waves per SIMD, each 32 v_exp_f32,
+ *   mode 1: two waves per SIMD, each 32 v_fma_f32,
+ *   mode 2: two waves per SIMD, each 8 MFMAs with the 32 v_exp_f32 of mode 0
  *           interleaved (four after each MFMA),
- *   mode 3: 8 MFMAs with the 32 v_fma_f32 of mode 1 interleaved,
- *   mode 4: the 8 MFMAs alone,
- *   mode 5: waves 0-3 (one on each SIMD) the 8 MFMAs, waves 4-7 (the other
- *           wave of each SIMD) the 32 v_exp_f32,
+ *   mode 3: as mode 2 with the 32 v_fma_f32,
+ *   mode 4: two waves per SIMD, each 8 MFMAs,
+ *   mode 5: per SIMD one wave with the 8 MFMAs, the other with the 32
+ *           v_exp_f32,
  *   mode 6: as mode 5 with the 32 v_fma_f32,
- *   mode 7: waves 0-3 the 8 MFMAs, waves 4-7 idle (one MFMA wave per SIMD),
- *   mode 8: waves 4-7 the 32 v_exp_f32, waves 0-3 idle,
- *   mode 9: waves 4-7 the 32 v_fma_f32, waves 0-3 idle,
- * timed with the shader clock of wave 0 of every workgroup (and in modes 5..9
- * of wave 4, the slower of the two reported) and averaged: the issue cost of
- * the exponentials against plain FMAs and of MFMAs, with one or two waves per
- * SIMD, in the same wave or in the SIMD's other wave.  Data are synthetic.
- * BLOCKS until done.  *cycles receives the cycles per iteration.  Errors:
- * NULL, RANGE (mode not 0..9, iters < 4), HIP. */
-qi_status qi_calib_valu_cycles(int32_t mode, int32_t iters, double *cycles);
+ *   mode 7: one wave per SIMD, 8 MFMAs,
+ *   mode 8: one wave per SIMD, 32 v_exp_f32,
+ *   mode 9: one wave per SIMD, 32 v_fma_f32.
+ * Data are synthetic.  BLOCKS until done.  *ns receives the time per
+ * iteration.  Errors: NULL, RANGE (mode not 0..9, iters < 4), HIP. */
+qi_status qi_calib_valu_ns(int32_t mode, int32_t iters, double *ns);
 
 #ifdef __cplusplus
 }
