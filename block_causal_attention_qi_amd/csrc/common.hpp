@@ -37,8 +37,11 @@ QI_DEV f32x4 mfma16x16x32(u32x4 a, u32x4 b, f32x4 c) {
 
 // D = A(32x16) * B(16x32) + C, bf16 inputs, fp32 accumulate.  Lane l supplies
 // A[l%32][8*(l/32) .. +8) and B[8*(l/32) .. +8)[l%32]; element i of D (16 per
-// lane) is row 8*(i/4) + 4*(l/32) + i%4 of column l%32.  On gfx950 this shape
-// runs at twice the rate of the 16x16x32 one (measured on MI355X).
+// lane) is row 8*(i/4) + 4*(l/32) + i%4 of column l%32.  On gfx950 the two
+// shapes give the same fp32 results bit for bit (measured on MI355X).  In a
+// register-only loop this shape reaches about 1.7x the FLOP rate of the
+// 16x16x32 one; fed from LDS in the 256 x 256 GEMM tile the 16x16x32 form runs
+// faster.
 QI_DEV f32x16 mfma32x32x16(u32x4 a, u32x4 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
 }

@@ -12,16 +12,19 @@
 //              [heads][128][Tp] buffers (text rows -> text K/V, which is the
 //              cache slot on a capture pass).
 //
-// The MFMA (32x32x16 bf16, the full-rate shape on gfx950) is issued
-// "transposed": its A operand is a 32-row slice of W (output features) and its
-// B operand a 32-row slice of the activations (tokens), so each lane ends up
-// holding groups of 4 CONSECUTIVE output features of one token.  That puts
-// every RoPE pair (2k, 2k+1) and every float4 residual update inside one lane.
+// The MFMA (32x32x16 bf16, or 16x16x32 bf16 in the 256 x 256 kernel; both
+// give the same fp32 results bit for bit on gfx950) is issued "transposed":
+// its A operand is a slice of W rows (output features) and its B operand a
+// slice of activation rows (tokens), so each lane ends up holding groups of 4
+// CONSECUTIVE output features of one token.  That puts every RoPE pair
+// (2k, 2k+1) and every float4 residual update inside one lane.
 //
 // Row-count invariance (the MLX page's row-count hazard in "Text K/V reuse"):
-// every output element is produced by the same MFMA instruction over the same
-// K order whatever M is and wherever the row sits in its tile, so a row's
-// result does not depend on how many rows the pass has.  No atomics.  The
+// every output element is produced by MFMAs over the same K order, with the
+// same fp32 result, whatever M is, whichever tile shape the launcher picks and
+// wherever the row sits in its tile, and the epilogues round without fused
+// multiply-adds, so a row's result does not depend on how many rows the pass
+// has.  No atomics.  The
 // residual GEMMs of a small image (few rows, too few tiles for the chip) are
 // split over K; the split is chosen from the image's token count N alone, so
 // the joint and the image-only passes of one render (and both CFG branches)
@@ -113,6 +116,23 @@ QI_DEV void tile_of(int bid, int nTM, int nTN, int &tm, int &tn) {
 }
 
 // ---------------------------------------------------------------- epilogue
+// Epilogue arithmetic with every product rounded on its own (no fused
+// multiply-add), written out so that the compiler cannot contract it one way
+// in one kernel instance and another way in the next: every tile shape, and
+// the joint and image-only passes, then round a row's outputs identically.
+// x + gate * v, per component
+QI_DEV f32x4 gated_add(f32x4 x, f32x4 gate, f32x4 v) {
+  f32x4 r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) r[i] = __fadd_rn(x[i], __fmul_rn(gate[i], v[i]));
+  return r;
+}
+// The RoPE rotation of the pair (a, b) by the angle with cosine c and sine s:
+// (a c - b s, a s + b c).
+QI_DEV float2 rope_pair(float a, float b, float c, float s) {
+  return float2{__fsub_rn(__fmul_rn(a, c), __fmul_rn(b, s)), __fadd_rn(__fmul_rn(a, s), __fmul_rn(b, c))};
+}
+
 // The 4 consecutive outputs n..n+3 of token m (accumulators v).
 template <int EPI>
 QI_DEV void store4(const GemmArgs &g, int m, int n, f32x4 v) {
@@ -123,7 +143,7 @@ QI_DEV void store4(const GemmArgs &g, int m, int n, f32x4 v) {
   } else if constexpr (EPI == EPI_RESID) {
     const float *gp = g.gate + (m < g.L_rows ? 0 : g.gate_img_off) + n;
     f32x4 *xp = (f32x4 *)(g.X + (size_t)m * g.ldx + n);
-    *xp = *xp + *(const f32x4 *)gp * v;
+    *xp = gated_add(*xp, *(const f32x4 *)gp, v);
   }
 }
 
@@ -258,9 +278,8 @@ QI_DEV void qkv_epilogue(const GemmArgs &g, int m0, int n_tile, int wrow, int n0
         const float2 cs = __builtin_bit_cast(float2, cl2[slot]);
         const float2 sn = __builtin_bit_cast(float2, sl2[slot]);
         const f32x4 v = quad(acc[f][t], j);
-        const float y0 = v[0] * cs.x - v[1] * sn.x, y1 = v[0] * sn.x + v[1] * cs.x;
-        const float y2 = v[2] * cs.y - v[3] * sn.y, y3 = v[2] * sn.y + v[3] * cs.y;
-        y[t][f][j] = u32x2{pack_bf16x2(y0, y1), pack_bf16x2(y2, y3)};
+        const float2 y01 = rope_pair(v[0], v[1], cs.x, sn.x), y23 = rope_pair(v[2], v[3], cs.y, sn.y);
+        y[t][f][j] = u32x2{pack_bf16x2(y01.x, y01.y), pack_bf16x2(y23.x, y23.y)};
       }
   }
   __syncthreads();  // every wave is done with the staged tables
@@ -466,17 +485,17 @@ __global__ __launch_bounds__(256) void resid_reduce_kernel(const GemmArgs g) {
   for (int s = 1; s < g.ksplit; ++s) v += *(const f32x4 *)(p + s * mn);
   const float *gp = g.gate + (m < g.L_rows ? 0 : g.gate_img_off) + n;
   f32x4 *xp = (f32x4 *)(g.X + (size_t)m * g.ldx + n);
-  *xp = *xp + *(const f32x4 *)gp * v;
+  *xp = gated_add(*xp, *(const f32x4 *)gp, v);
 }
 
-// ---------------------------------------------------------------- 256-row W tiles, 8 waves
-// Large-M shape: one 256 x 256 tile per workgroup of 8 waves (2 along tokens
-// x 4 along W rows; wave tile 128 tokens x 64 W rows, MFMA 32x32x16), one
-// workgroup per CU.  A 256-row operand tile costs 4x fewer fetched bytes per
-// FLOP than the 128 x 128 tile.  The same kernel with BMT = 128 token rows
-// (wave tile 64 x 64, the 128 x 128 kernels' MFMA sequence) serves a few
-// hundred rows: one workgroup per CU still, and 3/4 of the copied bytes per
-// FLOP of two 128 x 128 workgroups.
+// ---------------------------------------------------------------- 128 x 256 tiles, 8 waves
+// A few hundred token rows: one 128 x 256 tile per workgroup of 8 waves (2
+// along tokens x 4 along W rows; wave tile 64 tokens x 64 W rows, MFMA
+// 32x32x16), one workgroup per CU -- 3/4 of the copied bytes per FLOP of two
+// 128 x 128 workgroups.  (The template also has a 256-row form; the 256 x 256
+// shape runs on gemm_bf16_lds_kernel below.)  On this shape the 32x32x16
+// MFMA runs faster than the 16x16x32 one of the 256 x 256 kernel, and both
+// give the same fp32 results bit for bit.
 //
 // Operands go from global memory straight into LDS (buffer loads with the LDS
 // flag: lane l of a copy instruction lands 16 bytes at slot base + l), so no
@@ -501,9 +520,8 @@ __global__ __launch_bounds__(256) void resid_reduce_kernel(const GemmArgs g) {
 // uniform 64-row step.  Token rows past M are clamped to row M - 1 (loaded,
 // never stored), so every copy stays inside the operands.
 //
-// EPI_RESID may split K (BMT = 128 only in practice): as in the 128 x 128
-// kernels, chunk s of K writes fp32 partial sums and resid_reduce_kernel adds
-// them in order.
+// EPI_RESID may split K: as in the 128 x 128 kernels, chunk s of K writes
+// fp32 partial sums and resid_reduce_kernel adds them in order.
 namespace gemmL {
 constexpr int BN = 256, BK = 64, THREADS = 512;
 constexpr int FS = 2;                   // wave tile: 2 x 32 W rows
@@ -936,6 +954,366 @@ __global__ __launch_bounds__(gemmM::THREADS, 2) void gemm_bf16_mid_kernel(const 
       for (int f = 0; f < FS; ++f)
 #pragma unroll
         for (int j = 0; j < 4; ++j) store4<EPI>(g, m, tn * BN + wn * WF + f * 32 + 8 * j + h4, quad(acc[f][t], j));
+    }
+  }
+}
+
+// ---------------------------------------------------------------- 256 x 256 tiles, 16x16x32 MFMA
+// Large M: one 256 x 256 tile per workgroup of 8 waves (2 along tokens x 4
+// along W rows, wave tile 128 tokens x 64 W rows -- half a q / k / v head,
+// one gate and one up half of 32 SwiGLU outputs), one workgroup per CU.
+//
+// MFMA 16x16x32 bf16, issued as D[16 W rows][16 tokens]: lane l holds the 4
+// consecutive W rows 4 (l / 16) .. + 3 of token l % 16, so RoPE pairs and
+// float4 residual updates stay inside a lane, and one store instruction
+// covers 16 tokens x 16 consecutive features.  Against the 32x32x16 shape of
+// the other kernels it takes half the K per instruction and the same LDS
+// reads per FLOP; on the MI355X both shapes give the same fp32 result bit for
+// bit (checked over random and rounding-sensitive inputs, and on whole DiT
+// steps against the register-staged kernel), and on this tile the 16x16x32
+// form runs the gate/up, QKV and O-proj GEMMs 5-7% faster.
+//
+// Operands go from global memory straight into LDS (buffer loads with the LDS
+// flag: lane l of a copy instruction lands 16 bytes at slot base + l), so no
+// register staging and no LDS store instructions: measured on gfx950, a
+// ds_write_b128 costs the LDS about 2.5x a ds_read_b128 per byte.  Each K step
+// of 64 moves a 256-row A slice and a 256-row W slice.  The A slices
+// (activations, just written by the previous kernel, mostly cache hits) are
+// double-buffered and copied one step ahead; the W slices (weights, streamed
+// from HBM) are triple-buffered and copied two steps ahead.  The five stages
+// are separate LDS objects indexed by compile-time constants (the K loop is
+// unrolled by 6), so the compiler's waits for a copy cover the stage it
+// fills, and the barrier that ends a step waits only for the copies the next
+// step reads, leaving the newest W copies in flight.  The A copies are issued
+// among the first sub-step's MFMAs, the W copies among the second's.
+//
+// LDS layout of a slice: row r (64 bf16 = 8 chunks of 16 bytes), chunk c at
+// slot r * 8 + (c ^ ((r >> 1) & 7)) (see lds_slot).  Copy instruction j of
+// wave w fills slots (8 j + w) * 64 .. + 63: rows 64 j + 8 w + lane / 8,
+// slot lane % 8 holding chunk (lane % 8) ^ ((row >> 1) & 7) -- which does not
+// depend on j -- so each lane's source offset is fixed and j only adds a
+// uniform 64-row step.  Token rows past M are clamped to row M - 1
+// (loaded, never stored), so every copy stays inside the operands.  A
+// fragment (16 rows x 32 K) is one ds_read_b128 per lane: row l % 16, chunk
+// 4 kk + l / 16 of sub-step kk; the 16 rows of one read pass land on 16
+// distinct 16-byte bank groups.
+//
+// EPI_RESID may split K: chunk s of K writes fp32 partial sums and
+// resid_reduce_kernel adds them in order.
+namespace gemmT {
+constexpr int BK = 64;
+constexpr int RSRC_FLAGS = 0x00020000;  // raw buffer, 32-bit dwords
+}  // namespace gemmT
+
+template <int N, int I = 0, class F>
+QI_DEV void static_for(F &&f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<N, I + 1>(f);
+  }
+}
+
+// The V section of a QKV wave tile: NW = 4 blocks of 16 W rows from n0 (one
+// head, n0 % 64 == 0) and NT blocks of 16 tokens from mbase, stored
+// transposed into V^T [heads][128][ldv]: for one output feature the 16 lanes
+// l % 16 hold 16 consecutive tokens (32 contiguous bytes per store).
+template <int NT, int NW>
+QI_DEV void store_v_wave16(const GemmArgs &g, int mbase, int n0, const f32x4 (&acc)[NW][NT], int lane) {
+  const int w0 = n0 - 2 * g.H;
+  const int head = w0 >> 7, dh0 = w0 & 127;
+  const int fr = lane & 15, kq = lane >> 4;
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    const int m = mbase + 16 * t + fr;
+    if (m >= g.M) continue;
+    const bool txt = m < g.L_rows;
+    const int row = txt ? m : m - g.L_rows;
+    const int br = (txt || g.batch <= 1) ? 0 : row / g.seg_i;  // branch of an image row
+    const int brow = row - br * g.seg_i;
+    const int ldv = txt ? g.ldv_t : g.ldv_i;
+    u16 *base =
+        (txt ? g.vt_t : g.vt_i) + (size_t)br * g.H * ldv + ((size_t)head * 128 + dh0 + 4 * kq) * ldv + brow;
+#pragma unroll
+    for (int f = 0; f < NW; ++f)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) base[(size_t)(16 * f + r) * ldv] = f32_to_bf16(acc[f][t][r]);
+  }
+}
+
+// The QKV epilogue of a BM-token workgroup tile of the LDS-copy kernel (the
+// qkv_epilogue steps with the 16x16 accumulator layout): wave (wrow / WT,
+// n0) holds WT = 16 NT tokens x 64 W rows, half of one q or k head, as 4
+// consecutive features of one token per lane and accumulator.
+template <int BM, int THREADS, int NT, int NW, int NOBJ, int SLOTS>
+QI_DEV void qkv_epilogue16(const GemmArgs &g, int m0, int n_tile, int wrow, int n0, const f32x4 (&acc)[NW][NT],
+                           int tid, const LdsObjs<NOBJ, SLOTS> lo) {
+  static_assert(NW == 4, "a wave tile is half a head: 64 W rows");
+  constexpr int R = LdsObjs<NOBJ, SLOTS>::kRows;
+  constexpr int WT = 16 * NT;
+  constexpr int RS = WT * 8;       // 16-byte slots of one wave's region
+  constexpr int RPO = SLOTS / RS;  // regions per object
+  static_assert(RPO >= 1 && (THREADS / 64) <= RPO * NOBJ, "the waves' regions fit in the objects");
+  const int lane = tid & 63, wave = tid >> 6;
+  const int fr = lane & 15, kq = lane >> 4;
+  if (n_tile / g.H >= 2) {
+    store_v_wave16<NT, NW>(g, m0 + wrow, n0, acc, lane);
+    return;
+  }
+  const int sec = n0 / g.H;
+  const int w0 = n0 - sec * g.H;
+  const int head = w0 >> 7, dh0 = w0 & 127;
+  __syncthreads();
+  stage_rope_rows<BM, THREADS>(g, m0, lo, tid);
+  __syncthreads();
+  // outputs dh0 + 16 f + 4 kq + 0..3 are RoPE pairs 2q, 2q + 1 with
+  // q = dh0 / 4 + 4 f + kq
+  const int q0 = (dh0 >> 2) + kq;
+  u32x2 y[NT][NW];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    const int r = wrow + 16 * t + fr;
+    const u32x2 *cl2 = (const u32x2 *)lo.o(r / R), *sl2 = (const u32x2 *)lo.o(BM / R + r / R);
+#pragma unroll
+    for (int f = 0; f < NW; ++f) {
+      const int slot = (r % R) * 32 + ((q0 + 4 * f) ^ (r & 31));
+      const float2 cs = __builtin_bit_cast(float2, cl2[slot]);
+      const float2 sn = __builtin_bit_cast(float2, sl2[slot]);
+      const f32x4 v = acc[f][t];
+      const float2 y01 = rope_pair(v[0], v[1], cs.x, sn.x), y23 = rope_pair(v[2], v[3], cs.y, sn.y);
+      y[t][f] = u32x2{pack_bf16x2(y01.x, y01.y), pack_bf16x2(y23.x, y23.y)};
+    }
+  }
+  __syncthreads();  // every wave is done with the staged tables
+  u32x4 *reg = lo.o(wave / RPO) + (wave % RPO) * RS;
+  u32x2 *reg2 = (u32x2 *)reg;
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    const int rr = 16 * t + fr;
+#pragma unroll
+    for (int f = 0; f < NW; ++f) reg2[rr * 16 + ((4 * f + kq) ^ ((rr >> 1) & 15))] = y[t][f];
+  }
+  __syncthreads();
+  u16 *qk_t = sec == 0 ? g.q_t : g.k_t, *qk_i = sec == 0 ? g.q_i : g.k_i;
+#pragma unroll
+  for (int it = 0; it < WT * 8 / 64; ++it) {
+    const int i = lane + 64 * it;
+    const int rr = i >> 3, k = i & 7, x = (rr >> 1) & 15;
+    u32x4 v = reg[rr * 8 + (k ^ (x >> 1))];
+    if (x & 1) v = u32x4{v[2], v[3], v[0], v[1]};
+    const int m = m0 + wrow + rr;
+    if (m >= g.M) continue;
+    const bool txt = m < g.L_rows;
+    const int row = txt ? m : m - g.L_rows;
+    const int br = (txt || g.batch <= 1) ? 0 : row / g.seg_i;  // branch of an image row
+    const int brow = row - br * g.seg_i;
+    u16 *dst = (txt ? qk_t : qk_i) + (size_t)br * g.H * g.seg_i +
+               ((size_t)head * (txt ? g.seg_t : g.seg_i) + brow) * 128 + dh0 + 8 * k;
+    *(u32x4 *)dst = v;
+  }
+}
+
+template <int EPI, int BM, int BN, int WAVES>
+__global__ __launch_bounds__(64 * WAVES, WAVES == 8 ? 1 : 2) void gemm_bf16_lds_kernel(const GemmArgs g) {
+  using namespace gemmT;
+  static_assert(BM == 256 && BN == 256 && WAVES == 8, "the 256 x 256 tile");
+  constexpr int THREADS = 64 * WAVES, WN = WAVES / 2;
+  constexpr int WT = BM / 2, WF = BN / WN;  // wave tile: WT tokens x WF W rows
+  constexpr int NT = WT / 16, NW = WF / 16;
+  static_assert(WF == 64, "a wave tile holds 64 W rows");
+  constexpr int NCPA = BM * 8 / THREADS, NCPW = BN * 8 / THREADS;  // copy instructions per slice per thread
+  constexpr int RSTEP = 8 * WAVES;                                 // tile rows per copy instruction
+  if (g.skip && *g.skip) return;
+  __shared__ u32x4 sA0[BM * 8], sA1[BM * 8];
+  __shared__ u32x4 sW0[BN * 8], sW1[BN * 8], sW2[BN * 8];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave & 1, wn = wave >> 1;
+  const int nTM = (g.M + BM - 1) / BM;
+  const int nTN = EPI == EPI_SWIGLU ? g.F / (BN / 2) : g.N / BN;
+  const bool split = EPI == EPI_RESID && g.ksplit > 1;
+  const int ntile = nTM * nTN;
+  const int kchunk = split ? (int)(blockIdx.x / ntile) : 0;
+  const int kc = split ? g.K / g.ksplit : g.K;
+  int tm, tn;
+  tile_of(split ? (int)(blockIdx.x % ntile) : (int)blockIdx.x, nTM, nTN, tm, tn);
+  const int m0 = tm * BM;
+
+  // copy sources: tile row r0 + RSTEP j, chunk cch
+  const int r0 = 8 * wave + (lane >> 3);
+  const int cch = (lane & 7) ^ ((r0 >> 1) & 7);
+  const __amdgpu_buffer_rsrc_t ra =
+      __builtin_amdgcn_make_buffer_rsrc((void *)g.A, (short)0, (int)((size_t)g.M * g.lda * 2), RSRC_FLAGS);
+  const int wrows = EPI == EPI_SWIGLU ? 2 * g.F : g.N;
+  const __amdgpu_buffer_rsrc_t rw =
+      __builtin_amdgcn_make_buffer_rsrc((void *)g.W, (short)0, (int)((size_t)wrows * g.ldw * 2), RSRC_FLAGS);
+  int voff_a[NCPA];
+#pragma unroll
+  for (int j = 0; j < NCPA; ++j) voff_a[j] = (min(m0 + r0 + RSTEP * j, g.M - 1) * g.lda + cch * 8) * 2;
+  // SwiGLU: the tile's W rows alternate 32-row gate / up slices for the same
+  // 32 outputs: tile row r reads W row tn * BN/2 + (r >> 6) * 32 + (r & 31),
+  // plus F when bit 5 of r is set; for r = r0 + RSTEP j that is a per-lane
+  // part plus a uniform step
+  const int wrow0 = EPI == EPI_SWIGLU ? tn * (BN / 2) + (r0 & 31) + (RSTEP == 64 ? ((r0 >> 5) & 1) * g.F : 0)
+                                      : tn * BN + r0;
+  const int voff_w = (wrow0 * g.ldw + cch * 8) * 2;
+  auto wstep = [&](int j) {  // bytes
+    const int rows = EPI == EPI_SWIGLU ? (RSTEP == 64 ? 32 * j : (j >> 1) * 32 + (j & 1) * g.F) : RSTEP * j;
+    return rows * g.ldw * 2;
+  };
+  const int kbase = kchunk * kc * 2;  // the chunk's first K column, bytes
+  auto lds_ptr = [](u32x4 *p) { return (__attribute__((address_space(3))) void *)p; };
+  auto copy_a1 = [&](int kt, u32x4 *dst, int j) {
+#if __HIP_DEVICE_COMPILE__  // the host pass cannot resolve this builtin in a template
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, lds_ptr(dst + (WAVES * j + wave) * 64), 16, voff_a[j],
+                                             kbase + kt * BK * 2, 0, 0);
+#endif
+  };
+  auto copy_w1 = [&](int kt, u32x4 *dst, int j) {
+#if __HIP_DEVICE_COMPILE__
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, lds_ptr(dst + (WAVES * j + wave) * 64), 16, voff_w,
+                                             wstep(j) + kbase + kt * BK * 2, 0, 0);
+#endif
+  };
+
+  f32x4 acc[NW][NT];
+#pragma unroll
+  for (int a = 0; a < NW; ++a)
+#pragma unroll
+    for (int b = 0; b < NT; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // fragment rows: wave base + 16 i + lane % 16; rows 16 i apart share the
+  // swizzle term, so fragment i of sub-step kk sits at slot off[kk] + 128 i
+  const int fr = lane & 15, kq = lane >> 4, sw = (fr >> 1) & 7;
+  const int rowA = wm * WT + fr, rowW = wn * WF + fr;
+  int offA[2], offW[2];
+#pragma unroll
+  for (int kk = 0; kk < 2; ++kk) {
+    offA[kk] = rowA * 8 + ((4 * kk + kq) ^ sw);
+    offW[kk] = rowW * 8 + ((4 * kk + kq) ^ sw);
+  }
+  u32x4 fa[2][NT], fw[2][NW];
+  auto fload = [&](const u32x4 *sa, const u32x4 *sw_, int kk, int set) {
+#pragma unroll
+    for (int t = 0; t < NT; ++t) fa[set][t] = sa[offA[kk] + 128 * t];
+#pragma unroll
+    for (int f = 0; f < NW; ++f) fw[set][f] = sw_[offW[kk] + 128 * f];
+  };
+  auto mfma_kk = [&](int set) {
+#pragma unroll
+    for (int f = 0; f < NW; ++f)
+#pragma unroll
+      for (int t = 0; t < NT; ++t) acc[f][t] = mfma16x16x32(fw[set][f], fa[set][t], acc[f][t]);
+  };
+  // the sub-step's MFMAs with NR LDS reads and NC copies spread among them
+  auto interleave = [&](auto n_rd, auto n_cp) {
+    constexpr int NM = NW * NT, NR = decltype(n_rd)::value, NC = decltype(n_cp)::value;
+    constexpr int RSP = NR && NM / NR > 0 ? NM / NR : 1, CSP = NC && NM / NC > 0 ? NM / NC : 1;
+#pragma unroll
+    for (int i = 0; i < NM; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                    // one MFMA
+      if (i % RSP == 0 && i / RSP < NR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+      if (i % CSP == CSP / 2 && i / CSP < NC) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // one copy
+    }
+  };
+  using std::integral_constant;
+  auto SA = [&](auto i) -> u32x4 * {
+    if constexpr (decltype(i)::value == 0) return sA0;
+    else return sA1;
+  };
+  auto SW = [&](auto i) -> u32x4 * {
+    if constexpr (decltype(i)::value == 0) return sW0;
+    else if constexpr (decltype(i)::value == 1) return sW1;
+    else return sW2;
+  };
+
+  const int nk = kc / BK;
+  constexpr int CPS = NCPA + NCPW, CPK = (CPS + 1) / 2;  // copies per step and per sub-step
+  // Step kt reads A stage PA = kt % 2 and W stage PW = kt % 3 (sub-step 0's
+  // fragments already in register set 0).  Sub-step 0 copies A slice kt+1
+  // into the other A stage (and, when it has fewer copies than half a step,
+  // the first W copies), sub-step 1 the rest of W slice kt+2 into W stage
+  // (kt+2) % 3 -- stages read by step kt-1 and released by its barrier; past
+  // the last slice the copies repeat slice nk-1 into a stage never read
+  // again.  Sub-step 0 also reads sub-step 1's fragments.  The step ends with
+  // every copy but the NCPW newest (the W slice kt+2) landed -- vector-memory
+  // loads complete in issue order -- and its own LDS reads done, then the
+  // barrier, then the next step's sub-step 0 fragments.
+  auto step = [&](int kt, auto pa, auto pw) {
+    constexpr int PA = decltype(pa)::value, PW = decltype(pw)::value;
+    const u32x4 *a = SA(pa), *w = SW(pw);
+    u32x4 *da = SA(integral_constant<int, PA ^ 1>{});
+    u32x4 *dw = SW(integral_constant<int, (PW + 2) % 3>{});
+    const int ka = min(kt + 1, nk - 1), kw = min(kt + 2, nk - 1);
+    static_for<2>([&](auto kkc) {
+      constexpr int kk = decltype(kkc)::value;
+      constexpr int c0 = kk * CPK, c1 = kk ? CPS : CPK;
+#pragma unroll
+      for (int c = c0; c < c1; ++c) {
+        if (c < NCPA) copy_a1(ka, da, c);
+        else copy_w1(kw, dw, c - NCPA);
+      }
+      if constexpr (kk == 0) fload(a, w, 1, 1);
+      mfma_kk(kk);
+      interleave(integral_constant<int, kk == 0 ? NT + NW : 0>{}, integral_constant<int, c1 - c0>{});
+    });
+    // s_waitcnt vmcnt(NCPW) expcnt(7) lgkmcnt(0), then the barrier
+    __builtin_amdgcn_s_waitcnt((NCPW & 15) | (7 << 4) | ((NCPW >> 4) << 14));
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    fload(SA(integral_constant<int, PA ^ 1>{}), SW(integral_constant<int, (PW + 1) % 3>{}), 0, 0);
+  };
+  using C0 = integral_constant<int, 0>;
+  using C1 = integral_constant<int, 1>;
+  using C2 = integral_constant<int, 2>;
+#pragma unroll
+  for (int j = 0; j < NCPA; ++j) copy_a1(0, sA0, j);
+#pragma unroll
+  for (int j = 0; j < NCPW; ++j) copy_w1(0, sW0, j);
+  __builtin_amdgcn_sched_barrier(0);  // slice 0 is issued before W slice 1
+#pragma unroll
+  for (int j = 0; j < NCPW; ++j) copy_w1(min(1, nk - 1), sW1, j);
+  __builtin_amdgcn_s_waitcnt((NCPW & 15) | (7 << 4) | ((NCPW >> 4) << 14));
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  fload(sA0, sW0, 0, 0);
+  // groups of six steps (the stage pattern's period); the last group skips
+  // the steps past nk whole (copies, MFMAs and barrier), a uniform branch
+  for (int kt = 0; kt < nk; kt += 6) {
+    step(kt, C0{}, C0{});
+    if (kt + 1 < nk) step(kt + 1, C1{}, C1{});
+    if (kt + 2 < nk) step(kt + 2, C0{}, C2{});
+    if (kt + 3 < nk) step(kt + 3, C1{}, C0{});
+    if (kt + 4 < nk) step(kt + 4, C0{}, C1{});
+    if (kt + 5 < nk) step(kt + 5, C1{}, C2{});
+  }
+  // every copy has landed (vmcnt(0) expcnt(7) lgkmcnt(0)) and every fragment
+  // read is done before the epilogue reuses the stages
+  __builtin_amdgcn_s_waitcnt(7 << 4);
+  __syncthreads();
+
+  if constexpr (EPI == EPI_QKV) {
+    qkv_epilogue16<BM, THREADS, NT, NW>(g, m0, tn * BN, wm * WT, tn * BN + wn * WF, acc, tid,
+                                        LdsObjs<4, BM * 8>{sA0, sA1, sW0, sW1});
+    return;
+  }
+  const int h4 = 4 * kq;
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    const int m = m0 + wm * WT + 16 * t + fr;
+    if (m >= g.M) continue;
+    if constexpr (EPI == EPI_SWIGLU) {
+      // fragments 0, 1 hold the gate rows of outputs +0..15, +16..31, and
+      // fragments 2, 3 the up rows of the same outputs
+#pragma unroll
+      for (int f = 0; f < 2; ++f)
+        store4_swiglu(g, m, tn * (BN / 2) + wn * (WF / 2) + 16 * f + h4, acc[f][t], acc[f + 2][t]);
+    } else if (split) {
+      float *prow = g.part + ((size_t)kchunk * g.M + m) * g.N;
+#pragma unroll
+      for (int f = 0; f < NW; ++f) *(f32x4 *)(prow + tn * BN + wn * WF + 16 * f + h4) = acc[f][t];
+    } else {
+#pragma unroll
+      for (int f = 0; f < NW; ++f) store4<EPI>(g, m, tn * BN + wn * WF + 16 * f + h4, acc[f][t]);
     }
   }
 }

@@ -17,13 +17,6 @@
 #include "encoder.hpp"
 #include "gemm.hpp"
 
-#ifndef QI_GEMM_WM
-#define QI_GEMM_WM 2  // waves along tokens in the 256 x 256 GEMM tile
-#endif
-#ifndef QI_GEMM_WN
-#define QI_GEMM_WN 4  // waves along W rows
-#endif
-
 namespace {
 
 constexpr float kRmsEps = 1e-6f;
@@ -217,11 +210,9 @@ GemmShape gemm_shape(const GemmArgs &g, int &grid, int &cost) {
 template <int EPI>
 void launch_gemm_shape(const GemmArgs &g, GemmShape shape, int grid, hipStream_t s) {
   if (shape == SHAPE_256x256)
-    hipLaunchKernelGGL((gemm_bf16_large_kernel<EPI, QI_GEMM_WM, QI_GEMM_WN, 256>), dim3(grid), dim3(gemmL::THREADS),
-                       0, s, g);
+    hipLaunchKernelGGL((gemm_bf16_lds_kernel<EPI, 256, 256, 8>), dim3(grid), dim3(512), 0, s, g);
   else if (shape == SHAPE_128x256)
-    hipLaunchKernelGGL((gemm_bf16_large_kernel<EPI, QI_GEMM_WM, QI_GEMM_WN, 128>), dim3(grid), dim3(gemmL::THREADS),
-                       0, s, g);
+    hipLaunchKernelGGL((gemm_bf16_large_kernel<EPI, 2, 4, 128>), dim3(grid), dim3(gemmL::THREADS), 0, s, g);
   else
     hipLaunchKernelGGL((gemm_bf16_mid_kernel<EPI>), dim3(grid), dim3(gemmM::THREADS), 0, s, g);
 }

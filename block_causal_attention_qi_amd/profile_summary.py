@@ -59,7 +59,7 @@ def _rows(path):
 
 def kind_of(name: str, prev: str | None) -> str:
     import re
-    m = re.search(r"gemm_bf16_(?:large_|mid_)?kernel<(\d)", name)
+    m = re.search(r"gemm_bf16_(?:large_|mid_|lds_)?kernel<(\d)", name)
     if m:
         epi = int(m.group(1))  # the epilogue: 0 fp32 store, 1 residual, 2 SwiGLU, 3 QKV
         if epi == 2:

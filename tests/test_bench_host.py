@@ -38,9 +38,9 @@ def test_committed_counter_summary_names_its_fingerprint_and_kernels():
 
 
 def test_profile_summary_classifies_launches_by_name_and_step():
-    assert kind_of("void gemm_bf16_large_kernel<1, 2, 4, 256>(GemmArgs)", "attention") == "gemm_o"
+    assert kind_of("void gemm_bf16_lds_kernel<1, 256, 256, 8>(GemmArgs)", "attention") == "gemm_o"
     assert kind_of("void gemm_bf16_mid_kernel<1>(GemmArgs)", "gemm_o") == "gemm_o"  # the O-proj's row tail
-    assert kind_of("void gemm_bf16_large_kernel<1, 2, 4, 256>(GemmArgs)", "gemm_gate_up") == "gemm_down"
+    assert kind_of("void gemm_bf16_lds_kernel<1, 256, 256, 8>(GemmArgs)", "gemm_gate_up") == "gemm_down"
     assert kind_of("void gemm_bf16_large_kernel<3, 2, 4, 128>(GemmArgs)", None) == "gemm_qkv"
     assert kind_of("void gemm_bf16_kernel<0, 128, 128>(GemmArgs)", None) == "gemm_txt"
     assert kind_of("void block_causal_attn_kernel<8>(AttnBatch)", None) == "attention"
@@ -48,10 +48,10 @@ def test_profile_summary_classifies_launches_by_name_and_step():
     # a joint step (it runs the text projection; its first norm is the text norm), then an
     # image-only step; the joint pass splits the O-proj into a head and a row tail
     joint = ["mod_gemv_kernel<8>", "rmsnorm_mod_kernel<16>", "gemm_bf16_kernel<0, 128, 128>", "img_embed_kernel<4>",
-             "rmsnorm_mod_kernel<16>", "gemm_bf16_large_kernel<3, 2, 4, 256>", "block_causal_attn_kernel<8>",
-             "gemm_bf16_large_kernel<1, 2, 4, 256>", "gemm_bf16_mid_kernel<1>", "head_kernel<2>", "euler_kernel"]
-    img = ["mod_gemv_kernel<8>", "img_embed_kernel<4>", "rmsnorm_mod_kernel<16>", "gemm_bf16_large_kernel<3, 2, 4, 256>",
-           "block_causal_attn_kernel<8>", "gemm_bf16_large_kernel<1, 2, 4, 256>", "head_kernel<2>", "euler_kernel"]
+             "rmsnorm_mod_kernel<16>", "gemm_bf16_lds_kernel<3, 256, 256, 8>", "block_causal_attn_kernel<8>",
+             "gemm_bf16_lds_kernel<1, 256, 256, 8>", "gemm_bf16_mid_kernel<1>", "head_kernel<2>", "euler_kernel"]
+    img = ["mod_gemv_kernel<8>", "img_embed_kernel<4>", "rmsnorm_mod_kernel<16>", "gemm_bf16_lds_kernel<3, 256, 256, 8>",
+           "block_causal_attn_kernel<8>", "gemm_bf16_lds_kernel<1, 256, 256, 8>", "head_kernel<2>", "euler_kernel"]
     lab = label_launches(joint + img)
     assert lab[1] == ("norm_mod", "joint (text)") and lab[2] == ("gemm_txt", "joint (text)")
     assert lab[4] == ("norm_mod", "joint")
