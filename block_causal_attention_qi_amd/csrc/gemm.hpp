@@ -982,10 +982,9 @@ __global__ __launch_bounds__(gemmM::THREADS, 2) void gemm_bf16_mid_kernel(const 
 // double-buffered and copied one step ahead; the W slices (weights, streamed
 // from HBM) are triple-buffered and copied two steps ahead.  The five stages
 // are separate LDS objects indexed by compile-time constants (the K loop is
-// unrolled by 6), so the compiler's waits for a copy cover the stage it
-// fills, and the barrier that ends a step waits only for the copies the next
-// step reads, leaving the newest W copies in flight.  The A copies are issued
-// among the first sub-step's MFMAs, the W copies among the second's.
+// unrolled by 6).  Each step has one barrier, in its middle, once its stages
+// are read; the freed stages are refilled, and the next step's first
+// fragments read, during the step's second half (see the K loop).
 //
 // LDS layout of a slice: row r (64 bf16 = 8 chunks of 16 bytes), chunk c at
 // slot r * 8 + (c ^ ((r >> 1) & 7)) (see lds_slot).  Copy instruction j of
@@ -1161,18 +1160,24 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 8 ? 1 : 2) void gemm_bf16_lds_
     return rows * g.ldw * 2;
   };
   const int kbase = kchunk * kc * 2;  // the chunk's first K column, bytes
-  auto lds_ptr = [](u32x4 *p) { return (__attribute__((address_space(3))) void *)p; };
-  auto copy_a1 = [&](int kt, u32x4 *dst, int j) {
-#if __HIP_DEVICE_COMPILE__  // the host pass cannot resolve this builtin in a template
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, lds_ptr(dst + (WAVES * j + wave) * 64), 16, voff_a[j],
-                                             kbase + kt * BK * 2, 0, 0);
-#endif
+  // LDS DMA issued through inline asm (M0 = the wave's LDS destination, then
+  // buffer_load_dwordx4 ... lds).  The compiler then does not count these
+  // copies as pending LDS writes: with the builtin it adds waits of its own
+  // before fragment reads of other stages (down to vmcnt(0) where the
+  // six-step groups join), which stall the pipeline.  The order is kept by
+  // the explicit waits and barriers below: every stage is read only after the
+  // wait and barrier that follow its copies, and copied into only after the
+  // barrier that follows its last reads; nothing else in this kernel uses M0.
+  const int wv = __builtin_amdgcn_readfirstlane(wave);
+  auto dma = [&](const __amdgpu_buffer_rsrc_t &rs, u32x4 *dst, int voff, int soff) {
+    const uint32_t lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void *)dst;
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds" ::"s"(lds), "v"(voff), "s"(rs),
+                 "s"(soff)
+                 : "m0");
   };
+  auto copy_a1 = [&](int kt, u32x4 *dst, int j) { dma(ra, dst + (WAVES * j + wv) * 64, voff_a[j], kbase + kt * BK * 2); };
   auto copy_w1 = [&](int kt, u32x4 *dst, int j) {
-#if __HIP_DEVICE_COMPILE__
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, lds_ptr(dst + (WAVES * j + wave) * 64), 16, voff_w,
-                                             wstep(j) + kbase + kt * BK * 2, 0, 0);
-#endif
+    dma(rw, dst + (WAVES * j + wv) * 64, voff_w, wstep(j) + kbase + kt * BK * 2);
   };
 
   f32x4 acc[NW][NT];
@@ -1227,57 +1232,64 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 8 ? 1 : 2) void gemm_bf16_lds_
   };
 
   const int nk = kc / BK;
-  constexpr int CPS = NCPA + NCPW, CPK = (CPS + 1) / 2;  // copies per step and per sub-step
-  // Step kt reads A stage PA = kt % 2 and W stage PW = kt % 3 (sub-step 0's
-  // fragments already in register set 0).  Sub-step 0 copies A slice kt+1
-  // into the other A stage (and, when it has fewer copies than half a step,
-  // the first W copies), sub-step 1 the rest of W slice kt+2 into W stage
-  // (kt+2) % 3 -- stages read by step kt-1 and released by its barrier; past
-  // the last slice the copies repeat slice nk-1 into a stage never read
-  // again.  Sub-step 0 also reads sub-step 1's fragments.  The step ends with
-  // every copy but the NCPW newest (the W slice kt+2) landed -- vector-memory
-  // loads complete in issue order -- and its own LDS reads done, then the
-  // barrier, then the next step's sub-step 0 fragments.
+  constexpr int CPS = NCPA + NCPW;  // copies per step
+  using C0 = integral_constant<int, 0>;
+  using C1 = integral_constant<int, 1>;
+  using C2 = integral_constant<int, 2>;
+  // Step kt reads A stage PA = kt % 2 and W stage PW = kt % 3, its sub-step
+  // 0 fragments already in register set 0, and has one barrier, in the
+  // middle:
+  //   sub-step 0's MFMAs run with sub-step 1's fragment reads among them;
+  //   wait for the copies of A and W slice kt+1 (all copies but the NCPW
+  //   newest, the W slice kt+2 -- vector-memory loads complete in issue
+  //   order) and for this wave's LDS reads, then the barrier: every wave is
+  //   done reading stages PA and PW, and slice kt+1 is in LDS;
+  //   sub-step 1's MFMAs run with, among them, the copies of A slice kt+2
+  //   into stage PA and W slice kt+3 into stage PW, and the reads of step
+  //   kt+1's sub-step 0 fragments.
+  // So a fragment read is always a sub-step ahead of its MFMAs, the barrier
+  // waits on nothing the MFMAs need, and an A copy has one step to land, a W
+  // copy two.  Past the last slice the copies repeat slice nk-1 into stages
+  // never read again.
   auto step = [&](int kt, auto pa, auto pw) {
     constexpr int PA = decltype(pa)::value, PW = decltype(pw)::value;
-    const u32x4 *a = SA(pa), *w = SW(pw);
-    u32x4 *da = SA(integral_constant<int, PA ^ 1>{});
-    u32x4 *dw = SW(integral_constant<int, (PW + 2) % 3>{});
-    const int ka = min(kt + 1, nk - 1), kw = min(kt + 2, nk - 1);
-    static_for<2>([&](auto kkc) {
-      constexpr int kk = decltype(kkc)::value;
-      constexpr int c0 = kk * CPK, c1 = kk ? CPS : CPK;
-#pragma unroll
-      for (int c = c0; c < c1; ++c) {
-        if (c < NCPA) copy_a1(ka, da, c);
-        else copy_w1(kw, dw, c - NCPA);
-      }
-      if constexpr (kk == 0) fload(a, w, 1, 1);
-      mfma_kk(kk);
-      interleave(integral_constant<int, kk == 0 ? NT + NW : 0>{}, integral_constant<int, c1 - c0>{});
-    });
+    u32x4 *a = SA(pa), *w = SW(pw);
+    const int ka = min(kt + 2, nk - 1), kw = min(kt + 3, nk - 1);
+    fload(a, w, 1, 1);
+    mfma_kk(0);
+    interleave(integral_constant<int, NT + NW>{}, integral_constant<int, 0>{});
     // s_waitcnt vmcnt(NCPW) expcnt(7) lgkmcnt(0), then the barrier
     __builtin_amdgcn_s_waitcnt((NCPW & 15) | (7 << 4) | ((NCPW >> 4) << 14));
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
+#pragma unroll
+    for (int j = 0; j < NCPA; ++j) copy_a1(ka, a, j);
+#pragma unroll
+    for (int j = 0; j < NCPW; ++j) copy_w1(kw, w, j);
     fload(SA(integral_constant<int, PA ^ 1>{}), SW(integral_constant<int, (PW + 1) % 3>{}), 0, 0);
+    mfma_kk(1);
+    interleave(integral_constant<int, NT + NW>{}, integral_constant<int, CPS>{});
   };
-  using C0 = integral_constant<int, 0>;
-  using C1 = integral_constant<int, 1>;
-  using C2 = integral_constant<int, 2>;
+  // slices 0 and 1 of both operands and W slice 2, in that order; wait for
+  // slice 0 (all but the 2 NCPW + NCPA newest copies)
 #pragma unroll
   for (int j = 0; j < NCPA; ++j) copy_a1(0, sA0, j);
 #pragma unroll
   for (int j = 0; j < NCPW; ++j) copy_w1(0, sW0, j);
-  __builtin_amdgcn_sched_barrier(0);  // slice 0 is issued before W slice 1
+#pragma unroll
+  for (int j = 0; j < NCPA; ++j) copy_a1(min(1, nk - 1), sA1, j);
 #pragma unroll
   for (int j = 0; j < NCPW; ++j) copy_w1(min(1, nk - 1), sW1, j);
-  __builtin_amdgcn_s_waitcnt((NCPW & 15) | (7 << 4) | ((NCPW >> 4) << 14));
+#pragma unroll
+  for (int j = 0; j < NCPW; ++j) copy_w1(min(2, nk - 1), sW2, j);
+  constexpr int NPRO = NCPA + 2 * NCPW;
+  __builtin_amdgcn_s_waitcnt((NPRO & 15) | (7 << 4) | ((NPRO >> 4) << 14));
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
   fload(sA0, sW0, 0, 0);
   // groups of six steps (the stage pattern's period); the last group skips
-  // the steps past nk whole (copies, MFMAs and barrier), a uniform branch
+  // the steps past nk whole, a uniform branch.  (Six unguarded steps plus a
+  // separate tail of up to five steps make the compiler spill.)
   for (int kt = 0; kt < nk; kt += 6) {
     step(kt, C0{}, C0{});
     if (kt + 1 < nk) step(kt + 1, C1{}, C1{});
