@@ -172,29 +172,53 @@ struct LdsObjs {
 // one half-wave reads at a fixed q hit 32 distinct bank pairs.  A 16-byte
 // chunk k (q = 2k, 2k + 1) of the table row lands at the even slot
 // (2k) ^ (r & 30), its halves swapped when r is odd.
+// The RoPE rows of a tile's BM tokens, loaded from global memory into
+// registers (load) and then written to LDS (store), so that a kernel can
+// issue the loads before the barrier that frees the LDS.
+template <int BM, int THREADS>
+struct RopeRows {
+  static_assert((BM * 16) % THREADS == 0, "whole passes over the tile's rows");
+  static constexpr int IT = BM * 16 / THREADS;  // 16-byte chunks per thread and table
+  u32x4 c[IT], s[IT];
+  QI_DEV void load(const GemmArgs &g, int m0, int tid) {
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {
+      const int i = tid + THREADS * it;
+      const int r = i >> 4, k = i & 15;
+      const int m = m0 + r;
+      if (m >= g.M) continue;
+      const bool txt = m < g.L_rows;
+      const size_t off = (size_t)(txt ? m : m - g.L_rows) * 64 + 4 * k;
+      c[it] = *(const u32x4 *)((txt ? g.cos_t : g.cos_i) + off);
+      s[it] = *(const u32x4 *)((txt ? g.sin_t : g.sin_i) + off);
+    }
+  }
+  template <int NOBJ, int SLOTS>
+  QI_DEV void store(const GemmArgs &g, int m0, const LdsObjs<NOBJ, SLOTS> lo, int tid) const {
+    constexpr int R = LdsObjs<NOBJ, SLOTS>::kRows;
+    static_assert(NOBJ >= 2 * (BM / R) && BM % R == 0, "a cos and a sin object per R rows");
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {
+      const int i = tid + THREADS * it;
+      const int r = i >> 4, k = i & 15;
+      if (m0 + r >= g.M) continue;
+      u32x4 cv = c[it], sv = s[it];
+      if (r & 1) {
+        cv = u32x4{cv[2], cv[3], cv[0], cv[1]};
+        sv = u32x4{sv[2], sv[3], sv[0], sv[1]};
+      }
+      const int chunk = (r % R) * 16 + (k ^ ((r & 30) >> 1));
+      lo.o(r / R)[chunk] = cv;
+      lo.o(BM / R + r / R)[chunk] = sv;
+    }
+  }
+};
+
 template <int BM, int THREADS, int NOBJ, int SLOTS>
 QI_DEV void stage_rope_rows(const GemmArgs &g, int m0, const LdsObjs<NOBJ, SLOTS> lo, int tid) {
-  constexpr int R = LdsObjs<NOBJ, SLOTS>::kRows;
-  static_assert((BM * 16) % THREADS == 0, "whole passes over the tile's rows");
-  static_assert(NOBJ >= 2 * (BM / R) && BM % R == 0, "a cos and a sin object per R rows");
-#pragma unroll
-  for (int it = 0; it < BM * 16 / THREADS; ++it) {
-    const int i = tid + THREADS * it;
-    const int r = i >> 4, k = i & 15;
-    const int m = m0 + r;
-    if (m >= g.M) continue;
-    const bool txt = m < g.L_rows;
-    const size_t off = (size_t)(txt ? m : m - g.L_rows) * 64 + 4 * k;
-    u32x4 c = *(const u32x4 *)((txt ? g.cos_t : g.cos_i) + off);
-    u32x4 sn = *(const u32x4 *)((txt ? g.sin_t : g.sin_i) + off);
-    if (r & 1) {
-      c = u32x4{c[2], c[3], c[0], c[1]};
-      sn = u32x4{sn[2], sn[3], sn[0], sn[1]};
-    }
-    const int chunk = (r % R) * 16 + (k ^ ((r & 30) >> 1));
-    lo.o(r / R)[chunk] = c;
-    lo.o(BM / R + r / R)[chunk] = sn;
-  }
+  RopeRows<BM, THREADS> rows;
+  rows.load(g, m0, tid);
+  rows.store(g, m0, lo, tid);
 }
 
 // The V section of a QKV wave tile: FS blocks of 32 W rows starting at n0
@@ -1039,13 +1063,15 @@ QI_DEV void store_v_wave16(const GemmArgs &g, int mbase, int n0, const f32x4 (&a
   }
 }
 
-// The QKV epilogue of a BM-token workgroup tile of the LDS-copy kernel (the
+// The QKV epilogue of a BM-token workgroup tile of the 256 x 256 kernel (the
 // qkv_epilogue steps with the 16x16 accumulator layout): wave (wrow / WT,
 // n0) holds WT = 16 NT tokens x 64 W rows, half of one q or k head, as 4
-// consecutive features of one token per lane and accumulator.
+// consecutive features of one token per lane and accumulator.  The caller
+// has loaded the tile's RoPE rows (q / k tiles) and passed a barrier after
+// which the LDS is free.
 template <int BM, int THREADS, int NT, int NW, int NOBJ, int SLOTS>
 QI_DEV void qkv_epilogue16(const GemmArgs &g, int m0, int n_tile, int wrow, int n0, const f32x4 (&acc)[NW][NT],
-                           int tid, const LdsObjs<NOBJ, SLOTS> lo) {
+                           int tid, const LdsObjs<NOBJ, SLOTS> lo, const RopeRows<BM, THREADS> &rope) {
   static_assert(NW == 4, "a wave tile is half a head: 64 W rows");
   constexpr int R = LdsObjs<NOBJ, SLOTS>::kRows;
   constexpr int WT = 16 * NT;
@@ -1061,8 +1087,7 @@ QI_DEV void qkv_epilogue16(const GemmArgs &g, int m0, int n_tile, int wrow, int 
   const int sec = n0 / g.H;
   const int w0 = n0 - sec * g.H;
   const int head = w0 >> 7, dh0 = w0 & 127;
-  __syncthreads();
-  stage_rope_rows<BM, THREADS>(g, m0, lo, tid);
+  rope.store(g, m0, lo, tid);  // the caller's barrier freed the LDS
   __syncthreads();
   // outputs dh0 + 16 f + 4 kq + 0..3 are RoPE pairs 2q, 2q + 1 with
   // q = dh0 / 4 + 4 f + kq
@@ -1249,23 +1274,28 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 8 ? 1 : 2) void gemm_bf16_lds_
   //   kt+1's sub-step 0 fragments.
   // So a fragment read is always a sub-step ahead of its MFMAs, the barrier
   // waits on nothing the MFMAs need, and an A copy has one step to land, a W
-  // copy two.  Past the last slice the copies repeat slice nk-1 into stages
-  // never read again.
+  // copy two.  Slices past the last are not copied (uniform branches), so no
+  // copy is left to wait for when the K loop ends; where W slice kt+2 was not
+  // copied, the wait is for every copy.
   auto step = [&](int kt, auto pa, auto pw) {
     constexpr int PA = decltype(pa)::value, PW = decltype(pw)::value;
     u32x4 *a = SA(pa), *w = SW(pw);
-    const int ka = min(kt + 2, nk - 1), kw = min(kt + 3, nk - 1);
     fload(a, w, 1, 1);
     mfma_kk(0);
     interleave(integral_constant<int, NT + NW>{}, integral_constant<int, 0>{});
-    // s_waitcnt vmcnt(NCPW) expcnt(7) lgkmcnt(0), then the barrier
-    __builtin_amdgcn_s_waitcnt((NCPW & 15) | (7 << 4) | ((NCPW >> 4) << 14));
+    // s_waitcnt vmcnt(NCPW or 0) expcnt(7) lgkmcnt(0), then the barrier
+    if (kt == 0 || kt + 2 < nk) __builtin_amdgcn_s_waitcnt((NCPW & 15) | (7 << 4) | ((NCPW >> 4) << 14));
+    else __builtin_amdgcn_s_waitcnt(7 << 4);
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
+    if (kt + 2 < nk) {
 #pragma unroll
-    for (int j = 0; j < NCPA; ++j) copy_a1(ka, a, j);
+      for (int j = 0; j < NCPA; ++j) copy_a1(kt + 2, a, j);
+    }
+    if (kt + 3 < nk) {
 #pragma unroll
-    for (int j = 0; j < NCPW; ++j) copy_w1(kw, w, j);
+      for (int j = 0; j < NCPW; ++j) copy_w1(kt + 3, w, j);
+    }
     fload(SA(integral_constant<int, PA ^ 1>{}), SW(integral_constant<int, (PW + 1) % 3>{}), 0, 0);
     mfma_kk(1);
     interleave(integral_constant<int, NT + NW>{}, integral_constant<int, CPS>{});
@@ -1298,16 +1328,20 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 8 ? 1 : 2) void gemm_bf16_lds_
     if (kt + 4 < nk) step(kt + 4, C0{}, C1{});
     if (kt + 5 < nk) step(kt + 5, C1{}, C2{});
   }
-  // every copy has landed (vmcnt(0) expcnt(7) lgkmcnt(0)) and every fragment
-  // read is done before the epilogue reuses the stages
-  __builtin_amdgcn_s_waitcnt(7 << 4);
-  __syncthreads();
-
   if constexpr (EPI == EPI_QKV) {
+    // the q / k tiles' RoPE rows are loaded while the last copies land; every
+    // copy has landed (vmcnt(0) expcnt(7) lgkmcnt(0)) and every fragment read
+    // is done before the epilogue reuses the stages
+    RopeRows<BM, THREADS> rope;
+    if ((tn * BN) / g.H < 2) rope.load(g, m0, tid);
+    __builtin_amdgcn_s_waitcnt(7 << 4);
+    __syncthreads();
     qkv_epilogue16<BM, THREADS, NT, NW>(g, m0, tn * BN, wm * WT, tn * BN + wn * WF, acc, tid,
-                                        LdsObjs<4, BM * 8>{sA0, sA1, sW0, sW1});
+                                        LdsObjs<4, BM * 8>{sA0, sA1, sW0, sW1}, rope);
     return;
   }
+  // no copy is left in flight (the other epilogues do not use the LDS)
+  __builtin_amdgcn_s_waitcnt(7 << 4);
   const int h4 = 4 * kq;
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
