@@ -13,13 +13,12 @@
 //
 // Per workgroup: 32 queries per wave, 8 waves (two per SIMD) or, for small
 // images, 4 (one per SIMD); key tiles of 64 copied global -> LDS directly and
-// double buffered.  A single wave issues
-// VALU work at about half rate and hides only a few VALU instructions behind
-// each of its own MFMAs (measured on MI355X), so each wave is software
-// pipelined over three tiles (the softmax of tile t runs between the score
-// MFMAs of tile t+1 and the PV MFMAs of tile t-1, a few VALU instructions per
-// MFMA) and the second wave on each SIMD fills the rest.  MFMA 32x32x16 bf16
-// (the full-rate shape on gfx950).
+// double buffered.  VALU work interleaved among a wave's own MFMAs hides about
+// two thirds of its issue time behind them (measured on MI355X; an
+// exponential leaves about 1.1 ns exposed), so each wave is software pipelined
+// over three tiles: the softmax of tile t runs between the score MFMAs of
+// tile t+1 and the PV MFMAs of tile t-1, a few VALU instructions per MFMA.
+// MFMA 32x32x16 bf16.
 // S^T = K Q^T: the A operand takes the tile's K rows in the order
 // kappa(i) = 16*(i/16) + 8*((i/4)&1) + 4*((i/8)&1) + (i&3), which leaves each
 // lane holding 8 CONSECUTIVE keys of one query per 16-key step.  Those
