@@ -116,21 +116,26 @@ QI_DEV void tile_of(int bid, int nTM, int nTN, int &tm, int &tn) {
 }
 
 // ---------------------------------------------------------------- epilogue
-// Epilogue arithmetic with every product rounded on its own (no fused
-// multiply-add), written out so that the compiler cannot contract it one way
-// in one kernel instance and another way in the next: every tile shape, and
-// the joint and image-only passes, then round a row's outputs identically.
+// Epilogue arithmetic with every product rounded on its own: contraction into
+// fused multiply-adds is switched off for the operators written in these
+// bodies, so the compiler cannot fuse them one way in one kernel instance and
+// another way in the next (it did: two instances of the same RoPE expression
+// differed in one rounding).  Every tile shape, and the joint and image-only
+// passes, then round a row's outputs identically.  (HIP's *_rn helpers do not
+// give this: once inlined they are contractible.)
 // x + gate * v, per component
 QI_DEV f32x4 gated_add(f32x4 x, f32x4 gate, f32x4 v) {
+#pragma clang fp contract(off)
   f32x4 r;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) r[i] = __fadd_rn(x[i], __fmul_rn(gate[i], v[i]));
+  for (int i = 0; i < 4; ++i) r[i] = x[i] + gate[i] * v[i];
   return r;
 }
 // The RoPE rotation of the pair (a, b) by the angle with cosine c and sine s:
 // (a c - b s, a s + b c).
 QI_DEV float2 rope_pair(float a, float b, float c, float s) {
-  return float2{__fsub_rn(__fmul_rn(a, c), __fmul_rn(b, s)), __fadd_rn(__fmul_rn(a, s), __fmul_rn(b, c))};
+#pragma clang fp contract(off)
+  return float2{a * c - b * s, a * s + b * c};
 }
 
 // The 4 consecutive outputs n..n+3 of token m (accumulators v).
