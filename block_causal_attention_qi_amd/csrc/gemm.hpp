@@ -521,10 +521,9 @@ __global__ __launch_bounds__(256) void resid_reduce_kernel(const GemmArgs g) {
 // A few hundred token rows: one 128 x 256 tile per workgroup of 8 waves (2
 // along tokens x 4 along W rows; wave tile 64 tokens x 64 W rows, MFMA
 // 32x32x16), one workgroup per CU -- 3/4 of the copied bytes per FLOP of two
-// 128 x 128 workgroups.  (The template also has a 256-row form; the 256 x 256
-// shape runs on gemm_bf16_lds_kernel below.)  On this shape the 32x32x16
-// MFMA runs faster than the 16x16x32 one of the 256 x 256 kernel, and both
-// give the same fp32 results bit for bit.
+// 128 x 128 workgroups.  (The 256 x 256 shape runs on gemm_bf16_lds_kernel
+// below.)  On this shape the 32x32x16 MFMA runs faster than the 16x16x32 one
+// of the 256 x 256 kernel, and both give the same fp32 results bit for bit.
 //
 // Operands go from global memory straight into LDS (buffer loads with the LDS
 // flag: lane l of a copy instruction lands 16 bytes at slot base + l), so no
@@ -558,11 +557,11 @@ constexpr int NCP = BN * 8 / THREADS;   // W copy instructions per slice per thr
 constexpr int RSRC_FLAGS = 0x00020000;  // raw buffer, 32-bit dwords
 }  // namespace gemmL
 
-template <int EPI, int WMN, int WNN, int BMT = 256>
+template <int EPI, int WMN, int WNN, int BMT = 128>
 __global__ __launch_bounds__(gemmL::THREADS, 1) void gemm_bf16_large_kernel(const GemmArgs g) {
   using namespace gemmL;
   static_assert(WMN == 2 && WNN == 4, "8 waves as 2 x 4");
-  static_assert(BMT == 256 || BMT == 128, "256 or 128 token rows");
+  static_assert(BMT == 128, "128 token rows (256-row tiles run on gemm_bf16_lds_kernel)");
   if (g.skip && *g.skip) return;
   constexpr int BM = BMT, TS = BM / (WMN * 32);
   constexpr int NCPA = BM * 8 / THREADS;  // A copy instructions per slice per thread (4 or 2)
@@ -735,12 +734,8 @@ __global__ __launch_bounds__(gemmL::THREADS, 1) void gemm_bf16_large_kernel(cons
 
   const int h4 = 4 * half;
   if constexpr (EPI == EPI_QKV) {
-    if constexpr (BM == 256)
-      qkv_epilogue<BM, THREADS, TS, FS>(g, m0, tn * BN, wm * WT, tn * BN + wn * WF, acc, tid,
-                                        LdsObjs<4>{sA0, sA1, sW0, sW1});
-    else
-      qkv_epilogue<BM, THREADS, TS, FS>(g, m0, tn * BN, wm * WT, tn * BN + wn * WF, acc, tid,
-                                        LdsObjs<4, BM * 8>{sA0, sA1, sW0, sW1});
+    qkv_epilogue<BM, THREADS, TS, FS>(g, m0, tn * BN, wm * WT, tn * BN + wn * WF, acc, tid,
+                                      LdsObjs<4, BM * 8>{sA0, sA1, sW0, sW1});
     return;
   }
 #pragma unroll
