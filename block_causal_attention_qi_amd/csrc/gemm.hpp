@@ -1028,6 +1028,9 @@ constexpr int BK = 64;
 constexpr int RSRC_FLAGS = 0x00020000;  // raw buffer, 32-bit dwords
 }  // namespace gemmT
 
+// MFMAs per interleaved instruction when n of them go among nm MFMAs
+constexpr int spacing(int nm, int n) { return n > 0 && nm / n > 0 ? nm / n : 1; }
+
 template <int N, int I = 0, class F>
 QI_DEV void static_for(F &&f) {
   if constexpr (I < N) {
@@ -1196,9 +1199,14 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 8 ? 1 : 2) void gemm_bf16_lds_
   const int wv = __builtin_amdgcn_readfirstlane(wave);
   auto dma = [&](const __amdgpu_buffer_rsrc_t &rs, u32x4 *dst, int voff, int soff) {
     const uint32_t lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void *)dst;
+// clang warns that M0 is a reserved register; declaring it clobbered is what
+// keeps the compiler from assuming its value across the statement
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
     asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds" ::"s"(lds), "v"(voff), "s"(rs),
                  "s"(soff)
                  : "m0");
+#pragma clang diagnostic pop
   };
   auto copy_a1 = [&](int kt, u32x4 *dst, int j) { dma(ra, dst + (WAVES * j + wv) * 64, voff_a[j], kbase + kt * BK * 2); };
   auto copy_w1 = [&](int kt, u32x4 *dst, int j) {
@@ -1237,7 +1245,7 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 8 ? 1 : 2) void gemm_bf16_lds_
   // the sub-step's MFMAs with NR LDS reads and NC copies spread among them
   auto interleave = [&](auto n_rd, auto n_cp) {
     constexpr int NM = NW * NT, NR = decltype(n_rd)::value, NC = decltype(n_cp)::value;
-    constexpr int RSP = NR && NM / NR > 0 ? NM / NR : 1, CSP = NC && NM / NC > 0 ? NM / NC : 1;
+    constexpr int RSP = spacing(NM, NR), CSP = spacing(NM, NC);
 #pragma unroll
     for (int i = 0; i < NM; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                    // one MFMA
