@@ -60,6 +60,35 @@ def test_linear_bf16_rows_do_not_depend_on_the_launch_split():
     assert_bits_equal(host(C1), host(C2)[:M], "4100 rows (head + tail launches) vs inside 8192 rows")
 
 
+def test_linear_bf16_past_32_bit_offsets_matches_the_lds_kernels():
+    """An A operand of more than 2 GiB (65544 rows x 16384) cannot be addressed
+    with the LDS-copy kernels' 32-bit buffer offsets and runs on the
+    register-staged 32x32x16 kernel; its rows must equal, bit for bit, the
+    same rows computed by the LDS-copy kernels from a smaller A (the first 4096
+    rows on 256 x 256 tiles with the 16x16x32 MFMA, the last 300 on 128 x 128
+    tiles with 32x32x16), and match an fp64 product of the bf16 operands."""
+    import torch
+    M, N, K = 65544, 4096, 16384
+    assert M * K * 2 > 2**31
+    g = torch.Generator(device="cuda").manual_seed(21)
+    a = torch.randn((M, K), generator=g, device="cuda").to(torch.bfloat16)
+    w = (torch.randn((N, K), generator=g, device="cuda") * 0.02).to(torch.bfloat16)
+    big = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    qi.linear_bf16(a.view(torch.int16), w.view(torch.int16), None, big)
+    rows = {"first 4096": slice(0, 4096), "last 300": slice(M - 300, M)}
+    for what, sl in rows.items():
+        sub = a[sl].contiguous()
+        small = torch.empty((sub.shape[0], N), dtype=torch.float32, device="cuda")
+        qi.linear_bf16(sub.view(torch.int16), w.view(torch.int16), None, small)
+        assert_bits_equal(host(big[sl]), host(small), f"{what} rows: register-staged vs LDS-copy kernels")
+    torch.cuda.synchronize()
+    pick = torch.tensor([0, 1, 4095, 33000, M - 1], device="cuda")
+    ref = a[pick].double().cpu() @ w.double().cpu().t()
+    got = big[pick].double().cpu()
+    assert float((got - ref).abs().max() / ref.abs().max()) < 2e-5
+    del a, big
+
+
 def _attn_inputs(heads, L, N, seed):
     q = bf16_bits(qs.normal_array((heads, L + N, 128), seed=seed))
     k = bf16_bits(qs.normal_array((heads, L + N, 128), seed=seed + 1))
