@@ -1003,12 +1003,12 @@ __global__ __launch_bounds__(gemmM::THREADS, 2) void gemm_bf16_mid_kernel(const 
 // ds_write_b128 costs the LDS about 2.5x a ds_read_b128 per byte.  Each K step
 // of 64 moves a 256-row A slice and a 256-row W slice.  The A slices
 // (activations, just written by the previous kernel, mostly cache hits) are
-// double-buffered and copied one step ahead; the W slices (weights, streamed
-// from HBM) are triple-buffered and copied two steps ahead.  The five stages
-// are separate LDS objects indexed by compile-time constants (the K loop is
-// unrolled by 6).  Each step has one barrier, in its middle, once its stages
-// are read; the freed stages are refilled, and the next step's first
-// fragments read, during the step's second half (see the K loop).
+// double-buffered, the W slices (weights, streamed from HBM) triple-buffered;
+// step k copies W slice k+2 during its first half and A slice k+2 during its
+// second, one copy instruction per few MFMAs.  The five stages are separate
+// LDS objects indexed by compile-time constants (the K loop is unrolled by
+// 6).  Each step has one barrier, in its middle, once its stages are read
+// (see the K loop).
 //
 // LDS layout of a slice: row r (64 bf16 = 8 chunks of 16 bytes), chunk c at
 // slot r * 8 + (c ^ ((r >> 1) & 7)) (see lds_slot).  Copy instruction j of
@@ -1236,23 +1236,6 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 8 ? 1 : 2) void gemm_bf16_lds_
 #pragma unroll
     for (int f = 0; f < NW; ++f) fw[set][f] = sw_[offW[kk] + 128 * f];
   };
-  auto mfma_kk = [&](int set) {
-#pragma unroll
-    for (int f = 0; f < NW; ++f)
-#pragma unroll
-      for (int t = 0; t < NT; ++t) acc[f][t] = mfma16x16x32(fw[set][f], fa[set][t], acc[f][t]);
-  };
-  // the sub-step's MFMAs with NR LDS reads and NC copies spread among them
-  auto interleave = [&](auto n_rd, auto n_cp) {
-    constexpr int NM = NW * NT, NR = decltype(n_rd)::value, NC = decltype(n_cp)::value;
-    constexpr int RSP = spacing(NM, NR), CSP = spacing(NM, NC);
-#pragma unroll
-    for (int i = 0; i < NM; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                    // one MFMA
-      if (i % RSP == 0 && i / RSP < NR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
-      if (i % CSP == CSP / 2 && i / CSP < NC) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // one copy
-    }
-  };
   using std::integral_constant;
   auto SA = [&](auto i) -> u32x4 * {
     if constexpr (decltype(i)::value == 0) return sA0;
@@ -1263,53 +1246,76 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 8 ? 1 : 2) void gemm_bf16_lds_
     else if constexpr (decltype(i)::value == 1) return sW1;
     else return sW2;
   };
+  // One sub-step's MFMAs (register set SET) in NC chunks: chunk c issues
+  // copy instruction c, then runs its share of the MFMAs with its share of
+  // the other sub-step's fragment reads (sub-step kk of stages ra_, rw_, into
+  // the other register set) among them.  The scheduling barriers around each
+  // chunk keep the copies one per NM / NC MFMAs: issued in a burst, the
+  // copies held each wave's next MFMAs back behind them.
+  auto phase = [&](auto set_c, const u32x4 *ra_, const u32x4 *rw_, int kk, auto nc, auto &&copy) {
+    constexpr int SET = decltype(set_c)::value, NC = decltype(nc)::value;
+    constexpr int NM = NW * NT, NR = NT + NW;
+    static_for<NC>([&](auto cc) {
+      constexpr int c = decltype(cc)::value;
+      constexpr int m0 = c * NM / NC, m1 = (c + 1) * NM / NC, r0 = c * NR / NC, r1 = (c + 1) * NR / NC;
+      copy(c);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int r = r0; r < r1; ++r) {
+        if (r < NT) fa[1 - SET][r] = ra_[offA[kk] + 128 * r];
+        else fw[1 - SET][r - NT] = rw_[offW[kk] + 128 * (r - NT)];
+      }
+#pragma unroll
+      for (int m = m0; m < m1; ++m)
+        acc[m / NT][m % NT] = mfma16x16x32(fw[SET][m / NT], fa[SET][m % NT], acc[m / NT][m % NT]);
+      constexpr int CM = m1 - m0, CR = r1 - r0, RSP = spacing(CM, CR);
+#pragma unroll
+      for (int i = 0; i < CM; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                    // one MFMA
+        if (i % RSP == 0 && i / RSP < CR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    });
+  };
 
   const int nk = kc / BK;
-  constexpr int CPS = NCPA + NCPW;  // copies per step
   using C0 = integral_constant<int, 0>;
   using C1 = integral_constant<int, 1>;
   using C2 = integral_constant<int, 2>;
   // Step kt reads A stage PA = kt % 2 and W stage PW = kt % 3, its sub-step
   // 0 fragments already in register set 0, and has one barrier, in the
   // middle:
-  //   sub-step 0's MFMAs run with sub-step 1's fragment reads among them;
+  //   sub-step 0's MFMAs run with sub-step 1's fragment reads and the copies
+  //   of W slice kt+2 into stage (kt+2) % 3 among them (that stage's slice,
+  //   kt-1, was last read before step kt-1's barrier);
   //   wait for the copies of A and W slice kt+1 (all copies but the NCPW
-  //   newest, the W slice kt+2 -- vector-memory loads complete in issue
-  //   order) and for this wave's LDS reads, then the barrier: every wave is
-  //   done reading stages PA and PW, and slice kt+1 is in LDS;
-  //   sub-step 1's MFMAs run with, among them, the copies of A slice kt+2
-  //   into stage PA and W slice kt+3 into stage PW, and the reads of step
-  //   kt+1's sub-step 0 fragments.
+  //   newest, W slice kt+2 -- vector-memory loads complete in issue order)
+  //   and for this wave's LDS reads, then the barrier: every wave is done
+  //   reading stage PA, and slice kt+1 is in LDS;
+  //   sub-step 1's MFMAs run with the copies of A slice kt+2 into stage PA
+  //   and the reads of step kt+1's sub-step 0 fragments among them.
   // So a fragment read is always a sub-step ahead of its MFMAs, the barrier
-  // waits on nothing the MFMAs need, and an A copy has one step to land, a W
-  // copy two.  Slices past the last are not copied (uniform branches), so no
-  // copy is left to wait for when the K loop ends; where W slice kt+2 was not
-  // copied, the wait is for every copy.
+  // waits on nothing the MFMAs need, and an A copy has about a step to land,
+  // a W copy a step and a half.
+  // The W and A copies go into different halves of the step, spread over
+  // each.  Past the last slice the copies repeat slice nk - 1 into a stage
+  // nobody reads again, so every step issues the same copies and waits the
+  // same count; the wait before the epilogue covers the last of them.
   auto step = [&](int kt, auto pa, auto pw) {
     constexpr int PA = decltype(pa)::value, PW = decltype(pw)::value;
     u32x4 *a = SA(pa), *w = SW(pw);
-    fload(a, w, 1, 1);
-    mfma_kk(0);
-    interleave(integral_constant<int, NT + NW>{}, integral_constant<int, 0>{});
-    // s_waitcnt vmcnt(NCPW or 0) expcnt(7) lgkmcnt(0), then the barrier
-    if (kt == 0 || kt + 2 < nk) __builtin_amdgcn_s_waitcnt((NCPW & 15) | (7 << 4) | ((NCPW >> 4) << 14));
-    else __builtin_amdgcn_s_waitcnt(7 << 4);
+    const int k2 = min(kt + 2, nk - 1);
+    u32x4 *wn = SW(integral_constant<int, (PW + 2) % 3>{});
+    phase(C0{}, a, w, 1, integral_constant<int, NCPW>{}, [&](int j) { copy_w1(k2, wn, j); });
+    // s_waitcnt vmcnt(NCPW) expcnt(7) lgkmcnt(0), then the barrier
+    __builtin_amdgcn_s_waitcnt((NCPW & 15) | (7 << 4) | ((NCPW >> 4) << 14));
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
-    if (kt + 2 < nk) {
-#pragma unroll
-      for (int j = 0; j < NCPA; ++j) copy_a1(kt + 2, a, j);
-    }
-    if (kt + 3 < nk) {
-#pragma unroll
-      for (int j = 0; j < NCPW; ++j) copy_w1(kt + 3, w, j);
-    }
-    fload(SA(integral_constant<int, PA ^ 1>{}), SW(integral_constant<int, (PW + 1) % 3>{}), 0, 0);
-    mfma_kk(1);
-    interleave(integral_constant<int, NT + NW>{}, integral_constant<int, CPS>{});
+    phase(C1{}, SA(integral_constant<int, PA ^ 1>{}), SW(integral_constant<int, (PW + 1) % 3>{}), 0,
+          integral_constant<int, NCPA>{}, [&](int j) { copy_a1(k2, a, j); });
   };
-  // slices 0 and 1 of both operands and W slice 2, in that order; wait for
-  // slice 0 (all but the 2 NCPW + NCPA newest copies)
+  // slices 0 and 1 of both operands, in that order; wait for slice 0 (all
+  // but the NCPA + NCPW newest copies)
 #pragma unroll
   for (int j = 0; j < NCPA; ++j) copy_a1(0, sA0, j);
 #pragma unroll
@@ -1318,9 +1324,7 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 8 ? 1 : 2) void gemm_bf16_lds_
   for (int j = 0; j < NCPA; ++j) copy_a1(min(1, nk - 1), sA1, j);
 #pragma unroll
   for (int j = 0; j < NCPW; ++j) copy_w1(min(1, nk - 1), sW1, j);
-#pragma unroll
-  for (int j = 0; j < NCPW; ++j) copy_w1(min(2, nk - 1), sW2, j);
-  constexpr int NPRO = NCPA + 2 * NCPW;
+  constexpr int NPRO = NCPA + NCPW;
   __builtin_amdgcn_s_waitcnt((NPRO & 15) | (7 << 4) | ((NPRO >> 4) << 14));
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
@@ -1348,7 +1352,8 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 8 ? 1 : 2) void gemm_bf16_lds_
                                         LdsObjs<4, BM * 8>{sA0, sA1, sW0, sW1}, rope);
     return;
   }
-  // no copy is left in flight (the other epilogues do not use the LDS)
+  // the other epilogues do not use the LDS, but the last steps' repeated
+  // copies land before the workgroup gives its LDS up
   __builtin_amdgcn_s_waitcnt(7 << 4);
   const int h4 = 4 * kq;
 #pragma unroll
