@@ -157,27 +157,32 @@ __global__ __launch_bounds__(attn::Shape<WAVES>::THREADS, 1) void block_causal_a
     voff_i[j] = (vr * a.ldv_i + vc * 8) * 2;
   }
   auto lds_ptr = [](u32x4 *p) { return (__attribute__((address_space(3))) void *)p; };
-  auto copy_k = [&](int t, auto B) {
+  // copy instruction j of K / V^T tile t into buffer B
+  auto copy_k1 = [&](int t, auto B, int j) {
     u32x4 *sk = B.value ? sK1 : sK0;
     const bool tx = t < nt_t;
     const int key0 = (tx ? t : t - nt_t) * BKV;
 #if __HIP_DEVICE_COMPILE__  // the host pass cannot resolve this builtin in a template
-#pragma unroll
-    for (int j = 0; j < NLD; ++j)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(tx ? rk_t : rk_i, lds_ptr(sk + (j * WAVES + wave) * 64), 16,
-                                               koff[j] + key0 * 256, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(tx ? rk_t : rk_i, lds_ptr(sk + (j * WAVES + wave) * 64), 16,
+                                             koff[j] + key0 * 256, 0, 0, 0);
 #endif
   };
-  auto copy_v = [&](int t, auto B) {
+  auto copy_v1 = [&](int t, auto B, int j) {  // in bounds: ldv >= key0 + 64
     u32x4 *sv = B.value ? sV1 : sV0;
     const bool tx = t < nt_t;
     const int key0 = (tx ? t : t - nt_t) * BKV;
 #if __HIP_DEVICE_COMPILE__
-#pragma unroll
-    for (int j = 0; j < NLD; ++j)  // in bounds: ldv >= key0 + 64
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(tx ? rv_t : rv_i, lds_ptr(sv + (j * WAVES + wave) * 64), 16,
-                                               tx ? voff_t[j] : voff_i[j], key0 * 2, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(tx ? rv_t : rv_i, lds_ptr(sv + (j * WAVES + wave) * 64), 16,
+                                             tx ? voff_t[j] : voff_i[j], key0 * 2, 0, 0);
 #endif
+  };
+  auto copy_k = [&](int t, auto B) {
+#pragma unroll
+    for (int j = 0; j < NLD; ++j) copy_k1(t, B, j);
+  };
+  auto copy_v = [&](int t, auto B) {
+#pragma unroll
+    for (int j = 0; j < NLD; ++j) copy_v1(t, B, j);
   };
   // V^T columns past the segment's end (padding, any bit pattern) become exact
   // zeros, so that their zero probabilities contribute exact zeros.  Only the
@@ -235,7 +240,12 @@ __global__ __launch_bounds__(attn::Shape<WAVES>::THREADS, 1) void block_causal_a
   // iteration.  K runs two tiles ahead in LDS: iteration t copies K(t+2) into
   // sK[t&1], whose K(t) was consumed in iteration t-1.  V(t) is copied in
   // iteration t into sV[t&1] (its V(t-2) was consumed in iteration t-1) and
-  // consumed in iteration t+1.  The accumulators take tile t-1's PV product
+  // consumed in iteration t+1.  Their copy instructions, V first, go among
+  // the first 16 MFMA slots (issued together at the iteration's start, they
+  // held the wave's first MFMAs back: 2% more attention time); past the last
+  // tile the K copy repeats that tile into the buffer nobody reads again.
+  // The compiler waits for the copies before the barrier that ends the
+  // iteration.  The accumulators take tile t-1's PV product
   // in tile t-1's base and are rescaled to tile t's base after it, so the
   // arithmetic is the same sequence as rescale-then-accumulate per tile.
   constexpr std::integral_constant<int, 0> B0{};
@@ -273,8 +283,7 @@ __global__ __launch_bounds__(attn::Shape<WAVES>::THREADS, 1) void block_causal_a
     f32x16(&s_next)[2] = B.value ? sA : sB;
     u32x4(&pb)[4] = B.value ? pB : pA;
     const u32x4(&pb_prev)[4] = B.value ? pA : pB;
-    if (t + 2 < ntiles) copy_k(t + 2, B);
-    copy_v(t, B);
+    const int tk = min(t + 2, ntiles - 1);  // past the end: a copy nobody reads
 
     // element e of block kb holds key key0 + 32 kb + 16 (e >> 3) + 8 h + (e & 7)
     const bool tx = t < nt_t;
@@ -316,6 +325,12 @@ __global__ __launch_bounds__(attn::Shape<WAVES>::THREADS, 1) void block_causal_a
     float psum[2] = {0.f, 0.f};
 #pragma unroll
     for (int i = 0; i < 32; ++i) {
+      // this iteration's copies, V(t) first, spread over the first 16 slots
+#pragma unroll
+      for (int j = 0; j < NLD; ++j) {
+        if (i == (16 / (2 * NLD)) * j) copy_v1(t, B, j);
+        if (i == (16 / (2 * NLD)) * (NLD + j)) copy_k1(tk, B, j);
+      }
       const bool slot = HAS_PV.value || (i & 1) == 0;
       if (i + 2 < 32 && (HAS_PV.value || ((i + 2) & 1) == 0)) fr[(i + 2) % 3] = frag(i + 2);
       if (slot) {
