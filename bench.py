@@ -203,8 +203,8 @@ def cpu_baseline(wl4, extra_workloads=(2, 3, 5)):
     """The CPU oracle's throughput on the benchmark's workload (1024^2) as
     the same 40-step loop the GPU runs (1 joint + 39 image-only steps), from
     the bounded sample of cpu_oracle_config, plus the same figures for the
-    other workloads (the 2048^2 one image-only only: its joint block would
-    materialise 35 GB of fp32 scores)."""
+    other workloads (the 2048^2 one image-only only, which keeps the whole
+    sample near half a minute of CPU time)."""
     import qi_synth as qs
     info = host_info()
     per = {}

@@ -224,17 +224,21 @@ def sdpa(q: np.ndarray, k: np.ndarray, v: np.ndarray, causal: bool, bf16: bool =
     probabilities relative to the row max are rounded to bf16 before they
     multiply v; the normalising sum uses the unrounded values."""
     d = q.shape[-1]
-    s = np.matmul(q, np.swapaxes(k, -1, -2)) / math.sqrt(d)
-    if causal:
-        Tq, Tk = s.shape[-2], s.shape[-1]
-        mask = np.triu(np.ones((Tq, Tk), dtype=bool), k=1)
-        s = np.where(mask, -np.inf, s)
-    s = s - np.max(s, axis=-1, keepdims=True)
-    p = np.exp(s)
-    l = np.sum(p, axis=-1, keepdims=True)
-    if bf16:
-        p = round_bf16(p)
-    return np.matmul(p, v) / l
+    mask = np.triu(np.ones((q.shape[1], k.shape[1]), dtype=bool), k=1) if causal else None
+    out = np.empty(q.shape[:2] + (v.shape[-1],), dtype=np.result_type(q, k, v))
+    # one head at a time (the heads are independent; this keeps one head's
+    # [Tq, Tk] scores in memory, 2.3 GB in float64 at 16896 tokens)
+    for hd in range(q.shape[0]):
+        s = np.matmul(q[hd], k[hd].T) / math.sqrt(d)
+        if causal:
+            s = np.where(mask, -np.inf, s)
+        s = s - np.max(s, axis=-1, keepdims=True)
+        p = np.exp(s)
+        l = np.sum(p, axis=-1, keepdims=True)
+        if bf16:
+            p = round_bf16(p)
+        out[hd] = np.matmul(p, v[hd]) / l
+    return out
 
 
 def block_causal_attention(q_txt, k_txt, v_txt, q_img, k_img, v_img, bf16: bool = False):
