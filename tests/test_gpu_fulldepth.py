@@ -19,8 +19,8 @@ on sampled rows.
 
 Whole-step vel against the stored oracle velocities of
 tests/golden/make_fulldepth_vel.py (exact, bf16-compute in float64 and in
-float32 accumulation) at 384^2, 1024^2 and 2048^2 (there on every fourth
-image token, the rows the stored file keeps).  Through 32 random-init blocks bf16 rounding noise is
+float32 accumulation) at 384^2 and 1024^2, and the exact one at 2048^2 (on
+every fourth image token, the rows the stored file keeps).  Through 32 random-init blocks bf16 rounding noise is
 amplified beyond the 2e-2 bar (the bf16-compute oracle itself is that far
 from the exact one), so the whole-step gate is: the GPU's distance to the
 bf16-compute oracle is within 1.5x the spread between the two bf16 orders
@@ -204,7 +204,7 @@ def _golden(name):
     if not os.path.exists(path):
         pytest.skip(f"{path} not generated (python tests/golden/make_fulldepth_vel.py)")
     z = np.load(path)
-    g = {k: z[k] for k in ("exact", "bf16_f64", "bf16_f32")}
+    g = {k: z[k] for k in ("exact", "bf16_f64", "bf16_f32") if k in z.files}
     g["rows"] = z["rows"] if "rows" in z.files else None
     return g, json.loads(str(z["meta"]))
 
@@ -220,7 +220,7 @@ def _scaled_shared(shared, s):
 
 @pytest.mark.timeout(300)
 @pytest.mark.parametrize("case", ["dit32-384px-step0", "dit32-384px-step20", "dit32-384px-step39",
-                                  "dit32-1024px-step20", "dit32-2048px-step20"])
+                                  "dit32-1024px-step20"])
 def test_whole_step_vel_against_stored_oracle(model32, case):
     g, meta = _golden(case)
     wl = qs.workload({"384px": 3, "1024px": 4, "2048px": 5}[case.split("-")[1]])
@@ -237,6 +237,25 @@ def test_whole_step_vel_against_stored_oracle(model32, case):
                  bf16_cross_order_spread=spread)
     assert rec["rel_vs_bf16"] <= 1.5 * spread, rec
     assert rec["corr_vs_exact"] >= 1.0 - 1.5 * (1.0 - rec["bf16_oracle_corr_vs_exact"]), rec
+
+
+@pytest.mark.timeout(300)
+def test_whole_step_vel_2048px_against_exact_oracle(model32):
+    """The 2048^2 step (L 512, N 16384, all 32 blocks) against the exact
+    oracle on every fourth image token.  Its stored file holds the exact mode
+    only (the bf16-compute reading is too slow on the oracle's host at this
+    size), so there is no cross-order spread to gate on; the gate is the
+    bf16-compute oracle's own full-depth distance to the exact one measured at
+    384^2 and 1024^2 (rel L2 5.3e-2 to 7.3e-2, token correlation >= 0.992),
+    with margin: rel L2 <= 0.1 and correlation >= 0.99."""
+    g, meta = _golden("dit32-2048px-step20")
+    wl = qs.workload(5)
+    assert meta["workload"] == wl.name and g["rows"] is not None
+    vel = _gpu_step(model32, wl, meta["sampler_step"])[g["rows"]]
+    rec = record("whole_step_vel", case="dit32-2048px-step20", workload=wl.name,
+                 sampler_step=meta["sampler_step"], tokens=int(len(g["rows"])),
+                 rel_vs_exact=dit.rel_l2(vel, g["exact"]), corr_vs_exact=dit.min_token_corr(vel, g["exact"]))
+    assert rec["rel_vs_exact"] <= 0.1 and rec["corr_vs_exact"] >= 0.99, rec
 
 
 @pytest.mark.timeout(300)
