@@ -105,7 +105,10 @@ def calibrate():
     v = ctypes.c_double(0)
     _lib.check(lib.qi_calib_copy_gbs(a.data_ptr(), b.data_ptr(), n, 5, ctypes.byref(v)), "qi_calib_copy_gbs")
     res["copy_gbs_read_plus_write"] = round(v.value, 1)
-    del a, b
+    scratch = torch.empty(4096 * 256, dtype=torch.int32, device="cuda")
+    _lib.check(lib.qi_calib_read_gbs(a.data_ptr(), n, scratch.data_ptr(), 5, ctypes.byref(v)), "qi_calib_read_gbs")
+    res["read_gbs"] = round(v.value, 1)
+    del a, b, scratch
     lds = {}
     for mode, name in ((0, "8_ds_read_b128"), (1, "8_ds_write_b128"), (2, "8_mfma"),
                        (3, "8_mfma_6_reads_2_ds_writes"), (4, "8_mfma_6_reads_2_lds_copies")):

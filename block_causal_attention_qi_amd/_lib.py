@@ -114,6 +114,7 @@ CALIB_PATH = os.path.join(PKG, "lib", "libqi_calib.so")
 CALIB_SIGNATURES = {
     "qi_calib_mfma_tflops": (c_int32, [c_int32, c_int32, c_void_p]),
     "qi_calib_copy_gbs": (c_int32, [c_void_p, c_void_p, c_int64, c_int32, c_void_p]),
+    "qi_calib_read_gbs": (c_int32, [c_void_p, c_int64, c_void_p, c_int32, c_void_p]),
     "qi_calib_lds_cycles": (c_int32, [c_int32, c_int32, c_void_p]),
     "qi_calib_valu_ns": (c_int32, [c_int32, c_int32, c_void_p]),
 }

@@ -46,6 +46,25 @@ __global__ __launch_bounds__(256) void copy_kernel(const u32x4 *__restrict__ a, 
   for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) b[i] = a[i];
 }
 
+// Read-only stream: each thread sums 8 independent 16-byte loads per
+// iteration of a grid-stride loop; one word per thread is written to out
+// (gridDim.x * 256 words) only if the sum is a value random data never gives.
+__global__ __launch_bounds__(256) void read_kernel(const u32x4 *__restrict__ a, int64_t n, unsigned *out) {
+  const int64_t tid = (int64_t)blockIdx.x * 256 + threadIdx.x, nt = (int64_t)gridDim.x * 256;
+  unsigned s = 0;
+  for (int64_t base = tid; base < n; base += 8 * nt) {
+    u32x4 v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int64_t i = base + u * nt;
+      v[u] = i < n ? a[i] : u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) s ^= v[u][0] ^ v[u][1] ^ v[u][2] ^ v[u][3];
+  }
+  if (s == 0x9E3779B9u) out[tid] = s;
+}
+
 // One 512-thread workgroup per CU (8 waves, two per SIMD), 128 KB of LDS;
 // each iteration every wave issues the MODE's mix (qi_calib.h), every fourth
 // iteration ends with a barrier.  Wave 0 of each workgroup adds its shader
@@ -232,10 +251,11 @@ qi_status qi_calib_mfma_tflops(int32_t shape, int32_t iters, double *tflops) {
   return rc;
 }
 
-qi_status qi_calib_copy_gbs(const void *src, void *dst, int64_t bytes, int32_t reps, double *gbs) {
-  if (!src || !dst || !gbs) return QI_ERR_NULL;
-  if (bytes < 16 || bytes % 16 != 0 || reps < 1 || reps > 1000) return QI_ERR_RANGE;
-  if (((uintptr_t)src & 15) || ((uintptr_t)dst & 15)) return QI_ERR_ALIGN;
+// Best of `reps` timed launches of one stream kernel for each grid size in
+// grids (workgroups of 256 threads); returns the best time in ms.
+}  // extern "C"
+template <class Launch>
+static qi_status best_ms(int32_t reps, const int *grids, int ngrids, Launch &&launch, float *best_out) {
   hipStream_t st;
   hipEvent_t e0, e1;
   if (hipStreamCreate(&st) != hipSuccess) return QI_ERR_HIP;
@@ -243,21 +263,52 @@ qi_status qi_calib_copy_gbs(const void *src, void *dst, int64_t bytes, int32_t r
     (void)hipStreamDestroy(st);
     return QI_ERR_HIP;
   }
-  const int64_t n = bytes / 16;
   float best = 1e30f;
   qi_status rc = QI_OK;
-  for (int r = 0; r <= reps && rc == QI_OK; ++r) {
-    (void)hipEventRecord(e0, st);
-    hipLaunchKernelGGL(copy_kernel, dim3(256 * 16), dim3(256), 0, st, (const u32x4 *)src, (u32x4 *)dst, n);
-    (void)hipEventRecord(e1, st);
-    float ms = 0.f;
-    if (hipEventSynchronize(e1) != hipSuccess || hipEventElapsedTime(&ms, e0, e1) != hipSuccess) rc = QI_ERR_HIP;
-    if (r > 0 && ms < best) best = ms;  // r == 0 is a warm-up
-  }
-  *gbs = rc == QI_OK ? 2.0 * (double)bytes / (best * 1e-3) / 1e9 : 0.0;
+  for (int gi = 0; gi < ngrids && rc == QI_OK; ++gi)
+    for (int r = 0; r <= reps && rc == QI_OK; ++r) {
+      (void)hipEventRecord(e0, st);
+      launch(grids[gi], st);
+      (void)hipEventRecord(e1, st);
+      float ms = 0.f;
+      if (hipEventSynchronize(e1) != hipSuccess || hipEventElapsedTime(&ms, e0, e1) != hipSuccess) rc = QI_ERR_HIP;
+      if (r > 0 && ms < best) best = ms;  // r == 0 is a warm-up
+    }
+  *best_out = best;
   (void)hipEventDestroy(e0);
   (void)hipEventDestroy(e1);
   (void)hipStreamDestroy(st);
+  return rc;
+}
+
+// grid sizes tried by the stream measurements: 4 to 16 workgroups per CU
+static const int kStreamGrids[] = {1024, 2048, 4096};
+
+extern "C" {
+
+qi_status qi_calib_copy_gbs(const void *src, void *dst, int64_t bytes, int32_t reps, double *gbs) {
+  if (!src || !dst || !gbs) return QI_ERR_NULL;
+  if (bytes < 16 || bytes % 16 != 0 || reps < 1 || reps > 1000) return QI_ERR_RANGE;
+  if (((uintptr_t)src & 15) || ((uintptr_t)dst & 15)) return QI_ERR_ALIGN;
+  const int64_t n = bytes / 16;
+  float best = 0.f;
+  const qi_status rc = best_ms(reps, kStreamGrids, 3, [&](int grid, hipStream_t st) {
+    hipLaunchKernelGGL(copy_kernel, dim3(grid), dim3(256), 0, st, (const u32x4 *)src, (u32x4 *)dst, n);
+  }, &best);
+  *gbs = rc == QI_OK ? 2.0 * (double)bytes / (best * 1e-3) / 1e9 : 0.0;
+  return rc;
+}
+
+qi_status qi_calib_read_gbs(const void *src, int64_t bytes, void *scratch, int32_t reps, double *gbs) {
+  if (!src || !scratch || !gbs) return QI_ERR_NULL;
+  if (bytes < 16 || bytes % 16 != 0 || reps < 1 || reps > 1000) return QI_ERR_RANGE;
+  if ((uintptr_t)src & 15) return QI_ERR_ALIGN;
+  const int64_t n = bytes / 16;
+  float best = 0.f;
+  const qi_status rc = best_ms(reps, kStreamGrids, 3, [&](int grid, hipStream_t st) {
+    hipLaunchKernelGGL(read_kernel, dim3(grid), dim3(256), 0, st, (const u32x4 *)src, n, (unsigned *)scratch);
+  }, &best);
+  *gbs = rc == QI_OK ? (double)bytes / (best * 1e-3) / 1e9 : 0.0;
   return rc;
 }
 

@@ -30,8 +30,16 @@ qi_status qi_calib_mfma_tflops(int32_t shape, int32_t iters, double *tflops);
 /* Sustained device-to-device copy bandwidth (bytes read + written per second,
  * in GB/s) over `bytes` bytes (multiple of 16) between two caller buffers src
  * and dst (device, 16-byte aligned, not overlapping), best of `reps` timed
- * copies with HIP events; BLOCKS until done.  Errors: NULL, RANGE, ALIGN, HIP. */
+ * copies with HIP events, over grid-stride launches of 1024, 2048 and 4096
+ * workgroups of 256 threads; BLOCKS until done.  Errors: NULL, RANGE, ALIGN, HIP. */
 qi_status qi_calib_copy_gbs(const void *src, void *dst, int64_t bytes, int32_t reps, double *gbs);
+
+/* Sustained read-only bandwidth (bytes read per second, GB/s) over `bytes`
+ * bytes (multiple of 16) of src (device, 16-byte aligned), same launches and
+ * timing as qi_calib_copy_gbs; scratch is a device buffer of at least
+ * 4096 * 256 * 4 bytes that the kernel may write (it never does for real
+ * data).  BLOCKS until done.  Errors: NULL, RANGE, ALIGN, HIP. */
+qi_status qi_calib_read_gbs(const void *src, int64_t bytes, void *scratch, int32_t reps, double *gbs);
 
 /* Shader cycles per iteration of a CU-wide LDS / MFMA instruction mix: one
  * workgroup of 512 threads (8 waves, two per SIMD, 128 KB of LDS) per CU, each

@@ -53,7 +53,7 @@ def test_calibration_library_is_separate():
     lib = _lib.load()
     cal = _lib.load_calib()
     decl = _declared_symbols("qi_calib.h")
-    assert len(decl) == 4
+    assert len(decl) == 5
     for name in decl:
         assert hasattr(cal, name), name
         assert name in _lib.CALIB_SIGNATURES, f"binding misses {name}"
@@ -222,6 +222,9 @@ def test_capture_block_and_component_reject_bad_arguments():
     assert c(0, 10, None) == _lib.QI_ERR_NULL
     assert cal.qi_calib_copy_gbs(FAKE, FAKE, 15, 1, ctypes.byref(out)) == _lib.QI_ERR_RANGE
     assert cal.qi_calib_copy_gbs(FAKE_MIS, FAKE, 64, 1, ctypes.byref(out)) == _lib.QI_ERR_ALIGN
+    assert cal.qi_calib_read_gbs(FAKE, 15, FAKE, 1, ctypes.byref(out)) == _lib.QI_ERR_RANGE
+    assert cal.qi_calib_read_gbs(FAKE_MIS, 64, FAKE, 1, ctypes.byref(out)) == _lib.QI_ERR_ALIGN
+    assert cal.qi_calib_read_gbs(FAKE, 64, None, 1, ctypes.byref(out)) == _lib.QI_ERR_NULL
     assert cal.qi_calib_lds_cycles(5, 100, ctypes.byref(out)) == _lib.QI_ERR_RANGE
     assert cal.qi_calib_lds_cycles(0, 3, ctypes.byref(out)) == _lib.QI_ERR_RANGE
     assert cal.qi_calib_lds_cycles(0, 100, None) == _lib.QI_ERR_NULL
