@@ -106,9 +106,10 @@ F32 = np.float32
 def round_bf16(a: np.ndarray) -> np.ndarray:
     """Round to the nearest bf16 value (ties to even), keeping a's dtype:
     the 16 high bits of the float32 representation after rounding."""
-    u = np.ascontiguousarray(a, dtype=np.float32).view(np.uint32).astype(np.uint64)
-    u = (u + 0x7FFF + ((u >> 16) & 1)) >> 16 << 16
-    return u.astype(np.uint32).view(np.float32).astype(a.dtype)
+    u = np.array(a, dtype=np.float32, copy=True, order="C").view(np.uint32)
+    u += np.uint32(0x7FFF) + ((u >> 16) & np.uint32(1))  # wraps like the 32-bit word
+    u &= np.uint32(0xFFFF0000)
+    return u.view(np.float32).astype(a.dtype, copy=False)
 
 
 # ------------------------------------------------------------------ RoPE

@@ -62,7 +62,7 @@ CASES = [
 ROW_STRIDE = {"dit32-2048px-step20": 4}
 # The 2048^2 case keeps the exact mode only: the bf16-compute reading rounds
 # every attention probability (16384 x 16896 per head, 32 heads, 32 blocks),
-# which takes the oracle more than six hours on an 8-core host.
+# which takes the oracle several hours per mode on an 8-core host.
 CASE_MODES = {"dit32-2048px-step20": ("exact",)}
 
 
